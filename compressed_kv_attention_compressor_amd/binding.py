@@ -1,0 +1,167 @@
+"""ctypes binding of libds4c.so: the same entry points as include/ds4c.h.
+
+Argument marshalling only.  Every step of the compressor runs in the HIP
+library; if the library is missing or cannot be loaded, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds4c.so")
+
+DS4C_OK = 0
+DS4C_EINVAL = -1
+DS4C_ESHAPE = -2
+DS4C_ECAP = -3
+DS4C_EPOS = -4
+DS4C_EFORMAT = -5
+DS4C_EDEVICE = -6
+DS4C_F32 = 0
+DS4C_BF16 = 1
+KCLASS_PROJ, KCLASS_POOL, KCLASS_DECODE, KCLASS_INIT = 0, 1, 2, 3
+
+# Every function the header declares, with (restype, argtypes).
+SIGNATURES = {}
+
+
+class Lane(ctypes.Structure):
+    _fields_ = [("head_dim", c_int32), ("wkv", c_void_p), ("wgate", c_void_p),
+                ("ape", c_void_p), ("norm_w", c_void_p)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("ratio", c_int32), ("hidden", c_int32), ("n_rot", c_int32), ("in_dtype", c_int32),
+                ("rope_base", c_float), ("rms_eps", c_float), ("attn", Lane), ("index", Lane)]
+
+
+class Frontier(ctypes.Structure):
+    _fields_ = [("n_tokens", c_int64), ("n_comp", c_int64), ("n_index_comp", c_int64),
+                ("state", c_void_p)]
+
+
+_LP, _FP = POINTER(Layer), POINTER(Frontier)
+SIGNATURES.update({
+    "ds4c_frontier_bytes": (c_size_t, [_LP]),
+    "ds4c_workspace_bytes": (c_size_t, [_LP, c_int64]),
+    "ds4c_frontier_blob_bytes": (c_size_t, [_LP]),
+    "ds4c_frontier_init": (c_int, [_LP, _FP, c_void_p]),
+    "ds4c_compress_prefill": (c_int, [_LP, _FP, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
+                                      c_void_p, c_size_t, c_void_p, c_void_p, c_void_p]),
+    "ds4c_compress_decode_one": (c_int, [_LP, _FP, c_void_p, c_void_p, c_int64, c_void_p, c_int64,
+                                         c_void_p, c_void_p, c_void_p]),
+    "ds4c_frontier_save": (c_int, [_LP, _FP, c_void_p, c_size_t, POINTER(c_size_t), c_void_p]),
+    "ds4c_frontier_load": (c_int, [_LP, _FP, c_void_p, c_size_t, c_void_p]),
+    "ds4c_layer_ratio": (c_int, [c_int, c_int]),
+    "ds4c_prefill_chunk_cap": (c_int64, [c_int64, c_int64]),
+    "ds4c_status_str": (ctypes.c_char_p, [c_int]),
+    "ds4c_profile_enable": (c_int, [c_int]),
+    "ds4c_profile_read": (c_int, [POINTER(c_double), POINTER(c_int64), c_int]),
+})
+
+
+class DS4CError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                               "(python -m compressed_kv_attention_compressor_amd.build)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().ds4c_status_str(status).decode()
+
+
+def _ok(status: int, what: str) -> int:
+    if status < 0:
+        raise DS4CError(status, what)
+    return status
+
+
+def ds4c_frontier_bytes(layer: Layer) -> int:
+    return lib().ds4c_frontier_bytes(ctypes.byref(layer))
+
+
+def ds4c_workspace_bytes(layer: Layer, max_tokens: int) -> int:
+    return lib().ds4c_workspace_bytes(ctypes.byref(layer), max_tokens)
+
+
+def ds4c_frontier_blob_bytes(layer: Layer) -> int:
+    return lib().ds4c_frontier_blob_bytes(ctypes.byref(layer))
+
+
+def ds4c_frontier_init(layer: Layer, frontier: Frontier, stream: int = 0) -> int:
+    return _ok(lib().ds4c_frontier_init(ctypes.byref(layer), ctypes.byref(frontier), stream),
+               "ds4c_frontier_init")
+
+
+def ds4c_compress_prefill(layer: Layer, frontier: Frontier, x: int, T: int, attn_rows: int, attn_cap: int,
+                          index_rows: int, index_cap: int, workspace: int, ws_bytes: int,
+                          attn_prequant: int = 0, index_prequant: int = 0, stream: int = 0) -> int:
+    return _ok(lib().ds4c_compress_prefill(ctypes.byref(layer), ctypes.byref(frontier), x, T, attn_rows,
+                                           attn_cap, index_rows, index_cap, workspace, ws_bytes,
+                                           attn_prequant, index_prequant, stream),
+               "ds4c_compress_prefill")
+
+
+def ds4c_compress_decode_one(layer: Layer, frontier: Frontier, x: int, attn_rows: int, attn_cap: int,
+                             index_rows: int, index_cap: int, attn_prequant: int = 0,
+                             index_prequant: int = 0, stream: int = 0) -> int:
+    return _ok(lib().ds4c_compress_decode_one(ctypes.byref(layer), ctypes.byref(frontier), x, attn_rows,
+                                              attn_cap, index_rows, index_cap, attn_prequant,
+                                              index_prequant, stream),
+               "ds4c_compress_decode_one")
+
+
+def ds4c_frontier_save(layer: Layer, frontier: Frontier, stream: int = 0) -> bytes:
+    n = ds4c_frontier_blob_bytes(layer)
+    buf = ctypes.create_string_buffer(n)
+    written = c_size_t(0)
+    _ok(lib().ds4c_frontier_save(ctypes.byref(layer), ctypes.byref(frontier), buf, n,
+                                 ctypes.byref(written), stream), "ds4c_frontier_save")
+    return buf.raw[:written.value]
+
+
+def ds4c_frontier_load(layer: Layer, frontier: Frontier, blob: bytes, stream: int = 0) -> int:
+    buf = ctypes.create_string_buffer(bytes(blob), len(blob))
+    return _ok(lib().ds4c_frontier_load(ctypes.byref(layer), ctypes.byref(frontier), buf, len(blob), stream),
+               "ds4c_frontier_load")
+
+
+def ds4c_layer_ratio(variant: int, layer: int) -> int:
+    return lib().ds4c_layer_ratio(variant, layer)
+
+
+def ds4c_prefill_chunk_cap(prompt_len: int, override_cap: int = 0) -> int:
+    return lib().ds4c_prefill_chunk_cap(prompt_len, override_cap)
+
+
+def ds4c_profile_enable(on: bool) -> None:
+    _ok(lib().ds4c_profile_enable(1 if on else 0), "ds4c_profile_enable")
+
+
+def ds4c_profile_read():
+    """(ms[4], count[4]) accumulated per kernel class since the last read."""
+    ms = (c_double * 4)()
+    cnt = (c_int64 * 4)()
+    _ok(lib().ds4c_profile_read(ms, cnt, 4), "ds4c_profile_read")
+    return list(ms), list(cnt)

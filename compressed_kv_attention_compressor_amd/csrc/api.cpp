@@ -1,0 +1,572 @@
+// C-ABI entry points of the compressor library: argument validation, launch
+// plans, frontier counters, frontier save/load and optional kernel timing.
+// Every check runs before anything is enqueued; nothing here touches the
+// HIP runtime until the arguments have been accepted.
+#include "ds4c.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "kernel_args.h"
+#include "launch.h"
+
+namespace {
+
+using ds4c::DecodeArgs;
+using ds4c::FillArgs;
+using ds4c::LaneDev;
+using ds4c::PoolArgs;
+using ds4c::ProjArgs;
+
+constexpr size_t kCtrlBytes = 256;
+constexpr int64_t kMaxTokensPerCall = int64_t(1) << 22;
+constexpr uint32_t kBlobMagic = 0x46345344u;  // "DS4F" little-endian
+constexpr uint32_t kBlobVersion = 1;
+constexpr size_t kBlobHeader = 8 * 4 + 3 * 8;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+struct Shape {
+  int ratio = 0, coff = 0, n_lanes = 0;
+  int D[2] = {0, 0}, W[2] = {0, 0};
+  int N = 0;  // projection columns
+  size_t fr_tensor_bytes[2] = {0, 0};
+};
+
+int check_lane(const ds4c_lane& l, const ds4c_layer& L, bool attn) {
+  if (!pow2_in(l.head_dim, 64, 512)) return DS4C_ESHAPE;
+  if (L.n_rot > l.head_dim) return DS4C_ESHAPE;
+  if (attn && (l.head_dim - L.n_rot) % 64 != 0) return DS4C_ESHAPE;
+  if (!l.wkv || !l.wgate || !l.ape || !l.norm_w) return DS4C_EINVAL;
+  if (!aligned(l.wkv, 16) || !aligned(l.wgate, 16) || !aligned(l.ape, 16) || !aligned(l.norm_w, 16))
+    return DS4C_EINVAL;
+  return DS4C_OK;
+}
+
+int check_layer(const ds4c_layer* L, Shape* s) {
+  if (!L) return DS4C_EINVAL;
+  if (L->ratio != 4 && L->ratio != 128) return DS4C_EINVAL;
+  if (L->in_dtype != DS4C_F32 && L->in_dtype != DS4C_BF16) return DS4C_EINVAL;
+  if (!(std::isfinite(L->rope_base) && L->rope_base > 0.f)) return DS4C_EINVAL;
+  if (!(std::isfinite(L->rms_eps) && L->rms_eps >= 0.f)) return DS4C_EINVAL;
+  if (L->hidden <= 0 || L->hidden % 64 != 0 || L->hidden > 65536) return DS4C_ESHAPE;
+  if (L->n_rot <= 0 || L->n_rot % 2 != 0) return DS4C_ESHAPE;
+  int st = check_lane(L->attn, *L, true);
+  if (st) return st;
+  const ds4c_lane& ix = L->index;
+  if (L->ratio == 4) {
+    st = check_lane(ix, *L, false);
+    if (st) return st;
+  } else if (ix.head_dim != 0 || ix.wkv || ix.wgate || ix.ape || ix.norm_w) {
+    return DS4C_EINVAL;
+  }
+  s->ratio = L->ratio;
+  s->coff = L->ratio == 4 ? 2 : 1;
+  s->n_lanes = L->ratio == 4 ? 2 : 1;
+  s->N = 0;
+  for (int l = 0; l < s->n_lanes; ++l) {
+    s->D[l] = l == 0 ? L->attn.head_dim : ix.head_dim;
+    s->W[l] = s->coff * s->D[l];
+    s->N += 2 * s->W[l];
+    s->fr_tensor_bytes[l] = size_t(s->coff) * L->ratio * s->W[l] * sizeof(float);
+  }
+  return DS4C_OK;
+}
+
+size_t frontier_bytes(const Shape& s) {
+  size_t b = kCtrlBytes;
+  for (int l = 0; l < s.n_lanes; ++l) b += 2 * s.fr_tensor_bytes[l];
+  return b;
+}
+
+size_t blob_bytes(const Shape& s) { return kBlobHeader + frontier_bytes(s) - kCtrlBytes; }
+
+// Device addresses of a lane's frontier tensors inside `state`.
+void frontier_ptrs(const Shape& s, void* state, int lane, float** kv, float** sc) {
+  char* p = static_cast<char*>(state) + kCtrlBytes;
+  for (int l = 0; l < lane; ++l) p += 2 * s.fr_tensor_bytes[l];
+  *kv = reinterpret_cast<float*>(p);
+  *sc = reinterpret_cast<float*>(p + s.fr_tensor_bytes[lane]);
+}
+
+struct WsLayout {
+  size_t proj = 0, obuf = 0, tickets = 0, total = 0;
+  int64_t max_rows = 0;
+};
+
+WsLayout workspace_layout(const Shape& s, int64_t T) {
+  WsLayout w;
+  w.proj = 0;
+  size_t off = align256(size_t(T) * s.N * sizeof(float));
+  if (s.ratio == 128) {
+    w.max_rows = T / 128 + 1;
+    w.obuf = off;
+    off += align256(size_t(w.max_rows) * s.D[0] * sizeof(float));
+    w.tickets = off;
+    off += align256(size_t(w.max_rows) * sizeof(unsigned));
+  }
+  w.total = off;
+  return w;
+}
+
+int check_frontier(const Shape& s, const ds4c_frontier* f) {
+  if (!f || !f->state || !aligned(f->state, 256)) return DS4C_EINVAL;
+  if (f->n_tokens < 0) return DS4C_EPOS;
+  if (f->n_comp != f->n_tokens / s.ratio) return DS4C_EPOS;
+  if (f->n_index_comp != (s.ratio == 4 ? f->n_tokens / 4 : 0)) return DS4C_EPOS;
+  return DS4C_OK;
+}
+
+int check_rows(const Shape& s, int64_t k_hi, int64_t n_emit, float* attn_rows, int64_t attn_cap,
+               float* index_rows, int64_t index_cap, float* attn_pre, float* index_pre) {
+  if (attn_cap < 0 || index_cap < 0) return DS4C_EINVAL;
+  if (s.ratio == 128 && (index_rows || index_cap || index_pre)) return DS4C_EINVAL;
+  if (!aligned(attn_rows, 16) || !aligned(index_rows, 16) || !aligned(attn_pre, 16) ||
+      !aligned(index_pre, 16))
+    return DS4C_EINVAL;
+  if (n_emit > 0) {
+    if (!attn_rows) return DS4C_EINVAL;
+    if (k_hi > attn_cap) return DS4C_ECAP;
+    if (s.ratio == 4) {
+      if (!index_rows) return DS4C_EINVAL;
+      if (k_hi > index_cap) return DS4C_ECAP;
+    }
+  }
+  return DS4C_OK;
+}
+
+LaneDev lane_dev(const Shape& s, const ds4c_layer& L, void* state, int l, float* rows, float* pre) {
+  const ds4c_lane& src = l == 0 ? L.attn : L.index;
+  LaneDev d{};
+  d.ape = src.ape;
+  d.norm_w = src.norm_w;
+  d.rows = rows;
+  d.prequant = pre;
+  frontier_ptrs(s, state, l, &d.fr_kv, &d.fr_sc);
+  d.D = s.D[l];
+  d.W = s.W[l];
+  d.kv_col = l == 0 ? 0 : 2 * s.W[0];
+  d.sc_col = d.kv_col + s.W[l];
+  d.is_index = l;
+  return d;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel timing with HIP events.
+// ---------------------------------------------------------------------------
+struct ProfRec {
+  int cls;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void release_records() {
+  for (auto& r : g_prof) {
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  g_prof.clear();
+}
+
+template <class F>
+hipError_t timed(int cls, hipStream_t s, F&& launch) {
+  std::unique_lock<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) {
+    lk.unlock();
+    return launch();
+  }
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  if (e != hipSuccess) return e;
+  g_prof.push_back({cls, a, b});
+  return hipSuccess;
+}
+
+int dev_status(hipError_t e) { return e == hipSuccess ? DS4C_OK : DS4C_EDEVICE; }
+
+void fill_proj_segments(const ds4c_layer& L, const Shape& s, ds4c::ProjSeg* seg, int* n_seg) {
+  int n = 0, col = 0;
+  for (int l = 0; l < s.n_lanes; ++l) {
+    const ds4c_lane& src = l == 0 ? L.attn : L.index;
+    seg[n++] = {src.wkv, col, s.W[l]};
+    col += s.W[l];
+    seg[n++] = {src.wgate, col, s.W[l]};
+    col += s.W[l];
+  }
+  *n_seg = n;
+}
+
+// Live frontier rows after n tokens (rows the recurrence will read again):
+// ratio 4 keeps rows 0..3 once a window has been emitted and rows 4..3+c;
+// ratio 128 keeps rows 0..c-1, with c = n % ratio.
+bool row_live(int ratio, int64_t n, int row) {
+  const int64_t c = n % ratio, m = n - c;
+  if (ratio == 4) return row < 4 ? m >= 4 : row - 4 < c;
+  return row < c;
+}
+
+void put_u32(unsigned char* p, uint32_t v) { std::memcpy(p, &v, 4); }
+void put_u64(unsigned char* p, uint64_t v) { std::memcpy(p, &v, 8); }
+uint32_t get_u32(const unsigned char* p) { uint32_t v; std::memcpy(&v, p, 4); return v; }
+uint64_t get_u64(const unsigned char* p) { uint64_t v; std::memcpy(&v, p, 8); return v; }
+
+}  // namespace
+
+extern "C" {
+
+size_t ds4c_frontier_bytes(const ds4c_layer* layer) {
+  Shape s;
+  return check_layer(layer, &s) ? 0 : frontier_bytes(s);
+}
+
+size_t ds4c_workspace_bytes(const ds4c_layer* layer, int64_t max_tokens) {
+  Shape s;
+  if (check_layer(layer, &s) || max_tokens < 0 || max_tokens > kMaxTokensPerCall) return 0;
+  return workspace_layout(s, max_tokens).total;
+}
+
+size_t ds4c_frontier_blob_bytes(const ds4c_layer* layer) {
+  Shape s;
+  return check_layer(layer, &s) ? 0 : blob_bytes(s);
+}
+
+int ds4c_frontier_init(const ds4c_layer* layer, ds4c_frontier* frontier, void* stream) {
+  try {
+    Shape s;
+    int st = check_layer(layer, &s);
+    if (st) return st;
+    if (!frontier || !frontier->state || !aligned(frontier->state, 256)) return DS4C_EINVAL;
+    FillArgs f{};
+    f.n_lanes = s.n_lanes;
+    for (int l = 0; l < s.n_lanes; ++l) {
+      frontier_ptrs(s, frontier->state, l, &f.kv[l], &f.sc[l]);
+      f.n[l] = int64_t(s.fr_tensor_bytes[l] / sizeof(float));
+    }
+    f.ctrl = static_cast<unsigned*>(frontier->state);
+    f.n_ctrl = int(kCtrlBytes / sizeof(unsigned));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    st = dev_status(timed(DS4C_KCLASS_INIT, hs, [&] { return ds4c::launch_fill(f, hs); }));
+    if (st) return st;
+    frontier->n_tokens = frontier->n_comp = frontier->n_index_comp = 0;
+    return DS4C_OK;
+  } catch (...) {
+    return DS4C_EDEVICE;
+  }
+}
+
+int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, const void* x, int64_t T,
+                          float* attn_rows, int64_t attn_cap, float* index_rows, int64_t index_cap,
+                          void* workspace, size_t ws_bytes, float* attn_prequant, float* index_prequant,
+                          void* stream) {
+  try {
+    Shape s;
+    int st = check_layer(layer, &s);
+    if (st) return st;
+    st = check_frontier(s, frontier);
+    if (st) return st;
+    if (T < 0) return DS4C_EINVAL;
+    if (T > kMaxTokensPerCall) return DS4C_ESHAPE;
+    const int r = s.ratio;
+    const int64_t n0 = frontier->n_tokens, n = n0 + T;
+    const int64_t k_lo = n0 / r, k_hi = n / r, n_emit = k_hi - k_lo;
+    st = check_rows(s, k_hi, n_emit, attn_rows, attn_cap, index_rows, index_cap, attn_prequant,
+                    index_prequant);
+    if (st) return st;
+    if (T == 0) return DS4C_OK;
+    if (!x || !aligned(x, 16)) return DS4C_EINVAL;
+    const WsLayout wl = workspace_layout(s, T);
+    if (!workspace || !aligned(workspace, 256)) return DS4C_EINVAL;
+    if (ws_bytes < wl.total) return DS4C_ECAP;
+
+    char* ws = static_cast<char*>(workspace);
+    ProjArgs pa{};
+    pa.x = x;
+    pa.out = reinterpret_cast<float*>(ws + wl.proj);
+    pa.M = T;
+    pa.K = layer->hidden;
+    pa.N = s.N;
+    fill_proj_segments(*layer, s, pa.seg, &pa.n_seg);
+    if (r == 128) {
+      pa.zero_ptr = reinterpret_cast<unsigned*>(ws + wl.tickets);
+      pa.n_zero = int(n_emit);
+    }
+
+    PoolArgs po{};
+    po.proj = pa.out;
+    po.ld = s.N;
+    po.n0 = n0;
+    po.T = T;
+    po.k_lo = k_lo;
+    po.k_hi = k_hi;
+    if (r == 4) {
+      const int64_t c0 = n0 % 4;
+      const int64_t head = (n0 > 0 ? 1 : 0) + (c0 > 0 ? 1 : 0);
+      po.n_head = int(head < n_emit ? head : n_emit);
+    } else {
+      po.n_head = (n0 % 128 != 0 && n_emit > 0) ? 1 : 0;
+    }
+    po.ratio = r;
+    po.n_rot = layer->n_rot;
+    po.n_lanes = s.n_lanes;
+    po.rope_base = layer->rope_base;
+    po.rms_eps = layer->rms_eps;
+    po.lane[0] = lane_dev(s, *layer, frontier->state, 0, attn_rows, attn_prequant);
+    if (s.n_lanes > 1) po.lane[1] = lane_dev(s, *layer, frontier->state, 1, index_rows, index_prequant);
+    if (r == 128) {
+      po.o_buf = reinterpret_cast<float*>(ws + wl.obuf);
+      po.tickets = reinterpret_cast<unsigned*>(ws + wl.tickets);
+    }
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    st = dev_status(timed(DS4C_KCLASS_PROJ, hs, [&] { return ds4c::launch_proj(pa, layer->in_dtype, hs); }));
+    if (st) return st;
+    st = dev_status(timed(DS4C_KCLASS_POOL, hs, [&] { return ds4c::launch_pool(po, hs); }));
+    if (st) return st;
+    frontier->n_tokens = n;
+    frontier->n_comp = k_hi;
+    frontier->n_index_comp = r == 4 ? k_hi : 0;
+    return DS4C_OK;
+  } catch (...) {
+    return DS4C_EDEVICE;
+  }
+}
+
+int ds4c_compress_decode_one(const ds4c_layer* layer, ds4c_frontier* frontier, const void* x,
+                             float* attn_rows, int64_t attn_cap, float* index_rows, int64_t index_cap,
+                             float* attn_prequant, float* index_prequant, void* stream) {
+  try {
+    Shape s;
+    int st = check_layer(layer, &s);
+    if (st) return st;
+    st = check_frontier(s, frontier);
+    if (st) return st;
+    const int r = s.ratio;
+    const int64_t pos = frontier->n_tokens;
+    const int64_t k_hi = (pos + 1) / r, n_emit = k_hi - pos / r;
+    st = check_rows(s, k_hi, n_emit, attn_rows, attn_cap, index_rows, index_cap, attn_prequant,
+                    index_prequant);
+    if (st) return st;
+    if (!x || !aligned(x, 16)) return DS4C_EINVAL;
+
+    DecodeArgs d{};
+    d.x = x;
+    d.K = layer->hidden;
+    d.N = s.N;
+    fill_proj_segments(*layer, s, d.seg, &d.n_seg);
+    for (int i = 0; i < d.n_seg; ++i) {
+      d.seg_lane[i] = i / 2;
+      d.seg_score[i] = i % 2;
+    }
+    d.pos = pos;
+    d.ratio = r;
+    d.n_rot = layer->n_rot;
+    d.n_lanes = s.n_lanes;
+    d.rope_base = layer->rope_base;
+    d.rms_eps = layer->rms_eps;
+    d.lane[0] = lane_dev(s, *layer, frontier->state, 0, attn_rows, attn_prequant);
+    if (s.n_lanes > 1) d.lane[1] = lane_dev(s, *layer, frontier->state, 1, index_rows, index_prequant);
+    d.ticket = static_cast<unsigned*>(frontier->state);
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    st = dev_status(timed(DS4C_KCLASS_DECODE, hs, [&] { return ds4c::launch_decode(d, layer->in_dtype, hs); }));
+    if (st) return st;
+    frontier->n_tokens = pos + 1;
+    frontier->n_comp = k_hi;
+    frontier->n_index_comp = r == 4 ? k_hi : 0;
+    return DS4C_OK;
+  } catch (...) {
+    return DS4C_EDEVICE;
+  }
+}
+
+int ds4c_frontier_save(const ds4c_layer* layer, const ds4c_frontier* frontier, void* host_buf,
+                       size_t cap, size_t* written, void* stream) {
+  try {
+    Shape s;
+    int st = check_layer(layer, &s);
+    if (st) return st;
+    st = check_frontier(s, frontier);
+    if (st) return st;
+    if (!host_buf) return DS4C_EINVAL;
+    const size_t need = blob_bytes(s);
+    if (cap < need) return DS4C_ECAP;
+    unsigned char* out = static_cast<unsigned char*>(host_buf);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    size_t off = kBlobHeader;
+    for (int l = 0; l < s.n_lanes; ++l) {
+      float *kv, *sc;
+      frontier_ptrs(s, frontier->state, l, &kv, &sc);
+      if (hipMemcpyAsync(out + off, kv, s.fr_tensor_bytes[l], hipMemcpyDeviceToHost, hs) != hipSuccess)
+        return DS4C_EDEVICE;
+      off += s.fr_tensor_bytes[l];
+      if (hipMemcpyAsync(out + off, sc, s.fr_tensor_bytes[l], hipMemcpyDeviceToHost, hs) != hipSuccess)
+        return DS4C_EDEVICE;
+      off += s.fr_tensor_bytes[l];
+    }
+    if (hipStreamSynchronize(hs) != hipSuccess) return DS4C_EDEVICE;
+    // Canonical form of rows the recurrence never reads again.
+    off = kBlobHeader;
+    const int rows = s.coff * s.ratio;
+    for (int l = 0; l < s.n_lanes; ++l) {
+      float* kv = reinterpret_cast<float*>(out + off);
+      float* sc = reinterpret_cast<float*>(out + off + s.fr_tensor_bytes[l]);
+      for (int row = 0; row < rows; ++row) {
+        if (row_live(s.ratio, frontier->n_tokens, row)) continue;
+        for (int c = 0; c < s.W[l]; ++c) {
+          kv[size_t(row) * s.W[l] + c] = 0.f;
+          sc[size_t(row) * s.W[l] + c] = -INFINITY;
+        }
+      }
+      off += 2 * s.fr_tensor_bytes[l];
+    }
+    put_u32(out + 0, kBlobMagic);
+    put_u32(out + 4, kBlobVersion);
+    put_u32(out + 8, uint32_t(s.ratio));
+    put_u32(out + 12, uint32_t(s.coff));
+    put_u32(out + 16, uint32_t(s.D[0]));
+    put_u32(out + 20, uint32_t(s.n_lanes > 1 ? s.D[1] : 0));
+    put_u32(out + 24, uint32_t(layer->n_rot));
+    put_u32(out + 28, 0u);
+    put_u64(out + 32, uint64_t(frontier->n_tokens));
+    put_u64(out + 40, uint64_t(frontier->n_comp));
+    put_u64(out + 48, uint64_t(frontier->n_index_comp));
+    if (written) *written = need;
+    return DS4C_OK;
+  } catch (...) {
+    return DS4C_EDEVICE;
+  }
+}
+
+int ds4c_frontier_load(const ds4c_layer* layer, ds4c_frontier* frontier, const void* host_buf, size_t len,
+                       void* stream) {
+  try {
+    Shape s;
+    int st = check_layer(layer, &s);
+    if (st) return st;
+    if (!frontier || !frontier->state || !aligned(frontier->state, 256) || !host_buf) return DS4C_EINVAL;
+    const unsigned char* in = static_cast<const unsigned char*>(host_buf);
+    if (len != blob_bytes(s)) return DS4C_EFORMAT;
+    if (get_u32(in + 0) != kBlobMagic || get_u32(in + 4) != kBlobVersion) return DS4C_EFORMAT;
+    if (get_u32(in + 8) != uint32_t(s.ratio) || get_u32(in + 12) != uint32_t(s.coff) ||
+        get_u32(in + 16) != uint32_t(s.D[0]) ||
+        get_u32(in + 20) != uint32_t(s.n_lanes > 1 ? s.D[1] : 0) ||
+        get_u32(in + 24) != uint32_t(layer->n_rot) || get_u32(in + 28) != 0u)
+      return DS4C_EFORMAT;
+    const uint64_t nt = get_u64(in + 32), nc = get_u64(in + 40), ni = get_u64(in + 48);
+    if (nt > uint64_t(INT64_MAX) || nc != nt / uint64_t(s.ratio) || ni != (s.ratio == 4 ? nt / 4 : 0))
+      return DS4C_EFORMAT;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    size_t off = kBlobHeader;
+    for (int l = 0; l < s.n_lanes; ++l) {
+      float *kv, *sc;
+      frontier_ptrs(s, frontier->state, l, &kv, &sc);
+      if (hipMemcpyAsync(kv, in + off, s.fr_tensor_bytes[l], hipMemcpyHostToDevice, hs) != hipSuccess)
+        return DS4C_EDEVICE;
+      off += s.fr_tensor_bytes[l];
+      if (hipMemcpyAsync(sc, in + off, s.fr_tensor_bytes[l], hipMemcpyHostToDevice, hs) != hipSuccess)
+        return DS4C_EDEVICE;
+      off += s.fr_tensor_bytes[l];
+    }
+    if (hipStreamSynchronize(hs) != hipSuccess) return DS4C_EDEVICE;
+    frontier->n_tokens = int64_t(nt);
+    frontier->n_comp = int64_t(nc);
+    frontier->n_index_comp = int64_t(ni);
+    return DS4C_OK;
+  } catch (...) {
+    return DS4C_EDEVICE;
+  }
+}
+
+int ds4c_layer_ratio(int variant, int layer) {
+  if ((variant != 0 && variant != 1) || layer < 0) return -1;
+  if (layer < 2) return variant == 0 ? 0 : 128;
+  return layer % 2 == 0 ? 4 : 128;
+}
+
+int64_t ds4c_prefill_chunk_cap(int64_t prompt_len, int64_t override_cap) {
+  if (override_cap > 0) return override_cap;
+  if (prompt_len > 4096) return 4096;
+  return prompt_len > 1 ? prompt_len : 1;
+}
+
+const char* ds4c_status_str(int status) {
+  switch (status) {
+    case DS4C_OK: return "ok";
+    case DS4C_EINVAL: return "invalid argument";
+    case DS4C_ESHAPE: return "unsupported shape";
+    case DS4C_ECAP: return "buffer too small";
+    case DS4C_EPOS: return "inconsistent frontier counters";
+    case DS4C_EFORMAT: return "bad frontier blob";
+    case DS4C_EDEVICE: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int ds4c_profile_enable(int on) {
+  try {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    release_records();
+    g_prof_on = on != 0;
+    return DS4C_OK;
+  } catch (...) {
+    return DS4C_EDEVICE;
+  }
+}
+
+int ds4c_profile_read(double* ms, int64_t* count, int n) {
+  try {
+    if (!ms || !count || n < 0 || n > 4) return DS4C_EINVAL;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (int i = 0; i < n; ++i) {
+      ms[i] = 0.0;
+      count[i] = 0;
+    }
+    int st = DS4C_OK;
+    for (auto& r : g_prof) {
+      if (hipEventSynchronize(r.b) != hipSuccess) {
+        st = DS4C_EDEVICE;
+        continue;
+      }
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) {
+        st = DS4C_EDEVICE;
+        continue;
+      }
+      if (r.cls < n) {
+        ms[r.cls] += t;
+        count[r.cls] += 1;
+      }
+    }
+    release_records();
+    return st;
+  } catch (...) {
+    return DS4C_EDEVICE;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,215 @@
+// Device helpers shared by the compressor kernels (gfx950, wave64).
+//
+// The row epilogue (RMS norm, tail RoPE, FP8 or Hadamard+FP4 round trip)
+// runs on one wavefront holding one D-wide row, DPL = D/64 consecutive dims
+// per lane.  Reductions over the row or over a codec block are xor-butterfly
+// shuffles, so every lane ends with bitwise the same value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernel_args.h"
+
+namespace ds4c {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Maximum over aligned groups of G lanes (G a power of two <= 64).
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Block scales and element rounding (Part 3 §9 names E4M3 and FP4; the
+// formats are the OCP E4M3 "fn" and E2M1 element types).
+//
+// A block is scaled by 2^k with the smallest integer k for which its largest
+// magnitude fits the format's largest finite value, so nothing saturates.
+// frexpf gives amax = f * 2^e with f in [0.5, 1); the largest finite value
+// is 448 = 0.875 * 2^9 for E4M3 and 6 = 0.75 * 2^3 for E2M1.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int e4m3_block_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int e;
+  float f = frexpf(amax, &e);
+  return f <= 0.875f ? e - 9 : e - 8;
+}
+
+__device__ __forceinline__ int e2m1_block_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int e;
+  float f = frexpf(amax, &e);
+  return f <= 0.75f ? e - 3 : e - 2;
+}
+
+// Nearest value of a (sign, exponent, mantissa) grid, ties to even, for
+// |v| within the grid's finite range.  Between 2^E and 2^(E+1) the grid step
+// is 2^(E - mbits); below the smallest normal 2^emin the step is
+// 2^(emin - mbits).  Scaling by the step is exact, rintf rounds half to even
+// (even integer == even mantissa), and scaling back is exact.
+template <int MBITS, int EMIN>
+__device__ __forceinline__ float round_to_grid(float v) {
+  float a = fabsf(v);
+  int e;
+  frexpf(a, &e);  // a in [2^(e-1), 2^e)
+  int q = max(e - 1, EMIN) - MBITS;
+  float r = rintf(ldexpf(a, -q));
+  return copysignf(ldexpf(r, q), v);
+}
+
+__device__ __forceinline__ float rne_e4m3(float v) { return round_to_grid<3, -6>(v); }
+__device__ __forceinline__ float rne_e2m1(float v) { return round_to_grid<1, 0>(v); }
+
+// Vector load/store of DPL consecutive floats (DPL in {1, 2, 4, 8}); the
+// address is DPL*4-byte aligned (16-byte for DPL >= 4).
+template <int DPL>
+__device__ __forceinline__ void load_vec(float (&v)[DPL], const float* __restrict__ p) {
+  if constexpr (DPL == 1) {
+    v[0] = p[0];
+  } else if constexpr (DPL == 2) {
+    float2 t = *reinterpret_cast<const float2*>(p);
+    v[0] = t.x; v[1] = t.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < DPL; i += 4) {
+      float4 t = *reinterpret_cast<const float4*>(p + i);
+      v[i] = t.x; v[i + 1] = t.y; v[i + 2] = t.z; v[i + 3] = t.w;
+    }
+  }
+}
+
+template <int DPL>
+__device__ __forceinline__ void store_vec(float* __restrict__ p, const float (&v)[DPL]) {
+  if constexpr (DPL == 1) {
+    p[0] = v[0];
+  } else if constexpr (DPL == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < DPL; i += 4)
+      *reinterpret_cast<float4*>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row epilogue for one wave.  y[DPL] holds the pooled row's dims
+// lane*DPL .. lane*DPL+DPL-1 on entry.  Writes the final row (and the
+// pre-codec row if requested).
+// ---------------------------------------------------------------------------
+template <int DPL>
+__device__ __forceinline__ void finish_row_wave(float (&y)[DPL], const LaneDev& L, int n_rot,
+                                                float rope_base, float rms_eps, int64_t k,
+                                                int ratio, float* __restrict__ prequant_row,
+                                                float* __restrict__ out_row, int lane) {
+  const int D = DPL * kWave;
+  const int d0 = lane * DPL;
+
+  // RMS norm over the whole row: y = o * w / sqrt(mean(o^2) + eps).
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) ss = fmaf(y[i], y[i], ss);
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)D + rms_eps);
+  float w[DPL];
+  load_vec<DPL>(w, L.norm_w + d0);
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) y[i] = y[i] * w[i] * inv;
+
+  // Tail RoPE (Part 3 §8): the last n_rot dims, adjacent pairs (2i, 2i+1),
+  // angle = (k * ratio) * base^(-2i/n_rot), formed and evaluated in fp64.
+  const int n_nope = D - n_rot;
+  const double pos = (double)k * (double)ratio;
+  if constexpr (DPL >= 2) {
+    if (d0 >= n_nope) {
+#pragma unroll
+      for (int i = 0; i < DPL; i += 2) {
+        const int pi = (d0 + i - n_nope) >> 1;
+        const double ang = pos * pow((double)rope_base, -2.0 * (double)pi / (double)n_rot);
+        double s, c;
+        sincos(ang, &s, &c);
+        const float cf = (float)c, sf = (float)s;
+        const float a = y[i], b = y[i + 1];
+        y[i] = a * cf - b * sf;
+        y[i + 1] = a * sf + b * cf;
+      }
+    }
+  } else {
+    // One dim per lane: the pair partner is the neighbouring lane.
+    const float other = __shfl_xor(y[0], 1, kWave);
+    if (d0 >= n_nope) {
+      const int pi = (d0 - n_nope) >> 1;
+      const double ang = pos * pow((double)rope_base, -2.0 * (double)pi / (double)n_rot);
+      double s, c;
+      sincos(ang, &s, &c);
+      const float cf = (float)c, sf = (float)s;
+      if ((lane & 1) == 0)
+        y[0] = y[0] * cf - other * sf;  // a' = a cos - b sin
+      else
+        y[0] = other * sf + y[0] * cf;  // b' = a sin + b cos
+    }
+  }
+
+  if (prequant_row) store_vec<DPL>(prequant_row + d0, y);
+
+  if (!L.is_index) {
+    // FP8 E4M3 round trip on dims [0, n_nope) in blocks of 64 (64/DPL lanes).
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) amax = fmaxf(amax, fabsf(y[i]));
+    amax = group_max<kWave / DPL>(amax);
+    if (d0 < n_nope) {
+      const int kexp = e4m3_block_exp(amax);
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) y[i] = ldexpf(rne_e4m3(ldexpf(y[i], -kexp)), kexp);
+    }
+  } else {
+    // Orthonormal Walsh-Hadamard rotation (Sylvester order) of the whole row:
+    // butterflies (a, b) -> (a + b, a - b) on index pairs (j, j + h) for
+    // h = 1, 2, 4, ...; strides below DPL inside a lane, the rest across lanes.
+#pragma unroll
+    for (int h = 1; h < DPL; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        if ((i & h) == 0) {
+          const float a = y[i], b = y[i + h];
+          y[i] = a + b;
+          y[i + h] = a - b;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      const bool low = (lane & m) == 0;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        const float p = __shfl_xor(y[i], m, kWave);
+        y[i] = low ? (y[i] + p) : (p - y[i]);
+      }
+    }
+    const float scale = (float)(1.0 / sqrt((double)D));
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) y[i] *= scale;
+    // FP4 E2M1 round trip in blocks of 32 dims (32/DPL lanes).
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) amax = fmaxf(amax, fabsf(y[i]));
+    amax = group_max<32 / DPL>(amax);
+    const int kexp = e2m1_block_exp(amax);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) y[i] = ldexpf(rne_e2m1(ldexpf(y[i], -kexp)), kexp);
+  }
+
+  store_vec<DPL>(out_row + d0, y);
+}
+
+}  // namespace ds4c

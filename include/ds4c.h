@@ -1,0 +1,204 @@
+/*
+ * ds4c — the compressed-KV compressor of the ds4 (DwarfStar) DeepSeek-V4
+ * engine, as a C-ABI library for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of what is computed: Yoshiya Kato's Qiita series on ds4, "Part 3"
+ * (Metal グラフと圧縮 KV の実装を読む: compressor、indexer、HC、tail-only
+ * RoPE) and "Part 4" (KV キャッシュをディスクの一級市民にする: DwarfStar の
+ * KVC と DSV4 ペイロードを読む).  Section numbers below refer to those pages.
+ *
+ * Per layer and per lane, each token is projected by wkv (kv candidates)
+ * and wgate (scores); the learned position bias APE[pos % ratio] is added to
+ * the scores; kv and scores go into a small recurrent state (the
+ * "frontier"); when a ratio window closes, every output dim is the softmax
+ * (over the window's entries) weighted mean of its kv entries; the pooled
+ * row is RMS-normalised, its last n_rot dims are rotated (tail RoPE with
+ * the compression base), and it goes through the FP8 E4M3 round trip
+ * (attention lane, non-RoPE dims) or the Hadamard + FP4 E2M1 round trip
+ * (indexer lane).  Part 3 §4, §5, §8, §9.
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers unless the name starts with host_.
+ *   - All device buffers are owned by the caller.  prefill and decode_one
+ *     never allocate device memory.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  prefill,
+ *     decode_one and frontier_init only enqueue work and return; the
+ *     frontier's host counters are updated at enqueue (they depend only on
+ *     token counts).  save and load synchronise `stream`.
+ *   - Every argument is validated on the host before anything is enqueued.
+ *     On failure the call returns a negative ds4c_status, enqueues nothing,
+ *     writes nothing and leaves the frontier unchanged.
+ *   - One frontier must not be used by two calls at once; different
+ *     frontiers may be used from different threads.
+ *   - Little-endian hosts only (the frontier blob is little-endian).
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef DS4C_H
+#define DS4C_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ds4c_status {
+  DS4C_OK = 0,
+  DS4C_EINVAL = -1,  /* null or misaligned pointer, bad ratio/dtype, missing or extra lane */
+  DS4C_ESHAPE = -2,  /* a dimension the kernels do not support (see ds4c_layer) */
+  DS4C_ECAP = -3,    /* row buffer, workspace or host buffer too small */
+  DS4C_EPOS = -4,    /* frontier counters inconsistent with each other */
+  DS4C_EFORMAT = -5, /* frontier blob: bad magic, version, shape or length */
+  DS4C_EDEVICE = -6  /* a HIP runtime call failed */
+} ds4c_status;
+
+typedef enum ds4c_dtype { DS4C_F32 = 0, DS4C_BF16 = 1 } ds4c_dtype;
+
+/* One compressor lane (Part 3 §6 names the per-lane tensors: *_compressor_kv,
+ * *_compressor_gate, *_compressor_ape, *_compressor_norm).
+ * coff = 2 on ratio-4 layers, 1 on ratio-128 layers (Part 3 §5); W = coff*head_dim. */
+typedef struct ds4c_lane {
+  int32_t head_dim;     /* D: a power of two, 64 <= D <= 512 (one row per 64-lane wavefront).
+                           attention lane: (D - n_rot) % 64 == 0 (whole FP8 blocks). */
+  const void *wkv;      /* [W, hidden] row-major, layer in_dtype, 16-byte aligned */
+  const void *wgate;    /* [W, hidden] row-major, layer in_dtype, 16-byte aligned */
+  const float *ape;     /* [ratio, W] float32, 16-byte aligned */
+  const float *norm_w;  /* [D] float32 RMS-norm weight, 16-byte aligned */
+} ds4c_lane;
+
+/* One compressed layer.  ratio 4 layers have an attention and an indexer
+ * lane; ratio 128 layers only an attention lane (index must be all zero).
+ * Uncompressed layers (ratio 0, Part 3 §1) have no compressor: DS4C_EINVAL. */
+typedef struct ds4c_layer {
+  int32_t ratio;        /* 4 or 128 */
+  int32_t hidden;       /* K of the projections: hidden % 64 == 0, <= 65536 */
+  int32_t n_rot;        /* RoPE tail width (64 in ds4, Part 3 §8): even, 0 < n_rot <= D */
+  int32_t in_dtype;     /* ds4c_dtype of x, wkv and wgate */
+  float rope_base;      /* compression RoPE base (> 0): theta_i = base^(-2i/n_rot) */
+  float rms_eps;        /* RMS-norm epsilon (>= 0) */
+  ds4c_lane attn;       /* rows get the FP8 E4M3 round trip on dims [0, D - n_rot) */
+  ds4c_lane index;      /* rows get Hadamard(D)/sqrt(D) then FP4 E2M1, blocks of 32 */
+} ds4c_layer;
+
+/* Per-layer compressor state.  The caller owns it and allocates `state`
+ * (ds4c_frontier_bytes bytes of device memory, 256-byte aligned); the
+ * library keeps the counters.  n_tokens is the absolute position of the next
+ * token; n_comp / n_index_comp count the rows appended so far and always
+ * equal n_tokens / ratio (0 for the indexer on ratio-128 layers).  Part 3 §2
+ * (ds4_layer_cache), Part 4 §7 (frontier tensors). */
+typedef struct ds4c_frontier {
+  int64_t n_tokens;
+  int64_t n_comp;
+  int64_t n_index_comp;
+  void *state;
+} ds4c_frontier;
+
+/* Bytes of device memory a layer's frontier needs: a 256-byte control block
+ * then, per lane, kv and score tensors of [coff*ratio, W] float32. 0 if the
+ * layer descriptor is invalid. */
+size_t ds4c_frontier_bytes(const ds4c_layer *layer);
+
+/* Bytes of device workspace ds4c_compress_prefill needs for calls of up to
+ * max_tokens tokens: the [T, N] float32 projection (N = 2 * sum of lane
+ * widths) plus per-row pooling scratch on ratio-128 layers.  0 if invalid. */
+size_t ds4c_workspace_bytes(const ds4c_layer *layer, int64_t max_tokens);
+
+/* Bytes of the host blob ds4c_frontier_save writes for this layer. */
+size_t ds4c_frontier_blob_bytes(const ds4c_layer *layer);
+
+/* Empty state (every kv 0, every score -inf, control block 0) and counters
+ * 0.  Enqueued on `stream` as a fill kernel (no memset). */
+int ds4c_frontier_init(const ds4c_layer *layer, ds4c_frontier *frontier, void *stream);
+
+/* Compress a chunk of T tokens x [T, hidden] (in_dtype, row-major) at
+ * absolute positions frontier->n_tokens ... + T - 1 (Part 3 §3: chunks keep
+ * windows on absolute positions; the frontier carries partial windows).
+ *
+ * Appends n_emit = (n0+T)/ratio - n0/ratio rows to each lane (n0 = the
+ * frontier's n_tokens): row k (the window of tokens k*ratio ...) is written
+ * to attn_rows[k * D_attn ...] and index_rows[k * D_index ...], so rows
+ * n_comp .. n_comp+n_emit-1 of the caller's append-only buffers (Part 4 §6).
+ * attn_cap / index_cap are the buffers' capacities in rows; index_rows must
+ * be NULL with index_cap 0 on ratio-128 layers.
+ *
+ * attn_prequant / index_prequant (nullable, [n_emit, D]) receive each new
+ * row after RMS norm and tail RoPE, before its codec; row 0 is the call's
+ * first new row.
+ *
+ * workspace: device, >= ds4c_workspace_bytes(layer, T) bytes, 256-byte
+ * aligned, contents undefined on entry and exit.
+ *
+ * Errors: DS4C_EINVAL, DS4C_ESHAPE, DS4C_ECAP (rows or workspace),
+ * DS4C_EPOS (counters), DS4C_EDEVICE.  T == 0 is a no-op returning DS4C_OK. */
+int ds4c_compress_prefill(const ds4c_layer *layer, ds4c_frontier *frontier,
+                          const void *x, int64_t T,
+                          float *attn_rows, int64_t attn_cap,
+                          float *index_rows, int64_t index_cap,
+                          void *workspace, size_t ws_bytes,
+                          float *attn_prequant, float *index_prequant,
+                          void *stream);
+
+/* One decode token x [hidden] at position frontier->n_tokens (Part 3 §4:
+ * compressor_decode_one): project, store into frontier row
+ * (coff-1)*ratio + pos % ratio with the APE added to the score, and when
+ * (pos+1) % ratio == 0 pool the frontier into row pos/ratio of each lane
+ * (norm, tail RoPE, codec) and, on ratio-4 layers, copy rows 4..7 to rows
+ * 0..3 (Part 3 §5).  Rows and prequant as for prefill (prequant row 0 is
+ * the emitted row, if any).  Needs no workspace.  Same errors as prefill. */
+int ds4c_compress_decode_one(const ds4c_layer *layer, ds4c_frontier *frontier,
+                             const void *x,
+                             float *attn_rows, int64_t attn_cap,
+                             float *index_rows, int64_t index_cap,
+                             float *attn_prequant, float *index_prequant,
+                             void *stream);
+
+/* Serialise the frontier into host memory (Part 4 §5, §7: the compressor
+ * and indexer frontiers are saved with the rows so a reload continues
+ * mid-window; §6: state is written in logical order).  Layout, little-
+ * endian: u32 magic 0x46345344 ("DS4F"), u32 version 1, u32 ratio, u32 coff,
+ * u32 D_attn, u32 D_index (0 on ratio-128), u32 n_rot, u32 0; u64 n_tokens,
+ * n_comp, n_index_comp; then float32 attention kv [coff*ratio, W_attn],
+ * attention score, and on ratio-4 layers indexer kv and score.  Rows the
+ * recurrence will overwrite before reading them are written as kv 0,
+ * score -inf, so two runs that reach the same state write identical blobs.
+ * Synchronises `stream`.  *written receives the blob size (may be NULL).
+ * Errors: DS4C_EINVAL, DS4C_ECAP (cap too small), DS4C_EPOS, DS4C_EDEVICE. */
+int ds4c_frontier_save(const ds4c_layer *layer, const ds4c_frontier *frontier,
+                       void *host_buf, size_t cap, size_t *written, void *stream);
+
+/* Restore a blob written by ds4c_frontier_save into an existing frontier
+ * (Part 4 §12: restore copies bytes back into buffers that are already
+ * allocated; nothing is mapped).  The header must match this layer exactly
+ * (magic, version, ratio, coff, dims, n_rot), len must equal the blob size
+ * and the counters must be consistent, else DS4C_EFORMAT and nothing
+ * changes.  Synchronises `stream`. */
+int ds4c_frontier_load(const ds4c_layer *layer, ds4c_frontier *frontier,
+                       const void *host_buf, size_t len, void *stream);
+
+/* Compress ratio of layer `layer` of a 0 = Flash / 1 = Pro model (Part 3
+ * §1): Flash layers 0-1 -> 0 (uncompressed), Pro layers 0-1 -> 128; from
+ * layer 2 even -> 4, odd -> 128.  -1 for a bad variant or negative layer. */
+int ds4c_layer_ratio(int variant, int layer);
+
+/* Prefill chunk cap (Part 3 §3): `override` if > 0, else 4096 when the
+ * prompt is longer than 4096 tokens, else the prompt length (at least 1). */
+int64_t ds4c_prefill_chunk_cap(int64_t prompt_len, int64_t override_cap);
+
+/* Static description of a status code; never NULL. */
+const char *ds4c_status_str(int status);
+
+/* Kernel timing.  While enabled (on != 0), every kernel the library enqueues
+ * is bracketed by HIP events on its stream.  ds4c_profile_read waits for the
+ * recorded events, writes the accumulated milliseconds and launch counts of
+ * each kernel class (DS4C_KCLASS_*) into ms[n] and count[n] (n <= 4), and
+ * clears the record.  Enabling or disabling also clears it. */
+enum { DS4C_KCLASS_PROJ = 0, DS4C_KCLASS_POOL = 1, DS4C_KCLASS_DECODE = 2, DS4C_KCLASS_INIT = 3 };
+int ds4c_profile_enable(int on);
+int ds4c_profile_read(double *ms, int64_t *count, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS4C_H */

@@ -1,0 +1,203 @@
+"""The C-ABI library on the host, without a GPU.
+
+The library must load and export every symbol include/ds4c.h declares.  Every
+call here fails validation (or is host-only), so nothing is enqueued: the
+error paths must return their exact status before touching the HIP runtime.
+"""
+
+import ctypes
+import os
+import re
+import struct
+
+import numpy as np
+import pytest
+
+import oracle
+from compressed_kv_attention_compressor_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ds4c.h")
+
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ds4c_[a-z0-9_]+)\s*\(", text)))
+
+
+def make_layer(ratio=4, hidden=4096, da=512, di=128, dtype=B.DS4C_BF16, n_rot=64):
+    L = B.Layer()
+    L.ratio, L.hidden, L.n_rot, L.in_dtype = ratio, hidden, n_rot, dtype
+    L.rope_base, L.rms_eps = 160000.0, 1e-6
+    L.attn = B.Lane(da, FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000)
+    if ratio == 4:
+        L.index = B.Lane(di, FAKE + 0x400000, FAKE + 0x500000, FAKE + 0x600000, FAKE + 0x700000)
+    return L
+
+
+def frontier(n=0, ratio=4):
+    f = B.Frontier()
+    f.n_tokens, f.n_comp, f.n_index_comp = n, n // ratio, (n // 4 if ratio == 4 else 0)
+    f.state = FAKE + 0x10000000
+    return f
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    names = declared_functions()
+    assert len(names) == 13
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(B.SIGNATURES), "binding and header disagree"
+
+
+def test_sizes():
+    L = make_layer()
+    assert B.ds4c_frontier_bytes(L) == 256 + 2 * 8 * 1024 * 4 + 2 * 8 * 256 * 4
+    assert B.ds4c_workspace_bytes(L, 4096) == 4096 * 2560 * 4
+    assert B.ds4c_frontier_blob_bytes(L) == 56 + 2 * 8 * 1024 * 4 + 2 * 8 * 256 * 4
+    L3 = make_layer(ratio=128)
+    assert B.ds4c_frontier_bytes(L3) == 256 + 2 * 128 * 512 * 4
+    # projection + pooled rows [33, 512] + tickets, each 256-aligned
+    ws = 4096 * 1024 * 4 + ((33 * 512 * 4 + 255) // 256) * 256 + 256
+    assert B.ds4c_workspace_bytes(L3, 4096) == ws
+    assert B.ds4c_frontier_bytes(make_layer(ratio=3)) == 0
+
+
+def test_schedule_helpers_match_oracle():
+    for layer in range(40):
+        assert B.ds4c_layer_ratio(0, layer) == oracle.layer_compress_ratio(layer, "flash")
+        assert B.ds4c_layer_ratio(1, layer) == oracle.layer_compress_ratio(layer, "pro")
+    assert B.ds4c_layer_ratio(2, 5) == -1
+    for n in (1, 100, 4096, 4097, 65536):
+        assert B.ds4c_prefill_chunk_cap(n, 0) == oracle.prefill_chunk_cap(n)
+    assert B.ds4c_prefill_chunk_cap(65536, 512) == 512
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6, -99):
+        assert isinstance(B.status_str(code), str) and B.status_str(code)
+
+
+def _prefill(L, f, T=64, attn_cap=10**6, index_cap=10**6, ws=None, x=FAKE + 0x20000000, index_rows=None):
+    ws_bytes = B.ds4c_workspace_bytes(L, T) if ws is None else ws
+    idx = (FAKE + 0x40000000 if L.ratio == 4 else 0) if index_rows is None else index_rows
+    return B.lib().ds4c_compress_prefill(ctypes.byref(L), ctypes.byref(f), x, T,
+                                         FAKE + 0x30000000, attn_cap, idx, index_cap if L.ratio == 4 else 0,
+                                         FAKE + 0x50000000, ws_bytes, 0, 0, None)
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda L, f: setattr(L, "ratio", 0), B.DS4C_EINVAL),
+    (lambda L, f: setattr(L, "ratio", 8), B.DS4C_EINVAL),
+    (lambda L, f: setattr(L, "in_dtype", 7), B.DS4C_EINVAL),
+    (lambda L, f: setattr(L, "rope_base", -1.0), B.DS4C_EINVAL),
+    (lambda L, f: setattr(L, "rms_eps", float("nan")), B.DS4C_EINVAL),
+    (lambda L, f: setattr(L, "hidden", 100), B.DS4C_ESHAPE),
+    (lambda L, f: setattr(L, "n_rot", 63), B.DS4C_ESHAPE),
+    (lambda L, f: setattr(L.attn, "head_dim", 384), B.DS4C_ESHAPE),
+    (lambda L, f: setattr(L.attn, "head_dim", 1024), B.DS4C_ESHAPE),
+    (lambda L, f: setattr(L, "n_rot", 32), B.DS4C_ESHAPE),  # 512 - 32 not a whole FP8 block
+    (lambda L, f: setattr(L.index, "head_dim", 96), B.DS4C_ESHAPE),
+    (lambda L, f: setattr(L.attn, "wkv", None), B.DS4C_EINVAL),
+    (lambda L, f: setattr(L.index, "norm_w", FAKE + 4), B.DS4C_EINVAL),
+    (lambda L, f: setattr(f, "state", None), B.DS4C_EINVAL),
+    (lambda L, f: setattr(f, "state", FAKE + 16), B.DS4C_EINVAL),
+    (lambda L, f: setattr(f, "n_comp", 3), B.DS4C_EPOS),
+    (lambda L, f: setattr(f, "n_tokens", -4), B.DS4C_EPOS),
+])
+def test_prefill_rejects_bad_arguments(mutate, status):
+    L, f = make_layer(), frontier(n=8)
+    mutate(L, f)
+    before = (f.n_tokens, f.n_comp, f.n_index_comp)
+    assert _prefill(L, f) == status
+    assert (f.n_tokens, f.n_comp, f.n_index_comp) == before
+
+
+def test_prefill_capacity_and_workspace():
+    L = make_layer()
+    f = frontier(n=8)  # rows 0, 1 already appended; 64 more tokens -> rows up to 17
+    assert _prefill(L, f, T=64, attn_cap=17) == B.DS4C_ECAP
+    assert _prefill(L, f, T=64, index_cap=17) == B.DS4C_ECAP
+    assert _prefill(L, f, T=64, ws=B.ds4c_workspace_bytes(L, 64) - 1) == B.DS4C_ECAP
+    assert _prefill(L, f, T=-1) == B.DS4C_EINVAL
+    assert _prefill(L, f, T=64, x=FAKE + 8) == B.DS4C_EINVAL
+    assert _prefill(L, f, T=1 << 23) == B.DS4C_ESHAPE
+    # a ratio-128 layer must not be given indexer rows
+    L3, f3 = make_layer(ratio=128), frontier(ratio=128)
+    assert B.lib().ds4c_compress_prefill(ctypes.byref(L3), ctypes.byref(f3), FAKE, 64, FAKE, 10, FAKE, 10,
+                                         FAKE, 1 << 30, 0, 0, None) == B.DS4C_EINVAL
+    # ratio 128 with an indexer lane is refused
+    L3.index = B.Lane(128, FAKE, FAKE, FAKE, FAKE)
+    assert _prefill(L3, f3) == B.DS4C_EINVAL
+    # ratio 4 with no indexer lane is refused
+    L4 = make_layer()
+    L4.index = B.Lane()
+    assert _prefill(L4, frontier()) == B.DS4C_ESHAPE
+
+
+def test_prefill_zero_tokens_is_a_noop():
+    L, f = make_layer(), frontier(n=5)
+    assert _prefill(L, f, T=0) == B.DS4C_OK
+    assert (f.n_tokens, f.n_comp) == (5, 1)
+
+
+def test_decode_rejects_bad_arguments():
+    L, f = make_layer(), frontier(n=7)  # position 7 closes window 1 -> needs cap >= 2
+    lib = B.lib()
+    args = lambda cap: (ctypes.byref(L), ctypes.byref(f), FAKE, FAKE, cap, FAKE, cap, 0, 0, None)
+    assert lib.ds4c_compress_decode_one(*args(1)) == B.DS4C_ECAP
+    f.n_index_comp = 0
+    assert lib.ds4c_compress_decode_one(*args(10)) == B.DS4C_EPOS
+    f.n_index_comp = 1
+    assert lib.ds4c_compress_decode_one(ctypes.byref(L), ctypes.byref(f), 0, FAKE, 10, FAKE, 10, 0, 0,
+                                        None) == B.DS4C_EINVAL
+    assert f.n_tokens == 7
+
+
+def _blob_header(ratio=4, coff=2, da=512, di=128, n_rot=64, n=10, nc=2, ni=2, magic=0x46345344, version=1):
+    return struct.pack("<8I3Q", magic, version, ratio, coff, da, di, n_rot, 0, n, nc, ni)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(magic=0x12345678), dict(version=2), dict(ratio=128), dict(coff=1), dict(da=256),
+    dict(di=64), dict(n_rot=32), dict(nc=3), dict(ni=1),
+])
+def test_load_rejects_bad_blobs(kw):
+    L, f = make_layer(), frontier()
+    n = B.ds4c_frontier_blob_bytes(L)
+    blob = _blob_header(**kw) + b"\0" * (n - 56)
+    buf = ctypes.create_string_buffer(blob, len(blob))
+    assert B.lib().ds4c_frontier_load(ctypes.byref(L), ctypes.byref(f), buf, len(blob), None) == B.DS4C_EFORMAT
+    assert f.n_tokens == 0
+
+
+def test_load_rejects_wrong_length():
+    L, f = make_layer(), frontier()
+    n = B.ds4c_frontier_blob_bytes(L)
+    for size in (n - 1, n + 1, 55):
+        blob = (_blob_header() + b"\0" * n)[:size]
+        buf = ctypes.create_string_buffer(blob, len(blob))
+        assert B.lib().ds4c_frontier_load(ctypes.byref(L), ctypes.byref(f), buf, len(blob), None) == B.DS4C_EFORMAT
+
+
+def test_save_rejects_small_buffer():
+    L, f = make_layer(), frontier(n=12)
+    n = B.ds4c_frontier_blob_bytes(L)
+    buf = ctypes.create_string_buffer(n)
+    w = ctypes.c_size_t(0)
+    assert B.lib().ds4c_frontier_save(ctypes.byref(L), ctypes.byref(f), buf, n - 1, ctypes.byref(w),
+                                      None) == B.DS4C_ECAP
+    f.n_comp = 0
+    assert B.lib().ds4c_frontier_save(ctypes.byref(L), ctypes.byref(f), buf, n, ctypes.byref(w),
+                                      None) == B.DS4C_EPOS
+
+
+def test_profile_read_without_records():
+    B.ds4c_profile_enable(True)
+    ms, cnt = B.ds4c_profile_read()
+    assert ms == [0.0] * 4 and cnt == [0] * 4
+    B.ds4c_profile_enable(False)

@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case runs the same seeded inputs through both and compares
+element by element with the rules of tests/compare.py: pre-codec values
+within 2e-3 relative, codec outputs within one code, row counts, counters
+and frontier -inf positions exact.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from compressed_kv_attention_compressor_amd import synth
+from compressed_kv_attention_compressor_amd.layer import CompressorLayer
+from tests._helpers import oracle_spec
+from tests.compare import check_attn_rows, check_index_rows, check_prequant
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _tdtype(shape):
+    return torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+
+
+def make_gpu_layer(shape, params, max_tokens):
+    return CompressorLayer(shape.ratio, shape.hidden, params, dtype=shape.dtype, n_rot=shape.n_rot,
+                           rope_base=shape.rope_base, rms_eps=shape.rms_eps, max_tokens=max_tokens)
+
+
+def run_gpu(shape, params, x, plan):
+    """plan: list of chunk sizes; a negative entry -n means n single decode steps."""
+    layer = make_gpu_layer(shape, params, len(x))
+    xd = torch.from_numpy(x).to("cuda", _tdtype(shape))
+    pre = {k: [] for k in layer.kinds}
+    t = 0
+    for step in plan:
+        if step >= 0:
+            got = layer.prefill(xd[t:t + step], prequant=True)
+            t += step
+        else:
+            got = {k: [] for k in layer.kinds}
+            for _ in range(-step):
+                one = layer.decode_one(xd[t], prequant=True)
+                for k in layer.kinds:
+                    got[k].append(one[k])
+                t += 1
+            got = {k: torch.cat(v) for k, v in got.items()}
+        for k in layer.kinds:
+            pre[k].append(got[k].cpu().numpy())
+    assert t == len(x)
+    torch.cuda.synchronize()
+    out = {
+        "rows": {k: layer.live_rows(k).cpu().numpy() for k in layer.kinds},
+        "pre": {k: np.concatenate(v) for k, v in pre.items()},
+        "frontier": {k: (kv.cpu().numpy(), sc.cpu().numpy()) for k, (kv, sc) in layer.frontier_views().items()},
+        "counters": (layer.frontier.n_tokens, layer.frontier.n_comp, layer.frontier.n_index_comp),
+        "layer": layer,
+    }
+    return out
+
+
+def run_oracle(shape, params, x):
+    spec = oracle_spec(shape, params)
+    st = oracle.new_layer_state(spec)
+    oracle.prefill(spec, st, x)
+    return spec, st
+
+
+def compare_all(shape, g, spec, st, n):
+    r = shape.ratio
+    assert g["counters"] == (n, n // r, n // 4 if r == 4 else 0)
+    for lane in spec.lanes():
+        k = lane.kind
+        o_rows = np.array(st.lanes[k].rows).reshape(-1, lane.head_dim)
+        o_pre = np.array(st.lanes[k].prequant).reshape(-1, lane.head_dim)
+        assert g["rows"][k].shape == o_rows.shape
+        check_prequant(g["pre"][k], o_pre, f"{k} prequant")
+        if k == "attn":
+            check_attn_rows(g["rows"][k], o_rows, g["pre"][k], o_pre, shape.n_rot)
+        else:
+            check_index_rows(g["rows"][k], o_rows, g["pre"][k], o_pre)
+        # live frontier rows, pre-quant tolerance; -inf positions exact
+        kv_g, sc_g = g["frontier"][k]
+        for row, _tok in oracle.compressor.live_frontier_rows(r, n):
+            kv_o, sc_o = st.lanes[k].kv[row], st.lanes[k].score[row]
+            assert np.array_equal(np.isneginf(sc_g[row]), np.isneginf(sc_o))
+            fin = np.isfinite(sc_o)
+            check_prequant(kv_g[row], kv_o, f"{k} frontier kv row {row}")
+            check_prequant(sc_g[row][fin], sc_o[fin], f"{k} frontier score row {row}")
+
+
+def _workload(name):
+    w = synth.WORKLOADS[name]
+    p = synth.layer_params(w.wid, 0, w.layer)
+    x = synth.hidden_states(w.wid, w.layer.hidden, 0, w.tokens, w.layer.dtype)
+    return w, p, x
+
+
+@pytest.mark.parametrize("name", ["r4_small", "r4_flash", "r128_flash"])
+def test_workload_one_call(name):
+    _say(f"[parity] {name} one call")
+    w, p, x = _workload(name)
+    g = run_gpu(w.layer, p, x, [len(x)])
+    spec, st = run_oracle(w.layer, p, x)
+    compare_all(w.layer, g, spec, st, len(x))
+
+
+SMALL = {
+    "r4_d128": synth.LayerShape(ratio=4, hidden=256, d_attn=128, d_index=64, dtype="f32"),
+    "r4_d512_bf16": synth.LayerShape(ratio=4, hidden=256, d_attn=512, d_index=128, dtype="bf16"),
+    "r4_d256_idx512": synth.LayerShape(ratio=4, hidden=128, d_attn=256, d_index=512, dtype="bf16"),
+    "r128_d512": synth.LayerShape(ratio=128, hidden=256, d_attn=512, d_index=0, dtype="bf16"),
+    "r128_d128_f32": synth.LayerShape(ratio=128, hidden=192, d_attn=128, d_index=0, dtype="f32"),
+}
+
+
+def _small(name, n, seed=0, random_norm=True):
+    shape = SMALL[name]
+    p = synth.layer_params(90 + list(SMALL).index(name), 0, shape, seed=seed, random_norm=random_norm)
+    x = synth.hidden_states(90 + list(SMALL).index(name), shape.hidden, 0, n, shape.dtype, seed=seed)
+    return shape, p, x
+
+
+PLANS = {
+    "ragged": [1, 3, 5, 127, 129, 2, 64, 300, 69],
+    "decode_mix": [3, -6, 130, -3, 1, 120, -130, 337],
+    "aligned": [256, 256, 188],
+}
+
+
+@pytest.mark.parametrize("plan", list(PLANS))
+@pytest.mark.parametrize("name", list(SMALL))
+def test_chunked_and_decode(name, plan):
+    n = sum(abs(s) for s in PLANS[plan])
+    _say(f"[parity] {name} plan {plan} n={n}")
+    shape, p, x = _small(name, n)
+    g = run_gpu(shape, p, x, PLANS[plan])
+    spec, st = run_oracle(shape, p, x)
+    compare_all(shape, g, spec, st, n)
+
+
+@pytest.mark.parametrize("name", ["r4_d128", "r128_d512"])
+def test_single_tokens_and_tiny_calls(name):
+    _say(f"[parity] {name} tiny calls")
+    shape, p, x = _small(name, 260, seed=3)
+    plan = [1] * 9 + [-1] * 7 + [0, 2, 0] + [242]
+    g = run_gpu(shape, p, x, plan)
+    spec, st = run_oracle(shape, p, x)
+    compare_all(shape, g, spec, st, 260)
+
+
+@pytest.mark.parametrize("name", ["r4_d512_bf16", "r128_d512"])
+def test_save_load_continue(name):
+    _say(f"[parity] {name} save/load")
+    shape, p, x = _small(name, 600, seed=5)
+    xd = torch.from_numpy(x).to("cuda", _tdtype(shape))
+    full = make_gpu_layer(shape, p, 600)
+    full.prefill(xd)
+    for cut in (0, 3, 131, 259):
+        a = make_gpu_layer(shape, p, 600)
+        a.prefill(xd[:cut])
+        blob = a.save()
+        # the blob's header and live rows match the oracle's canonical frontier
+        spec, st = run_oracle(shape, p, x[:cut])
+        hdr = np.frombuffer(blob[:32], dtype="<u4")
+        cnt = np.frombuffer(blob[32:56], dtype="<u8")
+        assert list(hdr) == [0x46345344, 1, shape.ratio, shape.coff, shape.d_attn, shape.d_index, 64, 0]
+        assert list(cnt) == [cut, cut // shape.ratio, cut // 4 if shape.ratio == 4 else 0]
+        body = np.frombuffer(blob[56:], dtype="<f4")
+        canon = oracle.canonical_frontier(spec, st)
+        off = 0
+        for lane in spec.lanes():
+            kv_o, sc_o = canon[lane.kind]
+            m = kv_o.size
+            kv_g = body[off:off + m].reshape(kv_o.shape)
+            sc_g = body[off + m:off + 2 * m].reshape(sc_o.shape)
+            off += 2 * m
+            assert np.array_equal(np.isneginf(sc_g), np.isneginf(sc_o))
+            fin = np.isfinite(sc_o)
+            check_prequant(kv_g, kv_o, "blob kv")
+            check_prequant(sc_g[fin], sc_o[fin], "blob score")
+        assert off == body.size
+        # a second save of the same state is byte-identical
+        assert a.save() == blob
+        # load into a fresh layer (with garbage in its frontier) and continue
+        b = make_gpu_layer(shape, p, 600)
+        b.prefill(xd[300:300 + 37])  # scribble on b's frontier first
+        b.load(blob)
+        assert b.frontier.n_tokens == cut
+        b.rows = {k: v.clone() for k, v in b.rows.items()}
+        for k in b.kinds:
+            b.rows[k][: cut // shape.ratio] = a.rows[k][: cut // shape.ratio]
+        b.prefill(xd[cut:])
+        torch.cuda.synchronize()
+        for k in b.kinds:
+            assert torch.equal(b.live_rows(k), full.live_rows(k)), (cut, k)
+
+
+def test_deterministic_and_overwrites_poison():
+    _say("[parity] determinism")
+    w, p, x = _workload("r4_flash")
+    xd = torch.from_numpy(x).to("cuda", torch.bfloat16)
+    outs = []
+    for _ in range(2):
+        layer = make_gpu_layer(w.layer, p, len(x))
+        for v in layer.rows.values():
+            v.fill_(float("nan"))
+        layer.prefill(xd)
+        torch.cuda.synchronize()
+        for k in layer.kinds:
+            assert torch.isfinite(layer.live_rows(k)).all()
+        outs.append({k: layer.live_rows(k).clone() for k in layer.kinds})
+    for k in outs[0]:
+        assert torch.equal(outs[0][k], outs[1][k])
+
+
+def test_row_zero_of_ratio4_pools_current_half_only():
+    """Equal scores (zero gate weights and APE) make row 0 the mean of 4 tokens."""
+    _say("[parity] equal-score row 0")
+    shape = SMALL["r4_d128"]
+    p = synth.layer_params(99, 0, shape)
+    for k in p:
+        p[k]["wgate"][:] = 0
+        p[k]["ape"][:] = 0
+    x = synth.hidden_states(99, shape.hidden, 0, 12, "f32")
+    g = run_gpu(shape, p, x, [12])
+    spec, st = run_oracle(shape, p, x)
+    compare_all(shape, g, spec, st, 12)
