@@ -333,7 +333,7 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
     po.ratio = r;
     po.n_rot = layer->n_rot;
     po.n_lanes = s.n_lanes;
-    po.rope_base = layer->rope_base;
+    po.log2_base = std::log2((double)layer->rope_base);
     po.rms_eps = layer->rms_eps;
     po.lane[0] = lane_dev(s, *layer, frontier->state, 0, attn_rows, attn_prequant);
     if (s.n_lanes > 1) po.lane[1] = lane_dev(s, *layer, frontier->state, 1, index_rows, index_prequant);
@@ -386,7 +386,7 @@ int ds4c_compress_decode_one(const ds4c_layer* layer, ds4c_frontier* frontier, c
     d.ratio = r;
     d.n_rot = layer->n_rot;
     d.n_lanes = s.n_lanes;
-    d.rope_base = layer->rope_base;
+    d.log2_base = std::log2((double)layer->rope_base);
     d.rms_eps = layer->rms_eps;
     d.lane[0] = lane_dev(s, *layer, frontier->state, 0, attn_rows, attn_prequant);
     if (s.n_lanes > 1) d.lane[1] = lane_dev(s, *layer, frontier->state, 1, index_rows, index_prequant);

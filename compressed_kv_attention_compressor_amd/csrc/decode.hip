@@ -98,7 +98,7 @@ __device__ void r4_boundary(const DecodeArgs& a, const LaneDev& L, int64_t k, in
   float o[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) o[i] = s[i] > 0.f ? acc[i] / s[i] : 0.f;
-  finish_row_wave<DPL>(o, L, a.n_rot, a.rope_base, a.rms_eps, k, 4, L.prequant, L.rows + k * L.D, lane);
+  finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, L.prequant, L.rows + k * L.D, lane);
 }
 
 template <typename Tin, int DPLA, int DPLI>
@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
         }
         o[i] = den > 0.f ? num / den : 0.f;
       }
-      finish_row_wave<DPLA>(o, L, a.n_rot, a.rope_base, a.rms_eps, k, 128, L.prequant, L.rows + k * L.D, lane);
+      finish_row_wave<DPLA>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, L.prequant, L.rows + k * L.D, lane);
     }
   }
 }

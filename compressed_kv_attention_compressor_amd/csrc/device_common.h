@@ -101,6 +101,20 @@ __device__ __forceinline__ void store_vec(float* __restrict__ p, const float (&v
   }
 }
 
+// RoPE angle of pair i at position pos: pos * base^(-2i/n_rot), formed in
+// fp64 (positions reach 10^5 and beyond, where a float angle would be off by
+// more than 10^-3 rad), reduced exactly enough to [-pi, pi] in fp64, then
+// sin/cos in fp32 on the small remainder.
+__device__ __forceinline__ void rope_sincos(double pos, int i, int n_rot, double log2_base, float* s,
+                                            float* c) {
+  const double theta = exp2(-2.0 * (double)i / (double)n_rot * log2_base);
+  const double ang = pos * theta;
+  const double two_pi = 6.283185307179586476925;
+  const double turns = rint(ang * (1.0 / two_pi));
+  const float r = (float)fma(-turns, two_pi, ang);
+  sincosf(r, s, c);
+}
+
 // ---------------------------------------------------------------------------
 // Row epilogue for one wave.  y[DPL] holds the pooled row's dims
 // lane*DPL .. lane*DPL+DPL-1 on entry.  Writes the final row (and the
@@ -108,7 +122,7 @@ __device__ __forceinline__ void store_vec(float* __restrict__ p, const float (&v
 // ---------------------------------------------------------------------------
 template <int DPL>
 __device__ __forceinline__ void finish_row_wave(float (&y)[DPL], const LaneDev& L, int n_rot,
-                                                float rope_base, float rms_eps, int64_t k,
+                                                double log2_base, float rms_eps, int64_t k,
                                                 int ratio, float* __restrict__ prequant_row,
                                                 float* __restrict__ out_row, int lane) {
   const int D = DPL * kWave;
@@ -126,18 +140,15 @@ __device__ __forceinline__ void finish_row_wave(float (&y)[DPL], const LaneDev& 
   for (int i = 0; i < DPL; ++i) y[i] = y[i] * w[i] * inv;
 
   // Tail RoPE (Part 3 §8): the last n_rot dims, adjacent pairs (2i, 2i+1),
-  // angle = (k * ratio) * base^(-2i/n_rot), formed and evaluated in fp64.
+  // rotated by (k * ratio) * base^(-2i/n_rot) radians.
   const int n_nope = D - n_rot;
   const double pos = (double)k * (double)ratio;
   if constexpr (DPL >= 2) {
     if (d0 >= n_nope) {
 #pragma unroll
       for (int i = 0; i < DPL; i += 2) {
-        const int pi = (d0 + i - n_nope) >> 1;
-        const double ang = pos * pow((double)rope_base, -2.0 * (double)pi / (double)n_rot);
-        double s, c;
-        sincos(ang, &s, &c);
-        const float cf = (float)c, sf = (float)s;
+        float sf, cf;
+        rope_sincos(pos, (d0 + i - n_nope) >> 1, n_rot, log2_base, &sf, &cf);
         const float a = y[i], b = y[i + 1];
         y[i] = a * cf - b * sf;
         y[i + 1] = a * sf + b * cf;
@@ -147,11 +158,8 @@ __device__ __forceinline__ void finish_row_wave(float (&y)[DPL], const LaneDev& 
     // One dim per lane: the pair partner is the neighbouring lane.
     const float other = __shfl_xor(y[0], 1, kWave);
     if (d0 >= n_nope) {
-      const int pi = (d0 - n_nope) >> 1;
-      const double ang = pos * pow((double)rope_base, -2.0 * (double)pi / (double)n_rot);
-      double s, c;
-      sincos(ang, &s, &c);
-      const float cf = (float)c, sf = (float)s;
+      float sf, cf;
+      rope_sincos(pos, (d0 - n_nope) >> 1, n_rot, log2_base, &sf, &cf);
       if ((lane & 1) == 0)
         y[0] = y[0] * cf - other * sf;  // a' = a cos - b sin
       else

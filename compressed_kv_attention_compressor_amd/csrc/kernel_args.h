@@ -49,7 +49,7 @@ struct PoolArgs {
   int ratio;
   int n_rot;
   int n_lanes;
-  float rope_base;
+  double log2_base;     // log2 of the compression RoPE base
   float rms_eps;
   LaneDev lane[2];
   float* o_buf;         // ratio 128: [k_hi-k_lo, D] pooled rows
@@ -68,7 +68,7 @@ struct DecodeArgs {
   int ratio;
   int n_rot;
   int n_lanes;
-  float rope_base;
+  double log2_base;
   float rms_eps;
   LaneDev lane[2];
   unsigned* ticket;     // in the frontier control block; zero between calls

@@ -29,7 +29,7 @@ constexpr int kPoolThreads = 256;
 
 // Entries of one lane's column block for token p, DPL dims starting at
 // column c of the lane's W-wide kv / score blocks.
-template <int DPL>
+template <int R, int DPL>
 __device__ __forceinline__ void fetch_token(const PoolArgs& a, const LaneDev& L, int64_t p, int c,
                                             float (&kv)[DPL], float (&sc)[DPL]) {
   if (p < 0) {
@@ -37,15 +37,10 @@ __device__ __forceinline__ void fetch_token(const PoolArgs& a, const LaneDev& L,
     for (int i = 0; i < DPL; ++i) { kv[i] = 0.f; sc[i] = -INFINITY; }
     return;
   }
-  const int r = a.ratio;
+  const int pr = (int)(p & (R - 1));
   if (p < a.n0) {
-    int row;
-    if (r == 4) {
-      const int64_t m0 = a.n0 - (a.n0 & 3);
-      row = p >= m0 ? 4 + (int)(p & 3) : (int)(p & 3);
-    } else {
-      row = (int)(p % r);
-    }
+    int row = pr;
+    if (R == 4 && p >= a.n0 - (a.n0 & 3)) row = 4 + pr;
     load_vec<DPL>(kv, L.fr_kv + (int64_t)row * L.W + c);
     load_vec<DPL>(sc, L.fr_sc + (int64_t)row * L.W + c);
     return;
@@ -54,7 +49,7 @@ __device__ __forceinline__ void fetch_token(const PoolArgs& a, const LaneDev& L,
   load_vec<DPL>(kv, src + L.kv_col + c);
   load_vec<DPL>(sc, src + L.sc_col + c);
   float ape[DPL];
-  load_vec<DPL>(ape, L.ape + (int64_t)(p % r) * L.W + c);
+  load_vec<DPL>(ape, L.ape + pr * L.W + c);
 #pragma unroll
   for (int i = 0; i < DPL; ++i) sc[i] += ape[i];
 }
@@ -66,7 +61,7 @@ __device__ void r4_row(const PoolArgs& a, const LaneDev& L, int64_t k, int lane)
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int c = (e < 4 ? 0 : L.D) + lane * DPL;
-    fetch_token<DPL>(a, L, 4 * k - 4 + e, c, kv[e], sc[e]);
+    fetch_token<4, DPL>(a, L, 4 * k - 4 + e, c, kv[e], sc[e]);
   }
   float o[DPL];
 #pragma unroll
@@ -86,7 +81,7 @@ __device__ void r4_row(const PoolArgs& a, const LaneDev& L, int64_t k, int lane)
     o[i] = den > 0.f ? num / den : 0.f;
   }
   float* pre = L.prequant ? L.prequant + (k - a.k_lo) * L.D : nullptr;
-  finish_row_wave<DPL>(o, L, a.n_rot, a.rope_base, a.rms_eps, k, 4, pre, L.rows + k * L.D, lane);
+  finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, pre, L.rows + k * L.D, lane);
 }
 
 // Frontier carry after a call, by one whole workgroup, for both ratios.
@@ -94,53 +89,46 @@ __device__ void r4_row(const PoolArgs& a, const LaneDev& L, int64_t k, int lane)
 // in rows 0..3 and m .. n-1 in rows 4 .. 3+c; ratio 128 keeps m .. n-1 in
 // rows 0 .. c-1.  Only rows that change are written.  Every read of the
 // incoming frontier by this call's windows has completed before this runs.
+template <int R>
 __device__ void carry_frontier(const PoolArgs& a) {
-  const int r = a.ratio;
   const int64_t n = a.n0 + a.T;
-  const int64_t m = n - n % r;
-  const int tid = threadIdx.x;
-  if (r == 4) {
+  const int64_t m = n - (n & (R - 1));
+  const int c4 = threadIdx.x * 4;
+  if (R == 4) {
     const int64_t m0 = a.n0 - (a.n0 & 3);
     // Old tokens that move from the current half to the previous half.
     if (m > m0 && m - 4 < a.n0) {
       for (int l = 0; l < a.n_lanes; ++l) {
         const LaneDev& L = a.lane[l];
-        const int nv = L.W / 4;
-        const int64_t cnt = (a.n0 - (m - 4)) * nv;
-        for (int64_t i = tid; i < cnt; i += blockDim.x) {
-          const int64_t p = (m - 4) + i / nv;
-          const int c = (int)(i % nv) * 4;
+        for (int64_t p = m - 4; p < a.n0; ++p) {
           const int src = 4 + (int)(p & 3), dst = (int)(p & 3);
-          float4 kv = *reinterpret_cast<const float4*>(L.fr_kv + (int64_t)src * L.W + c);
-          float4 sc = *reinterpret_cast<const float4*>(L.fr_sc + (int64_t)src * L.W + c);
-          *reinterpret_cast<float4*>(L.fr_kv + (int64_t)dst * L.W + c) = kv;
-          *reinterpret_cast<float4*>(L.fr_sc + (int64_t)dst * L.W + c) = sc;
+          for (int c = c4; c < L.W; c += 4 * kPoolThreads) {
+            const float4 kv = *reinterpret_cast<const float4*>(L.fr_kv + src * L.W + c);
+            const float4 sc = *reinterpret_cast<const float4*>(L.fr_sc + src * L.W + c);
+            *reinterpret_cast<float4*>(L.fr_kv + dst * L.W + c) = kv;
+            *reinterpret_cast<float4*>(L.fr_sc + dst * L.W + c) = sc;
+          }
         }
       }
       __syncthreads();
     }
   }
   // New tokens from the projection workspace.
-  const int64_t first = r == 4 ? (m - 4 > a.n0 ? m - 4 : a.n0) : (m > a.n0 ? m : a.n0);
+  const int64_t first = R == 4 ? (m - 4 > a.n0 ? m - 4 : a.n0) : (m > a.n0 ? m : a.n0);
   for (int l = 0; l < a.n_lanes; ++l) {
     const LaneDev& L = a.lane[l];
-    const int nv = L.W / 4;
-    const int64_t cnt = (n - first) * nv;
-    for (int64_t i = tid; i < cnt; i += blockDim.x) {
-      const int64_t p = first + i / nv;
-      const int c = (int)(i % nv) * 4;
-      int row;
-      if (r == 4)
-        row = p >= m ? 4 + (int)(p & 3) : (int)(p & 3);
-      else
-        row = (int)(p - m);
+    for (int64_t p = first; p < n; ++p) {
+      const int pr = (int)(p & (R - 1));
+      const int row = R == 4 ? (p >= m ? 4 + pr : pr) : (int)(p - m);
       const float* src = a.proj + (p - a.n0) * a.ld;
-      float4 kv = *reinterpret_cast<const float4*>(src + L.kv_col + c);
-      float4 sc = *reinterpret_cast<const float4*>(src + L.sc_col + c);
-      const float4 ap = *reinterpret_cast<const float4*>(L.ape + (int64_t)(p % r) * L.W + c);
-      sc.x += ap.x; sc.y += ap.y; sc.z += ap.z; sc.w += ap.w;
-      *reinterpret_cast<float4*>(L.fr_kv + (int64_t)row * L.W + c) = kv;
-      *reinterpret_cast<float4*>(L.fr_sc + (int64_t)row * L.W + c) = sc;
+      for (int c = c4; c < L.W; c += 4 * kPoolThreads) {
+        const float4 kv = *reinterpret_cast<const float4*>(src + L.kv_col + c);
+        float4 sc = *reinterpret_cast<const float4*>(src + L.sc_col + c);
+        const float4 ap = *reinterpret_cast<const float4*>(L.ape + pr * L.W + c);
+        sc.x += ap.x; sc.y += ap.y; sc.z += ap.z; sc.w += ap.w;
+        *reinterpret_cast<float4*>(L.fr_kv + row * L.W + c) = kv;
+        *reinterpret_cast<float4*>(L.fr_sc + row * L.W + c) = sc;
+      }
     }
   }
 }
@@ -152,15 +140,16 @@ template <int DPLA, int DPLI>
 __global__ void __launch_bounds__(kPoolThreads) pool_r4_kernel(PoolArgs a) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
+  // Jobs are (window, lane) pairs, lane = job & 1 (ratio-4 layers have two).
   int64_t job;
   if (blockIdx.x == 0) {
-    job = wave < a.n_head * a.n_lanes ? wave : -1;
+    job = wave < 2 * a.n_head ? wave : -1;
   } else {
-    job = a.n_head * a.n_lanes + (int64_t)(blockIdx.x - 1) * (kPoolThreads / kWave) + wave;
+    job = 2 * a.n_head + (int64_t)(blockIdx.x - 1) * (kPoolThreads / kWave) + wave;
   }
   if (job >= 0) {
-    const int64_t k = a.k_lo + job / a.n_lanes;
-    const int l = (int)(job % a.n_lanes);
+    const int64_t k = a.k_lo + (job >> 1);
+    const int l = (int)(job & 1);
     if (k < a.k_hi) {
       if (l == 0)
         r4_row<DPLA>(a, a.lane[0], k, lane);
@@ -170,7 +159,7 @@ __global__ void __launch_bounds__(kPoolThreads) pool_r4_kernel(PoolArgs a) {
   }
   if (blockIdx.x == 0) {
     __syncthreads();
-    carry_frontier(a);
+    carry_frontier<4>(a);
   }
 }
 
@@ -188,7 +177,7 @@ __global__ void __launch_bounds__(kPoolThreads) pool_r128_kernel(PoolArgs a) {
   const LaneDev& L = a.lane[0];
   const int64_t n_rows = a.k_hi - a.k_lo;
   if (n_rows == 0) {
-    carry_frontier(a);
+    carry_frontier<128>(a);
     return;
   }
   const int S = L.D / 64;
@@ -201,7 +190,7 @@ __global__ void __launch_bounds__(kPoolThreads) pool_r128_kernel(PoolArgs a) {
 
   float kv[8][4], sc[8][4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) fetch_token<4>(a, L, 128 * k + tg + 16 * e, c, kv[e], sc[e]);
+  for (int e = 0; e < 8; ++e) fetch_token<128, 4>(a, L, 128 * k + tg + 16 * e, c, kv[e], sc[e]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float m = sc[0][i];
@@ -258,9 +247,9 @@ __global__ void __launch_bounds__(kPoolThreads) pool_r128_kernel(PoolArgs a) {
     for (int i = 0; i < DPL; ++i)
       o[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float* pre = L.prequant ? L.prequant + row * L.D : nullptr;
-    finish_row_wave<DPL>(o, L, a.n_rot, a.rope_base, a.rms_eps, k, 128, pre, L.rows + k * L.D, tid);
+    finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, pre, L.rows + k * L.D, tid);
   }
-  if (row == 0) carry_frontier(a);
+  if (row == 0) carry_frontier<128>(a);
 }
 
 __global__ void __launch_bounds__(kPoolThreads) frontier_fill_kernel(FillArgs f) {
@@ -295,7 +284,7 @@ void launch_r4_a(const PoolArgs& a, int dpli, int64_t grid, hipStream_t s) {
 hipError_t launch_pool(const PoolArgs& a, hipStream_t stream) {
   const int64_t n_rows = a.k_hi - a.k_lo;
   if (a.ratio == 4) {
-    const int64_t other_jobs = (n_rows - a.n_head) * a.n_lanes;
+    const int64_t other_jobs = (n_rows - a.n_head) * 2;
     const int64_t grid = 1 + (other_jobs + 3) / 4;
     const int dpla = a.lane[0].D / 64, dpli = a.lane[1].D / 64;
     switch (dpla) {

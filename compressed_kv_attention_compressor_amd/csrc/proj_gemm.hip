@@ -6,9 +6,12 @@
 //  * One 256-thread workgroup (4 waves) computes a BM x BN tile; each wave a
 //    (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks with fp32 accumulators.
 //    bf16 uses v_mfma_f32_32x32x16_bf16, float32 v_mfma_f32_32x32x2_f32.
-//  * K advances in tiles of 128 bytes per row (64 bf16 / 32 fp32), staged
-//    through LDS in 16-byte slots, double-buffered: the global loads of the
-//    next K tile are in flight while the MFMAs consume the current one.
+//  * K advances in tiles of 128 bytes per row (64 bf16 / 32 fp32) through a
+//    3-stage LDS ring filled by direct global->LDS 16-byte loads (no VGPR
+//    staging).  A K tile is issued two tiles ahead; the workgroup barrier
+//    sits in the middle of a tile so the next tile's first fragments are read
+//    while the current tile's last MFMAs run, and fragment registers are
+//    double-buffered across the four K sub-steps of a tile.
 //  * Slot (row, chunk) lives at row*8 + (chunk ^ f(row)) with
 //    f(row) = (row & 7) ^ ((row >> 3) & 1), so the 16-byte fragment reads of
 //    8 or 16 consecutive lanes (consecutive rows, same chunk) hit distinct banks.
@@ -66,30 +69,13 @@ __device__ __forceinline__ const Tin* weight_row(const ProjArgs& a, int n) {
   return reinterpret_cast<const Tin*>(w) + (int64_t)(n - c0) * a.K;
 }
 
-// Global -> registers: one 16-byte chunk per staged row, K offset k0.
-template <int A_PER, int B_PER, typename Tin>
-__device__ __forceinline__ void gload(u32x4 (&ra)[A_PER], u32x4 (&rb)[B_PER], const Tin* const (&ap)[A_PER],
-                                      const Tin* const (&bp)[B_PER], int k0) {
-#pragma unroll
-  for (int i = 0; i < A_PER; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + k0);
-#pragma unroll
-  for (int i = 0; i < B_PER; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + k0);
-}
-
-// Registers -> one LDS stage (A rows then B rows), swizzled 16-byte slots.
-template <int BM, int A_PER, int B_PER>
-__device__ __forceinline__ void sstore(u32x4* st, const u32x4 (&ra)[A_PER], const u32x4 (&rb)[B_PER], int t) {
-  const int c = t & 7;
-#pragma unroll
-  for (int i = 0; i < A_PER; ++i) {
-    const int row = (t >> 3) + 32 * i;
-    st[row * 8 + (c ^ swz(row))] = ra[i];
-  }
-#pragma unroll
-  for (int i = 0; i < B_PER; ++i) {
-    const int row = (t >> 3) + 32 * i;
-    st[(BM + row) * 8 + (c ^ swz(row))] = rb[i];
-  }
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
+// left at their maxima so they do not wait).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <typename Tin, int BM, int BN, int WM, int WN>
@@ -98,17 +84,18 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
   constexpr int BK = 8 * kElems;                  // K elements per tile (8 chunks per row)
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int A_PER = BM * 8 / kThreads, B_PER = BN * 8 / kThreads;
-  static_assert(WM * WN == 4, "four waves");
+  constexpr int kWaves = kThreads / 64;
+  constexpr int A_INS = BM / (8 * kWaves), B_INS = BN / (8 * kWaves);  // 8 rows per wave load
+  constexpr int kStage = (BM + BN) * 8;                                  // 16-byte slots per stage
+  static_assert(WM * WN == kWaves, "four waves");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "32x32 blocks");
-  static_assert((BM * 8) % kThreads == 0 && (BN * 8) % kThreads == 0, "whole chunks per thread");
-  __shared__ u32x4 smem[2][(BM + BN) * 8];
+  static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "whole wave loads");
+  __shared__ u32x4 smem[3 * kStage];
 
   const int t = threadIdx.x;
   if (blockIdx.x == 0)
     for (int i = t; i < a.n_zero; i += kThreads) a.zero_ptr[i] = 0u;
 
-  // XCD-contiguous logical tile id, then grouped (GM tile-rows) order.
   const int n_tiles = tiles_m * tiles_n;
   const int b = blockIdx.x;
   const int x = b % kXcds, j = b / kXcds;
@@ -123,28 +110,43 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BN;
 
-  // Global addresses of the chunks this thread stages: chunk (row, c) with
-  // row = t/8 + 32*i and c = t%8.  Rows past the end are clamped (loaded,
-  // never stored).
-  const int c_ld = t & 7;
-  const Tin* a_ptr[A_PER];
-  const Tin* b_ptr[B_PER];
-  const Tin* X = reinterpret_cast<const Tin*>(a.x);
-#pragma unroll
-  for (int i = 0; i < A_PER; ++i) {
-    int64_t r = m0 + (t >> 3) + 32 * i;
-    r = r < a.M ? r : a.M - 1;
-    a_ptr[i] = X + r * a.K + c_ld * kElems;
-  }
-#pragma unroll
-  for (int i = 0; i < B_PER; ++i) {
-    int n = n0 + (t >> 3) + 32 * i;
-    n = n < a.N ? n : a.N - 1;
-    b_ptr[i] = weight_row<Tin>(a, n) + c_ld * kElems;
-  }
-  u32x4 ra[A_PER], rb[B_PER];
-
   const int wave = t >> 6, lane = t & 63;
+  // Direct-to-LDS loads: a wave instruction fills 1 KiB of LDS = 8 rows x 8
+  // slots, lane l landing in slot l.  Lane l of the instruction covering rows
+  // r0..r0+7 therefore fetches chunk (l%8) ^ f(row) of row r0 + l/8.
+  const Tin* X = reinterpret_cast<const Tin*>(a.x);
+  const Tin* a_src[A_INS];
+  const Tin* b_src[B_INS];
+#pragma unroll
+  for (int i = 0; i < A_INS; ++i) {
+    const int row = (wave * A_INS + i) * 8 + (lane >> 3);
+    int64_t r = m0 + row;
+    r = r < a.M ? r : a.M - 1;
+    a_src[i] = X + r * a.K + ((lane & 7) ^ swz(row)) * kElems;
+  }
+#pragma unroll
+  for (int i = 0; i < B_INS; ++i) {
+    const int row = (wave * B_INS + i) * 8 + (lane >> 3);
+    int n = n0 + row;
+    n = n < a.N ? n : a.N - 1;
+    b_src[i] = weight_row<Tin>(a, n) + ((lane & 7) ^ swz(row)) * kElems;
+  }
+  auto issue = [&](int kt, int st) {
+    const int k0 = kt * BK;
+    __attribute__((address_space(3))) u32x4* base =
+        (__attribute__((address_space(3))) u32x4*)(smem + st * kStage);
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + k0),
+                                       (__attribute__((address_space(3))) void*)(base + (wave * A_INS + i) * 64),
+                                       16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + k0),
+                                       (__attribute__((address_space(3))) void*)(base + (BM + (wave * B_INS + i) * 8) * 8),
+                                       16, 0, 0);
+  };
+
   const int wm = wave / WN, wn = wave % WN;
   const int h = lane >> 5, r32 = lane & 31;
   f32x16 acc[FM][FN];
@@ -153,34 +155,68 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x16{};
 
-  const int nk = a.K / BK;
-  gload<A_PER, B_PER>(ra, rb, a_ptr, b_ptr, 0);
-  sstore<BM, A_PER, B_PER>(smem[0], ra, rb, t);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int s = kt & 1;
-    if (kt + 1 < nk) gload<A_PER, B_PER>(ra, rb, a_ptr, b_ptr, (kt + 1) * BK);
+  // Fragment registers, double-buffered across K sub-steps.
+  u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  auto frags = [&](u32x4 (&fa)[FM], u32x4 (&fb)[FN], int st, int kk) {
+    const u32x4* base = smem + st * kStage;
+    const int c = 2 * kk + h;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c = 2 * kk + h;
-      u32x4 af[FM], bfr[FN];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int row = wm * TM + fm * 32 + r32;
-        af[fm] = smem[s][row * 8 + (c ^ swz(row))];
-      }
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int row = wn * TN + fn * 32 + r32;
-        bfr[fn] = smem[s][(BM + row) * 8 + (c ^ swz(row))];
-      }
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) mfma_chunk<Tin>(af[fm], bfr[fn], acc[fm][fn]);
+    for (int fm = 0; fm < FM; ++fm) {
+      const int row = wm * TM + fm * 32 + r32;
+      fa[fm] = base[row * 8 + (c ^ swz(row))];
     }
-    if (kt + 1 < nk) sstore<BM, A_PER, B_PER>(smem[s ^ 1], ra, rb, t);
-    __syncthreads();
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int row = wn * TN + fn * 32 + r32;
+      fb[fn] = base[(BM + row) * 8 + (c ^ swz(row))];
+    }
+  };
+  auto mma = [&](const u32x4 (&fa)[FM], const u32x4 (&fb)[FN]) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) mfma_chunk<Tin>(fa[fm], fb[fn], acc[fm][fn]);
+  };
+  // Interleave hint: one MFMA, one LDS read, repeated, then the rest of the MFMAs.
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < FM + FN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN) > 0 ? FM * FN - (FM + FN) : 0, 0);
+  };
+
+  const int nk = a.K / BK;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  if (nk > 1)
+    wait_vm<A_INS + B_INS>();
+  else
+    wait_vm<0>();
+  asm volatile("s_barrier" ::: "memory");
+  frags(fa0, fb0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt % 3;
+    frags(fa1, fb1, st, 1);
+    mma(fa0, fb0);
+    interleave();
+    frags(fa0, fb0, st, 2);
+    mma(fa1, fb1);
+    interleave();
+    if (kt + 1 < nk) {
+      // Tile kt+1 has landed for every wave, and every wave is done with tile
+      // kt-1, whose stage the issue below refills.
+      wait_vm<0>();
+      asm volatile("s_barrier" ::: "memory");
+      if (kt + 2 < nk) issue(kt + 2, (kt + 2) % 3);
+    }
+    frags(fa1, fb1, st, 3);
+    mma(fa0, fb0);
+    interleave();
+    if (kt + 1 < nk) frags(fa0, fb0, (kt + 1) % 3, 0);
+    mma(fa1, fb1);
+    interleave();
   }
 
   // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4.
