@@ -96,20 +96,20 @@ void frontier_ptrs(const Shape& s, void* state, int lane, float** kv, float** sc
 }
 
 struct WsLayout {
-  size_t proj = 0, obuf = 0, tickets = 0, total = 0;
+  size_t proj = 0, part = 0, total = 0;
   int64_t max_rows = 0;
 };
 
+// Projection [T, N] float32, then on ratio-128 layers the pool partials:
+// per emitted row, 2 token halves x (max, sum, weighted sum) x D floats.
 WsLayout workspace_layout(const Shape& s, int64_t T) {
   WsLayout w;
   w.proj = 0;
   size_t off = align256(size_t(T) * s.N * sizeof(float));
   if (s.ratio == 128) {
     w.max_rows = T / 128 + 1;
-    w.obuf = off;
-    off += align256(size_t(w.max_rows) * s.D[0] * sizeof(float));
-    w.tickets = off;
-    off += align256(size_t(w.max_rows) * sizeof(unsigned));
+    w.part = off;
+    off += align256(size_t(w.max_rows) * 2 * 3 * s.D[0] * sizeof(float));
   }
   w.total = off;
   return w;
@@ -311,10 +311,6 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
     pa.K = layer->hidden;
     pa.N = s.N;
     fill_proj_segments(*layer, s, pa.seg, &pa.n_seg);
-    if (r == 128) {
-      pa.zero_ptr = reinterpret_cast<unsigned*>(ws + wl.tickets);
-      pa.n_zero = int(n_emit);
-    }
 
     PoolArgs po{};
     po.proj = pa.out;
@@ -337,15 +333,16 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
     po.rms_eps = layer->rms_eps;
     po.lane[0] = lane_dev(s, *layer, frontier->state, 0, attn_rows, attn_prequant);
     if (s.n_lanes > 1) po.lane[1] = lane_dev(s, *layer, frontier->state, 1, index_rows, index_prequant);
-    if (r == 128) {
-      po.o_buf = reinterpret_cast<float*>(ws + wl.obuf);
-      po.tickets = reinterpret_cast<unsigned*>(ws + wl.tickets);
-    }
+    if (r == 128) po.part = reinterpret_cast<float*>(ws + wl.part);
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
     st = dev_status(timed(DS4C_KCLASS_PROJ, hs, [&] { return ds4c::launch_proj(pa, layer->in_dtype, hs); }));
     if (st) return st;
-    st = dev_status(timed(DS4C_KCLASS_POOL, hs, [&] { return ds4c::launch_pool(po, hs); }));
+    st = dev_status(timed(DS4C_KCLASS_POOL, hs, [&] {
+      hipError_t e = hipSuccess;
+      for (int ph = 0; ph < ds4c::pool_launches(r) && e == hipSuccess; ++ph) e = ds4c::launch_pool(po, ph, hs);
+      return e;
+    }));
     if (st) return st;
     frontier->n_tokens = n;
     frontier->n_comp = k_hi;

@@ -101,46 +101,61 @@ __device__ __forceinline__ void store_vec(float* __restrict__ p, const float (&v
   }
 }
 
-// RoPE angle of pair i at position pos: pos * base^(-2i/n_rot), formed in
-// fp64 (positions reach 10^5 and beyond, where a float angle would be off by
-// more than 10^-3 rad), reduced exactly enough to [-pi, pi] in fp64, then
-// sin/cos in fp32 on the small remainder.
+// sin and cos of 2*pi*t for |t| <= 1/2 (t in turns).  Quadrant q = rint(4t)
+// leaves r = 2*pi*(t - q/4) in [-pi/4, pi/4], where the Taylor series of sin
+// (to r^9) and cos (to r^8) are within 2e-9 of the true values; the quadrant
+// then swaps and negates them.
+__device__ __forceinline__ void sincos_turns(float t, float* s, float* c) {
+  const float q = rintf(4.0f * t);
+  const float r = (t - 0.25f * q) * 6.28318530717958647692f;
+  const float r2 = r * r;
+  const float sr = r * (1.0f + r2 * (-1.0f / 6 + r2 * (1.0f / 120 + r2 * (-1.0f / 5040 + r2 * (1.0f / 362880)))));
+  const float cr = 1.0f + r2 * (-0.5f + r2 * (1.0f / 24 + r2 * (-1.0f / 720 + r2 * (1.0f / 40320))));
+  const int qi = ((int)q) & 3;
+  *s = qi == 0 ? sr : qi == 1 ? cr : qi == 2 ? -sr : -cr;
+  *c = qi == 0 ? cr : qi == 1 ? -sr : qi == 2 ? -cr : sr;
+}
+
+// RoPE angle of pair i at position pos: pos * base^(-2i/n_rot) radians.  It
+// is formed in fp64 (positions reach 10^5 and beyond, where a float angle
+// would be off by more than 10^-3 rad) as a number of turns, whose fractional
+// part then goes to the float sin/cos above.
 __device__ __forceinline__ void rope_sincos(double pos, int i, int n_rot, double log2_base, float* s,
                                             float* c) {
   const double theta = exp2(-2.0 * (double)i / (double)n_rot * log2_base);
-  const double ang = pos * theta;
-  const double two_pi = 6.283185307179586476925;
-  const double turns = rint(ang * (1.0 / two_pi));
-  const float r = (float)fma(-turns, two_pi, ang);
-  sincosf(r, s, c);
+  const double turns = pos * theta * 0.15915494309189533577;  // 1 / (2 pi)
+  sincos_turns((float)(turns - rint(turns)), s, c);
 }
 
 // ---------------------------------------------------------------------------
-// Row epilogue for one wave.  y[DPL] holds the pooled row's dims
-// lane*DPL .. lane*DPL+DPL-1 on entry.  Writes the final row (and the
-// pre-codec row if requested).
+// Row epilogue.  A row of D dims is held by one or more waves; this lane
+// holds dims d0 .. d0+DPL-1.  `inv` is 1/sqrt(mean(o^2) + eps) of the whole
+// row.  Applies the norm weight, tail RoPE (Part 3 §8), writes the pre-codec
+// row if asked, then the lane codec (Part 3 §9), and writes the final row.
+// FP8 blocks (64 dims) must lie within one wave; the indexer's Hadamard
+// rotation needs the whole row in one wave (D == 64 * DPL).
 // ---------------------------------------------------------------------------
 template <int DPL>
-__device__ __forceinline__ void finish_row_wave(float (&y)[DPL], const LaneDev& L, int n_rot,
-                                                double log2_base, float rms_eps, int64_t k,
-                                                int ratio, float* __restrict__ prequant_row,
-                                                float* __restrict__ out_row, int lane) {
-  const int D = DPL * kWave;
-  const int d0 = lane * DPL;
-
-  // RMS norm over the whole row: y = o * w / sqrt(mean(o^2) + eps).
+__device__ __forceinline__ float row_sumsq(const float (&y)[DPL]) {
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) ss = fmaf(y[i], y[i], ss);
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)D + rms_eps);
+  return ss;
+}
+
+template <int DPL>
+__device__ __forceinline__ void finish_row_part(float (&y)[DPL], const LaneDev& L, float inv, int d0, int n_rot,
+                                                double log2_base, int64_t k, int ratio,
+                                                float* __restrict__ prequant_row, float* __restrict__ out_row,
+                                                int lane) {
+  const int D = L.D;
   float w[DPL];
   load_vec<DPL>(w, L.norm_w + d0);
 #pragma unroll
   for (int i = 0; i < DPL; ++i) y[i] = y[i] * w[i] * inv;
 
-  // Tail RoPE (Part 3 §8): the last n_rot dims, adjacent pairs (2i, 2i+1),
-  // rotated by (k * ratio) * base^(-2i/n_rot) radians.
+  // Tail RoPE: the last n_rot dims, adjacent pairs (2i, 2i+1), rotated by
+  // (k * ratio) * base^(-2i/n_rot) radians.
   const int n_nope = D - n_rot;
   const double pos = (double)k * (double)ratio;
   if constexpr (DPL >= 2) {
@@ -218,6 +233,20 @@ __device__ __forceinline__ void finish_row_wave(float (&y)[DPL], const LaneDev& 
   }
 
   store_vec<DPL>(out_row + d0, y);
+}
+
+__device__ __forceinline__ float rms_inv(float sumsq, int D, float eps) {
+  return 1.0f / sqrtf(sumsq / (float)D + eps);
+}
+
+// Whole row in one wave (D == 64 * DPL).
+template <int DPL>
+__device__ __forceinline__ void finish_row_wave(float (&y)[DPL], const LaneDev& L, int n_rot, double log2_base,
+                                                float rms_eps, int64_t k, int ratio,
+                                                float* __restrict__ prequant_row, float* __restrict__ out_row,
+                                                int lane) {
+  const float inv = rms_inv(wave_sum(row_sumsq<DPL>(y)), L.D, rms_eps);
+  finish_row_part<DPL>(y, L, inv, lane * DPL, n_rot, log2_base, k, ratio, prequant_row, out_row, lane);
 }
 
 }  // namespace ds4c

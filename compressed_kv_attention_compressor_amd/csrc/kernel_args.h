@@ -35,8 +35,6 @@ struct ProjArgs {
   int N;
   int n_seg;
   ProjSeg seg[4];
-  unsigned* zero_ptr;   // cleared by the first workgroup (pool tickets)
-  int n_zero;
 };
 
 struct PoolArgs {
@@ -52,8 +50,7 @@ struct PoolArgs {
   double log2_base;     // log2 of the compression RoPE base
   float rms_eps;
   LaneDev lane[2];
-  float* o_buf;         // ratio 128: [k_hi-k_lo, D] pooled rows
-  unsigned* tickets;    // ratio 128: [k_hi-k_lo] slice counters, zero on entry
+  float* part;          // ratio 128: [k_hi-k_lo][2 halves][max, sum, weighted sum][D]
 };
 
 struct DecodeArgs {

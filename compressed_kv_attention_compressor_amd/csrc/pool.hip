@@ -1,7 +1,6 @@
-// Fused compressor pool kernels: APE add, window gather (projection
-// workspace or carried frontier), per-dimension softmax pool, RMS norm, tail
-// RoPE, FP8 / Hadamard+FP4 round trip, row append and frontier carry, in one
-// launch per prefill call.
+// Compressor pool kernels: APE add, window gather (projection workspace or
+// carried frontier), per-dimension softmax pool, RMS norm, tail RoPE,
+// FP8 / Hadamard+FP4 round trip, row append and frontier carry.
 //
 // What is pooled (Part 3 §4, §5): for every output dim j, the window's
 // entries (kv, score + APE[pos % ratio]) are weighted by exp(score - max)
@@ -13,9 +12,14 @@
 // Tokens before the call (positions < n0) are read from the frontier: for
 // ratio 4 a token p lives in row 4 + p%4 when p >= n0 - n0%4, else in row
 // p%4 (it was moved there by the half shift); for ratio 128 in row p%128.
-// Only the first one or two windows of a call can touch such tokens; they
-// are handled by the workgroup that also rewrites the frontier, after it
-// has finished reading it.
+// Only the first one or two windows of a call can touch such tokens.
+//
+// Ratio 4 runs in one launch; the workgroup that pools the windows touching
+// the incoming frontier also rewrites it afterwards.  Ratio 128 runs in two:
+// a wide partial-pool launch with no cross-workgroup dependency, then a
+// finishing launch that merges the partials, normalises, rotates and
+// quantises each row and carries the frontier; the launch boundary orders
+// the finisher after every read of the incoming frontier.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -25,10 +29,8 @@ namespace ds4c {
 
 namespace {
 
-constexpr int kPoolThreads = 256;
-
-// Entries of one lane's column block for token p, DPL dims starting at
-// column c of the lane's W-wide kv / score blocks.
+// DPL dims of token p, starting at column c of the lane's W-wide kv / score
+// blocks (score with APE added).
 template <int R, int DPL>
 __device__ __forceinline__ void fetch_token(const PoolArgs& a, const LaneDev& L, int64_t p, int c,
                                             float (&kv)[DPL], float (&sc)[DPL]) {
@@ -41,8 +43,8 @@ __device__ __forceinline__ void fetch_token(const PoolArgs& a, const LaneDev& L,
   if (p < a.n0) {
     int row = pr;
     if (R == 4 && p >= a.n0 - (a.n0 & 3)) row = 4 + pr;
-    load_vec<DPL>(kv, L.fr_kv + (int64_t)row * L.W + c);
-    load_vec<DPL>(sc, L.fr_sc + (int64_t)row * L.W + c);
+    load_vec<DPL>(kv, L.fr_kv + row * L.W + c);
+    load_vec<DPL>(sc, L.fr_sc + row * L.W + c);
     return;
   }
   const float* src = a.proj + (p - a.n0) * a.ld;
@@ -54,25 +56,18 @@ __device__ __forceinline__ void fetch_token(const PoolArgs& a, const LaneDev& L,
   for (int i = 0; i < DPL; ++i) sc[i] += ape[i];
 }
 
-// One ratio-4 row of one lane on one wave.
-template <int DPL>
-__device__ void r4_row(const PoolArgs& a, const LaneDev& L, int64_t k, int lane) {
-  float kv[8][DPL], sc[8][DPL];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = (e < 4 ? 0 : L.D) + lane * DPL;
-    fetch_token<4, DPL>(a, L, 4 * k - 4 + e, c, kv[e], sc[e]);
-  }
-  float o[DPL];
+// Softmax pool of E entries per dim: o = sum w*kv / sum w, w = exp(s - max).
+template <int E, int DPL>
+__device__ __forceinline__ void pool_entries(const float (&kv)[E][DPL], const float (&sc)[E][DPL], float (&o)[DPL]) {
 #pragma unroll
   for (int i = 0; i < DPL; ++i) {
     float m = sc[0][i];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) m = fmaxf(m, sc[e][i]);
+    for (int e = 1; e < E; ++e) m = fmaxf(m, sc[e][i]);
     float den = 0.f, num = 0.f;
     if (m != -INFINITY) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < E; ++e) {
         const float w = expf(sc[e][i] - m);
         den += w;
         num = fmaf(w, kv[e][i], num);
@@ -80,20 +75,27 @@ __device__ void r4_row(const PoolArgs& a, const LaneDev& L, int64_t k, int lane)
     }
     o[i] = den > 0.f ? num / den : 0.f;
   }
-  float* pre = L.prequant ? L.prequant + (k - a.k_lo) * L.D : nullptr;
-  finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, pre, L.rows + k * L.D, lane);
 }
 
-// Frontier carry after a call, by one whole workgroup, for both ratios.
-// With n = n0 + T, c = n % ratio, m = n - c: ratio 4 keeps tokens m-4 .. m-1
-// in rows 0..3 and m .. n-1 in rows 4 .. 3+c; ratio 128 keeps m .. n-1 in
-// rows 0 .. c-1.  Only rows that change are written.  Every read of the
-// incoming frontier by this call's windows has completed before this runs.
+// Pooled dims c .. c+DPL-1 of ratio-4 window k of one lane.
+template <int DPL>
+__device__ __forceinline__ void r4_pool(const PoolArgs& a, const LaneDev& L, int64_t k, int c, float (&o)[DPL]) {
+  float kv[8][DPL], sc[8][DPL];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) fetch_token<4, DPL>(a, L, 4 * k - 4 + e, (e < 4 ? 0 : L.D) + c, kv[e], sc[e]);
+  pool_entries<8, DPL>(kv, sc, o);
+}
+
+// Frontier carry after a call, by one whole workgroup.  With n = n0 + T,
+// c = n % ratio, m = n - c: ratio 4 keeps tokens m-4 .. m-1 in rows 0..3 and
+// m .. n-1 in rows 4 .. 3+c; ratio 128 keeps m .. n-1 in rows 0 .. c-1.  Only
+// rows that change are written.  Every read of the incoming frontier by this
+// call's windows has completed before this runs.
 template <int R>
 __device__ void carry_frontier(const PoolArgs& a) {
   const int64_t n = a.n0 + a.T;
   const int64_t m = n - (n & (R - 1));
-  const int c4 = threadIdx.x * 4;
+  const int c4 = threadIdx.x * 4, step = 4 * blockDim.x;
   if (R == 4) {
     const int64_t m0 = a.n0 - (a.n0 & 3);
     // Old tokens that move from the current half to the previous half.
@@ -102,7 +104,7 @@ __device__ void carry_frontier(const PoolArgs& a) {
         const LaneDev& L = a.lane[l];
         for (int64_t p = m - 4; p < a.n0; ++p) {
           const int src = 4 + (int)(p & 3), dst = (int)(p & 3);
-          for (int c = c4; c < L.W; c += 4 * kPoolThreads) {
+          for (int c = c4; c < L.W; c += step) {
             const float4 kv = *reinterpret_cast<const float4*>(L.fr_kv + src * L.W + c);
             const float4 sc = *reinterpret_cast<const float4*>(L.fr_sc + src * L.W + c);
             *reinterpret_cast<float4*>(L.fr_kv + dst * L.W + c) = kv;
@@ -121,7 +123,7 @@ __device__ void carry_frontier(const PoolArgs& a) {
       const int pr = (int)(p & (R - 1));
       const int row = R == 4 ? (p >= m ? 4 + pr : pr) : (int)(p - m);
       const float* src = a.proj + (p - a.n0) * a.ld;
-      for (int c = c4; c < L.W; c += 4 * kPoolThreads) {
+      for (int c = c4; c < L.W; c += step) {
         const float4 kv = *reinterpret_cast<const float4*>(src + L.kv_col + c);
         float4 sc = *reinterpret_cast<const float4*>(src + L.sc_col + c);
         const float4 ap = *reinterpret_cast<const float4*>(L.ape + pr * L.W + c);
@@ -133,73 +135,79 @@ __device__ void carry_frontier(const PoolArgs& a) {
   }
 }
 
-// Ratio 4.  Workgroup 0 pools the n_head leading windows (one wave per
-// (window, lane), at most 2 x 2) and then carries the frontier; every other
-// workgroup pools four (window, lane) rows, one per wave.
-template <int DPLA, int DPLI>
-__global__ void __launch_bounds__(kPoolThreads) pool_r4_kernel(PoolArgs a) {
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  // Jobs are (window, lane) pairs, lane = job & 1 (ratio-4 layers have two).
-  int64_t job;
-  if (blockIdx.x == 0) {
-    job = wave < 2 * a.n_head ? wave : -1;
-  } else {
-    job = 2 * a.n_head + (int64_t)(blockIdx.x - 1) * (kPoolThreads / kWave) + wave;
-  }
-  if (job >= 0) {
-    const int64_t k = a.k_lo + (job >> 1);
-    const int l = (int)(job & 1);
-    if (k < a.k_hi) {
-      if (l == 0)
-        r4_row<DPLA>(a, a.lane[0], k, lane);
-      else
-        r4_row<DPLI>(a, a.lane[1], k, lane);
-    }
-  }
-  if (blockIdx.x == 0) {
+// One ratio-4 window on one workgroup: SA attention waves (D_attn/SA dims
+// each, DPLA per lane) and one indexer wave (the whole indexer row, DPLI per
+// lane).  The attention row's sum of squares is reduced through LDS.
+template <int SA, int DPLA, int DPLI>
+__device__ __forceinline__ void r4_window(const PoolArgs& a, int64_t k, float* s_ss) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (wave < SA) {
+    const LaneDev& L = a.lane[0];
+    const int d0 = wave * (kWave * DPLA) + lane * DPLA;
+    float o[DPLA];
+    r4_pool<DPLA>(a, L, k, d0, o);
+    const float ss = wave_sum(row_sumsq<DPLA>(o));
+    if (lane == 0) s_ss[wave] = ss;
     __syncthreads();
-    carry_frontier<4>(a);
+    float tot = 0.f;
+#pragma unroll
+    for (int s = 0; s < SA; ++s) tot += s_ss[s];
+    float* pre = L.prequant ? L.prequant + (k - a.k_lo) * L.D : nullptr;
+    finish_row_part<DPLA>(o, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, pre,
+                          L.rows + k * L.D, lane);
+  } else {
+    const LaneDev& L = a.lane[1];
+    float o[DPLI];
+    r4_pool<DPLI>(a, L, k, lane * DPLI, o);
+    __syncthreads();
+    float* pre = L.prequant ? L.prequant + (k - a.k_lo) * L.D : nullptr;
+    finish_row_wave<DPLI>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, pre, L.rows + k * L.D, lane);
   }
+  __syncthreads();
 }
 
-// Ratio 128.  Workgroup (row, slice) pools dims slice*64 .. slice*64+63 of
-// row k_lo + row over all 128 tokens: 16 dim groups of 4 x 16 token groups
-// of 8, merged through LDS.  It writes its 64 pooled dims to o_buf and takes
-// a ticket; the last of the row's D/64 slices normalises, rotates and
-// quantises the whole row.  The last slice of the first row also carries the
-// frontier (all slices of that row have finished reading it by then).  With
-// no row to emit, the single workgroup only carries the frontier.
-template <int DPL>
-__global__ void __launch_bounds__(kPoolThreads) pool_r128_kernel(PoolArgs a) {
-  __shared__ float s_m[16][64], s_s[16][64], s_a[16][64];
-  __shared__ int s_last;
-  const LaneDev& L = a.lane[0];
-  const int64_t n_rows = a.k_hi - a.k_lo;
-  if (n_rows == 0) {
-    carry_frontier<128>(a);
+// Ratio 4: one window per workgroup.  Workgroup 0 takes the (at most two)
+// leading windows that read the incoming frontier, one after the other, and
+// then carries the frontier; workgroup b > 0 takes window k_lo + n_head + b-1.
+template <int SA, int DPLA, int DPLI>
+__global__ void __launch_bounds__(64 * (SA + 1)) pool_r4_kernel(PoolArgs a) {
+  __shared__ float s_ss[SA];
+  if (blockIdx.x > 0) {
+    r4_window<SA, DPLA, DPLI>(a, a.k_lo + a.n_head + blockIdx.x - 1, s_ss);
     return;
   }
+  if (a.n_head > 0) r4_window<SA, DPLA, DPLI>(a, a.k_lo, s_ss);
+  if (a.n_head > 1) r4_window<SA, DPLA, DPLI>(a, a.k_lo + 1, s_ss);
+  carry_frontier<4>(a);
+}
+
+// Ratio 128, phase 1: workgroup (row, 64-dim slice, 64-token half) pools 64
+// tokens x 64 dims (16 dim groups of 4 x 16 token groups of 4), merges the
+// 16 groups through LDS and writes the (max, sum, weighted sum) partial of
+// each dim: part[row][half][0..2][D].
+__global__ void __launch_bounds__(256) pool_r128_partial_kernel(PoolArgs a) {
+  __shared__ float s_m[16][64], s_s[16][64], s_a[16][64];
+  const LaneDev& L = a.lane[0];
   const int S = L.D / 64;
-  const int64_t row = blockIdx.x / S;
-  const int slice = blockIdx.x % S;
+  const int half = blockIdx.x & 1;
+  const int slice = (blockIdx.x >> 1) % S;
+  const int64_t row = (blockIdx.x >> 1) / S;
   const int64_t k = a.k_lo + row;
   const int tid = threadIdx.x;
   const int dg = tid & 15, tg = tid >> 4;
   const int c = slice * 64 + dg * 4;
-
-  float kv[8][4], sc[8][4];
+  float kv[4][4], sc[4][4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) fetch_token<128, 4>(a, L, 128 * k + tg + 16 * e, c, kv[e], sc[e]);
+  for (int e = 0; e < 4; ++e) fetch_token<128, 4>(a, L, 128 * k + 64 * half + tg + 16 * e, c, kv[e], sc[e]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float m = sc[0][i];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) m = fmaxf(m, sc[e][i]);
+    for (int e = 1; e < 4; ++e) m = fmaxf(m, sc[e][i]);
     float den = 0.f, num = 0.f;
     if (m != -INFINITY) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 4; ++e) {
         const float w = expf(sc[e][i] - m);
         den += w;
         num = fmaf(w, kv[e][i], num);
@@ -226,33 +234,57 @@ __global__ void __launch_bounds__(kPoolThreads) pool_r128_kernel(PoolArgs a) {
         }
       }
     }
-    a.o_buf[row * L.D + slice * 64 + tid] = den > 0.f ? num / den : 0.f;
-    __threadfence();
-    int last = 0;
-    if (tid == 0) {
-      const unsigned t = __hip_atomic_fetch_add(a.tickets + row, 1u, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-      last = t == (unsigned)(S - 1);
-      s_last = last;
-    }
+    float* out = a.part + ((row * 2 + half) * 3) * L.D + slice * 64 + tid;
+    out[0] = M;
+    out[L.D] = den;
+    out[2 * L.D] = num;
   }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid < 64) {
-    float o[DPL];
-    const float* src = a.o_buf + row * L.D + tid * DPL;
-    // Acquire-ordered loads of the other slices' results.
-#pragma unroll
-    for (int i = 0; i < DPL; ++i)
-      o[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    float* pre = L.prequant ? L.prequant + row * L.D : nullptr;
-    finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, pre, L.rows + k * L.D, tid);
-  }
-  if (row == 0) carry_frontier<128>(a);
 }
 
-__global__ void __launch_bounds__(kPoolThreads) frontier_fill_kernel(FillArgs f) {
+// Ratio 128, phase 2: one wave per row merges the two halves' partials and
+// finishes the row; workgroup 0 then carries the frontier.
+template <int DPL>
+__global__ void __launch_bounds__(256) pool_r128_finish_kernel(PoolArgs a) {
+  const LaneDev& L = a.lane[0];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row < a.k_hi - a.k_lo) {
+    const int d0 = lane * DPL;
+    float M[DPL], den[DPL], num[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) { M[i] = -INFINITY; den[i] = 0.f; num[i] = 0.f; }
+    float m[2][DPL], s[2][DPL], acc[2][DPL];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* p = a.part + ((row * 2 + h) * 3) * L.D + d0;
+      load_vec<DPL>(m[h], p);
+      load_vec<DPL>(s[h], p + L.D);
+      load_vec<DPL>(acc[h], p + 2 * L.D);
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) M[i] = fmaxf(M[i], m[h][i]);
+    }
+    float o[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      if (M[i] != -INFINITY) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (m[h][i] == -INFINITY) continue;
+          const float f = expf(m[h][i] - M[i]);
+          den[i] = fmaf(s[h][i], f, den[i]);
+          num[i] = fmaf(acc[h][i], f, num[i]);
+        }
+      }
+      o[i] = den[i] > 0.f ? num[i] / den[i] : 0.f;
+    }
+    const int64_t k = a.k_lo + row;
+    float* pre = L.prequant ? L.prequant + row * L.D : nullptr;
+    finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, pre, L.rows + k * L.D, lane);
+  }
+  if (blockIdx.x == 0) carry_frontier<128>(a);
+}
+
+__global__ void __launch_bounds__(256) frontier_fill_kernel(FillArgs f) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (int l = 0; l < f.n_lanes; ++l) {
@@ -264,50 +296,52 @@ __global__ void __launch_bounds__(kPoolThreads) frontier_fill_kernel(FillArgs f)
   if (i0 < f.n_ctrl) f.ctrl[i0] = 0u;
 }
 
-template <int A, int I>
-void launch_r4(const PoolArgs& a, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((pool_r4_kernel<A, I>), dim3((unsigned)grid), dim3(kPoolThreads), 0, s, a);
-}
-
-template <int A>
-void launch_r4_a(const PoolArgs& a, int dpli, int64_t grid, hipStream_t s) {
+template <int SA, int DPLA>
+void launch_r4_a(const PoolArgs& a, int dpli, unsigned grid, hipStream_t s) {
+  const dim3 block(64 * (SA + 1));
   switch (dpli) {
-    case 1: launch_r4<A, 1>(a, grid, s); break;
-    case 2: launch_r4<A, 2>(a, grid, s); break;
-    case 4: launch_r4<A, 4>(a, grid, s); break;
-    default: launch_r4<A, 8>(a, grid, s); break;
+    case 1: hipLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 1>), dim3(grid), block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 2>), dim3(grid), block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 4>), dim3(grid), block, 0, s, a); break;
+    default: hipLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 8>), dim3(grid), block, 0, s, a); break;
   }
 }
 
 }  // namespace
 
-hipError_t launch_pool(const PoolArgs& a, hipStream_t stream) {
+int pool_launches(int ratio) { return ratio == 4 ? 1 : 2; }
+
+hipError_t launch_pool(const PoolArgs& a, int phase, hipStream_t stream) {
   const int64_t n_rows = a.k_hi - a.k_lo;
   if (a.ratio == 4) {
-    const int64_t other_jobs = (n_rows - a.n_head) * 2;
-    const int64_t grid = 1 + (other_jobs + 3) / 4;
-    const int dpla = a.lane[0].D / 64, dpli = a.lane[1].D / 64;
-    switch (dpla) {
-      case 1: launch_r4_a<1>(a, dpli, grid, stream); break;
-      case 2: launch_r4_a<2>(a, dpli, grid, stream); break;
-      case 4: launch_r4_a<4>(a, dpli, grid, stream); break;
-      default: launch_r4_a<8>(a, dpli, grid, stream); break;
+    // Attention rows are split into waves of 128 dims (64 dims below 128).
+    const unsigned grid = (unsigned)(1 + n_rows - a.n_head);
+    const int da = a.lane[0].D, dpli = a.lane[1].D / 64;
+    switch (da) {
+      case 64: launch_r4_a<1, 1>(a, dpli, grid, stream); break;
+      case 128: launch_r4_a<1, 2>(a, dpli, grid, stream); break;
+      case 256: launch_r4_a<2, 2>(a, dpli, grid, stream); break;
+      default: launch_r4_a<4, 2>(a, dpli, grid, stream); break;
+    }
+  } else if (phase == 0) {
+    if (n_rows > 0) {
+      const unsigned grid = (unsigned)(n_rows * (a.lane[0].D / 64) * 2);
+      hipLaunchKernelGGL(pool_r128_partial_kernel, dim3(grid), dim3(256), 0, stream, a);
     }
   } else {
-    const int S = a.lane[0].D / 64;
-    const int64_t grid = n_rows == 0 ? 1 : n_rows * S;
-    switch (S) {
-      case 1: hipLaunchKernelGGL((pool_r128_kernel<1>), dim3((unsigned)grid), dim3(kPoolThreads), 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((pool_r128_kernel<2>), dim3((unsigned)grid), dim3(kPoolThreads), 0, stream, a); break;
-      case 4: hipLaunchKernelGGL((pool_r128_kernel<4>), dim3((unsigned)grid), dim3(kPoolThreads), 0, stream, a); break;
-      default: hipLaunchKernelGGL((pool_r128_kernel<8>), dim3((unsigned)grid), dim3(kPoolThreads), 0, stream, a); break;
+    const unsigned grid = (unsigned)(n_rows > 0 ? (n_rows + 3) / 4 : 1);
+    switch (a.lane[0].D / 64) {
+      case 1: hipLaunchKernelGGL((pool_r128_finish_kernel<1>), dim3(grid), dim3(256), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((pool_r128_finish_kernel<2>), dim3(grid), dim3(256), 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((pool_r128_finish_kernel<4>), dim3(grid), dim3(256), 0, stream, a); break;
+      default: hipLaunchKernelGGL((pool_r128_finish_kernel<8>), dim3(grid), dim3(256), 0, stream, a); break;
     }
   }
   return hipGetLastError();
 }
 
 hipError_t launch_fill(const FillArgs& f, hipStream_t stream) {
-  hipLaunchKernelGGL(frontier_fill_kernel, dim3(64), dim3(kPoolThreads), 0, stream, f);
+  hipLaunchKernelGGL(frontier_fill_kernel, dim3(64), dim3(256), 0, stream, f);
   return hipGetLastError();
 }
 

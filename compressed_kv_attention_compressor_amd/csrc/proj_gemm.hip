@@ -93,8 +93,6 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
   __shared__ u32x4 smem[3 * kStage];
 
   const int t = threadIdx.x;
-  if (blockIdx.x == 0)
-    for (int i = t; i < a.n_zero; i += kThreads) a.zero_ptr[i] = 0u;
 
   const int n_tiles = tiles_m * tiles_n;
   const int b = blockIdx.x;

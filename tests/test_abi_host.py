@@ -61,8 +61,8 @@ def test_sizes():
     assert B.ds4c_frontier_blob_bytes(L) == 56 + 2 * 8 * 1024 * 4 + 2 * 8 * 256 * 4
     L3 = make_layer(ratio=128)
     assert B.ds4c_frontier_bytes(L3) == 256 + 2 * 128 * 512 * 4
-    # projection + pooled rows [33, 512] + tickets, each 256-aligned
-    ws = 4096 * 1024 * 4 + ((33 * 512 * 4 + 255) // 256) * 256 + 256
+    # projection + pool partials [33 rows, 2 halves, 3, 512], 256-aligned
+    ws = 4096 * 1024 * 4 + ((33 * 2 * 3 * 512 * 4 + 255) // 256) * 256
     assert B.ds4c_workspace_bytes(L3, 4096) == ws
     assert B.ds4c_frontier_bytes(make_layer(ratio=3)) == 0
 
