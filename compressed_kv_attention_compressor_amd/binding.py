@@ -54,6 +54,12 @@ SIGNATURES.update({
                                          c_void_p, c_void_p, c_void_p]),
     "ds4c_frontier_save": (c_int, [_LP, _FP, c_void_p, c_size_t, POINTER(c_size_t), c_void_p]),
     "ds4c_frontier_load": (c_int, [_LP, _FP, c_void_p, c_size_t, c_void_p]),
+    "ds4c_stack_workspace_bytes": (c_size_t, [_LP, c_int, c_int64]),
+    "ds4c_compress_stack_prefill": (c_int, [_LP, c_int, _FP, c_void_p, c_int64, c_int64, POINTER(c_void_p),
+                                            POINTER(c_int64), POINTER(c_void_p), POINTER(c_int64), c_void_p,
+                                            c_size_t, c_void_p]),
+    "ds4c_compress_stack_decode_one": (c_int, [_LP, c_int, _FP, c_void_p, POINTER(c_void_p), POINTER(c_int64),
+                                               POINTER(c_void_p), POINTER(c_int64), c_void_p]),
     "ds4c_layer_ratio": (c_int, [c_int, c_int]),
     "ds4c_prefill_chunk_cap": (c_int64, [c_int64, c_int64]),
     "ds4c_status_str": (ctypes.c_char_p, [c_int]),
@@ -145,6 +151,32 @@ def ds4c_frontier_load(layer: Layer, frontier: Frontier, blob: bytes, stream: in
     buf = ctypes.create_string_buffer(bytes(blob), len(blob))
     return _ok(lib().ds4c_frontier_load(ctypes.byref(layer), ctypes.byref(frontier), buf, len(blob), stream),
                "ds4c_frontier_load")
+
+
+def ds4c_stack_workspace_bytes(layers, chunk_cap: int) -> int:
+    """layers: a ctypes array of Layer."""
+    return lib().ds4c_stack_workspace_bytes(layers, len(layers), chunk_cap)
+
+
+def _ptr_arrays(attn_rows, attn_cap, index_rows, index_cap):
+    n = len(attn_rows)
+    return ((c_void_p * n)(*attn_rows), (c_int64 * n)(*attn_cap),
+            (c_void_p * n)(*index_rows), (c_int64 * n)(*index_cap))
+
+
+def ds4c_compress_stack_prefill(layers, frontiers, x: int, T: int, chunk_cap: int, attn_rows, attn_cap,
+                                index_rows, index_cap, workspace: int, ws_bytes: int, stream: int = 0) -> int:
+    """layers / frontiers: ctypes arrays; the row arguments: one entry per layer (0 where unused)."""
+    ar, ac, ir, ic = _ptr_arrays(attn_rows, attn_cap, index_rows, index_cap)
+    return _ok(lib().ds4c_compress_stack_prefill(layers, len(layers), frontiers, x, T, chunk_cap, ar, ac, ir, ic,
+                                                 workspace, ws_bytes, stream), "ds4c_compress_stack_prefill")
+
+
+def ds4c_compress_stack_decode_one(layers, frontiers, x: int, attn_rows, attn_cap, index_rows, index_cap,
+                                   stream: int = 0) -> int:
+    ar, ac, ir, ic = _ptr_arrays(attn_rows, attn_cap, index_rows, index_cap)
+    return _ok(lib().ds4c_compress_stack_decode_one(layers, len(layers), frontiers, x, ar, ac, ir, ic, stream),
+               "ds4c_compress_stack_decode_one")
 
 
 def ds4c_layer_ratio(variant: int, layer: int) -> int:

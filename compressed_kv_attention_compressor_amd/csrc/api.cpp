@@ -499,6 +499,112 @@ int ds4c_frontier_load(const ds4c_layer* layer, ds4c_frontier* frontier, const v
   }
 }
 
+size_t ds4c_stack_workspace_bytes(const ds4c_layer* layers, int n_layers, int64_t chunk_cap) {
+  if (!layers || n_layers <= 0 || chunk_cap <= 0 || chunk_cap > kMaxTokensPerCall) return 0;
+  size_t need = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if (layers[l].ratio == 0) continue;
+    Shape s;
+    if (check_layer(&layers[l], &s)) return 0;
+    const size_t b = workspace_layout(s, chunk_cap).total;
+    need = b > need ? b : need;
+  }
+  return need;
+}
+
+int ds4c_compress_stack_prefill(const ds4c_layer* layers, int n_layers, ds4c_frontier* frontiers, const void* x,
+                                int64_t T, int64_t chunk_cap, float* const* attn_rows, const int64_t* attn_cap,
+                                float* const* index_rows, const int64_t* index_cap, void* workspace,
+                                size_t ws_bytes, void* stream) {
+  try {
+    if (!layers || !frontiers || n_layers <= 0 || !attn_rows || !attn_cap || !index_rows || !index_cap)
+      return DS4C_EINVAL;
+    if (T < 0) return DS4C_EINVAL;
+    if (chunk_cap <= 0) chunk_cap = ds4c_prefill_chunk_cap(T, 0);
+    if (chunk_cap > kMaxTokensPerCall) return DS4C_ESHAPE;
+    // Validate every compressed layer for the whole run before enqueueing.
+    int64_t n0 = -1;
+    int n_comp_layers = 0;
+    for (int l = 0; l < n_layers; ++l) {
+      if (layers[l].ratio == 0) continue;
+      Shape s;
+      int st = check_layer(&layers[l], &s);
+      if (st) return st;
+      st = check_frontier(s, &frontiers[l]);
+      if (st) return st;
+      if (n0 < 0) n0 = frontiers[l].n_tokens;
+      if (frontiers[l].n_tokens != n0) return DS4C_EPOS;
+      const int64_t k_lo = n0 / s.ratio, k_hi = (n0 + T) / s.ratio;
+      st = check_rows(s, k_hi, k_hi - k_lo, attn_rows[l], attn_cap[l], index_rows[l], index_cap[l], nullptr,
+                      nullptr);
+      if (st) return st;
+      ++n_comp_layers;
+    }
+    if (n_comp_layers == 0 || T == 0) return DS4C_OK;
+    if (!x || !aligned(x, 16)) return DS4C_EINVAL;
+    const int64_t chunk = chunk_cap < T ? chunk_cap : T;
+    if (!workspace || !aligned(workspace, 256)) return DS4C_EINVAL;
+    if (ws_bytes < ds4c_stack_workspace_bytes(layers, n_layers, chunk)) return DS4C_ECAP;
+    // All layers read the same x: its row size is the first compressed layer's.
+    size_t row_bytes = 0;
+    for (int l = 0; l < n_layers; ++l) {
+      if (layers[l].ratio == 0) continue;
+      const size_t b = size_t(layers[l].hidden) * (layers[l].in_dtype == DS4C_BF16 ? 2 : 4);
+      if (row_bytes == 0) row_bytes = b;
+      if (b != row_bytes) return DS4C_ESHAPE;
+    }
+    for (int64_t t0 = 0; t0 < T; t0 += chunk) {
+      const int64_t tc = T - t0 < chunk ? T - t0 : chunk;
+      const void* xc = static_cast<const char*>(x) + size_t(t0) * row_bytes;
+      for (int l = 0; l < n_layers; ++l) {
+        if (layers[l].ratio == 0) continue;
+        const int st = ds4c_compress_prefill(&layers[l], &frontiers[l], xc, tc, attn_rows[l], attn_cap[l],
+                                             index_rows[l], index_cap[l], workspace, ws_bytes, nullptr, nullptr,
+                                             stream);
+        if (st) return st;  // only a HIP failure can get here
+      }
+    }
+    return DS4C_OK;
+  } catch (...) {
+    return DS4C_EDEVICE;
+  }
+}
+
+int ds4c_compress_stack_decode_one(const ds4c_layer* layers, int n_layers, ds4c_frontier* frontiers,
+                                   const void* x, float* const* attn_rows, const int64_t* attn_cap,
+                                   float* const* index_rows, const int64_t* index_cap, void* stream) {
+  try {
+    if (!layers || !frontiers || n_layers <= 0 || !attn_rows || !attn_cap || !index_rows || !index_cap)
+      return DS4C_EINVAL;
+    int64_t n0 = -1;
+    for (int l = 0; l < n_layers; ++l) {
+      if (layers[l].ratio == 0) continue;
+      Shape s;
+      int st = check_layer(&layers[l], &s);
+      if (st) return st;
+      st = check_frontier(s, &frontiers[l]);
+      if (st) return st;
+      if (n0 < 0) n0 = frontiers[l].n_tokens;
+      if (frontiers[l].n_tokens != n0) return DS4C_EPOS;
+      const int64_t k_hi = (n0 + 1) / s.ratio;
+      st = check_rows(s, k_hi, k_hi - n0 / s.ratio, attn_rows[l], attn_cap[l], index_rows[l], index_cap[l],
+                      nullptr, nullptr);
+      if (st) return st;
+    }
+    if (n0 < 0) return DS4C_OK;
+    if (!x || !aligned(x, 16)) return DS4C_EINVAL;
+    for (int l = 0; l < n_layers; ++l) {
+      if (layers[l].ratio == 0) continue;
+      const int st = ds4c_compress_decode_one(&layers[l], &frontiers[l], x, attn_rows[l], attn_cap[l],
+                                              index_rows[l], index_cap[l], nullptr, nullptr, stream);
+      if (st) return st;
+    }
+    return DS4C_OK;
+  } catch (...) {
+    return DS4C_EDEVICE;
+  }
+}
+
 int ds4c_layer_ratio(int variant, int layer) {
   if ((variant != 0 && variant != 1) || layer < 0) return -1;
   if (layer < 2) return variant == 0 ? 0 : 128;

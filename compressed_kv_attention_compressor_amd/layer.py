@@ -138,3 +138,69 @@ class CompressorLayer:
 
     def load(self, blob: bytes) -> None:
         B.ds4c_frontier_load(self.layer, self.frontier, blob, self.stream())
+
+
+class CompressorStack:
+    """A stack of compressed layers driven by the native stack entry points.
+
+    ``layers[l]`` is a CompressorLayer, or None for an uncompressed layer
+    (ratio 0).  The chunk and layer loops run inside the library.
+    """
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        n = len(self.layers)
+        self.c_layers = (B.Layer * n)()
+        self.c_front = (B.Frontier * n)()
+        for i, L in enumerate(self.layers):
+            if L is None:
+                self.c_layers[i].ratio = 0
+            else:
+                self.c_layers[i] = L.layer
+        self._ws: Optional[torch.Tensor] = None
+        self._ws_chunk = 0
+
+    def _arrays(self):
+        ar = [L.rows["attn"].data_ptr() if L else 0 for L in self.layers]
+        ac = [L.cap if L else 0 for L in self.layers]
+        ir = [L.rows["index"].data_ptr() if L and "index" in L.rows else 0 for L in self.layers]
+        ic = [L.cap if L and "index" in L.rows else 0 for L in self.layers]
+        return ar, ac, ir, ic
+
+    def _push(self):
+        for i, L in enumerate(self.layers):
+            if L is not None:
+                self.c_front[i] = L.frontier
+
+    def _pull(self):
+        for i, L in enumerate(self.layers):
+            if L is not None:
+                f = self.c_front[i]
+                L.frontier.n_tokens, L.frontier.n_comp, L.frontier.n_index_comp = f.n_tokens, f.n_comp, f.n_index_comp
+
+    def reserve(self, chunk: int) -> None:
+        need = B.ds4c_stack_workspace_bytes(self.c_layers, chunk)
+        if self._ws is None or self._ws.numel() < need:
+            dev = next(L.device for L in self.layers if L is not None)
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def prefill(self, x: torch.Tensor, chunk_cap: int = 0) -> None:
+        T = x.shape[0]
+        chunk = chunk_cap if chunk_cap > 0 else B.ds4c_prefill_chunk_cap(T, 0)
+        self.reserve(min(chunk, max(T, 1)))
+        self._push()
+        ar, ac, ir, ic = self._arrays()
+        try:
+            B.ds4c_compress_stack_prefill(self.c_layers, self.c_front, x.data_ptr(), T, chunk, ar, ac, ir, ic,
+                                          self._ws.data_ptr(), self._ws.numel(), CompressorLayer.stream())
+        finally:
+            self._pull()
+
+    def decode_one(self, x: torch.Tensor) -> None:
+        self._push()
+        ar, ac, ir, ic = self._arrays()
+        try:
+            B.ds4c_compress_stack_decode_one(self.c_layers, self.c_front, x.data_ptr(), ar, ac, ir, ic,
+                                             CompressorLayer.stream())
+        finally:
+            self._pull()

@@ -176,6 +176,34 @@ int ds4c_frontier_save(const ds4c_layer *layer, const ds4c_frontier *frontier,
 int ds4c_frontier_load(const ds4c_layer *layer, ds4c_frontier *frontier,
                        const void *host_buf, size_t len, void *stream);
 
+/* A stack of layers (Part 3 §1: Flash layers 0-1 are uncompressed, then
+ * ratio 4 and 128 alternate; §3: long prompts are prefilled in chunks of at
+ * most 4096 tokens so windows stay on absolute positions).  Entry l of every
+ * array belongs to layer l; a layer whose ratio is 0 has no compressor and
+ * is skipped (its frontier and row entries are ignored and may be NULL).
+ * Every layer reads the same x: the caller supplies each layer's input.
+ *
+ * ds4c_stack_workspace_bytes: workspace for chunks of up to chunk_cap tokens
+ * (the largest need among the compressed layers).  0 if a descriptor is bad.
+ *
+ * ds4c_compress_stack_prefill: tokens x [T, hidden] at the frontiers'
+ * positions, in chunks of chunk_cap (<= 0: ds4c_prefill_chunk_cap(T, 0));
+ * for each chunk every layer in order.  All layers and the final row counts
+ * are validated before anything is enqueued (same errors as
+ * ds4c_compress_prefill; the frontiers must all be at the same position,
+ * else DS4C_EPOS).  Asynchronous on `stream`.
+ *
+ * ds4c_compress_stack_decode_one: one token x [hidden] through every layer. */
+size_t ds4c_stack_workspace_bytes(const ds4c_layer *layers, int n_layers, int64_t chunk_cap);
+int ds4c_compress_stack_prefill(const ds4c_layer *layers, int n_layers, ds4c_frontier *frontiers,
+                                const void *x, int64_t T, int64_t chunk_cap,
+                                float *const *attn_rows, const int64_t *attn_cap,
+                                float *const *index_rows, const int64_t *index_cap,
+                                void *workspace, size_t ws_bytes, void *stream);
+int ds4c_compress_stack_decode_one(const ds4c_layer *layers, int n_layers, ds4c_frontier *frontiers,
+                                   const void *x, float *const *attn_rows, const int64_t *attn_cap,
+                                   float *const *index_rows, const int64_t *index_cap, void *stream);
+
 /* Compress ratio of layer `layer` of a 0 = Flash / 1 = Pro model (Part 3
  * §1): Flash layers 0-1 -> 0 (uncompressed), Pro layers 0-1 -> 128; from
  * layer 2 even -> 4, odd -> 128.  -1 for a bad variant or negative layer. */

@@ -63,6 +63,7 @@ from .compressor import (  # noqa: F401
     window_rows,
     live_frontier_rows,
     canonical_frontier,
+    frontier_from_tokens,
     rows_emitted,
 )
 from .schedule import layer_compress_ratio, prefill_chunk_cap  # noqa: F401

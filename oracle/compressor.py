@@ -257,8 +257,9 @@ def window_rows(spec: LayerSpec, lane: LaneSpec, kv_all: np.ndarray,
                 score_all: np.ndarray, ks) -> Tuple[np.ndarray, np.ndarray]:
     """Closed form: rows ``ks`` of a lane straight from their token windows.
 
-    ``kv_all`` / ``score_all`` hold the projections (score without APE) of
-    tokens 0 .. n-1.  Row k of a ratio-128 lane pools tokens 128k .. 128k+127
+    ``kv_all[p]`` / ``score_all[p]`` are the projections (score without APE)
+    of the token at absolute position p: arrays indexed by position, or any
+    mapping holding at least the tokens of the requested windows.  Row k of a ratio-128 lane pools tokens 128k .. 128k+127
     on columns [0, D).  Row k of a ratio-4 lane pools tokens 4k-4 .. 4k-1 on
     columns [0, D) and tokens 4k .. 4k+3 on columns [D, 2D); tokens before 0
     are empty.  Returns (pre-quant rows, final rows), each [len(ks), D].
@@ -276,8 +277,8 @@ def window_rows(spec: LayerSpec, lane: LaneSpec, kv_all: np.ndarray,
             if p < 0:
                 continue
             c0 = d if (r == 4 and i >= 4) else 0
-            ekv[i] = kv_all[p, c0:c0 + d]
-            esc[i] = score_all[p, c0:c0 + d] + lane.ape[p % r, c0:c0 + d]
+            ekv[i] = kv_all[p][c0:c0 + d]
+            esc[i] = score_all[p][c0:c0 + d] + lane.ape[p % r, c0:c0 + d]
         o = softmax_pool(ekv, esc)
         y, final = finish_row(spec, lane, o, k)
         pre.append(y)
@@ -323,3 +324,23 @@ def canonical_frontier(spec: LayerSpec, state: LayerState):
             sc[row] = st.score[row]
         out[lane.kind] = (kv, sc)
     return out
+
+
+def frontier_from_tokens(spec: LayerSpec, n: int, kv_all, score_all):
+    """Closed form of the canonical state after n tokens (Part 3 §5, Part 4 §7).
+
+    Live row i holds the token live_frontier_rows assigns to it: its full
+    W-wide kv and its score plus APE[p % ratio]; every other row is (0, -inf).
+    ``kv_all[p]`` / ``score_all[p]`` as for ``window_rows``.
+    """
+    out = {}
+    for lane in spec.lanes():
+        shape = (spec.coff * spec.ratio, spec.coff * lane.head_dim)
+        kv = np.zeros(shape)
+        sc = np.full(shape, -np.inf)
+        for row, p in live_frontier_rows(spec.ratio, n):
+            kv[row] = kv_all[lane.kind][p]
+            sc[row] = score_all[lane.kind][p] + lane.ape[p % spec.ratio]
+        out[lane.kind] = (kv, sc)
+    return out
+

@@ -64,9 +64,18 @@ def check_codec_blocks(g_final: np.ndarray, o_final: np.ndarray, g_pre: np.ndarr
         for b0 in range(0, o_final.shape[1], block):
             sl = slice(b0, b0 + block)
             amax_o = float(np.max(np.abs(np.asarray(o_pre[r, sl], np.float32))))
-            amax_g = float(np.max(np.abs(np.asarray(g_pre[r, sl], np.float32))))
             ko = codecs.pow2_block_exponent(amax_o, qmax)
-            kg = codecs.pow2_block_exponent(amax_g, qmax)
+            if g_pre is not None:
+                amax_g = float(np.max(np.abs(np.asarray(g_pre[r, sl], np.float32))))
+                kg = codecs.pow2_block_exponent(amax_g, qmax)
+            else:
+                # No GPU pre-codec values: the GPU exponent is taken to be the
+                # oracle's unless the block sits within tolerance of a boundary.
+                kg = ko
+                for kk in (ko - 1, ko + 1):
+                    edge = math.ldexp(qmax, min(kk, ko))
+                    if abs(amax_o - edge) <= REL_TOL * edge:
+                        kg = kk
             gv, ov = g_final[r, sl], o_final[r, sl]
             if ko == kg:
                 dg = _ordered(enc(np.ldexp(gv, -ko)), sign)
@@ -94,12 +103,17 @@ def check_attn_rows(g_final, o_final, g_pre, o_pre, n_rot: int, what: str = "att
     check_prequant(g_final[:, nq:], o_final[:, nq:], what + " (RoPE tail)")
     if nq == 0:
         return 0
-    return check_codec_blocks(g_final[:, :nq], o_final[:, :nq], g_pre[:, :nq], o_pre[:, :nq], 64, "e4m3", what)
+    gp = None if g_pre is None else g_pre[:, :nq]
+    return check_codec_blocks(g_final[:, :nq], o_final[:, :nq], gp, o_pre[:, :nq], 64, "e4m3", what)
 
 
 def check_index_rows(g_final, o_final, g_pre, o_pre, what: str = "index rows") -> int:
+    """g_pre may be None (no GPU pre-codec rows); see check_codec_blocks."""
     d = o_final.shape[1]
-    zg = np.stack([codecs.wht_normalized(row) for row in np.asarray(g_pre, np.float64)]) if len(g_pre) else g_pre
+    if g_pre is None:
+        zg = None
+    else:
+        zg = np.stack([codecs.wht_normalized(row) for row in np.asarray(g_pre, np.float64)]) if len(g_pre) else g_pre
     zo = np.stack([codecs.wht_normalized(row) for row in np.asarray(o_pre, np.float64)]) if len(o_pre) else o_pre
     if len(o_final) == 0:
         return 0

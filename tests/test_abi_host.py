@@ -48,7 +48,7 @@ def frontier(n=0, ratio=4):
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 16
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B.SIGNATURES), "binding and header disagree"
@@ -201,3 +201,63 @@ def test_profile_read_without_records():
     ms, cnt = B.ds4c_profile_read()
     assert ms == [0.0] * 4 and cnt == [0] * 4
     B.ds4c_profile_enable(False)
+
+
+def _stack(n=4):
+    layers = (B.Layer * n)()
+    fronts = (B.Frontier * n)()
+    for i in range(n):
+        r = B.ds4c_layer_ratio(0, i)
+        if r == 0:
+            layers[i].ratio = 0
+            continue
+        layers[i] = make_layer(ratio=r)
+        f = frontier(n=0, ratio=r)
+        f.state = FAKE + 0x10000000 + i * 0x1000000
+        fronts[i] = f
+    return layers, fronts
+
+
+def _stack_call(layers, fronts, T=64, cap=10**6, ws=None, x=FAKE + 0x20000000):
+    n = len(layers)
+    ar = (ctypes.c_void_p * n)(*[FAKE + 0x30000000 if layers[i].ratio else 0 for i in range(n)])
+    ac = (ctypes.c_int64 * n)(*[cap] * n)
+    ir = (ctypes.c_void_p * n)(*[FAKE + 0x40000000 if layers[i].ratio == 4 else 0 for i in range(n)])
+    ic = (ctypes.c_int64 * n)(*[cap if layers[i].ratio == 4 else 0 for i in range(n)])
+    wsb = B.ds4c_stack_workspace_bytes(layers, min(T, 4096) or 1) if ws is None else ws
+    return B.lib().ds4c_compress_stack_prefill(layers, n, fronts, x, T, 0, ar, ac, ir, ic,
+                                               FAKE + 0x50000000, wsb, None)
+
+
+def test_stack_workspace_is_the_largest_layer_need():
+    layers, _ = _stack(4)  # ratios 0, 0, 4, 128
+    assert B.ds4c_stack_workspace_bytes(layers, 4096) == max(
+        B.ds4c_workspace_bytes(make_layer(ratio=4), 4096), B.ds4c_workspace_bytes(make_layer(ratio=128), 4096))
+    layers[2].ratio = 5
+    assert B.ds4c_stack_workspace_bytes(layers, 4096) == 0
+
+
+def test_stack_prefill_validates_everything_first():
+    layers, fronts = _stack(4)
+    fronts[3].n_tokens = 128  # ratio-128 layer ahead of the ratio-4 layer
+    fronts[3].n_comp = 1
+    assert _stack_call(layers, fronts) == B.DS4C_EPOS
+    assert fronts[2].n_tokens == 0 and fronts[3].n_tokens == 128
+    layers, fronts = _stack(4)
+    assert _stack_call(layers, fronts, T=400, cap=99) == B.DS4C_ECAP     # 100 rows needed on the ratio-4 layer
+    assert _stack_call(layers, fronts, T=64, ws=1024) == B.DS4C_ECAP
+    assert _stack_call(layers, fronts, T=0) == B.DS4C_OK
+    layers[3].attn.head_dim = 100
+    assert _stack_call(layers, fronts) == B.DS4C_ESHAPE
+    for i in range(4):
+        assert fronts[i].n_tokens == 0
+    # a stack with no compressed layer is a no-op
+    none = (B.Layer * 2)()
+    nf = (B.Frontier * 2)()
+    assert _stack_call(none, nf) == B.DS4C_OK
+
+
+def test_stack_rejects_layers_with_different_input_rows():
+    layers, fronts = _stack(6)  # ratios 0, 0, 4, 128, 4, 128
+    layers[5].hidden = 2048
+    assert _stack_call(layers, fronts) == B.DS4C_ESHAPE

@@ -413,3 +413,31 @@ def test_brute_force_tiny(ratio, n, hidden):
         # a value sits within rounding of a code boundary (none at these seeds)
         assert got.shape == brute[kind].shape
         assert np.allclose(got, brute[kind], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("ratio", [4, 128])
+@pytest.mark.parametrize("n", [0, 1, 3, 4, 7, 8, 127, 128, 131, 300])
+def test_frontier_closed_form_matches_recurrence(ratio, n):
+    spec = tiny_spec(ratio, 32, 128, 64, seed=11)
+    x = np.random.default_rng(20).normal(0, 1, (max(n, 1), 32))[:n]
+    st = _run(spec, x) if n else C.new_layer_state(spec)
+    proj = _projections(spec, x) if n else {l.kind: (np.zeros((0, 256)), np.zeros((0, 256))) for l in spec.lanes()}
+    closed = C.frontier_from_tokens(spec, n, {k: v[0] for k, v in proj.items()}, {k: v[1] for k, v in proj.items()})
+    canon = C.canonical_frontier(spec, st)
+    for kind in canon:
+        assert np.array_equal(closed[kind][0], canon[kind][0])
+        assert np.array_equal(closed[kind][1], canon[kind][1])
+
+
+def test_window_rows_accepts_sparse_token_maps():
+    spec = tiny_spec(4, 32, 128, 64, seed=12)
+    x = np.random.default_rng(21).normal(0, 1, (40, 32))
+    proj = _projections(spec, x)
+    lane = spec.attn
+    kv, sc = proj["attn"]
+    k = 7
+    sparse_kv = {p: kv[p] for p in range(4 * k - 4, 4 * k + 4)}
+    sparse_sc = {p: sc[p] for p in range(4 * k - 4, 4 * k + 4)}
+    a = C.window_rows(spec, lane, kv, sc, [k])
+    b = C.window_rows(spec, lane, sparse_kv, sparse_sc, [k])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
