@@ -1,17 +1,29 @@
 """Throughput of the compressed-KV compressor on one MI355X.
 
-A step is one ds4c_compress_prefill call over one 4096-token chunk of a
-layer (projection GEMM + fused store/pool/norm/RoPE/codec/append/frontier
-kernel), starting at position 0 each time (the frontier counters are reset on
-the host; a call at position 0 reads nothing from the frontier).  Inputs are
-resident in HBM before timing.  Prints one JSON line.
+Workloads (--workload):
+  r4_flash    (default) one Flash ratio-4 layer, one 4096-token chunk, hidden 4096,
+              head_dim 512, indexer head_dim 128, bf16.  A step is one
+              ds4c_compress_prefill call: projection GEMM + fused pool kernel.
+  r128_flash  the same for a ratio-128 layer (head_dim 512).
+  stack32     the 32-layer Flash stack (30 compressed layers), one 4096-token
+              chunk: a step is one ds4c_compress_stack_prefill call.
+  stack32_long the stack over a 65536-token prompt in 16 chunks of 4096, then
+              256 ds4c_compress_stack_decode_one steps: a step is all of it.
 
-  python bench.py [--steps K] [--warmup W] [--workload r4_flash|r128_flash]
+Every step starts from position 0 (the frontier counters are reset on the
+host; a call at position 0 reads nothing from the frontier).  Inputs are
+resident in HBM before timing.  Kernel times come from events the dispatch
+itself records around each kernel (the library's timing mode), over the
+timed region.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME]
+  python bench.py --copy-mib N     plain device copy of N MiB (counter calibration)
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -21,41 +33,63 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+METRIC = "compressor tokens/sec + compressed rows/sec; % HBM and MFMA peak (1 GPU)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+GEMM_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", "proj_gemm.hip")
 
 
-def algorithmic(shape, T):
-    """GEMM flops and pool-kernel bytes of one call at position 0."""
+def layer_algorithmic(shape, n0, T):
+    """GEMM flops and pool-kernel bytes of one prefill call (tokens n0 .. n0+T-1).
+
+    Pool bytes: every projected kv/score element read once, the APE table,
+    the rows written, and the live frontier rows written after the call.
+    """
     lanes = [shape.d_attn] + ([shape.d_index] if shape.d_index else [])
     W = [shape.coff * d for d in lanes]
     N = 2 * sum(W)
     flops = 2.0 * T * N * shape.hidden
-    n = T
-    n_emit = T // shape.ratio
+    n = n0 + T
+    n_emit = n // shape.ratio - n0 // shape.ratio
     c = n % shape.ratio
     m = n - c
-    if shape.ratio == 4:
-        live = (4 if m >= 4 else 0) + c
-    else:
-        live = c
-    bytes_ = (T * N * 4                                  # kv + score read once
-              + shape.ratio * sum(W) * 4                  # APE
-              + n_emit * sum(lanes) * 4                   # rows written
-              + live * sum(W) * 2 * 4)                    # frontier written
-    return flops, bytes_, n_emit * len(lanes), N
+    live = ((4 if m >= 4 else 0) + c) if shape.ratio == 4 else c
+    pool_bytes = T * N * 4 + shape.ratio * sum(W) * 4 + n_emit * sum(lanes) * 4 + live * sum(W) * 2 * 4
+    return flops, pool_bytes, n_emit * len(lanes), N
 
 
-def cpu_baseline(workload, x, params, budget_s=12.0):
-    """The oracle as it is, timed on this host over whole 4096-token steps."""
-    import numpy as np
+def read_traffic(workload: str):
+    """HBM bytes per GEMM launch from the committed counter summary, or None.
+
+    The summary names the sha256 of the projection kernel source it was taken
+    on; a different source means the counters are stale and none is used.
+    """
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if kv.get("gemm_source_sha256") != src:
+        return None
+    try:
+        return float(kv["gemm_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(shape, x, params, budget_s=12.0):
+    """The oracle as it is, timed on this host over whole prefill steps of the layer."""
     from threadpoolctl import threadpool_info
 
     import oracle
     from tests._helpers import oracle_spec
 
-    spec = oracle_spec(workload.layer, params)
+    spec = oracle_spec(shape, params)
     steps, t0 = 0, time.perf_counter()
     while True:
         st = oracle.new_layer_state(spec)
@@ -66,51 +100,113 @@ def cpu_baseline(workload, x, params, budget_s=12.0):
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": steps * len(x) / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{steps} full {len(x)}-token prefill steps of the same layer ({el:.1f} s); "
-                      f"float64 NumPy, BLAS threads {threads}, Python recurrence single-threaded"}
+            "sample": f"{steps} full {len(x)}-token prefill steps of one ratio-{shape.ratio} layer "
+                      f"({el:.1f} s); float64 NumPy, BLAS threads {threads}, recurrence single-threaded"}
+
+
+def copy_calibration(mib: int, reps: int = 20) -> None:
+    import torch
+
+    n = mib * 1024 * 1024 // 4
+    a = torch.randn(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    print(json.dumps({"copy_mib": mib, "bytes_read_per_launch": mib * 2 ** 20,
+                      "bytes_written_per_launch": mib * 2 ** 20, "reps": reps, "us_per_copy": el / reps * 1e6}),
+          flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="r4_flash", choices=["r4_flash", "r128_flash"])
+    ap.add_argument("--steps", type=int, default=0, help="timed steps (default depends on the workload)")
+    ap.add_argument("--warmup", type=int, default=-1)
+    ap.add_argument("--workload", default="r4_flash", choices=["r4_flash", "r128_flash", "stack32", "stack32_long"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)",
-              file=sys.stderr)
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_mib:
+        copy_calibration(args.copy_mib)
+        return
 
     import torch
 
     from compressed_kv_attention_compressor_amd import binding as B
     from compressed_kv_attention_compressor_amd import synth
-    from compressed_kv_attention_compressor_amd.layer import CompressorLayer
+    from compressed_kv_attention_compressor_amd.layer import CompressorLayer, CompressorStack
 
     w = synth.WORKLOADS[args.workload]
-    shape, T = w.layer, w.tokens
-    params = synth.layer_params(w.wid, 0, shape)
-    x_np = synth.hidden_states(w.wid, shape.hidden, 0, T, shape.dtype)
-    layer = CompressorLayer(shape.ratio, shape.hidden, params, dtype=shape.dtype, n_rot=shape.n_rot,
-                            rope_base=shape.rope_base, rms_eps=shape.rms_eps, max_tokens=T)
-    x = torch.from_numpy(x_np).to("cuda", torch.bfloat16 if shape.dtype == "bf16" else torch.float32)
-    layer.reserve(T)
-    flops, pool_bytes, rows_per_step, N = algorithmic(shape, T)
+    long_run = args.workload == "stack32_long"
+    steps = args.steps or (3 if long_run else 20 if w.layer is None else 50)
+    warmup = args.warmup if args.warmup >= 0 else (1 if long_run else 5)
+    T, Td = w.tokens, w.decode_tokens
 
-    def step():
-        f = layer.frontier
-        f.n_tokens = f.n_comp = f.n_index_comp = 0
-        layer.prefill(x)
+    if w.layer is not None:
+        shapes = [(0, w.layer)]
+        params = {0: synth.layer_params(w.wid, 0, w.layer)}
+    else:
+        shapes = [(l, synth.stack_layer_shape(B.ds4c_layer_ratio(0, l))) for l in range(w.n_layers)]
+        params = {l: synth.layer_params(w.wid, l, s) for l, s in shapes if s is not None}
+    hidden = 4096 if w.layer is None else w.layer.hidden
+    dtype = "bf16" if w.layer is None else w.layer.dtype
+    x_np = synth.hidden_states(w.wid, hidden, 0, T + Td, dtype)
+    x = torch.from_numpy(x_np).to("cuda", torch.bfloat16 if dtype == "bf16" else torch.float32)
+    layers = [None if s is None else
+              CompressorLayer(s.ratio, s.hidden, params[l], dtype=s.dtype, n_rot=s.n_rot, rope_base=s.rope_base,
+                              rms_eps=s.rms_eps, max_tokens=T + Td) for l, s in shapes]
 
-    for _ in range(args.warmup):
+    # Algorithmic work of one step.
+    flops = pool_bytes = 0.0
+    rows = 0
+    gemm_launches = 0
+    chunk = min(T, 4096)
+    for (l, s), L in zip(shapes, layers):
+        if s is None:
+            continue
+        for t0 in range(0, T, chunk):
+            f, pb, r_, _ = layer_algorithmic(s, t0, min(chunk, T - t0))
+            flops, pool_bytes, rows = flops + f, pool_bytes + pb, rows + r_
+            gemm_launches += 1
+        rows += ((T + Td) // s.ratio - T // s.ratio) * (2 if s.ratio == 4 else 1)
+
+    if w.layer is not None:
+        L = layers[0]
+        L.reserve(T)
+
+        def step():
+            f = L.frontier
+            f.n_tokens = f.n_comp = f.n_index_comp = 0
+            L.prefill(x[:T])
+    else:
+        stack = CompressorStack(layers)
+        stack.reserve(chunk)
+
+        def step():
+            for L in layers:
+                if L is not None:
+                    f = L.frontier
+                    f.n_tokens = f.n_comp = f.n_index_comp = 0
+            stack.prefill(x[:T], chunk_cap=chunk)
+            for i in range(Td):
+                stack.decode_one(x[T + i])
+
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     B.ds4c_profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
@@ -119,37 +215,60 @@ def main():
 
     gemm_ms = ms[B.KCLASS_PROJ] / max(cnt[B.KCLASS_PROJ], 1)
     pool_ms = ms[B.KCLASS_POOL] / max(cnt[B.KCLASS_POOL], 1)
-    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    pool_gbs = pool_bytes / (pool_ms * 1e-3) / 1e9
-    peak = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_FP32_TFLOPS
-    tokens_per_s = args.steps * T / el
+    flops_per_launch = flops / max(gemm_launches, 1)
+    pool_bytes_per_launch = pool_bytes / max(gemm_launches, 1)
+    gemm_tflops = flops_per_launch / (gemm_ms * 1e-3) / 1e12
+    pool_gbs = pool_bytes_per_launch / (pool_ms * 1e-3) / 1e9
+    peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
+    traffic = read_traffic(args.workload)
 
+    cfg = {"workload": w.name, "tokens": T, "decode_tokens": Td, "hidden": hidden, "chunk": chunk,
+           "layers": sum(1 for s in shapes if s[1] is not None), "dtype": dtype}
+    if w.layer is not None:
+        cfg.update({"ratio": w.layer.ratio, "head_dim": w.layer.d_attn, "index_head_dim": w.layer.d_index})
     out = {
-        "metric": "compressor tokens/sec + compressed rows/sec; % HBM and MFMA peak (1 GPU)",
-        "value": tokens_per_s,
+        "metric": METRIC,
+        "value": steps * (T + Td) / el,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": el / args.steps * 1e3,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": el / steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": shape.dtype,
+        "dtype": dtype,
         "data": "synthetic (seeded N(0,1) hidden states, N(0,0.02) weights, N(0,0.1) APE)",
-        "config": {"workload": w.name, "ratio": shape.ratio, "tokens": T, "hidden": shape.hidden,
-                   "head_dim": shape.d_attn, "index_head_dim": shape.d_index, "chunk": T,
-                   "gemm_mnk": [T, N, shape.hidden]},
-        "rows_per_s": args.steps * rows_per_step / el,
+        "config": cfg,
+        "rows_per_s": steps * rows / el,
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": gemm_tflops / peak, "traffic": None, "kernel": "proj_gemm",
-                     "avg_ms": gemm_ms},
+                     "frac": gemm_tflops / peak, "traffic": traffic, "kernel": "proj_mfma_kernel",
+                     "avg_ms": gemm_ms, "algorithmic_flops": flops_per_launch},
         "pool_roofline": {"bound": "hbm", "achieved": pool_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                          "frac": pool_gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "pool",
-                          "avg_ms": pool_ms, "algorithmic_bytes": pool_bytes},
+                          "frac": pool_gbs / PEAK_HBM_GBS, "kernel": "pool (all launches of one call)",
+                          "avg_ms": pool_ms, "algorithmic_bytes": pool_bytes_per_launch},
+        "kernel_launches": {"proj": cnt[B.KCLASS_PROJ], "pool": cnt[B.KCLASS_POOL], "decode": cnt[B.KCLASS_DECODE]},
     }
+    if cnt[B.KCLASS_DECODE]:
+        out["decode_avg_ms"] = ms[B.KCLASS_DECODE] / cnt[B.KCLASS_DECODE]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, x_np, params)
+        n_cpu = min(T, 4096)
+        if w.layer is not None:
+            out["cpu_baseline"] = cpu_baseline(w.layer, x_np[:n_cpu], params[0])
+        else:
+            # Whole-stack rate: time one layer of each ratio on the oracle and
+            # weight by how many layers of each ratio the stack has.
+            per_token_s, parts = 0.0, []
+            for r in (4, 128):
+                l_r = next(l for l, s in shapes if s is not None and s.ratio == r)
+                n_r = sum(1 for _, s in shapes if s is not None and s.ratio == r)
+                b = cpu_baseline(shapes[l_r][1], x_np[:n_cpu], params[l_r], budget_s=6.0)
+                per_token_s += n_r / b["value"]
+                parts.append(f"ratio {r}: {b['value']:.0f} tokens/s per layer x {n_r} layers")
+            out["cpu_baseline"] = {"value": 1.0 / per_token_s, "unit": "tokens/s", "cores": b["cores"],
+                                   "kind": "oracle",
+                                   "sample": f"{n_cpu}-token prefill steps of one layer of each ratio, about 6 s "
+                                             f"each, combined over the stack ({'; '.join(parts)}); float64 NumPy"}
     print(json.dumps(out), flush=True)
 
 

@@ -188,20 +188,18 @@ void release_records() {
   g_prof.clear();
 }
 
+// Runs launch(Timing) and, while timing is on, records the interval of the
+// kernels it enqueues under class `cls`.
 template <class F>
-hipError_t timed(int cls, hipStream_t s, F&& launch) {
+hipError_t timed(int cls, F&& launch) {
   std::unique_lock<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) {
     lk.unlock();
-    return launch();
+    return launch(ds4c::Timing{});
   }
   hipEvent_t a = take_event(), b = take_event();
   if (!a || !b) return hipErrorOutOfMemory;
-  hipError_t e = hipEventRecord(a, s);
-  if (e != hipSuccess) return e;
-  e = launch();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(b, s);
+  const hipError_t e = launch(ds4c::Timing{a, b});
   if (e != hipSuccess) return e;
   g_prof.push_back({cls, a, b});
   return hipSuccess;
@@ -270,7 +268,7 @@ int ds4c_frontier_init(const ds4c_layer* layer, ds4c_frontier* frontier, void* s
     f.ctrl = static_cast<unsigned*>(frontier->state);
     f.n_ctrl = int(kCtrlBytes / sizeof(unsigned));
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    st = dev_status(timed(DS4C_KCLASS_INIT, hs, [&] { return ds4c::launch_fill(f, hs); }));
+    st = dev_status(timed(DS4C_KCLASS_INIT, [&](const ds4c::Timing& tm) { return ds4c::launch_fill(f, hs, tm); }));
     if (st) return st;
     frontier->n_tokens = frontier->n_comp = frontier->n_index_comp = 0;
     return DS4C_OK;
@@ -336,11 +334,14 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
     if (r == 128) po.part = reinterpret_cast<float*>(ws + wl.part);
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    st = dev_status(timed(DS4C_KCLASS_PROJ, hs, [&] { return ds4c::launch_proj(pa, layer->in_dtype, hs); }));
+    st = dev_status(
+        timed(DS4C_KCLASS_PROJ, [&](const ds4c::Timing& tm) { return ds4c::launch_proj(pa, layer->in_dtype, hs, tm); }));
     if (st) return st;
-    st = dev_status(timed(DS4C_KCLASS_POOL, hs, [&] {
+    st = dev_status(timed(DS4C_KCLASS_POOL, [&](const ds4c::Timing& tm) {
+      const int n = ds4c::pool_launches(r);
       hipError_t e = hipSuccess;
-      for (int ph = 0; ph < ds4c::pool_launches(r) && e == hipSuccess; ++ph) e = ds4c::launch_pool(po, ph, hs);
+      for (int ph = 0; ph < n && e == hipSuccess; ++ph)
+        e = ds4c::launch_pool(po, ph, hs, ds4c::Timing{ph == 0 ? tm.start : nullptr, ph == n - 1 ? tm.stop : nullptr});
       return e;
     }));
     if (st) return st;
@@ -390,7 +391,8 @@ int ds4c_compress_decode_one(const ds4c_layer* layer, ds4c_frontier* frontier, c
     d.ticket = static_cast<unsigned*>(frontier->state);
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    st = dev_status(timed(DS4C_KCLASS_DECODE, hs, [&] { return ds4c::launch_decode(d, layer->in_dtype, hs); }));
+    st = dev_status(timed(DS4C_KCLASS_DECODE,
+                          [&](const ds4c::Timing& tm) { return ds4c::launch_decode(d, layer->in_dtype, hs, tm); }));
     if (st) return st;
     frontier->n_tokens = pos + 1;
     frontier->n_comp = k_hi;

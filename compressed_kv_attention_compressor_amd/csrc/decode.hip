@@ -194,35 +194,35 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
 }
 
 template <typename Tin, int A>
-void launch_dec_a(const DecodeArgs& a, int dpli, unsigned grid, hipStream_t s) {
+void launch_dec_a(const DecodeArgs& a, int dpli, unsigned grid, hipStream_t s, const Timing& tm) {
   switch (dpli) {
-    case 1: hipLaunchKernelGGL((decode_kernel<Tin, A, 1>), dim3(grid), dim3(kDecThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<Tin, A, 2>), dim3(grid), dim3(kDecThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<Tin, A, 4>), dim3(grid), dim3(kDecThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_kernel<Tin, A, 8>), dim3(grid), dim3(kDecThreads), 0, s, a); break;
+    case 1: hipExtLaunchKernelGGL((decode_kernel<Tin, A, 1>), dim3(grid), dim3(kDecThreads), 0, s, tm.start, tm.stop, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((decode_kernel<Tin, A, 2>), dim3(grid), dim3(kDecThreads), 0, s, tm.start, tm.stop, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((decode_kernel<Tin, A, 4>), dim3(grid), dim3(kDecThreads), 0, s, tm.start, tm.stop, 0, a); break;
+    default: hipExtLaunchKernelGGL((decode_kernel<Tin, A, 8>), dim3(grid), dim3(kDecThreads), 0, s, tm.start, tm.stop, 0, a); break;
   }
 }
 
 template <typename Tin>
-void launch_dec(const DecodeArgs& a, unsigned grid, hipStream_t s) {
+void launch_dec(const DecodeArgs& a, unsigned grid, hipStream_t s, const Timing& tm) {
   const int dpla = a.lane[0].D / 64;
   const int dpli = a.n_lanes > 1 ? a.lane[1].D / 64 : 1;
   switch (dpla) {
-    case 1: launch_dec_a<Tin, 1>(a, dpli, grid, s); break;
-    case 2: launch_dec_a<Tin, 2>(a, dpli, grid, s); break;
-    case 4: launch_dec_a<Tin, 4>(a, dpli, grid, s); break;
-    default: launch_dec_a<Tin, 8>(a, dpli, grid, s); break;
+    case 1: launch_dec_a<Tin, 1>(a, dpli, grid, s, tm); break;
+    case 2: launch_dec_a<Tin, 2>(a, dpli, grid, s, tm); break;
+    case 4: launch_dec_a<Tin, 4>(a, dpli, grid, s, tm); break;
+    default: launch_dec_a<Tin, 8>(a, dpli, grid, s, tm); break;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, const Timing& tm) {
   const unsigned grid = (unsigned)((a.N + 3) / 4);
   if (in_dtype == 1)
-    launch_dec<uint16_t>(a, grid, stream);
+    launch_dec<uint16_t>(a, grid, stream, tm);
   else
-    launch_dec<float>(a, grid, stream);
+    launch_dec<float>(a, grid, stream, tm);
   return hipGetLastError();
 }
 

@@ -297,13 +297,13 @@ __global__ void __launch_bounds__(256) frontier_fill_kernel(FillArgs f) {
 }
 
 template <int SA, int DPLA>
-void launch_r4_a(const PoolArgs& a, int dpli, unsigned grid, hipStream_t s) {
+void launch_r4_a(const PoolArgs& a, int dpli, unsigned grid, hipStream_t s, const Timing& tm) {
   const dim3 block(64 * (SA + 1));
   switch (dpli) {
-    case 1: hipLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 1>), dim3(grid), block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 2>), dim3(grid), block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 4>), dim3(grid), block, 0, s, a); break;
-    default: hipLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 8>), dim3(grid), block, 0, s, a); break;
+    case 1: hipExtLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 1>), dim3(grid), block, 0, s, tm.start, tm.stop, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 2>), dim3(grid), block, 0, s, tm.start, tm.stop, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 4>), dim3(grid), block, 0, s, tm.start, tm.stop, 0, a); break;
+    default: hipExtLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 8>), dim3(grid), block, 0, s, tm.start, tm.stop, 0, a); break;
   }
 }
 
@@ -311,37 +311,37 @@ void launch_r4_a(const PoolArgs& a, int dpli, unsigned grid, hipStream_t s) {
 
 int pool_launches(int ratio) { return ratio == 4 ? 1 : 2; }
 
-hipError_t launch_pool(const PoolArgs& a, int phase, hipStream_t stream) {
+hipError_t launch_pool(const PoolArgs& a, int phase, hipStream_t stream, const Timing& tm) {
   const int64_t n_rows = a.k_hi - a.k_lo;
   if (a.ratio == 4) {
     // Attention rows are split into waves of 128 dims (64 dims below 128).
     const unsigned grid = (unsigned)(1 + n_rows - a.n_head);
     const int da = a.lane[0].D, dpli = a.lane[1].D / 64;
     switch (da) {
-      case 64: launch_r4_a<1, 1>(a, dpli, grid, stream); break;
-      case 128: launch_r4_a<1, 2>(a, dpli, grid, stream); break;
-      case 256: launch_r4_a<2, 2>(a, dpli, grid, stream); break;
-      default: launch_r4_a<4, 2>(a, dpli, grid, stream); break;
+      case 64: launch_r4_a<1, 1>(a, dpli, grid, stream, tm); break;
+      case 128: launch_r4_a<1, 2>(a, dpli, grid, stream, tm); break;
+      case 256: launch_r4_a<2, 2>(a, dpli, grid, stream, tm); break;
+      default: launch_r4_a<4, 2>(a, dpli, grid, stream, tm); break;
     }
   } else if (phase == 0) {
     if (n_rows > 0) {
       const unsigned grid = (unsigned)(n_rows * (a.lane[0].D / 64) * 2);
-      hipLaunchKernelGGL(pool_r128_partial_kernel, dim3(grid), dim3(256), 0, stream, a);
+      hipExtLaunchKernelGGL(pool_r128_partial_kernel, dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a);
     }
   } else {
     const unsigned grid = (unsigned)(n_rows > 0 ? (n_rows + 3) / 4 : 1);
     switch (a.lane[0].D / 64) {
-      case 1: hipLaunchKernelGGL((pool_r128_finish_kernel<1>), dim3(grid), dim3(256), 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((pool_r128_finish_kernel<2>), dim3(grid), dim3(256), 0, stream, a); break;
-      case 4: hipLaunchKernelGGL((pool_r128_finish_kernel<4>), dim3(grid), dim3(256), 0, stream, a); break;
-      default: hipLaunchKernelGGL((pool_r128_finish_kernel<8>), dim3(grid), dim3(256), 0, stream, a); break;
+      case 1: hipExtLaunchKernelGGL((pool_r128_finish_kernel<1>), dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a); break;
+      case 2: hipExtLaunchKernelGGL((pool_r128_finish_kernel<2>), dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a); break;
+      case 4: hipExtLaunchKernelGGL((pool_r128_finish_kernel<4>), dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a); break;
+      default: hipExtLaunchKernelGGL((pool_r128_finish_kernel<8>), dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a); break;
     }
   }
   return hipGetLastError();
 }
 
-hipError_t launch_fill(const FillArgs& f, hipStream_t stream) {
-  hipLaunchKernelGGL(frontier_fill_kernel, dim3(64), dim3(256), 0, stream, f);
+hipError_t launch_fill(const FillArgs& f, hipStream_t stream, const Timing& tm) {
+  hipExtLaunchKernelGGL(frontier_fill_kernel, dim3(64), dim3(256), 0, stream, tm.start, tm.stop, 0, f);
   return hipGetLastError();
 }
 

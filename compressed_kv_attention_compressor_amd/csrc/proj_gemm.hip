@@ -237,19 +237,19 @@ struct TileCfg {
 };
 
 template <typename Tin>
-void launch_cfg(const ProjArgs& a, TileCfg c, hipStream_t stream) {
+void launch_cfg(const ProjArgs& a, TileCfg c, hipStream_t stream, const Timing& tm) {
   const int tiles_m = (int)((a.M + c.bm - 1) / c.bm);
   const int tiles_n = (a.N + c.bn - 1) / c.bn;
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   const int gm = 4;
   if (c.bm == 256)
-    hipLaunchKernelGGL((proj_mfma_kernel<Tin, 256, 160, 4, 1>), grid, dim3(kThreads), 0, stream, a, tiles_m,
+    hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 256, 160, 4, 1>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
                        tiles_n, gm);
   else if (c.bm == 128)
-    hipLaunchKernelGGL((proj_mfma_kernel<Tin, 128, 128, 2, 2>), grid, dim3(kThreads), 0, stream, a, tiles_m,
+    hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 128, 128, 2, 2>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
                        tiles_n, gm);
   else
-    hipLaunchKernelGGL((proj_mfma_kernel<Tin, 64, 64, 2, 2>), grid, dim3(kThreads), 0, stream, a, tiles_m,
+    hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 64, 64, 2, 2>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
                        tiles_n, gm);
 }
 
@@ -272,13 +272,13 @@ int proj_tile_rows(int64_t M, int N) {
   return pick;
 }
 
-hipError_t launch_proj(const ProjArgs& a, int in_dtype, hipStream_t stream) {
+hipError_t launch_proj(const ProjArgs& a, int in_dtype, hipStream_t stream, const Timing& tm) {
   const int bm = proj_tile_rows(a.M, a.N);
   const TileCfg c = bm == 256 ? TileCfg{256, 160} : bm == 128 ? TileCfg{128, 128} : TileCfg{64, 64};
   if (in_dtype == 1)
-    launch_cfg<uint16_t>(a, c, stream);
+    launch_cfg<uint16_t>(a, c, stream, tm);
   else
-    launch_cfg<float>(a, c, stream);
+    launch_cfg<float>(a, c, stream, tm);
   return hipGetLastError();
 }
 
