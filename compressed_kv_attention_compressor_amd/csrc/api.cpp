@@ -55,7 +55,7 @@ int check_layer(const ds4c_layer* L, Shape* s) {
   if (L->in_dtype != DS4C_F32 && L->in_dtype != DS4C_BF16) return DS4C_EINVAL;
   if (!(std::isfinite(L->rope_base) && L->rope_base > 0.f)) return DS4C_EINVAL;
   if (!(std::isfinite(L->rms_eps) && L->rms_eps >= 0.f)) return DS4C_EINVAL;
-  if (L->hidden <= 0 || L->hidden % 64 != 0 || L->hidden > 65536) return DS4C_ESHAPE;
+  if (L->hidden <= 0 || L->hidden % 64 != 0 || L->hidden > 16384) return DS4C_ESHAPE;
   if (L->n_rot <= 0 || L->n_rot % 2 != 0) return DS4C_ESHAPE;
   int st = check_lane(L->attn, *L, true);
   if (st) return st;
@@ -388,7 +388,6 @@ int ds4c_compress_decode_one(const ds4c_layer* layer, ds4c_frontier* frontier, c
     d.rms_eps = layer->rms_eps;
     d.lane[0] = lane_dev(s, *layer, frontier->state, 0, attn_rows, attn_prequant);
     if (s.n_lanes > 1) d.lane[1] = lane_dev(s, *layer, frontier->state, 1, index_rows, index_prequant);
-    d.ticket = static_cast<unsigned*>(frontier->state);
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
     st = dev_status(timed(DS4C_KCLASS_DECODE,

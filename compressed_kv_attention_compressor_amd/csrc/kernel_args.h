@@ -68,7 +68,6 @@ struct DecodeArgs {
   double log2_base;
   float rms_eps;
   LaneDev lane[2];
-  unsigned* ticket;     // in the frontier control block; zero between calls
 };
 
 struct FillArgs {

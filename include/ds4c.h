@@ -72,7 +72,7 @@ typedef struct ds4c_lane {
  * Uncompressed layers (ratio 0, Part 3 §1) have no compressor: DS4C_EINVAL. */
 typedef struct ds4c_layer {
   int32_t ratio;        /* 4 or 128 */
-  int32_t hidden;       /* K of the projections: hidden % 64 == 0, <= 65536 */
+  int32_t hidden;       /* K of the projections: hidden % 64 == 0, <= 16384 */
   int32_t n_rot;        /* RoPE tail width (64 in ds4, Part 3 §8): even, 0 < n_rot <= D */
   int32_t in_dtype;     /* ds4c_dtype of x, wkv and wgate */
   float rope_base;      /* compression RoPE base (> 0): theta_i = base^(-2i/n_rot) */
@@ -94,9 +94,9 @@ typedef struct ds4c_frontier {
   void *state;
 } ds4c_frontier;
 
-/* Bytes of device memory a layer's frontier needs: a 256-byte control block
- * then, per lane, kv and score tensors of [coff*ratio, W] float32. 0 if the
- * layer descriptor is invalid. */
+/* Bytes of device memory a layer's frontier needs: a 256-byte block reserved
+ * for the library then, per lane, kv and score tensors of [coff*ratio, W]
+ * float32. 0 if the layer descriptor is invalid. */
 size_t ds4c_frontier_bytes(const ds4c_layer *layer);
 
 /* Bytes of device workspace ds4c_compress_prefill needs for calls of up to
