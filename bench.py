@@ -59,6 +59,22 @@ def layer_algorithmic(shape, n0, T):
     return flops, pool_bytes, n_emit * len(lanes), N
 
 
+def proj_kernel_name(M: int, N: int) -> str:
+    """Projection kernel the library launches for an [M, N] output.
+
+    Mirrors the library's tile choice: the tile shape with the least work per
+    CU over ceil(tiles / 256) rounds, ties to the larger tile; 256 x 160 tiles
+    run on the eight-wave split-K kernel, the others on the four-wave one.
+    """
+    best, pick = None, 64
+    for bm, bn in ((256, 160), (128, 128), (64, 64)):
+        tiles = -(-M // bm) * -(-N // bn)
+        cost = -(-tiles // 256) * bm * bn
+        if best is None or cost < best:
+            best, pick = cost, bm
+    return "proj_splitk_kernel" if pick == 256 else "proj_mfma_kernel"
+
+
 def read_traffic(workload: str):
     """HBM bytes per GEMM launch from the committed counter summary, or None.
 
@@ -214,6 +230,8 @@ def main():
     B.ds4c_profile_enable(False)
 
     gemm_ms = ms[B.KCLASS_PROJ] / max(cnt[B.KCLASS_PROJ], 1)
+    gemm_kernel = " + ".join(sorted({proj_kernel_name(min(T, chunk), 2 * sum(s.coff * d for d in (s.d_attn, s.d_index) if d))
+                                     for _, s in shapes if s is not None}))
     pool_ms = ms[B.KCLASS_POOL] / max(cnt[B.KCLASS_POOL], 1)
     flops_per_launch = flops / max(gemm_launches, 1)
     pool_bytes_per_launch = pool_bytes / max(gemm_launches, 1)
@@ -242,7 +260,7 @@ def main():
         "config": cfg,
         "rows_per_s": steps * rows / el,
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": gemm_tflops / peak, "traffic": traffic, "kernel": "proj_mfma_kernel",
+                     "frac": gemm_tflops / peak, "traffic": traffic, "kernel": gemm_kernel,
                      "avg_ms": gemm_ms, "algorithmic_flops": flops_per_launch},
         "pool_roofline": {"bound": "hbm", "achieved": pool_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": pool_gbs / PEAK_HBM_GBS, "kernel": "pool (all launches of one call)",

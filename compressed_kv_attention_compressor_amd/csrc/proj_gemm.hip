@@ -2,25 +2,30 @@
 // blocks of a layer (wkv and wgate of each lane, Part 3 §4) written as one
 // [T, N] float32 matrix.  Both operands are K-contiguous (x rows, weight rows).
 //
-// MFMA design for gfx950 (wave64):
-//  * One 256-thread workgroup (4 waves) computes a BM x BN tile; each wave a
-//    (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks with fp32 accumulators.
-//    bf16 uses v_mfma_f32_32x32x16_bf16, float32 v_mfma_f32_32x32x2_f32.
-//  * K advances in tiles of 128 bytes per row (64 bf16 / 32 fp32) through a
-//    3-stage LDS ring filled by direct global->LDS 16-byte loads (no VGPR
-//    staging).  A K tile is issued two tiles ahead; the workgroup barrier
-//    sits in the middle of a tile so the next tile's first fragments are read
-//    while the current tile's last MFMAs run, and fragment registers are
-//    double-buffered across the four K sub-steps of a tile.
-//  * Slot (row, chunk) lives at row*8 + (chunk ^ f(row)) with
-//    f(row) = (row & 7) ^ ((row >> 3) & 1), so the 16-byte fragment reads of
-//    8 or 16 consecutive lanes (consecutive rows, same chunk) hit distinct banks.
-//  * Inside one MFMA the K order is free as long as A and B agree, so lane
-//    half h reads chunk 2*kk + h of the K tile for both operands.
+// MFMA design for gfx950 (wave64), two kernels sharing these rules:
+//  * 32x32 output blocks with fp32 accumulators: bf16 inputs use
+//    v_mfma_f32_32x32x16_bf16, float32 inputs v_mfma_f32_32x32x2_f32.
+//  * Operand rows reach LDS through buffer loads that write LDS directly
+//    (16 bytes per lane, no VGPR staging).  The buffer form matters: the
+//    flat/global form counts as an LDS access too, and while one is in
+//    flight every wait for LDS fragment data degenerates to a full drain.
+//  * The loop bodies have no branches (loads past the last K tile re-read
+//    the last tile into a buffer nothing reads again), so the compiler's
+//    wait counts stay exact; issue order inside a K sub-step is pinned:
+//    MFMA, fragment read for a later sub-step, and loads spread between.
+//  * Inside one MFMA the K order is free as long as both operands agree, so
+//    lane half h reads chunk 2*kk + h of a row's K tile for x and weights.
 //  * Workgroups are dealt to the 8 XCDs round-robin; tile ids are remapped so
 //    each XCD owns a contiguous range, walked in groups of GM tile-rows, which
 //    keeps the x rows and weight rows an XCD reads inside its own L2.
-//  * Weight rows are found per row (a tile may straddle two weight blocks).
+//  * A weight tile may straddle two weight blocks; blocks start at multiples
+//    of 16 columns, so each load instruction stays inside one block.
+//
+// proj_splitk_kernel (256 x 160 tiles, one per CU at 4096 x 2560): eight
+// waves, two per SIMD, split the four K sub-steps of each 64-column K tile
+// (128-byte rows, 3-stage ring); the partial sums are combined through LDS.
+// proj_mfma_kernel (128 x 128 and 64 x 64 tiles): four waves, 32-column K
+// stages (64-byte rows) in a 6-stage ring, loads issued five stages ahead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,6 +44,9 @@ constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// 64-byte rows (4 chunks): (row % 4, slot) is distinct over any 16 consecutive
+// rows and (row % 2, slot) over any 8, so fragment reads are conflict free.
+__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
 template <typename Tin>
 __device__ __forceinline__ void mfma_chunk(const u32x4& a, const u32x4& b, f32x16& acc);
@@ -57,18 +65,6 @@ __device__ __forceinline__ void mfma_chunk<float>(const u32x4& a, const u32x4& b
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[3]), __uint_as_float(b[3]), acc, 0, 0, 0);
 }
 
-// Start of weight row n of the concatenated [N, K] operand.  The blocks are
-// picked with constant indices only, so the argument block stays in SGPRs.
-template <typename Tin>
-__device__ __forceinline__ const Tin* weight_row(const ProjArgs& a, int n) {
-  const void* w = a.seg[0].w;
-  int c0 = a.seg[0].col0;
-  if (a.n_seg > 1 && n >= a.seg[1].col0) { w = a.seg[1].w; c0 = a.seg[1].col0; }
-  if (a.n_seg > 2 && n >= a.seg[2].col0) { w = a.seg[2].w; c0 = a.seg[2].col0; }
-  if (a.n_seg > 3 && n >= a.seg[3].col0) { w = a.seg[3].w; c0 = a.seg[3].col0; }
-  return reinterpret_cast<const Tin*>(w) + (int64_t)(n - c0) * a.K;
-}
-
 // Wait until at most N vector-memory operations of this wave are in flight
 // (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
 // left at their maxima so they do not wait).
@@ -78,22 +74,35 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// One 16-byte-per-lane load into LDS through a buffer descriptor over
+// [base, base + bytes); lane l's data lands at lds + 16*l.
+__device__ __forceinline__ void load_lds16(const void* base, int bytes, __attribute__((address_space(3))) void* lds,
+                                           uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000),
+                                           lds, 16, voff, soff, 0, 0);
+}
+
 template <typename Tin, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int tiles_m, int tiles_n, int gm) {
   constexpr int kElems = 16 / (int)sizeof(Tin);  // elements per 16-byte chunk
-  constexpr int BK = 8 * kElems;                  // K elements per tile (8 chunks per row)
+  constexpr int kElemBytes = (int)sizeof(Tin);
+  constexpr int BK = 4 * kElems;                  // K elements per stage (4 chunks = 64 bytes per row)
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int kWaves = kThreads / 64;
-  constexpr int A_INS = BM / (8 * kWaves), B_INS = BN / (8 * kWaves);  // 8 rows per wave load
-  constexpr int kStage = (BM + BN) * 8;                                  // 16-byte slots per stage
+  constexpr int kRows = BM + BN;
+  constexpr int kInsA = BM / 16, kInsB = BN / 16;  // 16 rows x 64 bytes per load instruction
+  constexpr int kDmaA = (kInsA + kWaves - 1) / kWaves, kDmaB = (kInsB + kWaves - 1) / kWaves;
+  constexpr int kDma = kDmaA + kDmaB;             // load instructions per wave per stage
+  constexpr int kNst = 6;                         // LDS stages
+  constexpr int kLead = kNst - 1;                 // stages issued ahead
+  constexpr int kStage = kRows * 4;               // 16-byte slots per stage
   static_assert(WM * WN == kWaves, "four waves");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "32x32 blocks");
-  static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "whole wave loads");
-  __shared__ u32x4 smem[3 * kStage];
+  static_assert(BM % 16 == 0 && BN % 16 == 0, "whole 16-row loads");
+  __shared__ u32x4 smem[kNst * kStage];
 
   const int t = threadIdx.x;
-
   const int n_tiles = tiles_m * tiles_n;
   const int b = blockIdx.x;
   const int x = b % kXcds, j = b / kXcds;
@@ -108,41 +117,62 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BN;
 
-  const int wave = t >> 6, lane = t & 63;
-  // Direct-to-LDS loads: a wave instruction fills 1 KiB of LDS = 8 rows x 8
-  // slots, lane l landing in slot l.  Lane l of the instruction covering rows
-  // r0..r0+7 therefore fetches chunk (l%8) ^ f(row) of row r0 + l/8.
-  const Tin* X = reinterpret_cast<const Tin*>(a.x);
-  const Tin* a_src[A_INS];
-  const Tin* b_src[B_INS];
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+
+  // Loads: instruction `ins` fills stage rows 16*ins .. 16*ins+15 (rows < BM
+  // are x rows m0 + r, the rest weight rows n0 + r - BM); lane l lands in
+  // slot l of the instruction's 1 KiB, i.e. row 16*ins + l/4, slot l%4, and
+  // so fetches logical chunk (l%4) ^ f(row).  A wave's first kDmaA
+  // instructions cover x rows, the rest weight rows; a wave without a k-th
+  // instruction of a kind repeats the last one (same bytes, same slots).
+  const int64_t rows_left = a.M - m0;  // >= 1
+  const char* x_base = reinterpret_cast<const char*>(a.x) + m0 * a.K * kElemBytes;
+  const int x_bytes = (int)((rows_left < BM ? rows_left : BM) * a.K * kElemBytes);
+  const void* l_base[kDma];
+  int l_bytes[kDma];
+  uint32_t l_off[kDma];
+  int l_slot[kDma];
 #pragma unroll
-  for (int i = 0; i < A_INS; ++i) {
-    const int row = (wave * A_INS + i) * 8 + (lane >> 3);
-    int64_t r = m0 + row;
-    r = r < a.M ? r : a.M - 1;
-    a_src[i] = X + r * a.K + ((lane & 7) ^ swz(row)) * kElems;
+  for (int i = 0; i < kDmaA; ++i) {
+    const int ins = min(wave + kWaves * i, kInsA - 1);
+    l_slot[i] = ins * 64;
+    const int row = ins * 16 + (lane >> 2);
+    const int r = row < rows_left ? row : (int)rows_left - 1;
+    l_base[i] = x_base;
+    l_bytes[i] = x_bytes;
+    l_off[i] = (uint32_t)((r * a.K + ((lane & 3) ^ swz4(row)) * kElems) * kElemBytes);
   }
 #pragma unroll
-  for (int i = 0; i < B_INS; ++i) {
-    const int row = (wave * B_INS + i) * 8 + (lane >> 3);
-    int n = n0 + row;
+  for (int i = 0; i < kDmaB; ++i) {
+    const int ins = min(wave + kWaves * i, kInsB - 1);
+    l_slot[kDmaA + i] = (kInsA + ins) * 64;
+    const int row = BM + ins * 16 + (lane >> 2);
+    // Weight blocks start at multiples of 16 columns, so the 16 rows of an
+    // instruction share a block; rows past N repeat row N-1.
+    int n_first = n0 + ins * 16;
+    n_first = n_first < a.N ? n_first : a.N - 1;
+    int n = n0 + row - BM;
     n = n < a.N ? n : a.N - 1;
-    b_src[i] = weight_row<Tin>(a, n) + ((lane & 7) ^ swz(row)) * kElems;
+    const void* w = a.seg[0].w;
+    int c0 = a.seg[0].col0, cn = a.seg[0].n;
+    if (a.n_seg > 1 && n_first >= a.seg[1].col0) { w = a.seg[1].w; c0 = a.seg[1].col0; cn = a.seg[1].n; }
+    if (a.n_seg > 2 && n_first >= a.seg[2].col0) { w = a.seg[2].w; c0 = a.seg[2].col0; cn = a.seg[2].n; }
+    if (a.n_seg > 3 && n_first >= a.seg[3].col0) { w = a.seg[3].w; c0 = a.seg[3].col0; cn = a.seg[3].n; }
+    l_base[kDmaA + i] = w;
+    l_bytes[kDmaA + i] = cn * a.K * kElemBytes;
+    l_off[kDmaA + i] = (uint32_t)(((n - c0) * a.K + ((lane & 3) ^ swz4(row)) * kElems) * kElemBytes);
   }
-  auto issue = [&](int kt, int st) {
-    const int k0 = kt * BK;
+  const int nh = a.K / BK;  // stages along K (even)
+  // Load instructions i0 .. i0+cnt-1 of stage `hs` (clamped to the last one).
+  auto issue = [&](int hs, int i0, int cnt) {
+    const int hc = min(hs, nh - 1);
+    const uint32_t soff = (uint32_t)(hc * BK * kElemBytes);
     __attribute__((address_space(3))) u32x4* base =
-        (__attribute__((address_space(3))) u32x4*)(smem + st * kStage);
+        (__attribute__((address_space(3))) u32x4*)(smem + (hs % kNst) * kStage);
 #pragma unroll
-    for (int i = 0; i < A_INS; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + k0),
-                                       (__attribute__((address_space(3))) void*)(base + (wave * A_INS + i) * 64),
-                                       16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < B_INS; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + k0),
-                                       (__attribute__((address_space(3))) void*)(base + (BM + (wave * B_INS + i) * 8) * 8),
-                                       16, 0, 0);
+    for (int i = 0; i < kDma; ++i)
+      if (i >= i0 && i < i0 + cnt)
+        load_lds16(l_base[i], l_bytes[i], (__attribute__((address_space(3))) void*)(base + l_slot[i]), l_off[i], soff);
   };
 
   const int wm = wave / WN, wn = wave % WN;
@@ -153,7 +183,190 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x16{};
 
-  // Fragment registers, double-buffered across K sub-steps.
+  // Fragment registers: one set per K sub-step of two consecutive stages,
+  // read one stage (two sub-steps) ahead.
+  u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN], fa2[FM], fb2[FN], fa3[FM], fb3[FN];
+  // Fragment f (0..FM+FN-1: x blocks, then weight blocks) of sub-step kk of stage hs.
+  auto frag = [&](u32x4 (&fa)[FM], u32x4 (&fb)[FN], int f, int hs, int kk) {
+    const u32x4* base = smem + (hs % kNst) * kStage;
+    const int c = 2 * kk + h;
+    if (f < FM) {
+      const int row = wm * TM + f * 32 + r32;
+      fa[f] = base[row * 4 + (c ^ swz4(row))];
+    } else {
+      const int row = BM + wn * TN + (f - FM) * 32 + r32;
+      fb[f - FM] = base[row * 4 + (c ^ swz4(row))];
+    }
+  };
+  auto frags = [&](u32x4 (&fa)[FM], u32x4 (&fb)[FN], int hs, int kk) {
+#pragma unroll
+    for (int f = 0; f < FM + FN; ++f) frag(fa, fb, f, hs, kk);
+  };
+  // One K sub-step in a fixed issue order: MFMA i, then (for the first FM+FN)
+  // fragment i of the sub-step two ahead, then (spread evenly) one of the nd
+  // loads i0.. of stage hs+kLead.
+  auto sub_step = [&](const u32x4 (&ca)[FM], const u32x4 (&cb)[FN], u32x4 (&na)[FM], u32x4 (&nb)[FN], int hs_next,
+                      int kk_next, int hs_load, int i0, int nd) {
+    constexpr int kM = FM * FN, kR = FM + FN;
+    int d = 0;
+#pragma unroll
+    for (int i = 0; i < kM; ++i) {
+      mfma_chunk<Tin>(ca[i / FN], cb[i % FN], acc[i / FN][i % FN]);
+      if (i < kR) frag(na, nb, i, hs_next, kk_next);
+      if (nd > 0 && (i * nd) / kM != ((i + 1) * nd) / kM) {
+        issue(hs_load, i0 + d, 1);
+        ++d;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Fewer MFMAs than fragments or loads (small tiles): issue the rest.
+#pragma unroll
+    for (int f = kM; f < kR; ++f) frag(na, nb, f, hs_next, kk_next);
+    for (; d < nd; ++d) issue(hs_load, i0 + d, 1);
+  };
+  constexpr int kD0 = kDma / 2, kD1 = kDma - kDma / 2;  // loads per sub-step
+  // Stage hs: barrier, then its two sub-steps with the next stage's fragment
+  // reads and stage hs+kLead's loads interleaved.  At the barrier the loads
+  // of stage hs+1 have landed for every wave (the kDma*(kLead-2) issued
+  // after them may be in flight), and every wave has finished reading stage
+  // hs-1, which this stage's loads refill.
+  auto stage = [&](int hs, const u32x4 (&ca)[FM], const u32x4 (&cb)[FN], const u32x4 (&da)[FM], const u32x4 (&db)[FN],
+                   u32x4 (&na)[FM], u32x4 (&nb)[FN], u32x4 (&ma)[FM], u32x4 (&mb)[FN]) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<kDma * (kLead - 2)>();
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    sub_step(ca, cb, na, nb, hs + 1, 0, hs + kLead, 0, kD0);
+    sub_step(da, db, ma, mb, hs + 1, 1, hs + kLead, kD0, kD1);
+  };
+
+#pragma unroll
+  for (int hs = 0; hs < kLead; ++hs) issue(hs, 0, kDma);
+  wait_vm<kDma * (kLead - 1)>();
+  asm volatile("s_barrier" ::: "memory");
+  frags(fa0, fb0, 0, 0);
+  frags(fa1, fb1, 0, 1);
+  for (int hs = 0; hs < nh; hs += 2) {
+    stage(hs, fa0, fb0, fa1, fb1, fa2, fb2, fa3, fb3);
+    stage(hs + 1, fa2, fb2, fa3, fb3, fa0, fb0, fa1, fb1);
+  }
+  wait_vm<0>();  // no LDS-bound load may outlive the loop
+
+  // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4.
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int n = n0 + wn * TN + fn * 32 + r32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = m0 + wm * TM + fm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (m < a.M && n < a.N) a.out[m * a.N + n] = acc[fm][fn][v];
+      }
+    }
+  }
+}
+
+// Eight-wave variant: two waves per SIMD split the K sub-steps of every tile.
+// Waves w and w+4 (same SIMD) own the same (BM/WM) x (BN/WN) output block;
+// group 0 (waves 0-3) runs K sub-steps 0 and 1 of each 128-byte K tile,
+// group 1 sub-steps 2 and 3, both reading the same LDS stage.  While one
+// wave of a SIMD waits for LDS data or the barrier, the other issues MFMAs.
+// The stage loads (BM + BN rows of 128 bytes, 8 rows per instruction) are
+// dealt to the eight waves round-robin.  At the end each group hands half
+// of its partial sums to the other through LDS and stores the other half.
+template <typename Tin, int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(512) proj_splitk_kernel(ProjArgs a, int tiles_m, int tiles_n, int gm) {
+  constexpr int kElems = 16 / (int)sizeof(Tin);
+  constexpr int BK = 8 * kElems;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int kRows = BM + BN;
+  constexpr int kIns = kRows / 8;            // load instructions per stage
+  constexpr int kMaxIns = (kIns + 7) / 8;    // per wave
+  constexpr int kStage = kRows * 8;          // 16-byte slots per stage
+  static_assert(WM * WN == 4, "four waves per group");
+  static_assert(FM == 2, "the final exchange splits the two 32-row blocks");
+  static_assert(kRows % 8 == 0, "whole 8-row loads");
+  static_assert(4 * FN * 16 * 64 * 4 <= 3 * kStage * 16, "exchange buffer fits the ring");
+  __shared__ u32x4 smem[3 * kStage];
+
+  const int t = threadIdx.x;
+  const int n_tiles = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int x = b % kXcds, j = b / kXcds;
+  const int q = n_tiles / kXcds, rem = n_tiles % kXcds;
+  const int logical = x * q + min(x, rem) + j;
+  const int group_size = gm * tiles_n;
+  const int first_m = (logical / group_size) * gm;
+  const int rows_in_group = min(tiles_m - first_m, gm);
+  const int in_group = logical % group_size;
+  const int tm = first_m + in_group % rows_in_group;
+  const int tn = in_group / rows_in_group;
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
+
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+  const int grp = wave >> 2, wq = wave & 3;
+  const int h = lane >> 5, r32 = lane & 31;
+
+  // Stage row r < BM is x row m0 + r, row BM + c is weight row n0 + c.
+  // Loads go through buffer descriptors with per-lane byte offsets; the K
+  // tile advances through the scalar offset.  Waves without an i-th
+  // instruction repeat the last one (same bytes into the same slots).
+  constexpr int kElemBytes = (int)sizeof(Tin);
+  const int64_t rows_left = a.M - m0;
+  const char* x_base = reinterpret_cast<const char*>(a.x) + m0 * a.K * kElemBytes;
+  const int x_bytes = (int)((rows_left < BM ? rows_left : BM) * a.K * kElemBytes);
+  const void* l_base[kMaxIns];
+  int l_bytes[kMaxIns];
+  uint32_t l_off[kMaxIns];
+  int l_slot[kMaxIns];
+#pragma unroll
+  for (int i = 0; i < kMaxIns; ++i) {
+    const int ins = min(wave + 8 * i, kIns - 1);
+    l_slot[i] = ins * 64;
+    const int row0 = ins * 8;  // uniform first row of the instruction
+    const int row = row0 + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);
+    if (row0 < BM) {
+      const int r = row < rows_left ? row : (int)rows_left - 1;
+      l_base[i] = x_base;
+      l_bytes[i] = x_bytes;
+      l_off[i] = (uint32_t)((r * a.K + chunk * kElems) * kElemBytes);
+    } else {
+      int n_first = n0 + row0 - BM;
+      n_first = n_first < a.N ? n_first : a.N - 1;
+      int n = n0 + row - BM;
+      n = n < a.N ? n : a.N - 1;
+      const void* w = a.seg[0].w;
+      int c0 = a.seg[0].col0, cn = a.seg[0].n;
+      if (a.n_seg > 1 && n_first >= a.seg[1].col0) { w = a.seg[1].w; c0 = a.seg[1].col0; cn = a.seg[1].n; }
+      if (a.n_seg > 2 && n_first >= a.seg[2].col0) { w = a.seg[2].w; c0 = a.seg[2].col0; cn = a.seg[2].n; }
+      if (a.n_seg > 3 && n_first >= a.seg[3].col0) { w = a.seg[3].w; c0 = a.seg[3].col0; cn = a.seg[3].n; }
+      l_base[i] = w;
+      l_bytes[i] = cn * a.K * kElemBytes;
+      l_off[i] = (uint32_t)(((n - c0) * a.K + chunk * kElems) * kElemBytes);
+    }
+  }
+  auto issue_one = [&](int kt, int st, int i) {
+    const uint32_t k0b = (uint32_t)(kt * BK * kElemBytes);
+    __attribute__((address_space(3))) u32x4* base =
+        (__attribute__((address_space(3))) u32x4*)(smem + st * kStage);
+    load_lds16(l_base[i], l_bytes[i], (__attribute__((address_space(3))) void*)(base + l_slot[i]), l_off[i], k0b);
+  };
+  auto issue = [&](int kt, int st) {
+#pragma unroll
+    for (int i = 0; i < kMaxIns; ++i) issue_one(kt, st, i);
+  };
+
+  const int wm = wq / WN, wn = wq % WN;
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x16{};
+
   u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   auto frags = [&](u32x4 (&fa)[FM], u32x4 (&fb)[FN], int st, int kk) {
     const u32x4* base = smem + st * kStage;
@@ -165,61 +378,92 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
     }
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
-      const int row = wn * TN + fn * 32 + r32;
-      fb[fn] = base[(BM + row) * 8 + (c ^ swz(row))];
+      const int row = BM + wn * TN + fn * 32 + r32;
+      fb[fn] = base[row * 8 + (c ^ swz(row))];
     }
   };
-  auto mma = [&](const u32x4 (&fa)[FM], const u32x4 (&fb)[FN]) {
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) mfma_chunk<Tin>(fa[fm], fb[fn], acc[fm][fn]);
-  };
-  // Interleave hint: one MFMA, one LDS read, repeated, then the rest of the MFMAs.
-  auto interleave = [&]() {
-#pragma unroll
-    for (int i = 0; i < FM + FN; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  // Fragment f (x blocks, then weight blocks) of K sub-step kk of stage st.
+  auto frag = [&](u32x4 (&fa)[FM], u32x4 (&fb)[FN], int f, int st, int kk) {
+    const u32x4* base = smem + st * kStage;
+    const int c = 2 * kk + h;
+    if (f < FM) {
+      const int row = wm * TM + f * 32 + r32;
+      fa[f] = base[row * 8 + (c ^ swz(row))];
+    } else {
+      const int row = BM + wn * TN + (f - FM) * 32 + r32;
+      fb[f - FM] = base[row * 8 + (c ^ swz(row))];
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN) > 0 ? FM * FN - (FM + FN) : 0, 0);
   };
-
+  // One K sub-step in a fixed issue order: MFMA i, then fragment i of the
+  // next sub-step, then (spread evenly) one of the nd loads of tile kt_load.
+  auto sub_step = [&](const u32x4 (&ca)[FM], const u32x4 (&cb)[FN], u32x4 (&na)[FM], u32x4 (&nb)[FN], int st_next,
+                      int kk_next, int kt_load, int st_load, int nd) {
+    constexpr int kM = FM * FN, kR = FM + FN;
+    int d = 0;
+#pragma unroll
+    for (int i = 0; i < kM; ++i) {
+      mfma_chunk<Tin>(ca[i / FN], cb[i % FN], acc[i / FN][i % FN]);
+      if (i < kR) frag(na, nb, i, st_next, kk_next);
+      if (nd > 0 && (i * nd) / kM != ((i + 1) * nd) / kM) {
+        issue_one(kt_load, st_load, d);
+        ++d;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Fewer MFMAs than fragments or loads: issue the rest.
+#pragma unroll
+    for (int f = kM; f < kR; ++f) frag(na, nb, f, st_next, kk_next);
+    for (; d < nd; ++d) issue_one(kt_load, st_load, d);
+  };
   const int nk = a.K / BK;
+  const int kk0 = 2 * grp;
   issue(0, 0);
-  if (nk > 1) issue(1, 1);
-  if (nk > 1)
-    wait_vm<A_INS + B_INS>();
-  else
-    wait_vm<0>();
+  issue(min(1, nk - 1), 1);
+  wait_vm<0>();
   asm volatile("s_barrier" ::: "memory");
-  frags(fa0, fb0, 0, 0);
+  frags(fa0, fb0, 0, kk0);
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt % 3;
-    frags(fa1, fb1, st, 1);
-    mma(fa0, fb0);
-    interleave();
-    frags(fa0, fb0, st, 2);
-    mma(fa1, fb1);
-    interleave();
-    if (kt + 1 < nk) {
-      // Tile kt+1 has landed for every wave, and every wave is done with tile
-      // kt-1, whose stage the issue below refills.
-      wait_vm<0>();
-      asm volatile("s_barrier" ::: "memory");
-      if (kt + 2 < nk) issue(kt + 2, (kt + 2) % 3);
+    sub_step(fa0, fb0, fa1, fb1, st, kk0 + 1, 0, 0, 0);
+    // Tile kt+1 has landed for every wave and every wave is done with tile
+    // kt-1, whose stage the loads below refill.  Past the last tile the
+    // loads re-read the last tile into a stage nothing reads again, so the
+    // loop body has no branches and the compiler's wait counts stay exact.
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<0>();
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    sub_step(fa1, fb1, fa0, fb0, (kt + 1) % 3, kk0, min(kt + 2, nk - 1), (kt + 2) % 3, kMaxIns);
+  }
+  wait_vm<0>();  // the exchange below reuses the ring
+
+  // Exchange: round r, group 1-r parks its partial sums of block fm = r in
+  // LDS (lane-major, conflict free) and group r adds them; group r then
+  // owns block r.
+  asm volatile("s_barrier" ::: "memory");
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (grp != r) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) red[((wq * FN + fn) * 16 + v) * 64 + lane] = acc[r][fn][v];
     }
-    frags(fa1, fb1, st, 3);
-    mma(fa0, fb0);
-    interleave();
-    if (kt + 1 < nk) frags(fa0, fb0, (kt + 1) % 3, 0);
-    mma(fa1, fb1);
-    interleave();
+    __syncthreads();
+    if (grp == r) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[r][fn][v] += red[((wq * FN + fn) * 16 + v) * 64 + lane];
+    }
+    __syncthreads();
   }
 
   // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4.
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
+    if (fm != grp) continue;
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       const int n = n0 + wn * TN + fn * 32 + r32;
@@ -243,7 +487,7 @@ void launch_cfg(const ProjArgs& a, TileCfg c, hipStream_t stream, const Timing& 
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   const int gm = 4;
   if (c.bm == 256)
-    hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 256, 160, 4, 1>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
+    hipExtLaunchKernelGGL((proj_splitk_kernel<Tin, 256, 160, 4, 1>), grid, dim3(512), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
                        tiles_n, gm);
   else if (c.bm == 128)
     hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 128, 128, 2, 2>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
