@@ -219,7 +219,9 @@ def main():
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    B.ds4c_profile_enable(True)
+    # Timed region: only the projection GEMM (the dominant kernel) is
+    # bracketed by dispatch-recorded events; each bracket costs queue time.
+    B.ds4c_profile_enable([B.KCLASS_PROJ])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -227,7 +229,16 @@ def main():
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms, cnt = B.ds4c_profile_read()
+    # A separate pass times the pool and decode kernels.
+    side_steps = max(1, min(steps, 10))
+    B.ds4c_profile_enable([B.KCLASS_POOL, B.KCLASS_DECODE])
+    for _ in range(side_steps):
+        step()
+    torch.cuda.synchronize()
+    ms2, cnt2 = B.ds4c_profile_read()
     B.ds4c_profile_enable(False)
+    for c in (B.KCLASS_POOL, B.KCLASS_DECODE):
+        ms[c], cnt[c] = ms2[c], cnt2[c]
 
     gemm_ms = ms[B.KCLASS_PROJ] / max(cnt[B.KCLASS_PROJ], 1)
     gemm_kernel = " + ".join(sorted({proj_kernel_name(min(T, chunk), 2 * sum(s.coff * d for d in (s.d_attn, s.d_index) if d))
@@ -264,8 +275,11 @@ def main():
                      "avg_ms": gemm_ms, "algorithmic_flops": flops_per_launch},
         "pool_roofline": {"bound": "hbm", "achieved": pool_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": pool_gbs / PEAK_HBM_GBS, "kernel": "pool (all launches of one call)",
+                          "measured": f"separate pass of {side_steps} steps",
                           "avg_ms": pool_ms, "algorithmic_bytes": pool_bytes_per_launch},
-        "kernel_launches": {"proj": cnt[B.KCLASS_PROJ], "pool": cnt[B.KCLASS_POOL], "decode": cnt[B.KCLASS_DECODE]},
+        "kernel_launches": {"proj (timed region)": cnt[B.KCLASS_PROJ],
+                            f"pool (pass of {side_steps} steps)": cnt[B.KCLASS_POOL],
+                            f"decode (pass of {side_steps} steps)": cnt[B.KCLASS_DECODE]},
     }
     if cnt[B.KCLASS_DECODE]:
         out["decode_avg_ms"] = ms[B.KCLASS_DECODE] / cnt[B.KCLASS_DECODE]

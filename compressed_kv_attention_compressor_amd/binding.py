@@ -22,6 +22,7 @@ DS4C_EDEVICE = -6
 DS4C_F32 = 0
 DS4C_BF16 = 1
 KCLASS_PROJ, KCLASS_POOL, KCLASS_DECODE, KCLASS_INIT = 0, 1, 2, 3
+PROFILE_ALL = 0xF
 
 # Every function the header declares, with (restype, argtypes).
 SIGNATURES = {}
@@ -187,8 +188,18 @@ def ds4c_prefill_chunk_cap(prompt_len: int, override_cap: int = 0) -> int:
     return lib().ds4c_prefill_chunk_cap(prompt_len, override_cap)
 
 
-def ds4c_profile_enable(on: bool) -> None:
-    _ok(lib().ds4c_profile_enable(1 if on else 0), "ds4c_profile_enable")
+def ds4c_profile_enable(classes=True) -> None:
+    """Time kernels of the given classes: True = all, False = none, or an
+    iterable of KCLASS_* values."""
+    if classes is True:
+        mask = PROFILE_ALL
+    elif classes is False or classes is None:
+        mask = 0
+    else:
+        mask = 0
+        for c in classes:
+            mask |= 1 << int(c)
+    _ok(lib().ds4c_profile_enable(mask), "ds4c_profile_enable")
 
 
 def ds4c_profile_read():

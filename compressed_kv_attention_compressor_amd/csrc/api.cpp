@@ -165,7 +165,7 @@ struct ProfRec {
   hipEvent_t a, b;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+int g_prof_mask = 0;  // bit c: kernels of class c are timed
 std::vector<ProfRec> g_prof;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -193,7 +193,7 @@ void release_records() {
 template <class F>
 hipError_t timed(int cls, F&& launch) {
   std::unique_lock<std::mutex> lk(g_prof_mu);
-  if (!g_prof_on) {
+  if (!(g_prof_mask & (1 << cls))) {
     lk.unlock();
     return launch(ds4c::Timing{});
   }
@@ -631,11 +631,12 @@ const char* ds4c_status_str(int status) {
   }
 }
 
-int ds4c_profile_enable(int on) {
+int ds4c_profile_enable(int class_mask) {
   try {
+    if (class_mask < 0 || class_mask > DS4C_PROFILE_ALL) return DS4C_EINVAL;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     release_records();
-    g_prof_on = on != 0;
+    g_prof_mask = class_mask;
     return DS4C_OK;
   } catch (...) {
     return DS4C_EDEVICE;

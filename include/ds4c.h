@@ -216,13 +216,18 @@ int64_t ds4c_prefill_chunk_cap(int64_t prompt_len, int64_t override_cap);
 /* Static description of a status code; never NULL. */
 const char *ds4c_status_str(int status);
 
-/* Kernel timing.  While enabled (on != 0), every kernel the library enqueues
- * is bracketed by HIP events on its stream.  ds4c_profile_read waits for the
- * recorded events, writes the accumulated milliseconds and launch counts of
- * each kernel class (DS4C_KCLASS_*) into ms[n] and count[n] (n <= 4), and
- * clears the record.  Enabling or disabling also clears it. */
+/* Kernel timing.  While enabled, every kernel of a selected class that the
+ * library enqueues is bracketed by HIP events recorded by its own dispatch on
+ * its stream; each bracket adds a few microseconds of queue time, so select
+ * only the classes being measured.  class_mask: bit c selects class c
+ * (DS4C_KCLASS_*), 0 turns timing off, DS4C_PROFILE_ALL selects every class;
+ * other values return DS4C_EINVAL.  ds4c_profile_read waits for the recorded
+ * events, writes the accumulated milliseconds and launch counts of each class
+ * into ms[n] and count[n] (n <= 4), and clears the record.  Enabling or
+ * disabling also clears it. */
 enum { DS4C_KCLASS_PROJ = 0, DS4C_KCLASS_POOL = 1, DS4C_KCLASS_DECODE = 2, DS4C_KCLASS_INIT = 3 };
-int ds4c_profile_enable(int on);
+enum { DS4C_PROFILE_ALL = 0xF };
+int ds4c_profile_enable(int class_mask);
 int ds4c_profile_read(double *ms, int64_t *count, int n);
 
 #ifdef __cplusplus

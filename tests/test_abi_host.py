@@ -200,7 +200,16 @@ def test_profile_read_without_records():
     B.ds4c_profile_enable(True)
     ms, cnt = B.ds4c_profile_read()
     assert ms == [0.0] * 4 and cnt == [0] * 4
+    B.ds4c_profile_enable([B.KCLASS_PROJ])
+    ms, cnt = B.ds4c_profile_read()
+    assert cnt == [0] * 4
     B.ds4c_profile_enable(False)
+
+
+def test_profile_mask_out_of_range():
+    assert B.lib().ds4c_profile_enable(-1) == B.DS4C_EINVAL
+    assert B.lib().ds4c_profile_enable(B.PROFILE_ALL + 1) == B.DS4C_EINVAL
+    assert B.lib().ds4c_profile_enable(0) == B.DS4C_OK
 
 
 def _stack(n=4):
