@@ -40,11 +40,19 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 GEMM_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", "proj_gemm.hip")
 
 
-def layer_algorithmic(shape, n0, T):
-    """GEMM flops and pool-kernel bytes of one prefill call (tokens n0 .. n0+T-1).
+def fused_call(shape, n0):
+    """A ratio-4 call that starts on a window boundary pools inside the projection epilogue."""
+    return shape.ratio == 4 and n0 % 4 == 0
 
-    Pool bytes: every projected kv/score element read once, the APE table,
-    the rows written, and the live frontier rows written after the call.
+
+def layer_algorithmic(shape, n0, T):
+    """GEMM flops and pool-launch bytes of one prefill call (tokens n0 .. n0+T-1).
+
+    Plain path, pool bytes: every projected kv/score element read once, the
+    APE table, the rows written, and the live frontier rows written after the
+    call.  Fused ratio-4 path (window pooling in the projection epilogue), the
+    finishing launch's bytes: the pooled rows read once, the rows written and
+    the live frontier rows written from the staged tokens (read once).
     """
     lanes = [shape.d_attn] + ([shape.d_index] if shape.d_index else [])
     W = [shape.coff * d for d in lanes]
@@ -55,7 +63,11 @@ def layer_algorithmic(shape, n0, T):
     c = n % shape.ratio
     m = n - c
     live = ((4 if m >= 4 else 0) + c) if shape.ratio == 4 else c
-    pool_bytes = T * N * 4 + shape.ratio * sum(W) * 4 + n_emit * sum(lanes) * 4 + live * sum(W) * 2 * 4
+    if fused_call(shape, n0):
+        kept = min(live, T)
+        pool_bytes = n_emit * sum(lanes) * 4 * 2 + kept * sum(W) * 2 * 4 * 2
+    else:
+        pool_bytes = T * N * 4 + shape.ratio * sum(W) * 4 + n_emit * sum(lanes) * 4 + live * sum(W) * 2 * 4
     return flops, pool_bytes, n_emit * len(lanes), N
 
 
@@ -241,7 +253,9 @@ def main():
         ms[c], cnt[c] = ms2[c], cnt2[c]
 
     gemm_ms = ms[B.KCLASS_PROJ] / max(cnt[B.KCLASS_PROJ], 1)
-    gemm_kernel = " + ".join(sorted({proj_kernel_name(min(T, chunk), 2 * sum(s.coff * d for d in (s.d_attn, s.d_index) if d))
+    all_fused = all(fused_call(s, 0) for _, s in shapes if s is not None)
+    gemm_kernel = " + ".join(sorted({"proj_splitk_kernel (fused ratio-4 pool epilogue)" if fused_call(s, 0) else
+                                     proj_kernel_name(min(T, chunk), 2 * sum(s.coff * d for d in (s.d_attn, s.d_index) if d))
                                      for _, s in shapes if s is not None}))
     pool_ms = ms[B.KCLASS_POOL] / max(cnt[B.KCLASS_POOL], 1)
     flops_per_launch = flops / max(gemm_launches, 1)
@@ -274,7 +288,9 @@ def main():
                      "frac": gemm_tflops / peak, "traffic": traffic, "kernel": gemm_kernel,
                      "avg_ms": gemm_ms, "algorithmic_flops": flops_per_launch},
         "pool_roofline": {"bound": "hbm", "achieved": pool_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                          "frac": pool_gbs / PEAK_HBM_GBS, "kernel": "pool (all launches of one call)",
+                          "frac": pool_gbs / PEAK_HBM_GBS,
+                          "kernel": "pool (all launches of one call)" if not all_fused else
+                                    "row finisher (window pooling runs in the projection epilogue)",
                           "measured": f"separate pass of {side_steps} steps",
                           "avg_ms": pool_ms, "algorithmic_bytes": pool_bytes_per_launch},
         "kernel_launches": {"proj (timed region)": cnt[B.KCLASS_PROJ],

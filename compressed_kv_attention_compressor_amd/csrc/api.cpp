@@ -98,10 +98,15 @@ void frontier_ptrs(const Shape& s, void* state, int lane, float** kv, float** sc
 struct WsLayout {
   size_t proj = 0, part = 0, total = 0;
   int64_t max_rows = 0;
+  // Fused ratio 4 (calls with n0 % 4 == 0), in the same buffer.
+  size_t f_o = 0, f_part = 0, f_stage = 0;
 };
 
-// Projection [T, N] float32, then on ratio-128 layers the pool partials:
-// per emitted row, 2 token halves x (max, sum, weighted sum) x D floats.
+// Plain path: projection [T, N] float32, then on ratio-128 layers the pool
+// partials: per emitted row, 2 token halves x (max, sum, weighted sum) x D
+// floats.  Fused ratio-4 path: pooled rows [T/4, D_attn + D_idx], the
+// tile-start partials [ceil(T/256)][2][3][D_attn + D_idx] and the tokens
+// the frontier keeps [7, N].  The buffer holds the larger of the two.
 WsLayout workspace_layout(const Shape& s, int64_t T) {
   WsLayout w;
   w.proj = 0;
@@ -112,6 +117,16 @@ WsLayout workspace_layout(const Shape& s, int64_t T) {
     off += align256(size_t(w.max_rows) * 2 * 3 * s.D[0] * sizeof(float));
   }
   w.total = off;
+  if (s.ratio == 4) {
+    const size_t d_tot = size_t(s.D[0]) + size_t(s.n_lanes > 1 ? s.D[1] : 0);
+    w.f_o = 0;
+    size_t f = align256(size_t(T / 4 + 1) * d_tot * sizeof(float));
+    w.f_part = f;
+    f += align256(size_t((T + 255) / 256 + 1) * 2 * 3 * d_tot * sizeof(float));
+    w.f_stage = f;
+    f += align256(size_t(7) * s.N * sizeof(float));
+    if (f > w.total) w.total = f;
+  }
   return w;
 }
 
@@ -332,6 +347,40 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
     po.lane[0] = lane_dev(s, *layer, frontier->state, 0, attn_rows, attn_prequant);
     if (s.n_lanes > 1) po.lane[1] = lane_dev(s, *layer, frontier->state, 1, index_rows, index_prequant);
     if (r == 128) po.part = reinterpret_cast<float*>(ws + wl.part);
+
+    if (r == 4 && n0 % 4 == 0) {
+      // Window pool fused into the projection epilogue; the pool launch
+      // only finishes the rows and carries the frontier.
+      const int64_t m_rel = T - T % 4;
+      ds4c::FuseArgs& f = pa.fuse;
+      f.on = 1;
+      f.d_attn = s.D[0];
+      f.d_idx = s.n_lanes > 1 ? s.D[1] : 0;
+      f.d_tot = f.d_attn + f.d_idx;
+      f.W[0] = s.W[0];
+      f.W[1] = s.n_lanes > 1 ? s.W[1] : 0;
+      f.n_orig = s.N;
+      f.n_emit = n_emit;
+      f.carry_lo = m_rel >= 4 ? m_rel - 4 : 0;
+      f.ape[0] = layer->attn.ape;
+      f.ape[1] = s.n_lanes > 1 ? layer->index.ape : nullptr;
+      f.o = reinterpret_cast<float*>(ws + wl.f_o);
+      f.part = reinterpret_cast<float*>(ws + wl.f_part);
+      f.stage = reinterpret_cast<float*>(ws + wl.f_stage);
+      for (int l = 0; l < s.n_lanes; ++l) {
+        float* kv = nullptr;
+        float* sc = nullptr;
+        frontier_ptrs(s, frontier->state, l, &kv, &sc);
+        f.fr_kv[l] = kv;
+        f.fr_sc[l] = sc;
+      }
+      po.o = f.o;
+      po.part = f.part;
+      po.stage = f.stage;
+      po.d_tot = f.d_tot;
+      po.carry_lo = f.carry_lo;
+      po.n_head = 0;
+    }
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
     st = dev_status(

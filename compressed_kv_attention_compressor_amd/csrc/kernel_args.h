@@ -27,14 +27,38 @@ struct ProjSeg {
   int n;
 };
 
+// Ratio-4 window pool fused into the projection epilogue (calls that start
+// on a window boundary).  Output column tile tn holds dims 40*tn .. 40*tn+39
+// of the concatenated lanes (attention dims, then indexer dims) as four runs
+// of 40 columns: kv of the previous half, kv of the current half, score of
+// the previous half, score of the current half.  Call-relative token t is
+// tile row t; window j pools tokens 4j-4 .. 4j-1 (previous half) and
+// 4j .. 4j+3 (current half).
+struct FuseArgs {
+  int on;               // 0: plain [M, N] output in ProjArgs::out
+  int d_attn, d_idx;    // head dims (d_idx = 0 without an indexer lane)
+  int d_tot;            // d_attn + d_idx: columns of o and part
+  int W[2];             // lane widths (2 * head dim)
+  int n_orig;           // columns of a staged token (the plain layout)
+  int64_t n_emit;       // windows the call emits
+  int64_t carry_lo;     // first call-relative token the frontier keeps
+  const float* ape[2];  // [4, W] per lane
+  float* o;             // [n_emit, d_tot]: pooled rows (before the norm) of windows j % 64 != 0
+  float* part;          // [M tiles][2 halves][max, sum, weighted sum][d_tot] of windows j % 64 == 0
+  float* stage;         // [T - carry_lo, n_orig]: kv and score + APE of the kept tokens
+  const float* fr_kv[2];  // incoming frontier rows 0..3 hold window 0's previous half
+  const float* fr_sc[2];
+};
+
 struct ProjArgs {
   const void* x;        // [M, K] row-major, bf16 or f32
-  float* out;           // [M, N] row-major f32
+  float* out;           // [M, N] row-major f32 (unfused)
   int64_t M;
   int K;
   int N;
   int n_seg;
-  ProjSeg seg[4];
+  ProjSeg seg[4];       // attention wkv, wgate, then indexer wkv, wgate
+  FuseArgs fuse;
 };
 
 struct PoolArgs {
@@ -50,7 +74,13 @@ struct PoolArgs {
   double log2_base;     // log2 of the compression RoPE base
   float rms_eps;
   LaneDev lane[2];
-  float* part;          // ratio 128: [k_hi-k_lo][2 halves][max, sum, weighted sum][D]
+  float* part;          // ratio 128: [k_hi-k_lo][2 halves][max, sum, weighted sum][D];
+                        // fused ratio 4: FuseArgs::part
+  // Fused ratio 4 (n0 % 4 == 0): the finisher reads these instead of proj.
+  const float* o;       // FuseArgs::o
+  const float* stage;   // FuseArgs::stage
+  int d_tot;
+  int64_t carry_lo;
 };
 
 struct DecodeArgs {

@@ -284,6 +284,119 @@ __global__ void __launch_bounds__(256) pool_r128_finish_kernel(PoolArgs a) {
   if (blockIdx.x == 0) carry_frontier<128>(a);
 }
 
+
+// ---------------------------------------------------------------------------
+// Fused ratio 4 (calls with n0 % 4 == 0): the projection epilogue has pooled
+// every window j = k - k_lo with j % 64 != 0 into o[j][dim] (attention dims,
+// then indexer dims) and left, for the windows j % 64 == 0, the previous and
+// current halves' (max, sum, weighted sum) partials in part[j/64][0] and
+// part[j/64][1] (window 0's previous half comes from the incoming frontier,
+// read by the projection launch).
+// ---------------------------------------------------------------------------
+template <int DPL>
+__device__ __forceinline__ void fused_pool_dims(const PoolArgs& a, int64_t j, int dg, float (&o)[DPL]) {
+  if (j % 64 != 0) {
+    load_vec<DPL>(o, a.o + j * a.d_tot + dg);
+    return;
+  }
+  const int64_t tm = j / 64;
+  float mc[DPL], sc[DPL], wc[DPL], mp[DPL], sp[DPL], wp[DPL];
+  const float* pc = a.part + (tm * 2 + 1) * 3 * a.d_tot + dg;
+  const float* pp = a.part + (tm * 2) * 3 * a.d_tot + dg;
+  load_vec<DPL>(mc, pc);
+  load_vec<DPL>(sc, pc + a.d_tot);
+  load_vec<DPL>(wc, pc + 2 * a.d_tot);
+  load_vec<DPL>(mp, pp);
+  load_vec<DPL>(sp, pp + a.d_tot);
+  load_vec<DPL>(wp, pp + 2 * a.d_tot);
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    const float m = fmaxf(mc[i], mp[i]);
+    float den = 0.f, num = 0.f;
+    if (m != -INFINITY) {
+      if (mc[i] != -INFINITY) {
+        const float f = expf(mc[i] - m);
+        den = sc[i] * f;
+        num = wc[i] * f;
+      }
+      if (mp[i] != -INFINITY) {
+        const float f = expf(mp[i] - m);
+        den = fmaf(sp[i], f, den);
+        num = fmaf(wp[i], f, num);
+      }
+    }
+    o[i] = den > 0.f ? num / den : 0.f;
+  }
+}
+
+template <int SA, int DPLA, int DPLI>
+__device__ __forceinline__ void r4_fused_window(const PoolArgs& a, int64_t j, float* s_ss) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t k = a.k_lo + j;
+  if (wave < SA) {
+    const LaneDev& L = a.lane[0];
+    const int d0 = wave * (kWave * DPLA) + lane * DPLA;
+    float o[DPLA];
+    fused_pool_dims<DPLA>(a, j, d0, o);
+    const float ss = wave_sum(row_sumsq<DPLA>(o));
+    if (lane == 0) s_ss[wave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int s = 0; s < SA; ++s) tot += s_ss[s];
+    float* pre = L.prequant ? L.prequant + j * L.D : nullptr;
+    finish_row_part<DPLA>(o, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, pre,
+                          L.rows + k * L.D, lane);
+  } else {
+    const LaneDev& L = a.lane[1];
+    float o[DPLI];
+    fused_pool_dims<DPLI>(a, j, a.lane[0].D + lane * DPLI, o);
+    __syncthreads();
+    float* pre = L.prequant ? L.prequant + j * L.D : nullptr;
+    finish_row_wave<DPLI>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, pre, L.rows + k * L.D, lane);
+  }
+}
+
+// Workgroups 0 .. n_emit-1 finish one window each; the kFusedCarryGroups
+// after them write the outgoing frontier from the staged tokens (the
+// projection launch was the last reader of the incoming one): with
+// m = T - T % 4 (call-relative), rows 0..3 take tokens m-4 .. m-1 when m >= 4
+// and rows 4.. take tokens m .. T-1.
+constexpr int kFusedCarryGroups = 4;
+
+template <int SA, int DPLA, int DPLI>
+__global__ void __launch_bounds__(64 * (SA + 1)) pool_r4_fused_kernel(PoolArgs a) {
+  __shared__ float s_ss[SA];
+  const int64_t n_emit = a.k_hi - a.k_lo;
+  if ((int64_t)blockIdx.x < n_emit) {
+    r4_fused_window<SA, DPLA, DPLI>(a, blockIdx.x, s_ss);
+    return;
+  }
+  const int64_t m = a.T - (a.T & 3);
+  const int64_t first = m >= 4 ? m - 4 : 0;
+  const int n_tok = (int)(a.T - first);
+  // Flat work list: per lane, per kept token, kv then score, W/4 float4 each.
+  const int64_t gid = (blockIdx.x - n_emit) * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)kFusedCarryGroups * blockDim.x;
+  int64_t base = 0;
+  for (int l = 0; l < a.n_lanes; ++l) {
+    const LaneDev& L = a.lane[l];
+    const int w4 = L.W / 4;
+    const int64_t count = (int64_t)n_tok * 2 * w4;
+    for (int64_t i = gid - base; i < count; i += stride) {
+      if (i < 0) continue;
+      const int c = (int)(i % w4) * 4;
+      const int kind = (int)((i / w4) & 1);
+      const int64_t t = first + i / (2 * w4);
+      const int row = t >= m ? 4 + (int)(t & 3) : (int)(t & 3);
+      const float* src = a.stage + (t - a.carry_lo) * a.ld + (kind ? L.sc_col : L.kv_col) + c;
+      float* dst = (kind ? L.fr_sc : L.fr_kv) + row * L.W + c;
+      *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
+    }
+    base += count;
+  }
+}
+
 __global__ void __launch_bounds__(256) frontier_fill_kernel(FillArgs f) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -296,14 +409,22 @@ __global__ void __launch_bounds__(256) frontier_fill_kernel(FillArgs f) {
   if (i0 < f.n_ctrl) f.ctrl[i0] = 0u;
 }
 
+template <int SA, int DPLA, int DPLI>
+void launch_r4_one(const PoolArgs& a, unsigned grid, hipStream_t s, const Timing& tm) {
+  const dim3 block(64 * (SA + 1));
+  if (a.o)
+    hipExtLaunchKernelGGL((pool_r4_fused_kernel<SA, DPLA, DPLI>), dim3(grid), block, 0, s, tm.start, tm.stop, 0, a);
+  else
+    hipExtLaunchKernelGGL((pool_r4_kernel<SA, DPLA, DPLI>), dim3(grid), block, 0, s, tm.start, tm.stop, 0, a);
+}
+
 template <int SA, int DPLA>
 void launch_r4_a(const PoolArgs& a, int dpli, unsigned grid, hipStream_t s, const Timing& tm) {
-  const dim3 block(64 * (SA + 1));
   switch (dpli) {
-    case 1: hipExtLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 1>), dim3(grid), block, 0, s, tm.start, tm.stop, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 2>), dim3(grid), block, 0, s, tm.start, tm.stop, 0, a); break;
-    case 4: hipExtLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 4>), dim3(grid), block, 0, s, tm.start, tm.stop, 0, a); break;
-    default: hipExtLaunchKernelGGL((pool_r4_kernel<SA, DPLA, 8>), dim3(grid), block, 0, s, tm.start, tm.stop, 0, a); break;
+    case 1: launch_r4_one<SA, DPLA, 1>(a, grid, s, tm); break;
+    case 2: launch_r4_one<SA, DPLA, 2>(a, grid, s, tm); break;
+    case 4: launch_r4_one<SA, DPLA, 4>(a, grid, s, tm); break;
+    default: launch_r4_one<SA, DPLA, 8>(a, grid, s, tm); break;
   }
 }
 
@@ -315,7 +436,7 @@ hipError_t launch_pool(const PoolArgs& a, int phase, hipStream_t stream, const T
   const int64_t n_rows = a.k_hi - a.k_lo;
   if (a.ratio == 4) {
     // Attention rows are split into waves of 128 dims (64 dims below 128).
-    const unsigned grid = (unsigned)(1 + n_rows - a.n_head);
+    const unsigned grid = a.o ? (unsigned)(n_rows + kFusedCarryGroups) : (unsigned)(1 + n_rows - a.n_head);
     const int da = a.lane[0].D, dpli = a.lane[1].D / 64;
     switch (da) {
       case 64: launch_r4_a<1, 1>(a, dpli, grid, stream, tm); break;

@@ -267,6 +267,172 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Fused ratio-4 epilogue (Part 3 §4-§5) of a 256-token x 40-dim tile (see
+// FuseArgs for the column runs).  The two wave groups' partial sums meet in
+// an LDS copy of the tile; then each (window, dim) of the tile is pooled:
+// window g >= 1 of the tile from its own rows, window 0's current half and
+// the next tile's window 0 previous half as (max, sum, weighted sum)
+// partials.  The tokens the frontier keeps are staged in the plain column
+// layout with APE added to their scores.
+// ---------------------------------------------------------------------------
+// LDS index of tile element (row, col): 160-float rows, rotated by 32
+// columns on odd 4-row groups so that the two half-waves of an accumulator
+// store (rows r and r + 4) hit different banks.
+__device__ __forceinline__ int tile_ix(int row, int col) {
+  const int c = col + (((row >> 2) & 1) << 5);
+  return row * 160 + (c < 160 ? c : c - 160);
+}
+
+// (max, sum, weighted sum) of four entries of one dim, without branches: an
+// all-empty half (every score -inf) gives (-inf, 0, 0).
+struct Part3 {
+  float m, s, w;
+};
+__device__ __forceinline__ Part3 half_pool(const float (&kv)[4], const float (&sc)[4]) {
+  Part3 p;
+  p.m = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  const float ms = p.m == -INFINITY ? 0.f : p.m;
+  p.s = 0.f;
+  p.w = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x = expf(sc[e] - ms);
+    p.s += x;
+    p.w = fmaf(x, kv[e], p.w);
+  }
+  return p;
+}
+
+template <int WM, int FN>
+__device__ __forceinline__ void fused_r4_epilogue(const ProjArgs& a, f32x16 (&acc)[2][FN], float* tile, int tm, int tn,
+                                                  int wq, int grp, int lane) {
+  const FuseArgs& f = a.fuse;
+  const int h = lane >> 5, r32 = lane & 31;
+  // The two groups' partial sums meet as in the plain epilogue (round r:
+  // group 1-r parks block fm = r lane-major, group r adds it), then each
+  // group stores its complete 32-row blocks into the tile.
+  asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (grp != r) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tile[((wq * FN + fn) * 16 + v) * 64 + lane] = acc[r][fn][v];
+    }
+    __syncthreads();
+    if (grp == r) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[r][fn][v] += tile[((wq * FN + fn) * 16 + v) * 64 + lane];
+    }
+    __syncthreads();
+  }
+  // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4.
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm) {
+    if (fm != grp) continue;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        tile[tile_ix(wq * 64 + fm * 32 + 8 * (v >> 2) + 4 * h + (v & 3), fn * 32 + r32)] = acc[fm][fn][v];
+  }
+  __syncthreads();
+
+  const int64_t t0 = (int64_t)tm * 256;  // call-relative token of tile row 0
+  const int64_t j0 = (int64_t)tm * 64;   // window of tile group 0
+  // Thread t < 480 owns dim 40*tn + t % 40 and walks the tile's 4-row groups
+  // g = t / 40, t / 40 + 12, ...: group g gives the current half of window g
+  // and, with group g-1, its full pool; group 63 also gives the previous half
+  // of the next tile's window 0.  Loads and arithmetic are unconditional.
+  const int dd = threadIdx.x % 40, g_first = threadIdx.x / 40;
+  const int dim = tn * 40 + dd;
+  if (threadIdx.x < 480 && dim < f.d_tot) {
+    const int l = dim < f.d_attn ? 0 : 1;
+    const int ld = dim - (l ? f.d_attn : 0), dl = l ? f.d_idx : f.d_attn, W = f.W[l];
+    float ape_p[4], ape_c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ape_p[e] = f.ape[l][e * W + ld];
+      ape_c[e] = f.ape[l][e * W + dl + ld];
+    }
+    for (int g = g_first; g < 64; g += 12) {
+      const int64_t jw = j0 + g;
+      const int gp = g > 0 ? g - 1 : 0;
+      float kc[4], sc[4], kq[4], sq[4], kp[4], sp[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kc[e] = tile[tile_ix(4 * g + e, 40 + dd)];
+        sc[e] = tile[tile_ix(4 * g + e, 120 + dd)] + ape_c[e];
+        kq[e] = tile[tile_ix(4 * g + e, dd)];
+        sq[e] = tile[tile_ix(4 * g + e, 80 + dd)] + ape_p[e];
+        kp[e] = tile[tile_ix(4 * gp + e, dd)];
+        sp[e] = tile[tile_ix(4 * gp + e, 80 + dd)] + ape_p[e];
+      }
+      const Part3 pc = half_pool(kc, sc);  // current half of window g
+      const Part3 pq = half_pool(kq, sq);  // previous half of window g+1
+      const Part3 pp = half_pool(kp, sp);  // previous half of window g
+      const float m = fmaxf(pc.m, pp.m);
+      const float ms = m == -INFINITY ? 0.f : m;
+      const float fc = expf(pc.m - ms), fp = expf(pp.m - ms);
+      const float den = fmaf(pc.s, fc, pp.s * fp), num = fmaf(pc.w, fc, pp.w * fp);
+      if (jw < f.n_emit) {
+        if (g > 0) {
+          f.o[jw * f.d_tot + dim] = den > 0.f ? num / den : 0.f;
+        } else {
+          float* q = f.part + ((int64_t)tm * 2 + 1) * 3 * f.d_tot + dim;
+          q[0] = pc.m;
+          q[f.d_tot] = pc.s;
+          q[2 * f.d_tot] = pc.w;
+          if (tm == 0) {
+            // Window 0's previous half: tokens n0-4 .. n0-1 in rows 0..3 of
+            // the incoming frontier (scores already hold their APE).
+            float kf[4], sf[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              kf[e] = f.fr_kv[l][e * W + ld];
+              sf[e] = f.fr_sc[l][e * W + ld];
+            }
+            const Part3 pf = half_pool(kf, sf);
+            float* q0 = f.part + dim;
+            q0[0] = pf.m;
+            q0[f.d_tot] = pf.s;
+            q0[2 * f.d_tot] = pf.w;
+          }
+        }
+      }
+      if (g == 63 && jw + 1 < f.n_emit) {
+        float* q = f.part + ((int64_t)(tm + 1) * 2 + 0) * 3 * f.d_tot + dim;
+        q[0] = pq.m;
+        q[f.d_tot] = pq.s;
+        q[2 * f.d_tot] = pq.w;
+      }
+    }
+  }
+  // Kept tokens: call-relative carry_lo .. M-1 that fall in this tile.
+  const int64_t s_lo = f.carry_lo > t0 ? f.carry_lo : t0;
+  const int64_t s_hi = a.M < t0 + 256 ? a.M : t0 + 256;
+  const int n_rows = s_hi > s_lo ? (int)(s_hi - s_lo) : 0;
+  for (int item = threadIdx.x; item < n_rows * 160; item += blockDim.x) {
+    const int r = item / 160, q = item - r * 160;
+    const int run = q / 40, dd = q - run * 40;
+    const int dim = tn * 40 + dd;
+    if (dim >= f.d_tot) continue;
+    const int64_t t = s_lo + r;
+    const int l = dim < f.d_attn ? 0 : 1;
+    const int ld = dim - (l ? f.d_attn : 0), dl = l ? f.d_idx : f.d_attn, W = f.W[l];
+    const int wcol = (run & 1) * dl + ld;  // column within the lane's W-wide block
+    float v = tile[tile_ix((int)(t - t0), q)];
+    if (run >= 2) v += f.ape[l][(int)(t & 3) * W + wcol];
+    const int col = (l ? 2 * f.W[0] : 0) + (run >= 2 ? W : 0) + wcol;
+    f.stage[(t - f.carry_lo) * f.n_orig + col] = v;
+  }
+}
+
 // Eight-wave variant: two waves per SIMD split the K sub-steps of every tile.
 // Waves w and w+4 (same SIMD) own the same (BM/WM) x (BN/WN) output block;
 // group 0 (waves 0-3) runs K sub-steps 0 and 1 of each 128-byte K tile,
@@ -275,7 +441,7 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
 // The stage loads (BM + BN rows of 128 bytes, 8 rows per instruction) are
 // dealt to the eight waves round-robin.  At the end each group hands half
 // of its partial sums to the other through LDS and stores the other half.
-template <typename Tin, int BM, int BN, int WM, int WN>
+template <typename Tin, int BM, int BN, int WM, int WN, bool FUSE>
 __global__ void __launch_bounds__(512) proj_splitk_kernel(ProjArgs a, int tiles_m, int tiles_n, int gm) {
   constexpr int kElems = 16 / (int)sizeof(Tin);
   constexpr int BK = 8 * kElems;
@@ -289,7 +455,11 @@ __global__ void __launch_bounds__(512) proj_splitk_kernel(ProjArgs a, int tiles_
   static_assert(FM == 2, "the final exchange splits the two 32-row blocks");
   static_assert(kRows % 8 == 0, "whole 8-row loads");
   static_assert(4 * FN * 16 * 64 * 4 <= 3 * kStage * 16, "exchange buffer fits the ring");
-  __shared__ u32x4 smem[3 * kStage];
+  static_assert(!FUSE || (BM == 256 && BN == 160), "the fused epilogue holds a 256 x 160 tile");
+  // The fused epilogue stages the whole fp32 tile (160 KiB) in LDS.
+  constexpr int kSmem = FUSE ? BM * BN / 4 : 3 * kStage;
+  static_assert(kSmem >= 3 * kStage, "ring fits");
+  __shared__ u32x4 smem[kSmem];
 
   const int t = threadIdx.x;
   const int n_tiles = tiles_m * tiles_n;
@@ -334,6 +504,28 @@ __global__ void __launch_bounds__(512) proj_splitk_kernel(ProjArgs a, int tiles_
       l_base[i] = x_base;
       l_bytes[i] = x_bytes;
       l_off[i] = (uint32_t)((r * a.K + chunk * kElems) * kElemBytes);
+    } else if constexpr (FUSE) {
+      // Tile column q: run q / 40 (kv prev, kv cur, score prev, score cur)
+      // of dim 40*tn + q % 40.  Runs, lanes and the padding past d_tot all
+      // start at multiples of 8, so an instruction's 8 rows are 8
+      // consecutive rows of one weight matrix (padding re-reads real rows).
+      const FuseArgs& f = a.fuse;
+      const int q0 = row0 - BM;
+      const int run = q0 / 40;
+      int dim0 = tn * 40 + q0 % 40;
+      dim0 = dim0 < f.d_tot ? dim0 : f.d_tot - 8;
+      const int l = dim0 < f.d_attn ? 0 : 1;
+      const int dl = l ? f.d_idx : f.d_attn;
+      const int wrow = dim0 - (l ? f.d_attn : 0) + (run & 1) * dl + (lane >> 3);
+      const int si = 2 * l + (run >> 1);
+      const void* w = a.seg[0].w;
+      int cn = a.seg[0].n;
+      if (si == 1) { w = a.seg[1].w; cn = a.seg[1].n; }
+      if (si == 2) { w = a.seg[2].w; cn = a.seg[2].n; }
+      if (si == 3) { w = a.seg[3].w; cn = a.seg[3].n; }
+      l_base[i] = w;
+      l_bytes[i] = cn * a.K * kElemBytes;
+      l_off[i] = (uint32_t)((wrow * a.K + chunk * kElems) * kElemBytes);
     } else {
       int n_first = n0 + row0 - BM;
       n_first = n_first < a.N ? n_first : a.N - 1;
@@ -437,6 +629,11 @@ __global__ void __launch_bounds__(512) proj_splitk_kernel(ProjArgs a, int tiles_
   }
   wait_vm<0>();  // the exchange below reuses the ring
 
+  if constexpr (FUSE) {
+    fused_r4_epilogue<WM>(a, acc, reinterpret_cast<float*>(smem), tm, tn, wq, grp, lane);
+    return;
+  }
+
   // Exchange: round r, group 1-r parks its partial sums of block fm = r in
   // LDS (lane-major, conflict free) and group r adds them; group r then
   // owns block r.
@@ -487,8 +684,8 @@ void launch_cfg(const ProjArgs& a, TileCfg c, hipStream_t stream, const Timing& 
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   const int gm = 4;
   if (c.bm == 256)
-    hipExtLaunchKernelGGL((proj_splitk_kernel<Tin, 256, 160, 4, 1>), grid, dim3(512), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
-                       tiles_n, gm);
+    hipExtLaunchKernelGGL((proj_splitk_kernel<Tin, 256, 160, 4, 1, false>), grid, dim3(512), 0, stream, tm.start, tm.stop, 0, a,
+                          tiles_m, tiles_n, gm);
   else if (c.bm == 128)
     hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 128, 128, 2, 2>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
                        tiles_n, gm);
@@ -517,6 +714,18 @@ int proj_tile_rows(int64_t M, int N) {
 }
 
 hipError_t launch_proj(const ProjArgs& a, int in_dtype, hipStream_t stream, const Timing& tm) {
+  if (a.fuse.on) {
+    const int tiles_m = (int)((a.M + 255) / 256);
+    const int tiles_n = (a.fuse.d_tot + 39) / 40;
+    const dim3 grid((unsigned)(tiles_m * tiles_n));
+    if (in_dtype == 1)
+      hipExtLaunchKernelGGL((proj_splitk_kernel<uint16_t, 256, 160, 4, 1, true>), grid, dim3(512), 0, stream, tm.start,
+                            tm.stop, 0, a, tiles_m, tiles_n, 4);
+    else
+      hipExtLaunchKernelGGL((proj_splitk_kernel<float, 256, 160, 4, 1, true>), grid, dim3(512), 0, stream, tm.start,
+                            tm.stop, 0, a, tiles_m, tiles_n, 4);
+    return hipGetLastError();
+  }
   const int bm = proj_tile_rows(a.M, a.N);
   const TileCfg c = bm == 256 ? TileCfg{256, 160} : bm == 128 ? TileCfg{128, 128} : TileCfg{64, 64};
   if (in_dtype == 1)

@@ -138,6 +138,8 @@ PLANS = {
     "ragged": [1, 3, 5, 127, 129, 2, 64, 300, 69],
     "decode_mix": [3, -6, 130, -3, 1, 120, -130, 337],
     "aligned": [256, 256, 188],
+    # calls on window boundaries spanning several 256-token tiles, short tails
+    "aligned_long": [4, 600, 64, 5, 3],
 }
 
 
@@ -167,11 +169,10 @@ def test_save_load_continue(name):
     _say(f"[parity] {name} save/load")
     shape, p, x = _small(name, 600, seed=5)
     xd = torch.from_numpy(x).to("cuda", _tdtype(shape))
-    full = make_gpu_layer(shape, p, 600)
-    full.prefill(xd)
+    spec_full, st_full = run_oracle(shape, p, x)
     for cut in (0, 3, 131, 259):
         a = make_gpu_layer(shape, p, 600)
-        a.prefill(xd[:cut])
+        pre_a = a.prefill(xd[:cut], prequant=True)
         blob = a.save()
         # the blob's header and live rows match the oracle's canonical frontier
         spec, st = run_oracle(shape, p, x[:cut])
@@ -203,10 +204,20 @@ def test_save_load_continue(name):
         b.rows = {k: v.clone() for k, v in b.rows.items()}
         for k in b.kinds:
             b.rows[k][: cut // shape.ratio] = a.rows[k][: cut // shape.ratio]
-        b.prefill(xd[cut:])
+        pre_b = b.prefill(xd[cut:], prequant=True)
         torch.cuda.synchronize()
-        for k in b.kinds:
-            assert torch.equal(b.live_rows(k), full.live_rows(k)), (cut, k)
+        # The continued state matches the oracle's uninterrupted run.  (The
+        # rows are bitwise equal to `full`'s only when both runs use the same
+        # projection tiling; a call that starts on a window boundary takes
+        # the fused path, so they are compared at the parity tolerances.)
+        g = {
+            "rows": {k: b.live_rows(k).cpu().numpy() for k in b.kinds},
+            "pre": {k: np.concatenate([pre_a[k].cpu().numpy(), pre_b[k].cpu().numpy()]) for k in b.kinds},
+            "frontier": {k: (kv.cpu().numpy(), sc.cpu().numpy()) for k, (kv, sc) in b.frontier_views().items()},
+            "counters": (b.frontier.n_tokens, b.frontier.n_comp, b.frontier.n_index_comp),
+            "layer": b,
+        }
+        compare_all(shape, g, spec_full, st_full, 600)
 
 
 def test_deterministic_and_overwrites_poison():

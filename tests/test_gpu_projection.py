@@ -1,8 +1,9 @@
 """White-box check of the projection GEMM through the C ABI.
 
-After a prefill call the first T*N floats of the workspace hold the
-projection [T, N] = x . [wkv_attn; wgate_attn; wkv_index; wgate_index]^T
-(scores without APE).  It is compared with the float64 product on the host
+After a prefill call that does not start on a window boundary (the plain
+path; one token is prefilled first) the first T*N floats of the workspace
+hold the projection [T, N] = x . [wkv_attn; wgate_attn; wkv_index;
+wgate_index]^T (scores without APE).  It is compared with the float64 product on the host
 against the floating-point error bound of a float32 accumulation:
 |g - o| <= 5e-5 * sum_k |x_k w_k|  (about 200x the typical rounding error and
 far below what a wrong index, operand or tile would produce).
@@ -36,11 +37,14 @@ def test_projection_matches_float64(name):
     print(f"[projection] {name} T={T}", flush=True)
     wid = 70 + list(CASES).index(name)
     p = synth.layer_params(wid, 0, shape)
-    x = synth.hidden_states(wid, shape.hidden, 0, T, shape.dtype)
-    layer = CompressorLayer(shape.ratio, shape.hidden, p, dtype=shape.dtype, max_tokens=T)
+    x_all = synth.hidden_states(wid, shape.hidden, 0, T + 1, shape.dtype)
+    layer = CompressorLayer(shape.ratio, shape.hidden, p, dtype=shape.dtype, max_tokens=T + 1)
     tdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
-    layer.prefill(torch.from_numpy(x).to("cuda", tdt))
+    xg = torch.from_numpy(x_all).to("cuda", tdt)
+    layer.prefill(xg[:1])
+    layer.prefill(xg[1:])
     torch.cuda.synchronize()
+    x = x_all[1:]
     kinds = ["attn"] + (["index"] if shape.ratio == 4 else [])
     w = np.concatenate([np.concatenate([p[k]["wkv"], p[k]["wgate"]]) for k in kinds]).astype(np.float64)
     N = w.shape[0]
