@@ -126,6 +126,13 @@ WsLayout workspace_layout(const Shape& s, int64_t T) {
     w.f_stage = f;
     f += align256(size_t(7) * s.N * sizeof(float));
     if (f > w.total) w.total = f;
+  } else {
+    // Fused ratio 128: pooled rows [T/128, D] and up to 127 kept tokens [127, N].
+    w.f_o = 0;
+    size_t f = align256(size_t(T / 128 + 1) * s.D[0] * sizeof(float));
+    w.f_stage = f;
+    f += align256(size_t(127) * s.N * sizeof(float));
+    if (f > w.total) w.total = f;
   }
   return w;
 }
@@ -348,12 +355,34 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
     if (s.n_lanes > 1) po.lane[1] = lane_dev(s, *layer, frontier->state, 1, index_rows, index_prequant);
     if (r == 128) po.part = reinterpret_cast<float*>(ws + wl.part);
 
+    if (r == 128 && n0 % 128 == 0) {
+      // Window pool fused into the projection epilogue (one 128-token tile
+      // is one window); the pool launch finishes rows and carries the frontier.
+      ds4c::FuseArgs& f = pa.fuse;
+      f.on = 1;
+      f.ratio = 128;
+      f.d_attn = s.D[0];
+      f.d_tot = s.D[0];
+      f.W[0] = s.W[0];
+      f.n_orig = s.N;
+      f.n_emit = n_emit;
+      f.carry_lo = T - T % 128;
+      f.ape[0] = layer->attn.ape;
+      f.o = reinterpret_cast<float*>(ws + wl.f_o);
+      f.stage = reinterpret_cast<float*>(ws + wl.f_stage);
+      po.o = f.o;
+      po.stage = f.stage;
+      po.d_tot = f.d_tot;
+      po.carry_lo = f.carry_lo;
+      po.n_head = 0;
+    }
     if (r == 4 && n0 % 4 == 0) {
       // Window pool fused into the projection epilogue; the pool launch
       // only finishes the rows and carries the frontier.
       const int64_t m_rel = T - T % 4;
       ds4c::FuseArgs& f = pa.fuse;
       f.on = 1;
+      f.ratio = 4;
       f.d_attn = s.D[0];
       f.d_idx = s.n_lanes > 1 ? s.D[1] : 0;
       f.d_tot = f.d_attn + f.d_idx;
@@ -387,7 +416,7 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
         timed(DS4C_KCLASS_PROJ, [&](const ds4c::Timing& tm) { return ds4c::launch_proj(pa, layer->in_dtype, hs, tm); }));
     if (st) return st;
     st = dev_status(timed(DS4C_KCLASS_POOL, [&](const ds4c::Timing& tm) {
-      const int n = ds4c::pool_launches(r);
+      const int n = ds4c::pool_launches(po);
       hipError_t e = hipSuccess;
       for (int ph = 0; ph < n && e == hipSuccess; ++ph)
         e = ds4c::launch_pool(po, ph, hs, ds4c::Timing{ph == 0 ? tm.start : nullptr, ph == n - 1 ? tm.stop : nullptr});

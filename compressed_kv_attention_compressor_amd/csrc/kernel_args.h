@@ -36,6 +36,8 @@ struct ProjSeg {
 // 4j .. 4j+3 (current half).
 struct FuseArgs {
   int on;               // 0: plain [M, N] output in ProjArgs::out
+  int ratio;            // 4: layout above; 128: tile tn holds dims 64*tn .. 64*tn+63 as
+                        // [kv (64) | score (64)] and tile row t is call-relative token t
   int d_attn, d_idx;    // head dims (d_idx = 0 without an indexer lane)
   int d_tot;            // d_attn + d_idx: columns of o and part
   int W[2];             // lane widths (2 * head dim)

@@ -18,9 +18,9 @@ struct Timing {
 };
 
 hipError_t launch_proj(const ProjArgs& a, int in_dtype, hipStream_t stream, const Timing& tm);
-// Ratio-4 layers pool in one launch, ratio-128 layers in two (phase 0: partial
-// pools, phase 1: merge, finish and frontier carry).
-int pool_launches(int ratio);
+// Ratio-4 layers and fused calls pool in one launch; plain ratio-128 calls in
+// two (phase 0: partial pools, phase 1: merge, finish and frontier carry).
+int pool_launches(const PoolArgs& a);
 hipError_t launch_pool(const PoolArgs& a, int phase, hipStream_t stream, const Timing& tm);
 hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, const Timing& tm);
 hipError_t launch_fill(const FillArgs& f, hipStream_t stream, const Timing& tm);

@@ -397,6 +397,42 @@ __global__ void __launch_bounds__(64 * (SA + 1)) pool_r4_fused_kernel(PoolArgs a
   }
 }
 
+
+// Fused ratio 128 (calls with n0 % 128 == 0): the projection epilogue has
+// pooled window j into o[j][D].  One wave finishes one row; the
+// kFusedCarryGroups workgroups after the rows write the outgoing frontier:
+// rows 0 .. c-1 take the trailing partial window's tokens m .. T-1.
+template <int DPL>
+__global__ void __launch_bounds__(256) pool_r128_fused_kernel(PoolArgs a) {
+  const LaneDev& L = a.lane[0];
+  const int64_t n_emit = a.k_hi - a.k_lo;
+  const int64_t row_groups = (n_emit + 3) / 4;
+  if ((int64_t)blockIdx.x < row_groups) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t j = (int64_t)blockIdx.x * 4 + wave;
+    if (j < n_emit) {
+      float o[DPL];
+      load_vec<DPL>(o, a.o + j * L.D + lane * DPL);
+      const int64_t k = a.k_lo + j;
+      float* pre = L.prequant ? L.prequant + j * L.D : nullptr;
+      finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, pre, L.rows + k * L.D, lane);
+    }
+    return;
+  }
+  const int64_t m = a.T - (a.T & 127);
+  const int w4 = L.W / 4;
+  const int64_t count = (a.T - m) * 2 * w4;
+  const int64_t gid = (blockIdx.x - row_groups) * (int64_t)blockDim.x + threadIdx.x;
+  for (int64_t i = gid; i < count; i += (int64_t)kFusedCarryGroups * blockDim.x) {
+    const int c = (int)(i % w4) * 4;
+    const int kind = (int)((i / w4) & 1);
+    const int64_t t = m + i / (2 * w4);
+    const float* src = a.stage + (t - a.carry_lo) * a.ld + (kind ? L.sc_col : L.kv_col) + c;
+    float* dst = (kind ? L.fr_sc : L.fr_kv) + (t - m) * L.W + c;
+    *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
+  }
+}
+
 __global__ void __launch_bounds__(256) frontier_fill_kernel(FillArgs f) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -430,7 +466,7 @@ void launch_r4_a(const PoolArgs& a, int dpli, unsigned grid, hipStream_t s, cons
 
 }  // namespace
 
-int pool_launches(int ratio) { return ratio == 4 ? 1 : 2; }
+int pool_launches(const PoolArgs& a) { return a.ratio == 4 || a.o ? 1 : 2; }
 
 hipError_t launch_pool(const PoolArgs& a, int phase, hipStream_t stream, const Timing& tm) {
   const int64_t n_rows = a.k_hi - a.k_lo;
@@ -443,6 +479,14 @@ hipError_t launch_pool(const PoolArgs& a, int phase, hipStream_t stream, const T
       case 128: launch_r4_a<1, 2>(a, dpli, grid, stream, tm); break;
       case 256: launch_r4_a<2, 2>(a, dpli, grid, stream, tm); break;
       default: launch_r4_a<4, 2>(a, dpli, grid, stream, tm); break;
+    }
+  } else if (a.o) {
+    const unsigned grid = (unsigned)((n_rows + 3) / 4 + kFusedCarryGroups);
+    switch (a.lane[0].D / 64) {
+      case 1: hipExtLaunchKernelGGL((pool_r128_fused_kernel<1>), dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a); break;
+      case 2: hipExtLaunchKernelGGL((pool_r128_fused_kernel<2>), dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a); break;
+      case 4: hipExtLaunchKernelGGL((pool_r128_fused_kernel<4>), dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a); break;
+      default: hipExtLaunchKernelGGL((pool_r128_fused_kernel<8>), dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a); break;
     }
   } else if (phase == 0) {
     if (n_rows > 0) {

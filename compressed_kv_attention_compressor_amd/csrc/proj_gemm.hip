@@ -82,7 +82,87 @@ __device__ __forceinline__ void load_lds16(const void* base, int bytes, __attrib
                                            lds, 16, voff, soff, 0, 0);
 }
 
-template <typename Tin, int BM, int BN, int WM, int WN>
+
+// ---------------------------------------------------------------------------
+// Fused ratio-128 epilogue (Part 3 §4): a 128-token x 64-dim tile is exactly
+// window j = tm of a call that starts on a window boundary.  The tile goes
+// through LDS; four lanes per dim pool 32 tokens each (APE added) and merge
+// their (max, sum, weighted sum) by shuffles; the tokens of a trailing
+// partial window are staged in the plain column layout for the frontier.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tile128_ix(int row, int col) {
+  return row * 128 + ((col + (((row >> 2) & 1) << 5)) & 127);
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void fused_r128_epilogue(const ProjArgs& a, const f32x16 (&acc)[FM][FN], float* tile, int tm,
+                                                    int tn, int wm, int wn, int lane) {
+  const FuseArgs& f = a.fuse;
+  const int h = lane >> 5, r32 = lane & 31;
+  asm volatile("s_barrier" ::: "memory");
+  // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4.
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        tile[tile128_ix(wm * FM * 32 + fm * 32 + 8 * (v >> 2) + 4 * h + (v & 3), wn * FN * 32 + fn * 32 + r32)] =
+            acc[fm][fn][v];
+  __syncthreads();
+  const int D = f.d_attn;
+  const int64_t t0 = (int64_t)tm * 128;
+  const int64_t jw = tm;
+  if (jw < f.n_emit) {
+    const int dd = threadIdx.x >> 2, qq = threadIdx.x & 3;
+    const int dim = tn * 64 + dd;
+    const float* ape = f.ape[0];
+    float kv[32], sc[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int row = qq * 32 + e;
+      kv[e] = tile[tile128_ix(row, dd)];
+      sc[e] = tile[tile128_ix(row, 64 + dd)] + ape[row * D + dim];
+    }
+    float m = sc[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) m = fmaxf(m, sc[e]);
+    const float ms = m == -INFINITY ? 0.f : m;
+    float s = 0.f, w = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const float x = expf(sc[e] - ms);
+      s += x;
+      w = fmaf(x, kv[e], w);
+    }
+    // Merge the four quarters (lanes 4*dd .. 4*dd+3 of this wave).
+#pragma unroll
+    for (int o = 1; o < 4; o <<= 1) {
+      const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64), w2 = __shfl_xor(w, o, 64);
+      const float mm = fmaxf(m, m2);
+      const float mms = mm == -INFINITY ? 0.f : mm;
+      const float f1 = expf(m - mms), f2 = expf(m2 - mms);
+      s = fmaf(s, f1, s2 * f2);
+      w = fmaf(w, f1, w2 * f2);
+      m = mm;
+    }
+    if (qq == 0) f.o[jw * D + dim] = s > 0.f ? w / s : 0.f;
+  }
+  // Kept tokens: call-relative carry_lo .. M-1 that fall in this tile.
+  const int64_t s_lo = f.carry_lo > t0 ? f.carry_lo : t0;
+  const int64_t s_hi = a.M < t0 + 128 ? a.M : t0 + 128;
+  const int n_rows = s_hi > s_lo ? (int)(s_hi - s_lo) : 0;
+  for (int item = threadIdx.x; item < n_rows * 128; item += blockDim.x) {
+    const int r = item >> 7, q = item & 127;
+    const int64_t t = s_lo + r;
+    const int dim = tn * 64 + (q & 63);
+    float v = tile[tile128_ix((int)(t - t0), q)];
+    if (q >= 64) v += f.ape[0][(int)(t & 127) * D + dim];
+    f.stage[(t - f.carry_lo) * f.n_orig + (q >= 64 ? D : 0) + dim] = v;
+  }
+}
+
+template <typename Tin, int BM, int BN, int WM, int WN, bool FUSE>
 __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int tiles_m, int tiles_n, int gm) {
   constexpr int kElems = 16 / (int)sizeof(Tin);  // elements per 16-byte chunk
   constexpr int kElemBytes = (int)sizeof(Tin);
@@ -100,6 +180,8 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
   static_assert(WM * WN == kWaves, "four waves");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "32x32 blocks");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "whole 16-row loads");
+  static_assert(!FUSE || (BM == 128 && BN == 128 && WM == 2 && WN == 2), "the fused epilogue holds one 128-token window");
+  static_assert(!FUSE || kNst * kStage * 16 >= BM * BN * 4, "the fp32 tile fits the ring");
   __shared__ u32x4 smem[kNst * kStage];
 
   const int t = threadIdx.x;
@@ -149,18 +231,29 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
     const int row = BM + ins * 16 + (lane >> 2);
     // Weight blocks start at multiples of 16 columns, so the 16 rows of an
     // instruction share a block; rows past N repeat row N-1.
-    int n_first = n0 + ins * 16;
-    n_first = n_first < a.N ? n_first : a.N - 1;
-    int n = n0 + row - BM;
-    n = n < a.N ? n : a.N - 1;
-    const void* w = a.seg[0].w;
-    int c0 = a.seg[0].col0, cn = a.seg[0].n;
-    if (a.n_seg > 1 && n_first >= a.seg[1].col0) { w = a.seg[1].w; c0 = a.seg[1].col0; cn = a.seg[1].n; }
-    if (a.n_seg > 2 && n_first >= a.seg[2].col0) { w = a.seg[2].w; c0 = a.seg[2].col0; cn = a.seg[2].n; }
-    if (a.n_seg > 3 && n_first >= a.seg[3].col0) { w = a.seg[3].w; c0 = a.seg[3].col0; cn = a.seg[3].n; }
-    l_base[kDmaA + i] = w;
-    l_bytes[kDmaA + i] = cn * a.K * kElemBytes;
-    l_off[kDmaA + i] = (uint32_t)(((n - c0) * a.K + ((lane & 3) ^ swz4(row)) * kElems) * kElemBytes);
+    if constexpr (FUSE) {
+      // Tile column q: kv (q < 64) or score of dim 64*tn + q % 64, i.e. row
+      // 64*tn + q % 64 of wkv or wgate.
+      const int q0 = ins * 16;
+      const int wrow = tn * 64 + (q0 & 63) + (lane >> 2);
+      const void* w = q0 < 64 ? a.seg[0].w : a.seg[1].w;
+      l_base[kDmaA + i] = w;
+      l_bytes[kDmaA + i] = a.seg[0].n * a.K * kElemBytes;
+      l_off[kDmaA + i] = (uint32_t)((wrow * a.K + ((lane & 3) ^ swz4(row)) * kElems) * kElemBytes);
+    } else {
+      int n_first = n0 + ins * 16;
+      n_first = n_first < a.N ? n_first : a.N - 1;
+      int n = n0 + row - BM;
+      n = n < a.N ? n : a.N - 1;
+      const void* w = a.seg[0].w;
+      int c0 = a.seg[0].col0, cn = a.seg[0].n;
+      if (a.n_seg > 1 && n_first >= a.seg[1].col0) { w = a.seg[1].w; c0 = a.seg[1].col0; cn = a.seg[1].n; }
+      if (a.n_seg > 2 && n_first >= a.seg[2].col0) { w = a.seg[2].w; c0 = a.seg[2].col0; cn = a.seg[2].n; }
+      if (a.n_seg > 3 && n_first >= a.seg[3].col0) { w = a.seg[3].w; c0 = a.seg[3].col0; cn = a.seg[3].n; }
+      l_base[kDmaA + i] = w;
+      l_bytes[kDmaA + i] = cn * a.K * kElemBytes;
+      l_off[kDmaA + i] = (uint32_t)(((n - c0) * a.K + ((lane & 3) ^ swz4(row)) * kElems) * kElemBytes);
+    }
   }
   const int nh = a.K / BK;  // stages along K (even)
   // Load instructions i0 .. i0+cnt-1 of stage `hs` (clamped to the last one).
@@ -251,6 +344,10 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
     stage(hs + 1, fa2, fb2, fa3, fb3, fa0, fb0, fa1, fb1);
   }
   wait_vm<0>();  // no LDS-bound load may outlive the loop
+  if constexpr (FUSE) {
+    fused_r128_epilogue<FM, FN>(a, acc, reinterpret_cast<float*>(smem), tm, tn, wm, wn, lane);
+    return;
+  }
 
   // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4.
 #pragma unroll
@@ -687,10 +784,10 @@ void launch_cfg(const ProjArgs& a, TileCfg c, hipStream_t stream, const Timing& 
     hipExtLaunchKernelGGL((proj_splitk_kernel<Tin, 256, 160, 4, 1, false>), grid, dim3(512), 0, stream, tm.start, tm.stop, 0, a,
                           tiles_m, tiles_n, gm);
   else if (c.bm == 128)
-    hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 128, 128, 2, 2>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
+    hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 128, 128, 2, 2, false>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
                        tiles_n, gm);
   else
-    hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 64, 64, 2, 2>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
+    hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 64, 64, 2, 2, false>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
                        tiles_n, gm);
 }
 
@@ -714,6 +811,18 @@ int proj_tile_rows(int64_t M, int N) {
 }
 
 hipError_t launch_proj(const ProjArgs& a, int in_dtype, hipStream_t stream, const Timing& tm) {
+  if (a.fuse.on && a.fuse.ratio == 128) {
+    const int tiles_m = (int)((a.M + 127) / 128);
+    const int tiles_n = a.fuse.d_attn / 64;
+    const dim3 grid((unsigned)(tiles_m * tiles_n));
+    if (in_dtype == 1)
+      hipExtLaunchKernelGGL((proj_mfma_kernel<uint16_t, 128, 128, 2, 2, true>), grid, dim3(kThreads), 0, stream, tm.start,
+                            tm.stop, 0, a, tiles_m, tiles_n, 4);
+    else
+      hipExtLaunchKernelGGL((proj_mfma_kernel<float, 128, 128, 2, 2, true>), grid, dim3(kThreads), 0, stream, tm.start,
+                            tm.stop, 0, a, tiles_m, tiles_n, 4);
+    return hipGetLastError();
+  }
   if (a.fuse.on) {
     const int tiles_m = (int)((a.M + 255) / 256);
     const int tiles_n = (a.fuse.d_tot + 39) / 40;
