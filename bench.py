@@ -41,8 +41,8 @@ GEMM_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc
 
 
 def fused_call(shape, n0):
-    """A ratio-4 call that starts on a window boundary pools inside the projection epilogue."""
-    return shape.ratio == 4 and n0 % 4 == 0
+    """A call that starts on a window boundary pools inside the projection epilogue."""
+    return n0 % shape.ratio == 0
 
 
 def layer_algorithmic(shape, n0, T):
@@ -50,9 +50,9 @@ def layer_algorithmic(shape, n0, T):
 
     Plain path, pool bytes: every projected kv/score element read once, the
     APE table, the rows written, and the live frontier rows written after the
-    call.  Fused ratio-4 path (window pooling in the projection epilogue), the
+    call.  Fused path (window pooling in the projection epilogue), the
     finishing launch's bytes: the pooled rows read once, the rows written and
-    the live frontier rows written from the staged tokens (read once).
+    the frontier rows the call writes from the staged tokens (read once).
     """
     lanes = [shape.d_attn] + ([shape.d_index] if shape.d_index else [])
     W = [shape.coff * d for d in lanes]
@@ -254,7 +254,8 @@ def main():
 
     gemm_ms = ms[B.KCLASS_PROJ] / max(cnt[B.KCLASS_PROJ], 1)
     all_fused = all(fused_call(s, 0) for _, s in shapes if s is not None)
-    gemm_kernel = " + ".join(sorted({"proj_splitk_kernel (fused ratio-4 pool epilogue)" if fused_call(s, 0) else
+    gemm_kernel = " + ".join(sorted({("proj_splitk_kernel (fused ratio-4 pool epilogue)" if s.ratio == 4 else
+                                      "proj_mfma_kernel (fused ratio-128 pool epilogue)") if fused_call(s, 0) else
                                      proj_kernel_name(min(T, chunk), 2 * sum(s.coff * d for d in (s.d_attn, s.d_index) if d))
                                      for _, s in shapes if s is not None}))
     pool_ms = ms[B.KCLASS_POOL] / max(cnt[B.KCLASS_POOL], 1)
