@@ -6,7 +6,9 @@
 // LDS) and stores them straight into frontier row (coff-1)*ratio + pos%ratio,
 // adding APE[pos%ratio] to scores.  Only when (pos+1) % ratio == 0 a second,
 // single-workgroup launch pools the frontier into row pos/ratio of each lane
-// (norm, tail RoPE, codec) and on ratio-4 layers copies rows 4..7 to 0..3.
+// (norm, tail RoPE, codec) and on ratio-4 layers copies rows 4..7 to 0..3;
+// it loads all of a lane's window entries at once, so the pool costs one
+// memory round trip rather than one per row.
 // The launch boundary orders the pool after every column store.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -91,47 +93,6 @@ __device__ __forceinline__ void column_target(const DecodeArgs& a, int col, int 
   }
 }
 
-// Running softmax-pool state of DPL dims over frontier rows [r0, r1) on
-// columns c .. c+DPL-1, folded one row at a time.
-template <int DPL>
-__device__ __forceinline__ void pool_rows(const LaneDev& L, int r0, int r1, int c, float (&m)[DPL],
-                                          float (&s)[DPL], float (&acc)[DPL]) {
-  for (int r = r0; r < r1; ++r) {
-    float kv[DPL], sc[DPL];
-    load_vec<DPL>(kv, L.fr_kv + (int64_t)r * L.W + c);
-    load_vec<DPL>(sc, L.fr_sc + (int64_t)r * L.W + c);
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      if (sc[i] == -INFINITY) continue;
-      if (sc[i] > m[i]) {
-        const float f = expf(m[i] - sc[i]);  // 0 when m is -inf
-        s[i] = s[i] * f + 1.f;
-        acc[i] = fmaf(acc[i], f, kv[i]);
-        m[i] = sc[i];
-      } else {
-        const float w = expf(sc[i] - m[i]);
-        s[i] += w;
-        acc[i] = fmaf(w, kv[i], acc[i]);
-      }
-    }
-  }
-}
-
-// Ratio-4 boundary for one lane on one wave: rows 0..3 on columns [0, D),
-// rows 4..7 on columns [D, 2D).
-template <int DPL>
-__device__ void r4_boundary(const DecodeArgs& a, const LaneDev& L, int64_t k, int lane) {
-  float m[DPL], s[DPL], acc[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) { m[i] = -INFINITY; s[i] = 0.f; acc[i] = 0.f; }
-  pool_rows<DPL>(L, 0, 4, lane * DPL, m, s, acc);
-  pool_rows<DPL>(L, 4, 8, L.D + lane * DPL, m, s, acc);
-  float o[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) o[i] = s[i] > 0.f ? acc[i] / s[i] : 0.f;
-  finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, L.prequant, L.rows + k * L.D, lane);
-}
-
 // Projection of one token into its frontier row.  Workgroup b covers
 // columns [8b, 8b+8), two per wave.
 template <typename Tin>
@@ -163,77 +124,146 @@ __global__ void __launch_bounds__(kDecThreads) decode_gemv_kernel(DecodeArgs a) 
   }
 }
 
-// Pool at a window boundary, on one workgroup: ratio 4 pools each lane on a
-// wave and then shifts; ratio 128 pools 32 rows per wave, merged in LDS.
-template <int DPLA, int DPLI>
-__global__ void __launch_bounds__(kDecThreads) decode_finish_kernel(DecodeArgs a) {
-  __shared__ float s_m[4][512], s_s[4][512], s_a[4][512];
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
-  const int r = a.ratio;
-  const int64_t k = a.pos / r;
-  if (r == 4) {
-    if (wave == 0)
-      r4_boundary<DPLA>(a, a.lane[0], k, lane);
-    else if (wave == 1 && a.n_lanes > 1)
-      r4_boundary<DPLI>(a, a.lane[1], k, lane);
-    __syncthreads();
-    // Half shift: rows 4..7 -> rows 0..3, full width, both tensors.
-    for (int l = 0; l < a.n_lanes; ++l) {
-      const LaneDev& L = a.lane[l];
-      const int nv = L.W / 4;
-      for (int i = tid; i < 4 * nv; i += kDecThreads) {
-        const int row = i / nv, c = (i % nv) * 4;
-        *reinterpret_cast<float4*>(L.fr_kv + row * L.W + c) =
-            *reinterpret_cast<const float4*>(L.fr_kv + (row + 4) * L.W + c);
-        *reinterpret_cast<float4*>(L.fr_sc + row * L.W + c) =
-            *reinterpret_cast<const float4*>(L.fr_sc + (row + 4) * L.W + c);
-      }
-    }
-  } else {
+// Ratio-4 window boundary on one workgroup of SA + 1 waves: SA attention
+// waves (DPLA dims per lane) and one indexer wave (DPLI per lane) load the
+// window's 8 entries of their dims at once -- rows 0..3 on columns [0, D),
+// rows 4..7 on columns [D, 2D) -- pool them like a prefill window, finish the
+// row (the attention row's sum of squares meets in LDS), and then the whole
+// workgroup copies rows 4..7 to rows 0..3.
+template <int SA, int DPLA, int DPLI>
+__global__ void __launch_bounds__(64 * (SA + 1)) decode_r4_finish_kernel(DecodeArgs a) {
+  __shared__ float s_ss[SA];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t k = a.pos / 4;
+  if (wave < SA) {
     const LaneDev& L = a.lane[0];
-    float m[DPLA], s[DPLA], acc[DPLA];
+    const int d0 = wave * (kWave * DPLA) + lane * DPLA;
+    float kv[8][DPLA], sc[8][DPLA], o[DPLA];
 #pragma unroll
-    for (int i = 0; i < DPLA; ++i) { m[i] = -INFINITY; s[i] = 0.f; acc[i] = 0.f; }
-    pool_rows<DPLA>(L, wave * 32, wave * 32 + 32, lane * DPLA, m, s, acc);
-#pragma unroll
-    for (int i = 0; i < DPLA; ++i) {
-      s_m[wave][lane * DPLA + i] = m[i];
-      s_s[wave][lane * DPLA + i] = s[i];
-      s_a[wave][lane * DPLA + i] = acc[i];
+    for (int e = 0; e < 8; ++e) {
+      const int c = (e < 4 ? 0 : L.D) + d0;
+      load_vec<DPLA>(kv[e], L.fr_kv + e * L.W + c);
+      load_vec<DPLA>(sc[e], L.fr_sc + e * L.W + c);
     }
+    pool_entries<8, DPLA>(kv, sc, o);
+    const float ss = wave_sum(row_sumsq<DPLA>(o));
+    if (lane == 0) s_ss[wave] = ss;
     __syncthreads();
-    if (wave == 0) {
-      float o[DPLA];
+    float tot = 0.f;
 #pragma unroll
-      for (int i = 0; i < DPLA; ++i) {
-        const int d = lane * DPLA + i;
-        float M = -INFINITY;
-        for (int g = 0; g < 4; ++g) M = fmaxf(M, s_m[g][d]);
-        float den = 0.f, num = 0.f;
-        if (M != -INFINITY) {
-          for (int g = 0; g < 4; ++g) {
-            if (s_m[g][d] == -INFINITY) continue;
-            const float f = expf(s_m[g][d] - M);
-            den = fmaf(s_s[g][d], f, den);
-            num = fmaf(s_a[g][d], f, num);
-          }
-        }
-        o[i] = den > 0.f ? num / den : 0.f;
+    for (int w = 0; w < SA; ++w) tot += s_ss[w];
+    finish_row_part<DPLA>(o, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, L.prequant,
+                          L.rows + k * L.D, lane);
+  } else {
+    if (a.n_lanes > 1) {
+      const LaneDev& L = a.lane[1];
+      float kv[8][DPLI], sc[8][DPLI], o[DPLI];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = (e < 4 ? 0 : L.D) + lane * DPLI;
+        load_vec<DPLI>(kv[e], L.fr_kv + e * L.W + c);
+        load_vec<DPLI>(sc[e], L.fr_sc + e * L.W + c);
       }
-      finish_row_wave<DPLA>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, L.prequant, L.rows + k * L.D, lane);
+      pool_entries<8, DPLI>(kv, sc, o);
+      __syncthreads();
+      finish_row_wave<DPLI>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, L.prequant, L.rows + k * L.D, lane);
+    } else {
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  // Half shift: rows 4..7 -> rows 0..3, full width, both tensors.
+  for (int l = 0; l < a.n_lanes; ++l) {
+    const LaneDev& L = a.lane[l];
+    const int nv = L.W / 4;
+    for (int i = threadIdx.x; i < 4 * nv; i += blockDim.x) {
+      const int row = i / nv, c = (i % nv) * 4;
+      *reinterpret_cast<float4*>(L.fr_kv + row * L.W + c) = *reinterpret_cast<const float4*>(L.fr_kv + (row + 4) * L.W + c);
+      *reinterpret_cast<float4*>(L.fr_sc + row * L.W + c) = *reinterpret_cast<const float4*>(L.fr_sc + (row + 4) * L.W + c);
     }
   }
 }
 
-template <int A>
-void launch_fin_a(const DecodeArgs& a, int dpli, hipStream_t s, const Timing& tm) {
-  const dim3 g(1), b(kDecThreads);
+// Ratio-128 window boundary on one workgroup of 16 waves: wave w pools
+// frontier rows 8w .. 8w+7 (two passes of four rows, each pass's loads issued
+// together) into a (max, sum, weighted sum) partial per dim; the partials
+// meet in LDS and wave 0 merges them and finishes the row.
+template <int DPL>
+__global__ void __launch_bounds__(1024) decode_r128_finish_kernel(DecodeArgs a) {
+  __shared__ float s_m[16][512], s_s[16][512], s_a[16][512];
+  const LaneDev& L = a.lane[0];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t k = a.pos / 128;
+  const int d0 = lane * DPL;
+  float m[DPL], den[DPL], num[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) { m[i] = -INFINITY; den[i] = 0.f; num[i] = 0.f; }
+  // Two passes of four rows (all loads of a pass issued together), merged
+  // into a running (max, sum, weighted sum).
+#pragma unroll
+  for (int e0 = 0; e0 < 8; e0 += 4) {
+    float kv[4][DPL], sc[4][DPL];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      load_vec<DPL>(kv[e], L.fr_kv + (wave * 8 + e0 + e) * L.W + d0);
+      load_vec<DPL>(sc[e], L.fr_sc + (wave * 8 + e0 + e) * L.W + d0);
+    }
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      float mp = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
+      const float mn = fmaxf(m[i], mp);
+      if (mn == -INFINITY) continue;
+      const float f = expf(m[i] - mn);  // 0 when m is -inf
+      den[i] *= f;
+      num[i] *= f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float w = expf(sc[e][i] - mn);
+        den[i] += w;
+        num[i] = fmaf(w, kv[e][i], num[i]);
+      }
+      m[i] = mn;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    s_m[wave][d0 + i] = m[i];
+    s_s[wave][d0 + i] = den[i];
+    s_a[wave][d0 + i] = num[i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float o[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    const int d = d0 + i;
+    float M = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) M = fmaxf(M, s_m[g][d]);
+    float den = 0.f, num = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        const float mg = s_m[g][d];
+        if (mg == -INFINITY) continue;
+        const float f = expf(mg - M);
+        den = fmaf(s_s[g][d], f, den);
+        num = fmaf(s_a[g][d], f, num);
+      }
+    }
+    o[i] = den > 0.f ? num / den : 0.f;
+  }
+  finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, L.prequant, L.rows + k * L.D, lane);
+}
+
+template <int SA, int DPLA>
+void launch_r4_fin(const DecodeArgs& a, int dpli, hipStream_t s, const Timing& tm) {
+  const dim3 g(1), b(64 * (SA + 1));
   switch (dpli) {
-    case 1: hipExtLaunchKernelGGL((decode_finish_kernel<A, 1>), g, b, 0, s, nullptr, tm.stop, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((decode_finish_kernel<A, 2>), g, b, 0, s, nullptr, tm.stop, 0, a); break;
-    case 4: hipExtLaunchKernelGGL((decode_finish_kernel<A, 4>), g, b, 0, s, nullptr, tm.stop, 0, a); break;
-    default: hipExtLaunchKernelGGL((decode_finish_kernel<A, 8>), g, b, 0, s, nullptr, tm.stop, 0, a); break;
+    case 1: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 1>), g, b, 0, s, nullptr, tm.stop, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 2>), g, b, 0, s, nullptr, tm.stop, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 4>), g, b, 0, s, nullptr, tm.stop, 0, a); break;
+    default: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 8>), g, b, 0, s, nullptr, tm.stop, 0, a); break;
   }
 }
 
@@ -251,13 +281,23 @@ hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, 
     hipExtLaunchKernelGGL(decode_gemv_kernel<float>, dim3(grid), dim3(kDecThreads), (uint32_t)lds, stream, tm.start,
                           stop, 0, a);
   if (boundary) {
-    const int dpla = a.lane[0].D / 64;
-    const int dpli = a.n_lanes > 1 ? a.lane[1].D / 64 : 1;
-    switch (dpla) {
-      case 1: launch_fin_a<1>(a, dpli, stream, tm); break;
-      case 2: launch_fin_a<2>(a, dpli, stream, tm); break;
-      case 4: launch_fin_a<4>(a, dpli, stream, tm); break;
-      default: launch_fin_a<8>(a, dpli, stream, tm); break;
+    if (a.ratio == 4) {
+      // Attention rows split over waves of 128 dims (64 below 128), as in prefill.
+      const int dpli = a.n_lanes > 1 ? a.lane[1].D / 64 : 1;
+      switch (a.lane[0].D) {
+        case 64: launch_r4_fin<1, 1>(a, dpli, stream, tm); break;
+        case 128: launch_r4_fin<1, 2>(a, dpli, stream, tm); break;
+        case 256: launch_r4_fin<2, 2>(a, dpli, stream, tm); break;
+        default: launch_r4_fin<4, 2>(a, dpli, stream, tm); break;
+      }
+    } else {
+      const dim3 g(1), b(1024);
+      switch (a.lane[0].D / 64) {
+        case 1: hipExtLaunchKernelGGL((decode_r128_finish_kernel<1>), g, b, 0, stream, nullptr, tm.stop, 0, a); break;
+        case 2: hipExtLaunchKernelGGL((decode_r128_finish_kernel<2>), g, b, 0, stream, nullptr, tm.stop, 0, a); break;
+        case 4: hipExtLaunchKernelGGL((decode_r128_finish_kernel<4>), g, b, 0, stream, nullptr, tm.stop, 0, a); break;
+        default: hipExtLaunchKernelGGL((decode_r128_finish_kernel<8>), g, b, 0, stream, nullptr, tm.stop, 0, a); break;
+      }
     }
   }
   return hipGetLastError();

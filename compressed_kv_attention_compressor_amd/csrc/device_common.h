@@ -127,6 +127,27 @@ __device__ __forceinline__ void rope_sincos(double pos, int i, int n_rot, double
   sincos_turns((float)(turns - rint(turns)), s, c);
 }
 
+// Softmax pool of E entries per dim: o = sum w*kv / sum w, w = exp(s - max).
+template <int E, int DPL>
+__device__ __forceinline__ void pool_entries(const float (&kv)[E][DPL], const float (&sc)[E][DPL], float (&o)[DPL]) {
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    float m = sc[0][i];
+#pragma unroll
+    for (int e = 1; e < E; ++e) m = fmaxf(m, sc[e][i]);
+    float den = 0.f, num = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float w = expf(sc[e][i] - m);
+        den += w;
+        num = fmaf(w, kv[e][i], num);
+      }
+    }
+    o[i] = den > 0.f ? num / den : 0.f;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Row epilogue.  A row of D dims is held by one or more waves; this lane
 // holds dims d0 .. d0+DPL-1.  `inv` is 1/sqrt(mean(o^2) + eps) of the whole

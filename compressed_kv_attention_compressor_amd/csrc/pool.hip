@@ -56,27 +56,6 @@ __device__ __forceinline__ void fetch_token(const PoolArgs& a, const LaneDev& L,
   for (int i = 0; i < DPL; ++i) sc[i] += ape[i];
 }
 
-// Softmax pool of E entries per dim: o = sum w*kv / sum w, w = exp(s - max).
-template <int E, int DPL>
-__device__ __forceinline__ void pool_entries(const float (&kv)[E][DPL], const float (&sc)[E][DPL], float (&o)[DPL]) {
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) {
-    float m = sc[0][i];
-#pragma unroll
-    for (int e = 1; e < E; ++e) m = fmaxf(m, sc[e][i]);
-    float den = 0.f, num = 0.f;
-    if (m != -INFINITY) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float w = expf(sc[e][i] - m);
-        den += w;
-        num = fmaf(w, kv[e][i], num);
-      }
-    }
-    o[i] = den > 0.f ? num / den : 0.f;
-  }
-}
-
 // Pooled dims c .. c+DPL-1 of ratio-4 window k of one lane.
 template <int DPL>
 __device__ __forceinline__ void r4_pool(const PoolArgs& a, const LaneDev& L, int64_t k, int c, float (&o)[DPL]) {
