@@ -454,10 +454,6 @@ int ds4c_compress_decode_one(const ds4c_layer* layer, ds4c_frontier* frontier, c
     d.K = layer->hidden;
     d.N = s.N;
     fill_proj_segments(*layer, s, d.seg, &d.n_seg);
-    for (int i = 0; i < d.n_seg; ++i) {
-      d.seg_lane[i] = i / 2;
-      d.seg_score[i] = i % 2;
-    }
     d.pos = pos;
     d.ratio = r;
     d.n_rot = layer->n_rot;

@@ -2,13 +2,14 @@
 // compressor_decode_one; Part 3 §5, the ratio-4 frontier).
 //
 // Every token: a GEMV launch in which each wave computes two projected
-// columns (dot products of weight rows with x, x staged once per workgroup in
-// LDS) and stores them straight into frontier row (coff-1)*ratio + pos%ratio,
-// adding APE[pos%ratio] to scores.  Only when (pos+1) % ratio == 0 a second,
-// single-workgroup launch pools the frontier into row pos/ratio of each lane
-// (norm, tail RoPE, codec) and on ratio-4 layers copies rows 4..7 to 0..3;
-// it loads all of a lane's window entries at once, so the pool costs one
-// memory round trip rather than one per row.
+// columns (dot products of weight rows with x) and stores them straight into
+// frontier row (coff-1)*ratio + pos%ratio, adding APE[pos%ratio] to scores.
+// Only when (pos+1) % ratio == 0 the frontier is pooled into row pos/ratio
+// of each lane (norm, tail RoPE, codec): on ratio-4 layers one workgroup
+// pools, shifts rows 4..7 to 0..3 and finishes the rows; on ratio-128 layers
+// a wide launch pools the 128 rows and a one-wave launch finishes the row.
+// Each of these reads all of its entries at once, so a boundary costs about
+// one memory round trip per launch.
 // The launch boundary orders the pool after every column store.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -20,116 +21,128 @@ namespace ds4c {
 
 namespace {
 
-constexpr int kDecThreads = 256;
+// One wave per workgroup: the grid (N/2 workgroups) then spreads evenly over the CUs.
+constexpr int kDecThreads = 64;
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
 constexpr int kColsPerWave = 2;
+// 16-byte steps a lane issues before it computes: with K up to 4096 bf16
+// (2048 fp32) values, a wave has both weight rows and x in flight at once.
+constexpr int kDotUnroll = 8;
 
-// Two dot products of K-long weight rows with x (in LDS), one wave, 16 bytes
-// per lane per step of each row.
+// acc += dot(w, x) over one 16-byte step.
+__device__ __forceinline__ float dot16(uint4 w, uint4 x, float acc, uint16_t) {
+  acc = fmaf(bf16_lo(w.x), bf16_lo(x.x), acc); acc = fmaf(bf16_hi(w.x), bf16_hi(x.x), acc);
+  acc = fmaf(bf16_lo(w.y), bf16_lo(x.y), acc); acc = fmaf(bf16_hi(w.y), bf16_hi(x.y), acc);
+  acc = fmaf(bf16_lo(w.z), bf16_lo(x.z), acc); acc = fmaf(bf16_hi(w.z), bf16_hi(x.z), acc);
+  acc = fmaf(bf16_lo(w.w), bf16_lo(x.w), acc); acc = fmaf(bf16_hi(w.w), bf16_hi(x.w), acc);
+  return acc;
+}
+__device__ __forceinline__ float dot16(uint4 w, uint4 x, float acc, float) {
+  acc = fmaf(__uint_as_float(w.x), __uint_as_float(x.x), acc);
+  acc = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), acc);
+  acc = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), acc);
+  acc = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), acc);
+  return acc;
+}
+
+// Two dot products of K-long weight rows with x, one wave.  Lane l takes
+// 16-byte step l of every 64-step span; a chunk of kDotUnroll spans is
+// loaded (x straight from global memory, where it stays cache-resident for
+// the whole grid) before any of it is used.  Steps past K load a clamped
+// in-bounds address and are zeroed, so the body has no branches.
 template <typename Tin>
 __device__ __forceinline__ void wave_dot2(const Tin* __restrict__ w0, const Tin* __restrict__ w1,
-                                          const Tin* __restrict__ xs, int K, int lane, float* d0, float* d1);
-
-template <>
-__device__ __forceinline__ void wave_dot2<uint16_t>(const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
-                                                    const uint16_t* __restrict__ xs, int K, int lane, float* d0,
-                                                    float* d1) {
+                                          const Tin* __restrict__ x, int K, int lane, float* d0, float* d1) {
+  constexpr int kVec = 16 / (int)sizeof(Tin), kSpan = kWave * kVec;
   float a0 = 0.f, a1 = 0.f;
-  for (int k = lane * 8; k < K; k += kWave * 8) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(xs + k);
-    const uint4 u = *reinterpret_cast<const uint4*>(w0 + k);
-    const uint4 v = *reinterpret_cast<const uint4*>(w1 + k);
-    const float x0 = bf16_lo(xv.x), x1 = bf16_hi(xv.x), x2 = bf16_lo(xv.y), x3 = bf16_hi(xv.y);
-    const float x4 = bf16_lo(xv.z), x5 = bf16_hi(xv.z), x6 = bf16_lo(xv.w), x7 = bf16_hi(xv.w);
-    a0 = fmaf(bf16_lo(u.x), x0, a0); a0 = fmaf(bf16_hi(u.x), x1, a0);
-    a0 = fmaf(bf16_lo(u.y), x2, a0); a0 = fmaf(bf16_hi(u.y), x3, a0);
-    a0 = fmaf(bf16_lo(u.z), x4, a0); a0 = fmaf(bf16_hi(u.z), x5, a0);
-    a0 = fmaf(bf16_lo(u.w), x6, a0); a0 = fmaf(bf16_hi(u.w), x7, a0);
-    a1 = fmaf(bf16_lo(v.x), x0, a1); a1 = fmaf(bf16_hi(v.x), x1, a1);
-    a1 = fmaf(bf16_lo(v.y), x2, a1); a1 = fmaf(bf16_hi(v.y), x3, a1);
-    a1 = fmaf(bf16_lo(v.z), x4, a1); a1 = fmaf(bf16_hi(v.z), x5, a1);
-    a1 = fmaf(bf16_lo(v.w), x6, a1); a1 = fmaf(bf16_hi(v.w), x7, a1);
+  for (int k0 = 0; k0 < K; k0 += kSpan * kDotUnroll) {
+    uint4 xv[kDotUnroll], u[kDotUnroll], v[kDotUnroll];
+#pragma unroll
+    for (int i = 0; i < kDotUnroll; ++i) {
+      const int k = min(k0 + i * kSpan + lane * kVec, K - kVec);
+      xv[i] = *reinterpret_cast<const uint4*>(x + k);
+      u[i] = *reinterpret_cast<const uint4*>(w0 + k);
+      v[i] = *reinterpret_cast<const uint4*>(w1 + k);
+    }
+#pragma unroll
+    for (int i = 0; i < kDotUnroll; ++i) {
+      const bool in = k0 + i * kSpan + lane * kVec < K;
+      const uint4 z = {0u, 0u, 0u, 0u};
+      const uint4 xi = in ? xv[i] : z;
+      a0 = dot16(in ? u[i] : z, xi, a0, Tin{});
+      a1 = dot16(in ? v[i] : z, xi, a1, Tin{});
+    }
   }
   *d0 = wave_sum(a0);
   *d1 = wave_sum(a1);
-}
-
-template <>
-__device__ __forceinline__ void wave_dot2<float>(const float* __restrict__ w0, const float* __restrict__ w1,
-                                                 const float* __restrict__ xs, int K, int lane, float* d0, float* d1) {
-  float a0 = 0.f, a1 = 0.f;
-  for (int k = lane * 4; k < K; k += kWave * 4) {
-    const float4 xv = *reinterpret_cast<const float4*>(xs + k);
-    const float4 u = *reinterpret_cast<const float4*>(w0 + k);
-    const float4 v = *reinterpret_cast<const float4*>(w1 + k);
-    a0 = fmaf(u.x, xv.x, a0); a0 = fmaf(u.y, xv.y, a0); a0 = fmaf(u.z, xv.z, a0); a0 = fmaf(u.w, xv.w, a0);
-    a1 = fmaf(v.x, xv.x, a1); a1 = fmaf(v.y, xv.y, a1); a1 = fmaf(v.z, xv.z, a1); a1 = fmaf(v.w, xv.w, a1);
-  }
-  *d0 = wave_sum(a0);
-  *d1 = wave_sum(a1);
-}
-
-// Weight row of projected column col, and where its value goes.
-template <typename Tin>
-__device__ __forceinline__ void column_target(const DecodeArgs& a, int col, int slot, int pr, const Tin** w,
-                                              float** dst, const float** ape_row) {
-  int sg = 0;
-  if (a.n_seg > 1 && col >= a.seg[1].col0) sg = 1;
-  if (a.n_seg > 2 && col >= a.seg[2].col0) sg = 2;
-  if (a.n_seg > 3 && col >= a.seg[3].col0) sg = 3;
-  const ProjSeg& S = a.seg[sg];
-  const int j = col - S.col0;
-  const LaneDev& L = a.lane[sg >> 1];
-  *w = reinterpret_cast<const Tin*>(S.w) + (int64_t)j * a.K;
-  if (sg & 1) {
-    *dst = L.fr_sc + (int64_t)slot * L.W + j;
-    *ape_row = L.ape + (int64_t)pr * L.W + j;
-  } else {
-    *dst = L.fr_kv + (int64_t)slot * L.W + j;
-    *ape_row = nullptr;
-  }
 }
 
 // Projection of one token into its frontier row.  Workgroup b covers
-// columns [8b, 8b+8), two per wave.
+// columns [2b, 2b+2); both lie in one column block (blocks have even sizes).
 template <typename Tin>
 __global__ void __launch_bounds__(kDecThreads) decode_gemv_kernel(DecodeArgs a) {
-  extern __shared__ __align__(16) unsigned char s_x_raw[];
-  Tin* s_x = reinterpret_cast<Tin*>(s_x_raw);
   const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
-  const Tin* x = reinterpret_cast<const Tin*>(a.x);
-  constexpr int kVec = 16 / (int)sizeof(Tin);
-  for (int k = tid * kVec; k < a.K; k += kDecThreads * kVec)
-    *reinterpret_cast<uint4*>(s_x + k) = *reinterpret_cast<const uint4*>(x + k);
-  __syncthreads();
-  const int r = a.ratio;
-  const int pr = (int)(a.pos % r);
-  const int slot = (r == 4 ? r : 0) + pr;
+  // Wave-uniform column index: the block selection and the argument fields
+  // it reads stay scalar, so the weight loads start after one round of
+  // argument loads.
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int c0 = (blockIdx.x * (kDecThreads / kWave) + wave) * kColsPerWave;
   if (c0 >= a.N) return;  // N is a multiple of 64: both columns exist
-  const Tin *w0, *w1;
-  float *d0, *d1;
-  const float *ape0, *ape1;
-  column_target<Tin>(a, c0, slot, pr, &w0, &d0, &ape0);
-  column_target<Tin>(a, c0 + 1, slot, pr, &w1, &d1, &ape1);
+  int sg = 0;
+  if (a.n_seg > 1 && c0 >= a.tgt[1].col0) sg = 1;
+  if (a.n_seg > 2 && c0 >= a.tgt[2].col0) sg = 2;
+  if (a.n_seg > 3 && c0 >= a.tgt[3].col0) sg = 3;
+  const GemvTarget& G = a.tgt[sg];
+  const int j = c0 - G.col0;
+  const Tin* w0 = reinterpret_cast<const Tin*>(G.w) + (int64_t)j * a.K;
+  // The APE pair is read with a vector load (a zero offset the compiler
+  // cannot see through), so no scalar load waits on global memory before
+  // the weight loads issue.
+  int zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  const float2 add = G.ape ? *reinterpret_cast<const float2*>(G.ape + j + zero) : float2{0.f, 0.f};
   float v0, v1;
-  wave_dot2<Tin>(w0, w1, s_x, a.K, lane, &v0, &v1);
-  if (lane == 0) {
-    *d0 = ape0 ? v0 + *ape0 : v0;
-    *d1 = ape1 ? v1 + *ape1 : v1;
+  wave_dot2<Tin>(w0, w0 + a.K, reinterpret_cast<const Tin*>(a.x), a.K, lane, &v0, &v1);
+  if (lane == 0) *reinterpret_cast<float2*>(G.dst + j) = float2{v0 + add.x, v1 + add.y};
+}
+
+// One thread's share of a ratio-4 boundary for dims [d0, d0+DPL) of lane L:
+// load the window's 8 entries (rows 0..3 on columns [0, D), rows 4..7 on
+// columns [D, 2D)) and rows 4..7 on columns [0, D), pool the entries into
+// o, and apply the half shift to the same columns (rows 0..3 <- rows 4..7 on
+// both halves).  The thread writes only addresses it has read itself, so
+// the shift needs no synchronisation with other threads.
+template <int DPL>
+__device__ __forceinline__ void r4_pool_and_shift(const LaneDev& L, int d0, float (&o)[DPL]) {
+  float kv[8][DPL], sc[8][DPL], kvs[4][DPL], scs[4][DPL];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = (e < 4 ? 0 : L.D) + d0;
+    load_vec<DPL>(kv[e], L.fr_kv + e * L.W + c);
+    load_vec<DPL>(sc[e], L.fr_sc + e * L.W + c);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    load_vec<DPL>(kvs[e], L.fr_kv + (e + 4) * L.W + d0);
+    load_vec<DPL>(scs[e], L.fr_sc + (e + 4) * L.W + d0);
+  }
+  pool_entries<8, DPL>(kv, sc, o);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    store_vec<DPL>(L.fr_kv + e * L.W + d0, kvs[e]);
+    store_vec<DPL>(L.fr_sc + e * L.W + d0, scs[e]);
+    store_vec<DPL>(L.fr_kv + e * L.W + L.D + d0, kv[e + 4]);
+    store_vec<DPL>(L.fr_sc + e * L.W + L.D + d0, sc[e + 4]);
   }
 }
 
 // Ratio-4 window boundary on one workgroup of SA + 1 waves: SA attention
-// waves (DPLA dims per lane) and one indexer wave (DPLI per lane) load the
-// window's 8 entries of their dims at once -- rows 0..3 on columns [0, D),
-// rows 4..7 on columns [D, 2D) -- pool them like a prefill window, finish the
-// row (the attention row's sum of squares meets in LDS), and then the whole
-// workgroup copies rows 4..7 to rows 0..3.
+// waves (DPLA dims per lane) and one indexer wave (DPLI per lane) pool and
+// shift their dims in one pass of loads, then finish the row (the attention
+// row's sum of squares meets in LDS).
 template <int SA, int DPLA, int DPLI>
 __global__ void __launch_bounds__(64 * (SA + 1)) decode_r4_finish_kernel(DecodeArgs a) {
   __shared__ float s_ss[SA];
@@ -138,14 +151,8 @@ __global__ void __launch_bounds__(64 * (SA + 1)) decode_r4_finish_kernel(DecodeA
   if (wave < SA) {
     const LaneDev& L = a.lane[0];
     const int d0 = wave * (kWave * DPLA) + lane * DPLA;
-    float kv[8][DPLA], sc[8][DPLA], o[DPLA];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = (e < 4 ? 0 : L.D) + d0;
-      load_vec<DPLA>(kv[e], L.fr_kv + e * L.W + c);
-      load_vec<DPLA>(sc[e], L.fr_sc + e * L.W + c);
-    }
-    pool_entries<8, DPLA>(kv, sc, o);
+    float o[DPLA];
+    r4_pool_and_shift<DPLA>(L, d0, o);
     const float ss = wave_sum(row_sumsq<DPLA>(o));
     if (lane == 0) s_ss[wave] = ss;
     __syncthreads();
@@ -155,105 +162,81 @@ __global__ void __launch_bounds__(64 * (SA + 1)) decode_r4_finish_kernel(DecodeA
     finish_row_part<DPLA>(o, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, L.prequant,
                           L.rows + k * L.D, lane);
   } else {
-    if (a.n_lanes > 1) {
-      const LaneDev& L = a.lane[1];
-      float kv[8][DPLI], sc[8][DPLI], o[DPLI];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = (e < 4 ? 0 : L.D) + lane * DPLI;
-        load_vec<DPLI>(kv[e], L.fr_kv + e * L.W + c);
-        load_vec<DPLI>(sc[e], L.fr_sc + e * L.W + c);
-      }
-      pool_entries<8, DPLI>(kv, sc, o);
-      __syncthreads();
+    const LaneDev& L = a.lane[1];
+    float o[DPLI];
+    if (a.n_lanes > 1) r4_pool_and_shift<DPLI>(L, lane * DPLI, o);
+    __syncthreads();
+    if (a.n_lanes > 1)
       finish_row_wave<DPLI>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, L.prequant, L.rows + k * L.D, lane);
-    } else {
-      __syncthreads();
-    }
-  }
-  __syncthreads();
-  // Half shift: rows 4..7 -> rows 0..3, full width, both tensors.
-  for (int l = 0; l < a.n_lanes; ++l) {
-    const LaneDev& L = a.lane[l];
-    const int nv = L.W / 4;
-    for (int i = threadIdx.x; i < 4 * nv; i += blockDim.x) {
-      const int row = i / nv, c = (i % nv) * 4;
-      *reinterpret_cast<float4*>(L.fr_kv + row * L.W + c) = *reinterpret_cast<const float4*>(L.fr_kv + (row + 4) * L.W + c);
-      *reinterpret_cast<float4*>(L.fr_sc + row * L.W + c) = *reinterpret_cast<const float4*>(L.fr_sc + (row + 4) * L.W + c);
-    }
   }
 }
 
-// Ratio-128 window boundary on one workgroup of 16 waves: wave w pools
-// frontier rows 8w .. 8w+7 (two passes of four rows, each pass's loads issued
-// together) into a (max, sum, weighted sum) partial per dim; the partials
-// meet in LDS and wave 0 merges them and finishes the row.
-template <int DPL>
-__global__ void __launch_bounds__(1024) decode_r128_finish_kernel(DecodeArgs a) {
-  __shared__ float s_m[16][512], s_s[16][512], s_a[16][512];
+// Ratio-128 window boundary, step 1 of 2: D/32 workgroups of eight row
+// groups each pool the frontier's 128 rows for 32 dims.  Thread t takes dim
+// 32b + t%32 and rows 16(t/32) .. 16(t/32)+15, all loads issued together;
+// the row groups' (max, sum, weighted sum) partials merge in LDS, and the
+// pooled value (not yet normalised) goes to the output row, which step 2
+// finishes in place.  Spreading the 128 rows over D/32 CUs keeps the step at
+// about one memory round trip.
+constexpr int kR128Dims = 32, kR128Groups = 8, kR128Rows = 16;
+static_assert(kR128Groups * kR128Rows == 128, "row groups cover a window");
+
+__global__ void __launch_bounds__(kR128Dims * kR128Groups) decode_r128_pool_kernel(DecodeArgs a) {
+  __shared__ float s_m[kR128Groups][kR128Dims], s_s[kR128Groups][kR128Dims], s_a[kR128Groups][kR128Dims];
   const LaneDev& L = a.lane[0];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int64_t k = a.pos / 128;
-  const int d0 = lane * DPL;
-  float m[DPL], den[DPL], num[DPL];
+  const int t = threadIdx.x, dl = t % kR128Dims, g = t / kR128Dims;
+  const int d = blockIdx.x * kR128Dims + dl;
+  float kv[kR128Rows][1], sc[kR128Rows][1];
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) { m[i] = -INFINITY; den[i] = 0.f; num[i] = 0.f; }
-  // Two passes of four rows (all loads of a pass issued together), merged
-  // into a running (max, sum, weighted sum).
+  for (int e = 0; e < kR128Rows; ++e) {
+    kv[e][0] = L.fr_kv[(g * kR128Rows + e) * L.W + d];
+    sc[e][0] = L.fr_sc[(g * kR128Rows + e) * L.W + d];
+  }
+  float m = sc[0][0];
 #pragma unroll
-  for (int e0 = 0; e0 < 8; e0 += 4) {
-    float kv[4][DPL], sc[4][DPL];
+  for (int e = 1; e < kR128Rows; ++e) m = fmaxf(m, sc[e][0]);
+  float den = 0.f, num = 0.f;
+  if (m != -INFINITY) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      load_vec<DPL>(kv[e], L.fr_kv + (wave * 8 + e0 + e) * L.W + d0);
-      load_vec<DPL>(sc[e], L.fr_sc + (wave * 8 + e0 + e) * L.W + d0);
-    }
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      float mp = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
-      const float mn = fmaxf(m[i], mp);
-      if (mn == -INFINITY) continue;
-      const float f = expf(m[i] - mn);  // 0 when m is -inf
-      den[i] *= f;
-      num[i] *= f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float w = expf(sc[e][i] - mn);
-        den[i] += w;
-        num[i] = fmaf(w, kv[e][i], num[i]);
-      }
-      m[i] = mn;
+    for (int e = 0; e < kR128Rows; ++e) {
+      const float w = expf(sc[e][0] - m);
+      den += w;
+      num = fmaf(w, kv[e][0], num);
     }
   }
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) {
-    s_m[wave][d0 + i] = m[i];
-    s_s[wave][d0 + i] = den[i];
-    s_a[wave][d0 + i] = num[i];
-  }
+  s_m[g][dl] = m;
+  s_s[g][dl] = den;
+  s_a[g][dl] = num;
   __syncthreads();
-  if (wave != 0) return;
-  float o[DPL];
+  if (t >= kR128Dims) return;
+  float M = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) {
-    const int d = d0 + i;
-    float M = -INFINITY;
+  for (int h = 0; h < kR128Groups; ++h) M = fmaxf(M, s_m[h][dl]);
+  float D = 0.f, A = 0.f;
+  if (M != -INFINITY) {
 #pragma unroll
-    for (int g = 0; g < 16; ++g) M = fmaxf(M, s_m[g][d]);
-    float den = 0.f, num = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        const float mg = s_m[g][d];
-        if (mg == -INFINITY) continue;
-        const float f = expf(mg - M);
-        den = fmaf(s_s[g][d], f, den);
-        num = fmaf(s_a[g][d], f, num);
-      }
+    for (int h = 0; h < kR128Groups; ++h) {
+      const float mh = s_m[h][dl];
+      const float f = mh == -INFINITY ? 0.f : expf(mh - M);
+      D = fmaf(s_s[h][dl], f, D);
+      A = fmaf(s_a[h][dl], f, A);
     }
-    o[i] = den > 0.f ? num / den : 0.f;
   }
-  finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, L.prequant, L.rows + k * L.D, lane);
+  L.rows[(a.pos / 128) * L.D + d] = D > 0.f ? A / D : 0.f;
+}
+
+// Ratio-128 window boundary, step 2 of 2: one wave reads the pooled row back
+// and finishes it (norm, tail RoPE, FP8 round trip) in place.  Every store
+// depends on the row's sum of squares, so all reads precede all writes.
+template <int DPL>
+__global__ void __launch_bounds__(kWave) decode_r128_finish_kernel(DecodeArgs a) {
+  const LaneDev& L = a.lane[0];
+  const int lane = threadIdx.x;
+  const int64_t k = a.pos / 128;
+  float* row = L.rows + k * L.D;
+  float o[DPL];
+  load_vec<DPL>(o, row + lane * DPL);
+  finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, L.prequant, row, lane);
 }
 
 template <int SA, int DPLA>
@@ -271,15 +254,25 @@ void launch_r4_fin(const DecodeArgs& a, int dpli, hipStream_t s, const Timing& t
 
 hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, const Timing& tm) {
   const bool boundary = (a.pos + 1) % a.ratio == 0;
-  const unsigned grid = (unsigned)((a.N + kColsPerWave * 4 - 1) / (kColsPerWave * 4));
-  const size_t lds = (size_t)a.K * (in_dtype == 1 ? 2 : 4);
+  constexpr int kColsPerBlock = kColsPerWave * (kDecThreads / kWave);
+  const unsigned grid = (unsigned)((a.N + kColsPerBlock - 1) / kColsPerBlock);
   hipEvent_t stop = boundary ? nullptr : tm.stop;
+  DecodeArgs g = a;
+  const int pr = (int)(a.pos % a.ratio), slot = (a.ratio == 4 ? 4 : 0) + pr;
+  for (int s = 0; s < a.n_seg; ++s) {
+    const LaneDev& L = a.lane[s >> 1];
+    const bool score = (s & 1) != 0;
+    g.tgt[s].w = a.seg[s].w;
+    g.tgt[s].dst = (score ? L.fr_sc : L.fr_kv) + (int64_t)slot * L.W;
+    g.tgt[s].ape = score ? L.ape + (int64_t)pr * L.W : nullptr;
+    g.tgt[s].col0 = a.seg[s].col0;
+  }
   if (in_dtype == 1)
-    hipExtLaunchKernelGGL(decode_gemv_kernel<uint16_t>, dim3(grid), dim3(kDecThreads), (uint32_t)lds, stream, tm.start,
-                          stop, 0, a);
+    hipExtLaunchKernelGGL(decode_gemv_kernel<uint16_t>, dim3(grid), dim3(kDecThreads), 0, stream, tm.start,
+                          stop, 0, g);
   else
-    hipExtLaunchKernelGGL(decode_gemv_kernel<float>, dim3(grid), dim3(kDecThreads), (uint32_t)lds, stream, tm.start,
-                          stop, 0, a);
+    hipExtLaunchKernelGGL(decode_gemv_kernel<float>, dim3(grid), dim3(kDecThreads), 0, stream, tm.start,
+                          stop, 0, g);
   if (boundary) {
     if (a.ratio == 4) {
       // Attention rows split over waves of 128 dims (64 below 128), as in prefill.
@@ -291,7 +284,9 @@ hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, 
         default: launch_r4_fin<4, 2>(a, dpli, stream, tm); break;
       }
     } else {
-      const dim3 g(1), b(1024);
+      hipExtLaunchKernelGGL(decode_r128_pool_kernel, dim3(a.lane[0].D / kR128Dims), dim3(kR128Dims * kR128Groups), 0,
+                            stream, nullptr, nullptr, 0, a);
+      const dim3 g(1), b(kWave);
       switch (a.lane[0].D / 64) {
         case 1: hipExtLaunchKernelGGL((decode_r128_finish_kernel<1>), g, b, 0, stream, nullptr, tm.stop, 0, a); break;
         case 2: hipExtLaunchKernelGGL((decode_r128_finish_kernel<2>), g, b, 0, stream, nullptr, tm.stop, 0, a); break;

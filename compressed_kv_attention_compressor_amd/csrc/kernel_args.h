@@ -85,14 +85,23 @@ struct PoolArgs {
   int64_t carry_lo;
 };
 
+// Where a decode column block goes for the current token.
+struct GemvTarget {
+  const void* w;        // weights [n, K] of the block
+  float* dst;           // frontier row (coff-1)*ratio + pos%ratio, at the block's first dim
+  const float* ape;     // APE row pos%ratio at the block's first dim (score blocks), else null
+  int col0;             // first output column of the block
+};
+
 struct DecodeArgs {
   const void* x;        // [K]
   int K;
   int N;
   int n_seg;
   ProjSeg seg[4];
-  int seg_lane[4];      // lane index of each segment
-  int seg_score[4];     // 1 if the segment holds scores, 0 if kv
+  // Column block s resolved for this token on the host (blocks are ordered
+  // attention kv, attention score, indexer kv, indexer score):
+  GemvTarget tgt[4];
   int64_t pos;
   int ratio;
   int n_rot;

@@ -154,6 +154,28 @@ def test_chunked_and_decode(name, plan):
     compare_all(shape, g, spec, st, n)
 
 
+# The largest hidden size the boundary accepts (16384), and fp32 at 4096:
+# decode dot products then run over several unrolled chunks, the prefill
+# GEMM over its longest K loop.
+LARGE_K = {
+    "r4_h16384_bf16": (synth.LayerShape(ratio=4, hidden=16384, d_attn=128, d_index=64, dtype="bf16"), [5, -7, 9, -3]),
+    "r128_h4096_f32": (synth.LayerShape(ratio=128, hidden=4096, d_attn=128, d_index=0, dtype="f32"), [100, -40, 20]),
+}
+
+
+@pytest.mark.parametrize("name", list(LARGE_K))
+def test_large_hidden_decode(name):
+    shape, plan = LARGE_K[name]
+    n = sum(abs(s) for s in plan)
+    _say(f"[parity] {name} plan {plan} n={n}")
+    wid = 80 + list(LARGE_K).index(name)
+    p = synth.layer_params(wid, 0, shape)
+    x = synth.hidden_states(wid, shape.hidden, 0, n, shape.dtype)
+    g = run_gpu(shape, p, x, plan)
+    spec, st = run_oracle(shape, p, x)
+    compare_all(shape, g, spec, st, n)
+
+
 @pytest.mark.parametrize("name", ["r4_d128", "r128_d512"])
 def test_single_tokens_and_tiny_calls(name):
     _say(f"[parity] {name} tiny calls")
