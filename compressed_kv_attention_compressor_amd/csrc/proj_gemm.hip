@@ -83,6 +83,12 @@ __device__ __forceinline__ void load_lds16(const void* base, int bytes, __attrib
 }
 
 
+// Softmax weight e^x for x <= 0 in the pooling epilogues: 2^(x log2 e)
+// through the hardware base-2 exponential.  Rounding x log2 e costs a
+// relative error of at most |x| * 2^-24 * ln 2 in the result (below 1e-6 for
+// |x| < 20) plus the instruction's own error of about one ulp; e^-inf = 0.
+__device__ __forceinline__ float pool_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
 // ---------------------------------------------------------------------------
 // Fused ratio-128 epilogue (Part 3 §4): a 128-token x 64-dim tile is exactly
 // window j = tm of a call that starts on a window boundary.  The tile goes
@@ -131,7 +137,7 @@ __device__ __forceinline__ void fused_r128_epilogue(const ProjArgs& a, const f32
     float s = 0.f, w = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      const float x = expf(sc[e] - ms);
+      const float x = pool_exp(sc[e] - ms);
       s += x;
       w = fmaf(x, kv[e], w);
     }
@@ -141,7 +147,7 @@ __device__ __forceinline__ void fused_r128_epilogue(const ProjArgs& a, const f32
       const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64), w2 = __shfl_xor(w, o, 64);
       const float mm = fmaxf(m, m2);
       const float mms = mm == -INFINITY ? 0.f : mm;
-      const float f1 = expf(m - mms), f2 = expf(m2 - mms);
+      const float f1 = pool_exp(m - mms), f2 = pool_exp(m2 - mms);
       s = fmaf(s, f1, s2 * f2);
       w = fmaf(w, f1, w2 * f2);
       m = mm;
@@ -369,10 +375,10 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
 // Fused ratio-4 epilogue (Part 3 §4-§5) of a 256-token x 40-dim tile (see
 // FuseArgs for the column runs).  The two wave groups' partial sums meet in
 // an LDS copy of the tile; then each (window, dim) of the tile is pooled:
-// window g >= 1 of the tile from its own rows, window 0's current half and
-// the next tile's window 0 previous half as (max, sum, weighted sum)
-// partials.  The tokens the frontier keeps are staged in the plain column
-// layout with APE added to their scores.
+// window g >= 1 of the tile from its own rows as one 8-entry softmax, window
+// 0's current half and the next tile's window 0 previous half as (max, sum,
+// weighted sum) partials.  The tokens the frontier keeps are staged in the
+// plain column layout with APE added to their scores.
 // ---------------------------------------------------------------------------
 // LDS index of tile element (row, col): 160-float rows, rotated by 32
 // columns on odd 4-row groups so that the two half-waves of an accumulator
@@ -395,11 +401,34 @@ __device__ __forceinline__ Part3 half_pool(const float (&kv)[4], const float (&s
   p.w = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float x = expf(sc[e] - ms);
+    const float x = pool_exp(sc[e] - ms);
     p.s += x;
     p.w = fmaf(x, kv[e], p.w);
   }
   return p;
+}
+
+// Softmax pool of one dim over a whole window: previous half (kp, sp) and
+// current half (kc, sc).  An all-empty window gives 0.
+__device__ __forceinline__ float window_pool(const float (&kp)[4], const float (&sp)[4], const float (&kc)[4],
+                                             const float (&sc)[4]) {
+  const float m =
+      fmaxf(fmaxf(fmaxf(sp[0], sp[1]), fmaxf(sp[2], sp[3])), fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+  const float ms = m == -INFINITY ? 0.f : m;
+  float den = 0.f, num = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x = pool_exp(sp[e] - ms);
+    den += x;
+    num = fmaf(x, kp[e], num);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x = pool_exp(sc[e] - ms);
+    den += x;
+    num = fmaf(x, kc[e], num);
+  }
+  return den > 0.f ? num / den : 0.f;
 }
 
 template <int WM, int FN>
@@ -407,28 +436,47 @@ __device__ __forceinline__ void fused_r4_epilogue(const ProjArgs& a, f32x16 (&ac
                                                   int wq, int grp, int lane) {
   const FuseArgs& f = a.fuse;
   const int h = lane >> 5, r32 = lane & 31;
-  // The two groups' partial sums meet as in the plain epilogue (round r:
-  // group 1-r parks block fm = r lane-major, group r adds it), then each
-  // group stores its complete 32-row blocks into the tile.
-  asm volatile("s_barrier" ::: "memory");
+  // Thread t < 480 pools dim 40*tn + t % 40 below; its APE values are read
+  // first so that their latency hides behind the combine.
+  const int dd = threadIdx.x % 40, rg = threadIdx.x / 40;
+  const int dim = tn * 40 + dd;
+  const bool pools = threadIdx.x < 480 && dim < f.d_tot;
+  const int l = dim < f.d_attn ? 0 : 1;
+  const int ld = dim - (l ? f.d_attn : 0), dl = l ? f.d_idx : f.d_attn, W = f.W[l];
+  const int ldc = pools ? ld : 0;  // in-bounds address for every thread
+  float ape_p[4], ape_c[4];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    if (grp != r) {
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) tile[((wq * FN + fn) * 16 + v) * 64 + lane] = acc[r][fn][v];
-    }
-    __syncthreads();
-    if (grp == r) {
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[r][fn][v] += tile[((wq * FN + fn) * 16 + v) * 64 + lane];
-    }
-    __syncthreads();
+  for (int e = 0; e < 4; ++e) {
+    ape_p[e] = f.ape[l][e * W + ldc];
+    ape_c[e] = f.ape[l][e * W + dl + ldc];
   }
+
+  // The two groups' partial sums meet: group g parks its partial of block
+  // fm = 1 - g lane-major (conflict free) in LDS half g, adds the other
+  // group's partial of block fm = g from half 1 - g, and stores the finished
+  // block into the tile.  Each element takes exactly one addition, so the
+  // result does not depend on which group owns it.
   // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4.
+  constexpr int kPark = 4 * FN * 16 * 64;  // floats parked per group
+  asm volatile("s_barrier" ::: "memory");  // every wave is done with the ring the tile overlaps
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm) {
+    if (fm == grp) continue;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tile[grp * kPark + ((wq * FN + fn) * 16 + v) * 64 + lane] = acc[fm][fn][v];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm) {
+    if (fm != grp) continue;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[fm][fn][v] += tile[(1 - grp) * kPark + ((wq * FN + fn) * 16 + v) * 64 + lane];
+  }
+  __syncthreads();
 #pragma unroll
   for (int fm = 0; fm < 2; ++fm) {
     if (fm != grp) continue;
@@ -442,72 +490,77 @@ __device__ __forceinline__ void fused_r4_epilogue(const ProjArgs& a, f32x16 (&ac
 
   const int64_t t0 = (int64_t)tm * 256;  // call-relative token of tile row 0
   const int64_t j0 = (int64_t)tm * 64;   // window of tile group 0
-  // Thread t < 480 owns dim 40*tn + t % 40 and walks the tile's 4-row groups
-  // g = t / 40, t / 40 + 12, ...: group g gives the current half of window g
-  // and, with group g-1, its full pool; group 63 also gives the previous half
-  // of the next tile's window 0.  Loads and arithmetic are unconditional.
-  const int dd = threadIdx.x % 40, g_first = threadIdx.x / 40;
-  const int dim = tn * 40 + dd;
-  if (threadIdx.x < 480 && dim < f.d_tot) {
-    const int l = dim < f.d_attn ? 0 : 1;
-    const int ld = dim - (l ? f.d_attn : 0), dl = l ? f.d_idx : f.d_attn, W = f.W[l];
-    float ape_p[4], ape_c[4];
+  // Thread t < 480 owns dim 40*tn + t % 40 and the 4-row groups [g_lo, g_hi)
+  // of range t / 40 (twelve ranges of five or six groups).  Group g holds
+  // the current half of window g and the previous half of window g + 1, so
+  // each group is read once: window g pools the previous half kept from
+  // group g - 1 with group g's current half.
+  if (pools) {
+    const int g_lo = rg * 64 / 12, g_hi = (rg + 1) * 64 / 12;
+    float kp[4], sp[4];  // previous half of the next window
+    if (g_lo > 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ape_p[e] = f.ape[l][e * W + ld];
-      ape_c[e] = f.ape[l][e * W + dl + ld];
+      for (int e = 0; e < 4; ++e) {
+        kp[e] = tile[tile_ix(4 * (g_lo - 1) + e, dd)];
+        sp[e] = tile[tile_ix(4 * (g_lo - 1) + e, 80 + dd)] + ape_p[e];
+      }
+    } else {
+      // Window j0: its previous half lies in the previous tile (or, for
+      // tile 0, in rows 0..3 of the incoming frontier, whose scores already
+      // hold their APE), so both halves are written as partials.
+      float kc[4], sc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kc[e] = tile[tile_ix(e, 40 + dd)];
+        sc[e] = tile[tile_ix(e, 120 + dd)] + ape_c[e];
+        kp[e] = tile[tile_ix(e, dd)];
+        sp[e] = tile[tile_ix(e, 80 + dd)] + ape_p[e];
+      }
+      if (j0 < f.n_emit) {
+        const Part3 pc = half_pool(kc, sc);
+        float* q = f.part + ((int64_t)tm * 2 + 1) * 3 * f.d_tot + dim;
+        q[0] = pc.m;
+        q[f.d_tot] = pc.s;
+        q[2 * f.d_tot] = pc.w;
+        if (tm == 0) {
+          float kf[4], sf[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kf[e] = f.fr_kv[l][e * W + ld];
+            sf[e] = f.fr_sc[l][e * W + ld];
+          }
+          const Part3 pf = half_pool(kf, sf);
+          float* q0 = f.part + dim;
+          q0[0] = pf.m;
+          q0[f.d_tot] = pf.s;
+          q0[2 * f.d_tot] = pf.w;
+        }
+      }
     }
-    for (int g = g_first; g < 64; g += 12) {
-      const int64_t jw = j0 + g;
-      const int gp = g > 0 ? g - 1 : 0;
-      float kc[4], sc[4], kq[4], sq[4], kp[4], sp[4];
+    for (int g = g_lo > 0 ? g_lo : 1; g < g_hi; ++g) {
+      float kc[4], sc[4], kq[4], sq[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         kc[e] = tile[tile_ix(4 * g + e, 40 + dd)];
         sc[e] = tile[tile_ix(4 * g + e, 120 + dd)] + ape_c[e];
         kq[e] = tile[tile_ix(4 * g + e, dd)];
         sq[e] = tile[tile_ix(4 * g + e, 80 + dd)] + ape_p[e];
-        kp[e] = tile[tile_ix(4 * gp + e, dd)];
-        sp[e] = tile[tile_ix(4 * gp + e, 80 + dd)] + ape_p[e];
       }
-      const Part3 pc = half_pool(kc, sc);  // current half of window g
-      const Part3 pq = half_pool(kq, sq);  // previous half of window g+1
-      const Part3 pp = half_pool(kp, sp);  // previous half of window g
-      const float m = fmaxf(pc.m, pp.m);
-      const float ms = m == -INFINITY ? 0.f : m;
-      const float fc = expf(pc.m - ms), fp = expf(pp.m - ms);
-      const float den = fmaf(pc.s, fc, pp.s * fp), num = fmaf(pc.w, fc, pp.w * fp);
-      if (jw < f.n_emit) {
-        if (g > 0) {
-          f.o[jw * f.d_tot + dim] = den > 0.f ? num / den : 0.f;
-        } else {
-          float* q = f.part + ((int64_t)tm * 2 + 1) * 3 * f.d_tot + dim;
-          q[0] = pc.m;
-          q[f.d_tot] = pc.s;
-          q[2 * f.d_tot] = pc.w;
-          if (tm == 0) {
-            // Window 0's previous half: tokens n0-4 .. n0-1 in rows 0..3 of
-            // the incoming frontier (scores already hold their APE).
-            float kf[4], sf[4];
+      const int64_t jw = j0 + g;
+      if (jw < f.n_emit) f.o[jw * f.d_tot + dim] = window_pool(kp, sp, kc, sc);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              kf[e] = f.fr_kv[l][e * W + ld];
-              sf[e] = f.fr_sc[l][e * W + ld];
-            }
-            const Part3 pf = half_pool(kf, sf);
-            float* q0 = f.part + dim;
-            q0[0] = pf.m;
-            q0[f.d_tot] = pf.s;
-            q0[2 * f.d_tot] = pf.w;
-          }
-        }
+      for (int e = 0; e < 4; ++e) {
+        kp[e] = kq[e];
+        sp[e] = sq[e];
       }
-      if (g == 63 && jw + 1 < f.n_emit) {
-        float* q = f.part + ((int64_t)(tm + 1) * 2 + 0) * 3 * f.d_tot + dim;
-        q[0] = pq.m;
-        q[f.d_tot] = pq.s;
-        q[2 * f.d_tot] = pq.w;
-      }
+    }
+    // Group 63's previous half opens the next tile's window 0.
+    if (g_hi == 64 && j0 + 64 < f.n_emit) {
+      const Part3 pq = half_pool(kp, sp);
+      float* q = f.part + ((int64_t)(tm + 1) * 2 + 0) * 3 * f.d_tot + dim;
+      q[0] = pq.m;
+      q[f.d_tot] = pq.s;
+      q[2 * f.d_tot] = pq.w;
     }
   }
   // Kept tokens: call-relative carry_lo .. M-1 that fall in this tile.
@@ -553,6 +606,7 @@ __global__ void __launch_bounds__(512) proj_splitk_kernel(ProjArgs a, int tiles_
   static_assert(kRows % 8 == 0, "whole 8-row loads");
   static_assert(4 * FN * 16 * 64 * 4 <= 3 * kStage * 16, "exchange buffer fits the ring");
   static_assert(!FUSE || (BM == 256 && BN == 160), "the fused epilogue holds a 256 x 160 tile");
+  static_assert(!FUSE || 2 * 4 * FN * 16 * 64 <= BM * BN, "both groups' parked partial sums fit the tile");
   // The fused epilogue stages the whole fp32 tile (160 KiB) in LDS.
   constexpr int kSmem = FUSE ? BM * BN / 4 : 3 * kStage;
   static_assert(kSmem >= 3 * kStage, "ring fits");
