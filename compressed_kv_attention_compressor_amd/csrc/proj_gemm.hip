@@ -600,15 +600,18 @@ __global__ void __launch_bounds__(512) proj_splitk_kernel(ProjArgs a, int tiles_
   constexpr int kRows = BM + BN;
   constexpr int kIns = kRows / 8;            // load instructions per stage
   constexpr int kMaxIns = (kIns + 7) / 8;    // per wave
-  constexpr int kStage = kRows * 8;          // 16-byte slots per stage
+  // 16-byte slots per stage: the operand rows, then one 64-slot pad that
+  // takes the spare issue of waves with fewer load instructions.
+  constexpr int kStage = kRows * 8 + 64;
   static_assert(WM * WN == 4, "four waves per group");
   static_assert(FM == 2, "the final exchange splits the two 32-row blocks");
   static_assert(kRows % 8 == 0, "whole 8-row loads");
   static_assert(4 * FN * 16 * 64 * 4 <= 3 * kStage * 16, "exchange buffer fits the ring");
+  static_assert(3 * kStage * 16 <= 160 * 1024, "ring fits the LDS");
   static_assert(!FUSE || (BM == 256 && BN == 160), "the fused epilogue holds a 256 x 160 tile");
   static_assert(!FUSE || 2 * 4 * FN * 16 * 64 <= BM * BN, "both groups' parked partial sums fit the tile");
   // The fused epilogue stages the whole fp32 tile (160 KiB) in LDS.
-  constexpr int kSmem = FUSE ? BM * BN / 4 : 3 * kStage;
+  constexpr int kSmem = FUSE && BM * BN / 4 > 3 * kStage ? BM * BN / 4 : 3 * kStage;
   static_assert(kSmem >= 3 * kStage, "ring fits");
   __shared__ u32x4 smem[kSmem];
 
@@ -634,7 +637,7 @@ __global__ void __launch_bounds__(512) proj_splitk_kernel(ProjArgs a, int tiles_
   // Stage row r < BM is x row m0 + r, row BM + c is weight row n0 + c.
   // Loads go through buffer descriptors with per-lane byte offsets; the K
   // tile advances through the scalar offset.  Waves without an i-th
-  // instruction repeat the last one (same bytes into the same slots).
+  // instruction issue an empty load into the stage's pad instead.
   constexpr int kElemBytes = (int)sizeof(Tin);
   const int64_t rows_left = a.M - m0;
   const char* x_base = reinterpret_cast<const char*>(a.x) + m0 * a.K * kElemBytes;
@@ -690,6 +693,13 @@ __global__ void __launch_bounds__(512) proj_splitk_kernel(ProjArgs a, int tiles_
       l_base[i] = w;
       l_bytes[i] = cn * a.K * kElemBytes;
       l_off[i] = (uint32_t)(((n - c0) * a.K + chunk * kElems) * kElemBytes);
+    }
+    if (wave + 8 * i >= kIns) {
+      // Spare issue of a wave with fewer instructions: an empty buffer range
+      // (every lane out of range, nothing fetched) into the stage's pad.
+      l_slot[i] = kRows * 8;
+      l_bytes[i] = 0;
+      l_off[i] = 0;
     }
   }
   auto issue_one = [&](int kt, int st, int i) {
