@@ -73,6 +73,12 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// The same, and until every LDS access of this wave has completed.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
 
 // One 16-byte-per-lane load into LDS through a buffer descriptor over
 // [base, base + bytes); lane l's data lands at lds + 16*l.
@@ -772,21 +778,24 @@ __global__ void __launch_bounds__(512) proj_splitk_kernel(ProjArgs a, int tiles_
   const int kk0 = 2 * grp;
   issue(0, 0);
   issue(min(1, nk - 1), 1);
-  wait_vm<0>();
+  issue(min(2, nk - 1), 2);
+  wait_vm<2 * kMaxIns>();  // tile 0 (loads complete in issue order)
   asm volatile("s_barrier" ::: "memory");
   frags(fa0, fb0, 0, kk0);
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt % 3;
     sub_step(fa0, fb0, fa1, fb1, st, kk0 + 1, 0, 0, 0);
-    // Tile kt+1 has landed for every wave and every wave is done with tile
-    // kt-1, whose stage the loads below refill.  Past the last tile the
-    // loads re-read the last tile into a stage nothing reads again, so the
+    // Past the barrier tile kt+1 has landed for every wave (only this wave's
+    // kMaxIns loads of tile kt+2 may still be in flight) and every wave's
+    // reads of stage st have completed, so the loads below refill stage st
+    // with tile kt+3, two iterations ahead of its use.  Past the last tile
+    // they re-read the last tile into a stage nothing reads again, so the
     // loop body has no branches and the compiler's wait counts stay exact.
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<0>();
+    wait_vm_lds<kMaxIns>();
     asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    sub_step(fa1, fb1, fa0, fb0, (kt + 1) % 3, kk0, min(kt + 2, nk - 1), (kt + 2) % 3, kMaxIns);
+    sub_step(fa1, fb1, fa0, fb0, (kt + 1) % 3, kk0, min(kt + 3, nk - 1), st, kMaxIns);
   }
   wait_vm<0>();  // the exchange below reuses the ring
 
