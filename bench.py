@@ -255,7 +255,7 @@ def main():
     gemm_ms = ms[B.KCLASS_PROJ] / max(cnt[B.KCLASS_PROJ], 1)
     all_fused = all(fused_call(s, 0) for _, s in shapes if s is not None)
     gemm_kernel = " + ".join(sorted({("proj_splitk_kernel (fused ratio-4 pool epilogue)" if s.ratio == 4 else
-                                      "proj_mfma_kernel (fused ratio-128 pool epilogue)") if fused_call(s, 0) else
+                                      "proj_r128_splitk4_kernel (fused ratio-128 pool epilogue)") if fused_call(s, 0) else
                                      proj_kernel_name(min(T, chunk), 2 * sum(s.coff * d for d in (s.d_attn, s.d_index) if d))
                                      for _, s in shapes if s is not None}))
     pool_ms = ms[B.KCLASS_POOL] / max(cnt[B.KCLASS_POOL], 1)

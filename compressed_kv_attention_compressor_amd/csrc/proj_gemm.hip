@@ -2,7 +2,7 @@
 // blocks of a layer (wkv and wgate of each lane, Part 3 §4) written as one
 // [T, N] float32 matrix.  Both operands are K-contiguous (x rows, weight rows).
 //
-// MFMA design for gfx950 (wave64), two kernels sharing these rules:
+// MFMA design for gfx950 (wave64), three kernels sharing these rules:
 //  * 32x32 output blocks with fp32 accumulators: bf16 inputs use
 //    v_mfma_f32_32x32x16_bf16, float32 inputs v_mfma_f32_32x32x2_f32.
 //  * Operand rows reach LDS through buffer loads that write LDS directly
@@ -24,8 +24,14 @@
 // proj_splitk_kernel (256 x 160 tiles, one per CU at 4096 x 2560): eight
 // waves, two per SIMD, split the four K sub-steps of each 64-column K tile
 // (128-byte rows, 3-stage ring); the partial sums are combined through LDS.
-// proj_mfma_kernel (128 x 128 and 64 x 64 tiles): four waves, 32-column K
-// stages (64-byte rows) in a 6-stage ring, loads issued five stages ahead.
+// With a fused epilogue it pools ratio-4 windows.
+// proj_r128_splitk4_kernel (128 x 128 tiles, a call on ratio-128 window
+// boundaries): eight waves, a four-way split of K over 128 x 64 wave blocks
+// (128-byte rows, 4-stage ring); one tile is one window, pooled in the
+// epilogue.
+// proj_mfma_kernel (128 x 128 and 64 x 64 tiles, plain output): four waves,
+// 32-column K stages (64-byte rows) in a 6-stage ring, loads issued five
+// stages ahead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -95,86 +101,14 @@ __device__ __forceinline__ void load_lds16(const void* base, int bytes, __attrib
 // |x| < 20) plus the instruction's own error of about one ulp; e^-inf = 0.
 __device__ __forceinline__ float pool_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 
-// ---------------------------------------------------------------------------
-// Fused ratio-128 epilogue (Part 3 §4): a 128-token x 64-dim tile is exactly
-// window j = tm of a call that starts on a window boundary.  The tile goes
-// through LDS; four lanes per dim pool 32 tokens each (APE added) and merge
-// their (max, sum, weighted sum) by shuffles; the tokens of a trailing
-// partial window are staged in the plain column layout for the frontier.
-// ---------------------------------------------------------------------------
+// LDS index of element (row, col) of a 128 x 128 fp32 tile: rotated by 32
+// columns on odd 4-row groups so that the two half-waves of an accumulator
+// store (rows r and r + 4) hit different banks.
 __device__ __forceinline__ int tile128_ix(int row, int col) {
   return row * 128 + ((col + (((row >> 2) & 1) << 5)) & 127);
 }
 
-template <int FM, int FN>
-__device__ __forceinline__ void fused_r128_epilogue(const ProjArgs& a, const f32x16 (&acc)[FM][FN], float* tile, int tm,
-                                                    int tn, int wm, int wn, int lane) {
-  const FuseArgs& f = a.fuse;
-  const int h = lane >> 5, r32 = lane & 31;
-  asm volatile("s_barrier" ::: "memory");
-  // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4.
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        tile[tile128_ix(wm * FM * 32 + fm * 32 + 8 * (v >> 2) + 4 * h + (v & 3), wn * FN * 32 + fn * 32 + r32)] =
-            acc[fm][fn][v];
-  __syncthreads();
-  const int D = f.d_attn;
-  const int64_t t0 = (int64_t)tm * 128;
-  const int64_t jw = tm;
-  if (jw < f.n_emit) {
-    const int dd = threadIdx.x >> 2, qq = threadIdx.x & 3;
-    const int dim = tn * 64 + dd;
-    const float* ape = f.ape[0];
-    float kv[32], sc[32];
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int row = qq * 32 + e;
-      kv[e] = tile[tile128_ix(row, dd)];
-      sc[e] = tile[tile128_ix(row, 64 + dd)] + ape[row * D + dim];
-    }
-    float m = sc[0];
-#pragma unroll
-    for (int e = 1; e < 32; ++e) m = fmaxf(m, sc[e]);
-    const float ms = m == -INFINITY ? 0.f : m;
-    float s = 0.f, w = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const float x = pool_exp(sc[e] - ms);
-      s += x;
-      w = fmaf(x, kv[e], w);
-    }
-    // Merge the four quarters (lanes 4*dd .. 4*dd+3 of this wave).
-#pragma unroll
-    for (int o = 1; o < 4; o <<= 1) {
-      const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64), w2 = __shfl_xor(w, o, 64);
-      const float mm = fmaxf(m, m2);
-      const float mms = mm == -INFINITY ? 0.f : mm;
-      const float f1 = pool_exp(m - mms), f2 = pool_exp(m2 - mms);
-      s = fmaf(s, f1, s2 * f2);
-      w = fmaf(w, f1, w2 * f2);
-      m = mm;
-    }
-    if (qq == 0) f.o[jw * D + dim] = s > 0.f ? w / s : 0.f;
-  }
-  // Kept tokens: call-relative carry_lo .. M-1 that fall in this tile.
-  const int64_t s_lo = f.carry_lo > t0 ? f.carry_lo : t0;
-  const int64_t s_hi = a.M < t0 + 128 ? a.M : t0 + 128;
-  const int n_rows = s_hi > s_lo ? (int)(s_hi - s_lo) : 0;
-  for (int item = threadIdx.x; item < n_rows * 128; item += blockDim.x) {
-    const int r = item >> 7, q = item & 127;
-    const int64_t t = s_lo + r;
-    const int dim = tn * 64 + (q & 63);
-    float v = tile[tile128_ix((int)(t - t0), q)];
-    if (q >= 64) v += f.ape[0][(int)(t & 127) * D + dim];
-    f.stage[(t - f.carry_lo) * f.n_orig + (q >= 64 ? D : 0) + dim] = v;
-  }
-}
-
-template <typename Tin, int BM, int BN, int WM, int WN, bool FUSE>
+template <typename Tin, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int tiles_m, int tiles_n, int gm) {
   constexpr int kElems = 16 / (int)sizeof(Tin);  // elements per 16-byte chunk
   constexpr int kElemBytes = (int)sizeof(Tin);
@@ -192,8 +126,6 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
   static_assert(WM * WN == kWaves, "four waves");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "32x32 blocks");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "whole 16-row loads");
-  static_assert(!FUSE || (BM == 128 && BN == 128 && WM == 2 && WN == 2), "the fused epilogue holds one 128-token window");
-  static_assert(!FUSE || kNst * kStage * 16 >= BM * BN * 4, "the fp32 tile fits the ring");
   __shared__ u32x4 smem[kNst * kStage];
 
   const int t = threadIdx.x;
@@ -243,29 +175,18 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
     const int row = BM + ins * 16 + (lane >> 2);
     // Weight blocks start at multiples of 16 columns, so the 16 rows of an
     // instruction share a block; rows past N repeat row N-1.
-    if constexpr (FUSE) {
-      // Tile column q: kv (q < 64) or score of dim 64*tn + q % 64, i.e. row
-      // 64*tn + q % 64 of wkv or wgate.
-      const int q0 = ins * 16;
-      const int wrow = tn * 64 + (q0 & 63) + (lane >> 2);
-      const void* w = q0 < 64 ? a.seg[0].w : a.seg[1].w;
-      l_base[kDmaA + i] = w;
-      l_bytes[kDmaA + i] = a.seg[0].n * a.K * kElemBytes;
-      l_off[kDmaA + i] = (uint32_t)((wrow * a.K + ((lane & 3) ^ swz4(row)) * kElems) * kElemBytes);
-    } else {
-      int n_first = n0 + ins * 16;
-      n_first = n_first < a.N ? n_first : a.N - 1;
-      int n = n0 + row - BM;
-      n = n < a.N ? n : a.N - 1;
-      const void* w = a.seg[0].w;
-      int c0 = a.seg[0].col0, cn = a.seg[0].n;
-      if (a.n_seg > 1 && n_first >= a.seg[1].col0) { w = a.seg[1].w; c0 = a.seg[1].col0; cn = a.seg[1].n; }
-      if (a.n_seg > 2 && n_first >= a.seg[2].col0) { w = a.seg[2].w; c0 = a.seg[2].col0; cn = a.seg[2].n; }
-      if (a.n_seg > 3 && n_first >= a.seg[3].col0) { w = a.seg[3].w; c0 = a.seg[3].col0; cn = a.seg[3].n; }
-      l_base[kDmaA + i] = w;
-      l_bytes[kDmaA + i] = cn * a.K * kElemBytes;
-      l_off[kDmaA + i] = (uint32_t)(((n - c0) * a.K + ((lane & 3) ^ swz4(row)) * kElems) * kElemBytes);
-    }
+    int n_first = n0 + ins * 16;
+    n_first = n_first < a.N ? n_first : a.N - 1;
+    int n = n0 + row - BM;
+    n = n < a.N ? n : a.N - 1;
+    const void* w = a.seg[0].w;
+    int c0 = a.seg[0].col0, cn = a.seg[0].n;
+    if (a.n_seg > 1 && n_first >= a.seg[1].col0) { w = a.seg[1].w; c0 = a.seg[1].col0; cn = a.seg[1].n; }
+    if (a.n_seg > 2 && n_first >= a.seg[2].col0) { w = a.seg[2].w; c0 = a.seg[2].col0; cn = a.seg[2].n; }
+    if (a.n_seg > 3 && n_first >= a.seg[3].col0) { w = a.seg[3].w; c0 = a.seg[3].col0; cn = a.seg[3].n; }
+    l_base[kDmaA + i] = w;
+    l_bytes[kDmaA + i] = cn * a.K * kElemBytes;
+    l_off[kDmaA + i] = (uint32_t)(((n - c0) * a.K + ((lane & 3) ^ swz4(row)) * kElems) * kElemBytes);
   }
   const int nh = a.K / BK;  // stages along K (even)
   // Load instructions i0 .. i0+cnt-1 of stage `hs` (clamped to the last one).
@@ -356,10 +277,6 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
     stage(hs + 1, fa2, fb2, fa3, fb3, fa0, fb0, fa1, fb1);
   }
   wait_vm<0>();  // no LDS-bound load may outlive the loop
-  if constexpr (FUSE) {
-    fused_r128_epilogue<FM, FN>(a, acc, reinterpret_cast<float*>(smem), tm, tn, wm, wn, lane);
-    return;
-  }
 
   // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4.
 #pragma unroll
@@ -847,6 +764,257 @@ struct TileCfg {
   int bm, bn;
 };
 
+// ---------------------------------------------------------------------------
+// proj_r128_splitk4_kernel: the fused ratio-128 projection (128 x 128 tiles,
+// one window per tile) on eight waves, two per SIMD.  Wave w = 2s + n owns
+// the 128 x 64 output block n (4 x 2 accumulators) and runs K sub-step s of
+// every 64-column K tile, a four-way split of K: per MFMA it reads 0.75 KiB
+// of fragments, against 1 KiB for a 64 x 64 block, and two waves per SIMD
+// keep the LDS busy.  Stages are 128-byte rows in a 4-stage ring; after the
+// barrier of iteration j stage j % 4 is free and is refilled with tile j + 4.
+// The partial sums meet in two fixed rounds, ((s0 + s2) + (s1 + s3)).
+// ---------------------------------------------------------------------------
+template <typename Tin>
+__global__ void __launch_bounds__(512) proj_r128_splitk4_kernel(ProjArgs a, int tiles_m, int tiles_n, int gm) {
+  constexpr int BM = 128, BN = 128, kNst = 4;
+  constexpr int kElems = 16 / (int)sizeof(Tin);
+  constexpr int kElemBytes = (int)sizeof(Tin);
+  constexpr int BK = 8 * kElems;
+  constexpr int FM = 4, FN = 2;
+  constexpr int kRows = BM + BN;
+  constexpr int kIns = kRows / 8;          // 8-row load instructions per stage
+  constexpr int kMaxIns = kIns / 8;        // per wave
+  constexpr int kStage = kRows * 8;        // 16-byte slots per stage
+  static_assert(kIns % 8 == 0, "every wave issues the same loads");
+  static_assert(kNst * kStage * 16 <= 160 * 1024, "ring fits the LDS");
+  static_assert(4 * 8192 * 4 <= kNst * kStage * 16, "parked partial sums fit the ring");
+  __shared__ u32x4 smem[kNst * kStage];
+
+  const int t = threadIdx.x;
+  const int n_tiles = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int x = b % kXcds, j = b / kXcds;
+  const int q = n_tiles / kXcds, rem = n_tiles % kXcds;
+  const int logical = x * q + min(x, rem) + j;
+  const int group_size = gm * tiles_n;
+  const int first_m = (logical / group_size) * gm;
+  const int rows_in_group = min(tiles_m - first_m, gm);
+  const int in_group = logical % group_size;
+  const int tm = first_m + in_group % rows_in_group;
+  const int tn = in_group / rows_in_group;
+  const int64_t m0 = (int64_t)tm * BM;
+
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+  const int ks = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+
+  // Stage row r < BM is x row m0 + r; row BM + q is weight row 64*tn + q%64
+  // of wkv (q < 64) or wgate.  Instruction i of this wave covers rows
+  // 8*(wave + 8i) .. +7; the K tile advances through the scalar offset.
+  const int64_t rows_left = a.M - m0;
+  const char* x_base = reinterpret_cast<const char*>(a.x) + m0 * a.K * kElemBytes;
+  const int x_bytes = (int)((rows_left < BM ? rows_left : BM) * a.K * kElemBytes);
+  const void* l_base[kMaxIns];
+  int l_bytes[kMaxIns];
+  uint32_t l_off[kMaxIns];
+  int l_slot[kMaxIns];
+#pragma unroll
+  for (int i = 0; i < kMaxIns; ++i) {
+    const int ins = wave + 8 * i;
+    l_slot[i] = ins * 64;
+    const int row0 = ins * 8;
+    const int row = row0 + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);
+    if (row0 < BM) {
+      const int r = row < rows_left ? row : (int)rows_left - 1;
+      l_base[i] = x_base;
+      l_bytes[i] = x_bytes;
+      l_off[i] = (uint32_t)((r * a.K + chunk * kElems) * kElemBytes);
+    } else {
+      const int q0 = row0 - BM;
+      const int wrow = tn * 64 + (q0 & 63) + (lane >> 3);
+      l_base[i] = q0 < 64 ? a.seg[0].w : a.seg[1].w;
+      l_bytes[i] = a.seg[0].n * a.K * kElemBytes;
+      l_off[i] = (uint32_t)((wrow * a.K + chunk * kElems) * kElemBytes);
+    }
+  }
+  auto issue = [&](int kt, int st) {
+    const uint32_t k0b = (uint32_t)(kt * BK * kElemBytes);
+    __attribute__((address_space(3))) u32x4* base = (__attribute__((address_space(3))) u32x4*)(smem + st * kStage);
+#pragma unroll
+    for (int i = 0; i < kMaxIns; ++i)
+      load_lds16(l_base[i], l_bytes[i], (__attribute__((address_space(3))) void*)(base + l_slot[i]), l_off[i], k0b);
+  };
+  auto issue_one = [&](int kt, int st, int i) {
+    const uint32_t k0b = (uint32_t)(kt * BK * kElemBytes);
+    __attribute__((address_space(3))) u32x4* base = (__attribute__((address_space(3))) u32x4*)(smem + st * kStage);
+    load_lds16(l_base[i], l_bytes[i], (__attribute__((address_space(3))) void*)(base + l_slot[i]), l_off[i], k0b);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x16{};
+  // Fragment f (x blocks, then weight blocks) of this wave's sub-step of stage st.
+  const int c = 2 * ks + h;
+  auto frag = [&](u32x4 (&fa)[FM], u32x4 (&fb)[FN], int f, int st) {
+    const u32x4* base = smem + st * kStage;
+    if (f < FM) {
+      const int row = f * 32 + r32;
+      fa[f] = base[row * 8 + (c ^ swz(row))];
+    } else {
+      const int row = BM + wn * 64 + (f - FM) * 32 + r32;
+      fb[f - FM] = base[row * 8 + (c ^ swz(row))];
+    }
+  };
+  // One tile: MFMA i, then fragment i of the next tile, then (spread
+  // evenly) the loads of tile kt_load into stage st_load.
+  auto step = [&](const u32x4 (&ca)[FM], const u32x4 (&cb)[FN], u32x4 (&na)[FM], u32x4 (&nb)[FN], int st_next,
+                  int kt_load, int st_load) {
+    constexpr int kM = FM * FN, kR = FM + FN;
+    int d = 0;
+#pragma unroll
+    for (int i = 0; i < kM; ++i) {
+      mfma_chunk<Tin>(ca[i / FN], cb[i % FN], acc[i / FN][i % FN]);
+      if (i < kR) frag(na, nb, i, st_next);
+      if ((i * kMaxIns) / kM != ((i + 1) * kMaxIns) / kM) {
+        issue_one(kt_load, st_load, d);
+        ++d;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  const int nk = a.K / BK;
+#pragma unroll
+  for (int s = 0; s < kNst; ++s) issue(min(s, nk - 1), s);
+  wait_vm<(kNst - 1) * kMaxIns>();  // tile 0 (loads complete in issue order)
+  asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+  for (int f = 0; f < FM + FN; ++f) frag(fa0, fb0, f, 0);
+  // Past the barrier of tile kt, tile kt+1 has landed for every wave (this
+  // wave's loads of tiles kt+2 and kt+3 may still be in flight) and every
+  // wave's reads of stage kt % 4 have completed, so the step refills it with
+  // tile kt+4.  Past the last tile the loads re-read the last tile into a
+  // stage nothing reads again, so the loop body has no branches.
+  auto tile_step = [&](const u32x4 (&ca)[FM], const u32x4 (&cb)[FN], u32x4 (&na)[FM], u32x4 (&nb)[FN], int kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_lds<(kNst - 2) * kMaxIns>();
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    step(ca, cb, na, nb, (kt + 1) % kNst, min(kt + kNst, nk - 1), kt % kNst);
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    tile_step(fa0, fb0, fa1, fb1, kt);
+    tile_step(fa1, fb1, fa0, fb0, kt + 1);
+  }
+  if (kt < nk) tile_step(fa0, fb0, fa1, fb1, kt);  // odd number of K tiles
+  wait_vm<0>();  // the epilogue reuses the ring
+
+  // Epilogue (Part 3 §4): the tile is window j = tm of a call that starts
+  // on a window boundary.  APE values first, so that their latency hides
+  // behind the combine.
+  const FuseArgs& f = a.fuse;
+  const int D = f.d_attn;
+  const int64_t t0 = m0;
+  const int64_t jw = tm;
+  const int dd = t >> 3, qq = t & 7;
+  const int dim = tn * 64 + dd;
+  float ape[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) ape[e] = f.ape[0][(qq * 16 + e) * D + dim];
+  float* tile = reinterpret_cast<float*>(smem);
+  constexpr int kPark = FM * FN * 16 * 64;  // floats of one wave's partial sums
+  asm volatile("s_barrier" ::: "memory");  // every wave is done with the ring
+  // Round 1: splits 2 and 3 park lane-major, splits 0 and 1 add them.
+  if (ks >= 2) {
+#pragma unroll
+    for (int i = 0; i < FM * FN; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tile[((ks - 2) * 2 + wn) * kPark + (i * 16 + v) * 64 + lane] = acc[i / FN][i % FN][v];
+  }
+  __syncthreads();
+  if (ks < 2) {
+#pragma unroll
+    for (int i = 0; i < FM * FN; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i / FN][i % FN][v] += tile[(ks * 2 + wn) * kPark + (i * 16 + v) * 64 + lane];
+  }
+  __syncthreads();
+  // Round 2: split 1 parks, split 0 adds.
+  if (ks == 1) {
+#pragma unroll
+    for (int i = 0; i < FM * FN; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tile[wn * kPark + (i * 16 + v) * 64 + lane] = acc[i / FN][i % FN][v];
+  }
+  __syncthreads();
+  if (ks == 0) {
+#pragma unroll
+    for (int i = 0; i < FM * FN; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i / FN][i % FN][v] += tile[wn * kPark + (i * 16 + v) * 64 + lane];
+  }
+  __syncthreads();
+  // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4.
+  if (ks == 0) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          tile[tile128_ix(fm * 32 + 8 * (v >> 2) + 4 * h + (v & 3), wn * 64 + fn * 32 + r32)] = acc[fm][fn][v];
+  }
+  __syncthreads();
+  // Eight lanes per dim pool 16 tokens each and merge by shuffles.
+  if (jw < f.n_emit) {
+    float kv[16], sc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = qq * 16 + e;
+      kv[e] = tile[tile128_ix(row, dd)];
+      sc[e] = tile[tile128_ix(row, 64 + dd)] + ape[e];
+    }
+    float m = sc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) m = fmaxf(m, sc[e]);
+    const float ms = m == -INFINITY ? 0.f : m;
+    float s = 0.f, w = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float xw = pool_exp(sc[e] - ms);
+      s += xw;
+      w = fmaf(xw, kv[e], w);
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64), w2 = __shfl_xor(w, o, 64);
+      const float mm = fmaxf(m, m2);
+      const float mms = mm == -INFINITY ? 0.f : mm;
+      const float f1 = pool_exp(m - mms), f2 = pool_exp(m2 - mms);
+      s = fmaf(s, f1, s2 * f2);
+      w = fmaf(w, f1, w2 * f2);
+      m = mm;
+    }
+    if (qq == 0) f.o[jw * D + dim] = s > 0.f ? w / s : 0.f;
+  }
+  // Kept tokens: call-relative carry_lo .. M-1 that fall in this tile.
+  const int64_t s_lo = f.carry_lo > t0 ? f.carry_lo : t0;
+  const int64_t s_hi = a.M < t0 + 128 ? a.M : t0 + 128;
+  const int n_rows = s_hi > s_lo ? (int)(s_hi - s_lo) : 0;
+  for (int item = t; item < n_rows * 128; item += 512) {
+    const int r = item >> 7, qc = item & 127;
+    const int64_t tok = s_lo + r;
+    const int d = tn * 64 + (qc & 63);
+    float v = tile[tile128_ix((int)(tok - t0), qc)];
+    if (qc >= 64) v += f.ape[0][(int)(tok & 127) * D + d];
+    f.stage[(tok - f.carry_lo) * f.n_orig + (qc >= 64 ? D : 0) + d] = v;
+  }
+}
+
 template <typename Tin>
 void launch_cfg(const ProjArgs& a, TileCfg c, hipStream_t stream, const Timing& tm) {
   const int tiles_m = (int)((a.M + c.bm - 1) / c.bm);
@@ -857,10 +1025,10 @@ void launch_cfg(const ProjArgs& a, TileCfg c, hipStream_t stream, const Timing& 
     hipExtLaunchKernelGGL((proj_splitk_kernel<Tin, 256, 160, 4, 1, false>), grid, dim3(512), 0, stream, tm.start, tm.stop, 0, a,
                           tiles_m, tiles_n, gm);
   else if (c.bm == 128)
-    hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 128, 128, 2, 2, false>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
+    hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 128, 128, 2, 2>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
                        tiles_n, gm);
   else
-    hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 64, 64, 2, 2, false>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
+    hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 64, 64, 2, 2>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
                        tiles_n, gm);
 }
 
@@ -889,11 +1057,11 @@ hipError_t launch_proj(const ProjArgs& a, int in_dtype, hipStream_t stream, cons
     const int tiles_n = a.fuse.d_attn / 64;
     const dim3 grid((unsigned)(tiles_m * tiles_n));
     if (in_dtype == 1)
-      hipExtLaunchKernelGGL((proj_mfma_kernel<uint16_t, 128, 128, 2, 2, true>), grid, dim3(kThreads), 0, stream, tm.start,
-                            tm.stop, 0, a, tiles_m, tiles_n, 4);
+      hipExtLaunchKernelGGL((proj_r128_splitk4_kernel<uint16_t>), grid, dim3(512), 0, stream, tm.start, tm.stop, 0, a,
+                            tiles_m, tiles_n, 4);
     else
-      hipExtLaunchKernelGGL((proj_mfma_kernel<float, 128, 128, 2, 2, true>), grid, dim3(kThreads), 0, stream, tm.start,
-                            tm.stop, 0, a, tiles_m, tiles_n, 4);
+      hipExtLaunchKernelGGL((proj_r128_splitk4_kernel<float>), grid, dim3(512), 0, stream, tm.start, tm.stop, 0, a,
+                            tiles_m, tiles_n, 4);
     return hipGetLastError();
   }
   if (a.fuse.on) {

@@ -124,6 +124,8 @@ SMALL = {
     "r4_d256_idx512": synth.LayerShape(ratio=4, hidden=128, d_attn=256, d_index=512, dtype="bf16"),
     "r128_d512": synth.LayerShape(ratio=128, hidden=256, d_attn=512, d_index=0, dtype="bf16"),
     "r128_d128_f32": synth.LayerShape(ratio=128, hidden=192, d_attn=128, d_index=0, dtype="f32"),
+    # three 64-wide K tiles: the ratio-128 projection's odd-tile tail
+    "r128_d256_h192_bf16": synth.LayerShape(ratio=128, hidden=192, d_attn=256, d_index=0, dtype="bf16"),
 }
 
 
