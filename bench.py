@@ -300,6 +300,30 @@ def main():
     }
     if cnt[B.KCLASS_DECODE]:
         out["decode_avg_ms"] = ms[B.KCLASS_DECODE] / cnt[B.KCLASS_DECODE]
+    if w.layer is not None and T > w.layer.ratio:
+        # Calls that start inside a window keep the separate pool launch(es):
+        # one token, then the rest of the chunk from n0 = 1; the second call's
+        # pool is timed.  Warm: it reads the projection output the call's own
+        # GEMM has just written.
+        L = layers[0]
+        pl_ms, pl_cnt = 0.0, 0
+        for _ in range(side_steps):
+            f = L.frontier
+            f.n_tokens = f.n_comp = f.n_index_comp = 0
+            L.prefill(x[:1])
+            B.ds4c_profile_enable([B.KCLASS_POOL])
+            L.prefill(x[1:T])
+            m_, c_ = B.ds4c_profile_read()
+            B.ds4c_profile_enable(False)
+            pl_ms, pl_cnt = pl_ms + m_[B.KCLASS_POOL], pl_cnt + c_[B.KCLASS_POOL]
+        _, pl_bytes, _, _ = layer_algorithmic(w.layer, 1, T - 1)
+        pl_avg = pl_ms / max(pl_cnt, 1)
+        pl_gbs = pl_bytes / (pl_avg * 1e-3) / 1e9
+        out["plain_pool_roofline"] = {
+            "bound": "hbm", "achieved": pl_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": pl_gbs / PEAK_HBM_GBS,
+            "kernel": "pool_r4_kernel" if w.layer.ratio == 4 else "pool_r128_partial_kernel + pool_r128_finish_kernel",
+            "measured": f"{pl_cnt} calls of {T - 1} tokens from n0 = 1, warm (reads the projection written just before)",
+            "avg_ms": pl_avg, "algorithmic_bytes": pl_bytes}
     if not args.no_cpu_baseline:
         n_cpu = min(T, 4096)
         if w.layer is not None:

@@ -339,13 +339,6 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
     po.T = T;
     po.k_lo = k_lo;
     po.k_hi = k_hi;
-    if (r == 4) {
-      const int64_t c0 = n0 % 4;
-      const int64_t head = (n0 > 0 ? 1 : 0) + (c0 > 0 ? 1 : 0);
-      po.n_head = int(head < n_emit ? head : n_emit);
-    } else {
-      po.n_head = (n0 % 128 != 0 && n_emit > 0) ? 1 : 0;
-    }
     po.ratio = r;
     po.n_rot = layer->n_rot;
     po.n_lanes = s.n_lanes;
@@ -374,7 +367,6 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
       po.stage = f.stage;
       po.d_tot = f.d_tot;
       po.carry_lo = f.carry_lo;
-      po.n_head = 0;
     }
     if (r == 4 && n0 % 4 == 0) {
       // Window pool fused into the projection epilogue; the pool launch
@@ -408,7 +400,6 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
       po.stage = f.stage;
       po.d_tot = f.d_tot;
       po.carry_lo = f.carry_lo;
-      po.n_head = 0;
     }
 
     hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -69,7 +69,6 @@ struct PoolArgs {
   int64_t n0;           // tokens before this call
   int64_t T;            // tokens in this call
   int64_t k_lo, k_hi;   // rows emitted: windows k_lo .. k_hi-1
-  int n_head;           // leading windows that read the incoming frontier
   int ratio;
   int n_rot;
   int n_lanes;

@@ -14,12 +14,12 @@
 // p%4 (it was moved there by the half shift); for ratio 128 in row p%128.
 // Only the first one or two windows of a call can touch such tokens.
 //
-// Ratio 4 runs in one launch; the workgroup that pools the windows touching
-// the incoming frontier also rewrites it afterwards.  Ratio 128 runs in two:
-// a wide partial-pool launch with no cross-workgroup dependency, then a
-// finishing launch that merges the partials, normalises, rotates and
-// quantises each row and carries the frontier; the launch boundary orders
-// the finisher after every read of the incoming frontier.
+// Ratio 4 runs in two launches: one window per workgroup, then a wide copy
+// that carries the frontier.  Ratio 128 runs in two: a wide partial-pool
+// launch with no cross-workgroup dependency, then a finishing launch that
+// merges the partials, normalises, rotates and quantises each row while
+// extra workgroups carry the frontier.  In both, a launch boundary orders the
+// carry after every read of the incoming frontier.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -114,6 +114,54 @@ __device__ void carry_frontier(const PoolArgs& a) {
   }
 }
 
+// The frontier carry spread over n_groups workgroups: kept token p's kv and
+// score (APE added) go from the projection workspace to row p - (m - 4)
+// (ratio 4) or p - m (ratio 128), one float4 per thread and step.  A short
+// ratio-4 call that also moves old tokens within the frontier (rows 4.. ->
+// 0..3) runs carry_frontier on workgroup 0 alone, because its new tokens may
+// overwrite rows the move reads.  W / 4 is a power of two, so items decode
+// by shifts.
+template <int R>
+__device__ void carry_frontier_wide(const PoolArgs& a, int group, int n_groups) {
+  const int64_t n = a.n0 + a.T;
+  const int64_t m = n - (n & (R - 1));
+  if (R == 4 && m > a.n0 - (a.n0 & 3) && m - 4 < a.n0) {
+    if (group == 0) carry_frontier<R>(a);
+    return;
+  }
+  const int64_t first = R == 4 ? (m - 4 > a.n0 ? m - 4 : a.n0) : (m > a.n0 ? m : a.n0);
+  const int row0 = R == 4 ? (int)(first - (m - 4)) : (int)(first - m);
+  const int pr0 = (int)(first & (R - 1));
+  const float* src0 = a.proj + (first - a.n0) * a.ld;
+  const int gid = group * (int)blockDim.x + (int)threadIdx.x, stride = n_groups * (int)blockDim.x;
+  for (int l = 0; l < a.n_lanes; ++l) {
+    const LaneDev& L = a.lane[l];
+    const int sh = __builtin_ctz(L.W / 4), mask = L.W / 4 - 1;
+    const int count = (int)(n - first) * 2 << sh;
+    for (int i = gid; i < count; i += stride) {
+      const int tk = i >> sh, j = tk >> 1, c = (i & mask) * 4;
+      float4 v = *reinterpret_cast<const float4*>(src0 + (int64_t)j * a.ld + ((tk & 1) ? L.sc_col : L.kv_col) + c);
+      if (tk & 1) {
+        const float4 ap = *reinterpret_cast<const float4*>(L.ape + ((pr0 + j) & (R - 1)) * L.W + c);
+        v.x += ap.x; v.y += ap.y; v.z += ap.z; v.w += ap.w;
+      }
+      *reinterpret_cast<float4*>(((tk & 1) ? L.fr_sc : L.fr_kv) + (row0 + j) * L.W + c) = v;
+    }
+  }
+}
+
+// Workgroups for the wide carry: one float4 per thread (256 threads per
+// workgroup), at most 64 workgroups.
+int carry_groups(const PoolArgs& a) {
+  const int64_t n = a.n0 + a.T, R = a.ratio;
+  const int64_t m = n - n % R;
+  const int64_t first = R == 4 ? (m - 4 > a.n0 ? m - 4 : a.n0) : (m > a.n0 ? m : a.n0);
+  int64_t items = 0;
+  for (int l = 0; l < a.n_lanes; ++l) items += (n - first) * 2 * (a.lane[l].W / 4);
+  const int64_t g = (items + 255) / 256;
+  return (int)(g < 1 ? 1 : g > 64 ? 64 : g);
+}
+
 // One ratio-4 window on one workgroup: SA attention waves (D_attn/SA dims
 // each, DPLA per lane) and one indexer wave (the whole indexer row, DPLI per
 // lane).  The attention row's sum of squares is reduced through LDS.
@@ -145,19 +193,18 @@ __device__ __forceinline__ void r4_window(const PoolArgs& a, int64_t k, float* s
   __syncthreads();
 }
 
-// Ratio 4: one window per workgroup.  Workgroup 0 takes the (at most two)
-// leading windows that read the incoming frontier, one after the other, and
-// then carries the frontier; workgroup b > 0 takes window k_lo + n_head + b-1.
+// Ratio 4: one window per workgroup, window k_lo + b on workgroup b.  The
+// leading windows read the incoming frontier; the carry that rewrites it is
+// the next launch (pool_r4_carry_kernel).
 template <int SA, int DPLA, int DPLI>
 __global__ void __launch_bounds__(64 * (SA + 1)) pool_r4_kernel(PoolArgs a) {
   __shared__ float s_ss[SA];
-  if (blockIdx.x > 0) {
-    r4_window<SA, DPLA, DPLI>(a, a.k_lo + a.n_head + blockIdx.x - 1, s_ss);
-    return;
-  }
-  if (a.n_head > 0) r4_window<SA, DPLA, DPLI>(a, a.k_lo, s_ss);
-  if (a.n_head > 1) r4_window<SA, DPLA, DPLI>(a, a.k_lo + 1, s_ss);
-  carry_frontier<4>(a);
+  if (a.k_lo + (int64_t)blockIdx.x >= a.k_hi) return;  // a call without windows launches one empty workgroup
+  r4_window<SA, DPLA, DPLI>(a, a.k_lo + blockIdx.x, s_ss);
+}
+
+__global__ void __launch_bounds__(256) pool_r4_carry_kernel(PoolArgs a) {
+  carry_frontier_wide<4>(a, blockIdx.x, gridDim.x);
 }
 
 // Ratio 128, phase 1: workgroup (row, 64-dim slice, 64-token half) pools 64
@@ -171,6 +218,7 @@ __global__ void __launch_bounds__(256) pool_r128_partial_kernel(PoolArgs a) {
   const int half = blockIdx.x & 1;
   const int slice = (blockIdx.x >> 1) % S;
   const int64_t row = (blockIdx.x >> 1) / S;
+  if (row >= a.k_hi - a.k_lo) return;  // a call without windows launches one empty workgroup
   const int64_t k = a.k_lo + row;
   const int tid = threadIdx.x;
   const int dg = tid & 15, tg = tid >> 4;
@@ -225,6 +273,12 @@ __global__ void __launch_bounds__(256) pool_r128_partial_kernel(PoolArgs a) {
 template <int DPL>
 __global__ void __launch_bounds__(256) pool_r128_finish_kernel(PoolArgs a) {
   const LaneDev& L = a.lane[0];
+  const int row_groups = (int)((a.k_hi - a.k_lo + 3) / 4);
+  if ((int)blockIdx.x >= row_groups) {
+    // The partial-pool launch was the last reader of the incoming frontier.
+    carry_frontier_wide<128>(a, blockIdx.x - row_groups, gridDim.x - row_groups);
+    return;
+  }
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row < a.k_hi - a.k_lo) {
@@ -260,7 +314,6 @@ __global__ void __launch_bounds__(256) pool_r128_finish_kernel(PoolArgs a) {
     float* pre = L.prequant ? L.prequant + row * L.D : nullptr;
     finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, pre, L.rows + k * L.D, lane);
   }
-  if (blockIdx.x == 0) carry_frontier<128>(a);
 }
 
 
@@ -445,13 +498,16 @@ void launch_r4_a(const PoolArgs& a, int dpli, unsigned grid, hipStream_t s, cons
 
 }  // namespace
 
-int pool_launches(const PoolArgs& a) { return a.ratio == 4 || a.o ? 1 : 2; }
+int pool_launches(const PoolArgs& a) { return a.o ? 1 : 2; }
 
 hipError_t launch_pool(const PoolArgs& a, int phase, hipStream_t stream, const Timing& tm) {
   const int64_t n_rows = a.k_hi - a.k_lo;
-  if (a.ratio == 4) {
+  if (a.ratio == 4 && !a.o && phase == 1) {
+    hipExtLaunchKernelGGL(pool_r4_carry_kernel, dim3(carry_groups(a)), dim3(256), 0, stream, tm.start, tm.stop, 0, a);
+  } else if (a.ratio == 4) {
     // Attention rows are split into waves of 128 dims (64 dims below 128).
-    const unsigned grid = a.o ? (unsigned)(n_rows + kFusedCarryGroups) : (unsigned)(1 + n_rows - a.n_head);
+    // Every launch is made, empty or not, so that profiling brackets stay whole.
+    const unsigned grid = a.o ? (unsigned)(n_rows + kFusedCarryGroups) : (unsigned)(n_rows > 0 ? n_rows : 1);
     const int da = a.lane[0].D, dpli = a.lane[1].D / 64;
     switch (da) {
       case 64: launch_r4_a<1, 1>(a, dpli, grid, stream, tm); break;
@@ -468,12 +524,10 @@ hipError_t launch_pool(const PoolArgs& a, int phase, hipStream_t stream, const T
       default: hipExtLaunchKernelGGL((pool_r128_fused_kernel<8>), dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a); break;
     }
   } else if (phase == 0) {
-    if (n_rows > 0) {
-      const unsigned grid = (unsigned)(n_rows * (a.lane[0].D / 64) * 2);
-      hipExtLaunchKernelGGL(pool_r128_partial_kernel, dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a);
-    }
+    const unsigned grid = (unsigned)(n_rows > 0 ? n_rows * (a.lane[0].D / 64) * 2 : 1);
+    hipExtLaunchKernelGGL(pool_r128_partial_kernel, dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a);
   } else {
-    const unsigned grid = (unsigned)(n_rows > 0 ? (n_rows + 3) / 4 : 1);
+    const unsigned grid = (unsigned)((n_rows + 3) / 4 + carry_groups(a));
     switch (a.lane[0].D / 64) {
       case 1: hipExtLaunchKernelGGL((pool_r128_finish_kernel<1>), dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a); break;
       case 2: hipExtLaunchKernelGGL((pool_r128_finish_kernel<2>), dim3(grid), dim3(256), 0, stream, tm.start, tm.stop, 0, a); break;
