@@ -40,9 +40,24 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 GEMM_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", "proj_gemm.hip")
 
 
-def fused_call(shape, n0):
-    """A call that starts on a window boundary pools inside the projection epilogue."""
-    return n0 % shape.ratio == 0
+def fused_call(shape, n0, T):
+    """Whether the library pools this call inside the projection epilogue.
+
+    Mirrors the library's rule: the call starts on a window boundary and the
+    fused grid is not too small (ratio 4: 80 workgroups of 256 x 160; ratio
+    128: 32 of 128 x 128), or the hidden size is small enough that every
+    path is short.
+    """
+    if n0 % shape.ratio:
+        return False
+    d_tot = shape.d_attn + (shape.d_index or 0)
+    if shape.ratio == 4:
+        grid, tile, need = -(-T // 256) * -(-d_tot // 40), 256 * 160, 80
+    else:
+        grid, tile, need = -(-T // 128) * (d_tot // 64), 128 * 128, 32
+    if -(-grid // 256) * tile * shape.hidden < 256 * 160 * 1024:
+        return True
+    return grid >= need
 
 
 def layer_algorithmic(shape, n0, T):
@@ -63,7 +78,7 @@ def layer_algorithmic(shape, n0, T):
     c = n % shape.ratio
     m = n - c
     live = ((4 if m >= 4 else 0) + c) if shape.ratio == 4 else c
-    if fused_call(shape, n0):
+    if fused_call(shape, n0, T):
         kept = min(live, T)
         pool_bytes = n_emit * sum(lanes) * 4 * 2 + kept * sum(W) * 2 * 4 * 2
     else:
@@ -71,20 +86,36 @@ def layer_algorithmic(shape, n0, T):
     return flops, pool_bytes, n_emit * len(lanes), N
 
 
-def proj_kernel_name(M: int, N: int) -> str:
-    """Projection kernel the library launches for an [M, N] output.
+def proj_plan(M: int, N: int, K: int):
+    """(tile rows, K splits) of the library's plain projection for an [M, N] output.
 
-    Mirrors the library's tile choice: the tile shape with the least work per
-    CU over ceil(tiles / 256) rounds, ties to the larger tile; 256 x 160 tiles
-    run on the eight-wave split-K kernel, the others on the four-wave one.
+    Mirrors the library: per tile shape, the K split that keeps the splits
+    resident in one round, then the least estimated time from measured
+    per-round times (75, 42 and 25 us for 256 x 160, 128 x 128 and 64 x 64
+    at K = 4096; extra 64 x 64 tiles per CU cost 0.7 of a round each).
     """
-    best, pick = None, 64
-    for bm, bn in ((256, 160), (128, 128), (64, 64)):
+    best = None
+    for bm, bn, rnd in ((256, 160, 75.0), (128, 128, 42.0), (64, 64, 25.0)):
         tiles = -(-M // bm) * -(-N // bn)
-        cost = -(-tiles // 256) * bm * bn
-        if best is None or cost < best:
-            best, pick = cost, bm
-    return "proj_splitk_kernel" if pick == 256 else "proj_mfma_kernel"
+        s = 1
+        while bm != 256 and s < 16:
+            s2 = 2 * s
+            if tiles * s2 > (512 if bm == 64 else 256) or M * s2 > 1024 or K % (64 * s2) or K // s2 < 128:
+                break
+            s = s2
+        per_cu = -(-(tiles * s) // 256)
+        rounds = 1.0 + 0.7 * (per_cu - 1) if bm == 64 else float(per_cu)
+        us = rounds * rnd * K / s / 4096.0
+        if best is None or us < best[0]:
+            best = (us, bm, s)
+    return best[1], best[2]
+
+
+def proj_kernel_name(M: int, N: int, K: int) -> str:
+    """Projection kernel the library launches for a plain [M, N] output."""
+    bm, s = proj_plan(M, N, K)
+    name = "proj_splitk_kernel" if bm == 256 else "proj_mfma_kernel"
+    return name + (f" (K split {s})" if s > 1 else "")
 
 
 def read_traffic(workload: str):
@@ -253,10 +284,10 @@ def main():
         ms[c], cnt[c] = ms2[c], cnt2[c]
 
     gemm_ms = ms[B.KCLASS_PROJ] / max(cnt[B.KCLASS_PROJ], 1)
-    all_fused = all(fused_call(s, 0) for _, s in shapes if s is not None)
+    all_fused = all(fused_call(s, 0, min(T, chunk)) for _, s in shapes if s is not None)
     gemm_kernel = " + ".join(sorted({("proj_splitk_kernel (fused ratio-4 pool epilogue)" if s.ratio == 4 else
-                                      "proj_r128_splitk4_kernel (fused ratio-128 pool epilogue)") if fused_call(s, 0) else
-                                     proj_kernel_name(min(T, chunk), 2 * sum(s.coff * d for d in (s.d_attn, s.d_index) if d))
+                                      "proj_r128_splitk4_kernel (fused ratio-128 pool epilogue)") if fused_call(s, 0, min(T, chunk)) else
+                                     proj_kernel_name(min(T, chunk), 2 * sum(s.coff * d for d in (s.d_attn, s.d_index) if d), s.hidden)
                                      for _, s in shapes if s is not None}))
     pool_ms = ms[B.KCLASS_POOL] / max(cnt[B.KCLASS_POOL], 1)
     flops_per_launch = flops / max(gemm_launches, 1)

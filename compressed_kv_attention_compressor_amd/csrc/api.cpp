@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -110,7 +111,10 @@ struct WsLayout {
 WsLayout workspace_layout(const Shape& s, int64_t T) {
   WsLayout w;
   w.proj = 0;
-  size_t off = align256(size_t(T) * s.N * sizeof(float));
+  // A K-split projection of a short call writes up to
+  // max(T, min(kSplitRows, 16 T)) rows of partial sums.
+  const int64_t split_rows = std::min(ds4c::kSplitRows, 16 * T);
+  size_t off = align256(size_t(std::max(T, split_rows)) * s.N * sizeof(float));
   if (s.ratio == 128) {
     w.max_rows = T / 128 + 1;
     w.part = off;
@@ -322,6 +326,12 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
     const WsLayout wl = workspace_layout(s, T);
     if (!workspace || !aligned(workspace, 256)) return DS4C_EINVAL;
     if (ws_bytes < wl.total) return DS4C_ECAP;
+    // One token is one step of the recurrence: the decode path does it in
+    // one GEMV launch (plus the pool launch at a window boundary) instead of
+    // a projection, a plane sum, a pool and a carry launch.
+    if (T == 1)
+      return ds4c_compress_decode_one(layer, frontier, x, attn_rows, attn_cap, index_rows, index_cap, attn_prequant,
+                                      index_prequant, stream);
 
     char* ws = static_cast<char*>(workspace);
     ProjArgs pa{};
@@ -331,6 +341,14 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
     pa.K = layer->hidden;
     pa.N = s.N;
     fill_proj_segments(*layer, s, pa.seg, &pa.n_seg);
+    // Window pooling joins the projection epilogue when the call starts on a
+    // window boundary and the fused grid is wide enough; otherwise the plain
+    // projection runs, with K split for short calls.
+    const bool fused = n0 % r == 0 && ds4c::use_fused_projection(r, T, s.N, layer->hidden,
+                                                                  s.D[0] + (s.n_lanes > 1 ? s.D[1] : 0));
+    pa.k_split = fused ? 1 : ds4c::proj_plan(T, s.N, layer->hidden).k_split;
+    pa.k_len = layer->hidden / pa.k_split;
+    pa.split_stride = T * s.N;
 
     PoolArgs po{};
     po.proj = pa.out;
@@ -348,7 +366,7 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
     if (s.n_lanes > 1) po.lane[1] = lane_dev(s, *layer, frontier->state, 1, index_rows, index_prequant);
     if (r == 128) po.part = reinterpret_cast<float*>(ws + wl.part);
 
-    if (r == 128 && n0 % 128 == 0) {
+    if (r == 128 && fused) {
       // Window pool fused into the projection epilogue (one 128-token tile
       // is one window); the pool launch finishes rows and carries the frontier.
       ds4c::FuseArgs& f = pa.fuse;
@@ -368,7 +386,7 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
       po.d_tot = f.d_tot;
       po.carry_lo = f.carry_lo;
     }
-    if (r == 4 && n0 % 4 == 0) {
+    if (r == 4 && fused) {
       // Window pool fused into the projection epilogue; the pool launch
       // only finishes the rows and carries the frontier.
       const int64_t m_rel = T - T % 4;

@@ -54,10 +54,15 @@ struct FuseArgs {
 
 struct ProjArgs {
   const void* x;        // [M, K] row-major, bf16 or f32
-  float* out;           // [M, N] row-major f32 (unfused)
+  float* out;           // [M, N] row-major f32 (unfused); with a K split, plane s of
+                        // k_split planes at out + s * split_stride holds the sum over
+                        // K columns [s * k_len, (s + 1) * k_len)
   int64_t M;
   int K;
   int N;
+  int k_split;          // 1, or the number of K ranges (plain 64x64 / 128x128 kernel only)
+  int k_len;            // K / k_split, a multiple of 64
+  int64_t split_stride; // floats between output planes (M * N)
   int n_seg;
   ProjSeg seg[4];       // attention wkv, wgate, then indexer wkv, wgate
   FuseArgs fuse;

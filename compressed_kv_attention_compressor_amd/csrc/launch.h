@@ -17,6 +17,25 @@ struct Timing {
   hipEvent_t stop = nullptr;
 };
 
+// Plain (unfused) projection: tile rows (256, 128 or 64) and the number of K
+// ranges, chosen by estimated time.  A call with few output tiles splits K
+// so that more workgroups run; split s writes plane s of the output and a
+// second launch adds the planes into plane 0 in order.  A split keeps
+// k_split * M <= kSplitRows, so the planes of a call with M tokens take at
+// most max(M, min(kSplitRows, 16 M)) rows of N floats.
+constexpr int64_t kSplitRows = 1024;
+struct ProjPlan {
+  int bm;
+  int k_split;
+};
+ProjPlan proj_plan(int64_t M, int N, int K);
+// Whether a call that starts on a window boundary pools inside the
+// projection epilogue (M tokens, N projection columns, K = hidden, d_tot =
+// pooled dims of all lanes): yes unless the fused grid is so small that the
+// plain path is faster (measured), which happens for short calls.  Calls
+// with small hidden sizes always take the fused path.
+bool use_fused_projection(int ratio, int64_t M, int N, int K, int d_tot);
+
 hipError_t launch_proj(const ProjArgs& a, int in_dtype, hipStream_t stream, const Timing& tm);
 // Ratio-4 layers and fused calls pool in one launch; plain ratio-128 calls in
 // two (phase 0: partial pools, phase 1: merge, finish and frontier carry).

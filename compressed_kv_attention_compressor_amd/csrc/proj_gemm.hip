@@ -188,11 +188,14 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
     l_bytes[kDmaA + i] = cn * a.K * kElemBytes;
     l_off[kDmaA + i] = (uint32_t)(((n - c0) * a.K + ((lane & 3) ^ swz4(row)) * kElems) * kElemBytes);
   }
-  const int nh = a.K / BK;  // stages along K (even)
+  // K range of this workgroup: split blockIdx.y of a.k_split covers columns
+  // k0 .. k0 + a.k_len - 1 and writes its own output plane.
+  const int k0 = (int)blockIdx.y * a.k_len;
+  const int nh = a.k_len / BK;  // stages along K (even)
   // Load instructions i0 .. i0+cnt-1 of stage `hs` (clamped to the last one).
   auto issue = [&](int hs, int i0, int cnt) {
     const int hc = min(hs, nh - 1);
-    const uint32_t soff = (uint32_t)(hc * BK * kElemBytes);
+    const uint32_t soff = (uint32_t)((k0 + hc * BK) * kElemBytes);
     __attribute__((address_space(3))) u32x4* base =
         (__attribute__((address_space(3))) u32x4*)(smem + (hs % kNst) * kStage);
 #pragma unroll
@@ -279,6 +282,7 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
   wait_vm<0>();  // no LDS-bound load may outlive the loop
 
   // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4.
+  float* out = a.out + (int64_t)blockIdx.y * a.split_stride;
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
@@ -287,7 +291,7 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t m = m0 + wm * TM + fm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (m < a.M && n < a.N) a.out[m * a.N + n] = acc[fm][fn][v];
+        if (m < a.M && n < a.N) out[m * a.N + n] = acc[fm][fn][v];
       }
     }
   }
@@ -764,6 +768,22 @@ struct TileCfg {
   int bm, bn;
 };
 
+// K-split projection: plane 0 += planes 1 .. n_split-1, added in order, so
+// the sum is the same on every run.
+__global__ void __launch_bounds__(256) proj_sum_planes_kernel(float4* out, int64_t n4, int n_split, int64_t stride4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    float4 v = out[i];
+    for (int s = 1; s < n_split; ++s) {
+      const float4 w = out[i + s * stride4];
+      v.x += w.x;
+      v.y += w.y;
+      v.z += w.z;
+      v.w += w.w;
+    }
+    out[i] = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // proj_r128_splitk4_kernel: the fused ratio-128 projection (128 x 128 tiles,
 // one window per tile) on eight waves, two per SIMD.  Wave w = 2s + n owns
@@ -1019,11 +1039,11 @@ template <typename Tin>
 void launch_cfg(const ProjArgs& a, TileCfg c, hipStream_t stream, const Timing& tm) {
   const int tiles_m = (int)((a.M + c.bm - 1) / c.bm);
   const int tiles_n = (a.N + c.bn - 1) / c.bn;
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)a.k_split);
   const int gm = 4;
-  if (c.bm == 256)
-    hipExtLaunchKernelGGL((proj_splitk_kernel<Tin, 256, 160, 4, 1, false>), grid, dim3(512), 0, stream, tm.start, tm.stop, 0, a,
-                          tiles_m, tiles_n, gm);
+  if (c.bm == 256)  // no K split on this kernel (the planner never asks for one)
+    hipExtLaunchKernelGGL((proj_splitk_kernel<Tin, 256, 160, 4, 1, false>), dim3(grid.x), dim3(512), 0, stream, tm.start,
+                          tm.stop, 0, a, tiles_m, tiles_n, gm);
   else if (c.bm == 128)
     hipExtLaunchKernelGGL((proj_mfma_kernel<Tin, 128, 128, 2, 2>), grid, dim3(kThreads), 0, stream, tm.start, tm.stop, 0, a, tiles_m,
                        tiles_n, gm);
@@ -1034,21 +1054,71 @@ void launch_cfg(const ProjArgs& a, TileCfg c, hipStream_t stream, const Timing& 
 
 }  // namespace
 
-// Tile shape with the least work per CU: ceil(tiles / 256 CUs) rounds of
-// bm*bn outputs each; ties go to the larger tile (fewer K-tile reloads).
-int proj_tile_rows(int64_t M, int N) {
-  const TileCfg cfgs[] = {{256, 160}, {128, 128}, {64, 64}};
-  int64_t best = -1;
-  int pick = 64;
-  for (const TileCfg& c : cfgs) {
-    const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    const int64_t cost = ((tiles + 255) / 256) * c.bm * c.bn;
-    if (best < 0 || cost < best) {
-      best = cost;
-      pick = c.bm;
+namespace {
+
+// Measured time of one tile per CU over K = 4096 on one MI355X, in
+// microseconds: 256 x 160, 128 x 128 and 64 x 64.  Two 64 x 64 tiles share a
+// CU at once; each further tile per CU adds kExtra64 of a round.  Only the
+// ratios matter for the choices below.
+constexpr double kRoundUs256 = 75.0, kRoundUs128 = 42.0, kRoundUs64 = 25.0, kExtra64 = 0.7;
+// Fused grids below these sizes leave enough CUs idle that the plain, K-split
+// projection plus a pool pass over its output is as fast or faster (measured
+// break-even on hidden 4096: ratio 4 between 1024 and 1280 tokens, 80
+// workgroups of 256 x 160; ratio 128 at about 512 tokens, 32 workgroups).
+constexpr int64_t kMinFusedGrid4 = 80, kMinFusedGrid128 = 32;
+
+int tile_cols(int bm) { return bm == 256 ? 160 : bm; }
+int64_t tile_slots(int bm) { return bm == 64 ? 512 : 256; }
+double round_us(int bm) { return bm == 256 ? kRoundUs256 : bm == 128 ? kRoundUs128 : kRoundUs64; }
+
+// K ranges for a plain projection with `tiles` output tiles: the largest
+// power of two (at most 16) that keeps every split resident in one round,
+// k_split * M <= kSplitRows, and whole 64-column K ranges of at least 128.
+int split_for(int bm, int64_t tiles, int64_t M, int K) {
+  int s = 1;
+  if (bm == 256) return s;  // the 256 x 160 kernel has no K split
+  while (s < 16) {
+    const int s2 = 2 * s;
+    if (tiles * s2 > tile_slots(bm) || M * s2 > kSplitRows || K % (64 * s2) != 0 || K / s2 < 128) break;
+    s = s2;
+  }
+  return s;
+}
+
+double plan_us(int bm, int64_t M, int N, int K, int* k_split) {
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + tile_cols(bm) - 1) / tile_cols(bm));
+  const int s = split_for(bm, tiles, M, K);
+  if (k_split) *k_split = s;
+  const int64_t per_cu = (tiles * s + 255) / 256;
+  const double rounds = bm == 64 ? 1.0 + kExtra64 * (double)(per_cu - 1) : (double)per_cu;
+  return rounds * round_us(bm) * ((double)K / s / 4096.0);
+}
+
+}  // namespace
+
+// Plain projection plan: the tile shape with the least estimated time,
+// ties to the larger tile (fewer K-tile reloads).
+ProjPlan proj_plan(int64_t M, int N, int K) {
+  ProjPlan best{256, 1};
+  double best_us = -1.0;
+  for (int bm : {256, 128, 64}) {
+    int s = 1;
+    const double us = plan_us(bm, M, N, K, &s);
+    if (best_us < 0.0 || us < best_us) {
+      best_us = us;
+      best = ProjPlan{bm, s};
     }
   }
-  return pick;
+  return best;
+}
+
+bool use_fused_projection(int ratio, int64_t M, int N, int K, int d_tot) {
+  (void)N;
+  const int64_t grid_f = ratio == 4 ? ((M + 255) / 256) * ((d_tot + 39) / 40) : ((M + 127) / 128) * (d_tot / 64);
+  const int64_t tile_f = ratio == 4 ? 256 * 160 : 128 * 128;
+  // Short either way (small hidden sizes): keep the fused path.
+  if (((grid_f + 255) / 256) * tile_f * K < int64_t(256 * 160) * 1024) return true;
+  return grid_f >= (ratio == 4 ? kMinFusedGrid4 : kMinFusedGrid128);
 }
 
 hipError_t launch_proj(const ProjArgs& a, int in_dtype, hipStream_t stream, const Timing& tm) {
@@ -1076,12 +1146,21 @@ hipError_t launch_proj(const ProjArgs& a, int in_dtype, hipStream_t stream, cons
                             tm.stop, 0, a, tiles_m, tiles_n, 4);
     return hipGetLastError();
   }
-  const int bm = proj_tile_rows(a.M, a.N);
-  const TileCfg c = bm == 256 ? TileCfg{256, 160} : bm == 128 ? TileCfg{128, 128} : TileCfg{64, 64};
+  const ProjPlan pl = proj_plan(a.M, a.N, a.K);
+  if (pl.k_split != a.k_split || (int64_t)a.k_len * a.k_split != a.K || a.split_stride != a.M * a.N)
+    return hipErrorInvalidValue;
+  const TileCfg c = pl.bm == 256 ? TileCfg{256, 160} : pl.bm == 128 ? TileCfg{128, 128} : TileCfg{64, 64};
+  const Timing t_gemm{tm.start, a.k_split > 1 ? nullptr : tm.stop};
   if (in_dtype == 1)
-    launch_cfg<uint16_t>(a, c, stream, tm);
+    launch_cfg<uint16_t>(a, c, stream, t_gemm);
   else
-    launch_cfg<float>(a, c, stream, tm);
+    launch_cfg<float>(a, c, stream, t_gemm);
+  if (a.k_split > 1) {
+    const int64_t n4 = a.M * a.N / 4;
+    const int64_t g = (n4 + 255) / 256;
+    hipExtLaunchKernelGGL(proj_sum_planes_kernel, dim3((unsigned)(g < 1024 ? g : 1024)), dim3(256), 0, stream, nullptr,
+                          tm.stop, 0, reinterpret_cast<float4*>(a.out), n4, a.k_split, a.split_stride / 4);
+  }
   return hipGetLastError();
 }
 

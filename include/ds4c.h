@@ -101,7 +101,9 @@ size_t ds4c_frontier_bytes(const ds4c_layer *layer);
 
 /* Bytes of device workspace ds4c_compress_prefill needs for calls of up to
  * max_tokens tokens: the [T, N] float32 projection (N = 2 * sum of lane
- * widths) plus per-row pooling scratch on ratio-128 layers.  0 if invalid. */
+ * widths; a short call that splits K over several ranges keeps up to
+ * min(1024, 16 T) rows of partial sums, so T rows become max(T, min(1024,
+ * 16 T))) plus per-row pooling scratch on ratio-128 layers.  0 if invalid. */
 size_t ds4c_workspace_bytes(const ds4c_layer *layer, int64_t max_tokens);
 
 /* Bytes of the host blob ds4c_frontier_save writes for this layer. */
@@ -128,6 +130,9 @@ int ds4c_frontier_init(const ds4c_layer *layer, ds4c_frontier *frontier, void *s
  *
  * workspace: device, >= ds4c_workspace_bytes(layer, T) bytes, 256-byte
  * aligned, contents undefined on entry and exit.
+ *
+ * A call with T == 1 runs the decode step (as ds4c_compress_decode_one, same
+ * results; the workspace is still validated but not touched).
  *
  * Errors: DS4C_EINVAL, DS4C_ESHAPE, DS4C_ECAP (rows or workspace),
  * DS4C_EPOS (counters), DS4C_EDEVICE.  T == 0 is a no-op returning DS4C_OK. */

@@ -244,6 +244,27 @@ def test_save_load_continue(name):
         compare_all(shape, g, spec_full, st_full, 600)
 
 
+# Flash-size calls of every length class: a call with few output tiles runs
+# the plain projection with K split over up to 16 ranges (planes added in a
+# second launch), a long call on a window boundary pools in the projection
+# epilogue, and ragged lengths cover partial tiles on both paths.
+FLASH_PLANS = {
+    "r4_flash": [1, 3, 256, 127, 1, 1536, 2172],
+    "r128_flash": [1, 127, 64, 64, 2500, 1340],
+}
+
+
+@pytest.mark.parametrize("name", list(FLASH_PLANS))
+def test_flash_short_and_ragged_calls(name):
+    plan = FLASH_PLANS[name]
+    _say(f"[parity] {name} plan {plan}")
+    w, p, x = _workload(name)
+    assert sum(plan) == len(x)
+    g = run_gpu(w.layer, p, x, plan)
+    spec, st = run_oracle(w.layer, p, x)
+    compare_all(w.layer, g, spec, st, len(x))
+
+
 def test_deterministic_and_overwrites_poison():
     _say("[parity] determinism")
     w, p, x = _workload("r4_flash")

@@ -24,10 +24,18 @@ CASES = {
     "bf16_256x160_ragged_m": (synth.FLASH_R4, 4000),
     "bf16_128x128": (synth.FLASH_R128, 4096),
     "bf16_128x128_ragged": (synth.FLASH_R128, 4000),
-    "bf16_64x64": (synth.LayerShape(ratio=4, hidden=256, d_attn=512, d_index=128, dtype="bf16"), 700),
-    "f32_64x64": (synth.LayerShape(ratio=4, hidden=256, d_attn=128, d_index=64, dtype="f32"), 64),
+    "bf16_64x64": (synth.LayerShape(ratio=4, hidden=256, d_attn=128, d_index=64, dtype="bf16"), 700),
+    "f32_64x64": (synth.LayerShape(ratio=4, hidden=256, d_attn=128, d_index=64, dtype="f32"), 1000),
+    "bf16_128x128_small_k": (synth.LayerShape(ratio=4, hidden=256, d_attn=512, d_index=128, dtype="bf16"), 700),
     "f32_128x128": (synth.LayerShape(ratio=128, hidden=192, d_attn=512, d_index=0, dtype="f32"), 4000),
     "f32_256x160": (synth.LayerShape(ratio=4, hidden=128, d_attn=512, d_index=128, dtype="f32"), 4000),
+    # short calls: K split over 16 / 8 / 4 / 2 ranges, planes added in order
+    "bf16_128x128_split8": (synth.FLASH_R4, 64),
+    "bf16_128x128_split4": (synth.FLASH_R4, 200),
+    "bf16_64x64_split16": (synth.FLASH_R128, 5),
+    "bf16_64x64_split2": (synth.FLASH_R128, 300),
+    "f32_64x64_split2": (synth.LayerShape(ratio=4, hidden=256, d_attn=128, d_index=64, dtype="f32"), 300),
+    "f32_64x64_split8": (synth.LayerShape(ratio=128, hidden=4096, d_attn=128, d_index=0, dtype="f32"), 100),
 }
 
 
