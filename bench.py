@@ -64,8 +64,10 @@ def layer_algorithmic(shape, n0, T):
     """GEMM flops and pool-launch bytes of one prefill call (tokens n0 .. n0+T-1).
 
     Plain path, pool bytes: every projected kv/score element read once, the
-    APE table, the rows written, and the live frontier rows written after the
-    call.  Fused path (window pooling in the projection epilogue), the
+    APE table, the rows written, and (ratio 128, whose finishing launch also
+    carries the frontier) the live frontier rows written after the call; a
+    ratio-4 call carries its frontier in a separate launch, counted by
+    carry_bytes.  Fused path (window pooling in the projection epilogue), the
     finishing launch's bytes: the pooled rows read once, the rows written and
     the frontier rows the call writes from the staged tokens (read once).
     """
@@ -82,8 +84,19 @@ def layer_algorithmic(shape, n0, T):
         kept = min(live, T)
         pool_bytes = n_emit * sum(lanes) * 4 * 2 + kept * sum(W) * 2 * 4 * 2
     else:
-        pool_bytes = T * N * 4 + shape.ratio * sum(W) * 4 + n_emit * sum(lanes) * 4 + live * sum(W) * 2 * 4
+        pool_bytes = T * N * 4 + shape.ratio * sum(W) * 4 + n_emit * sum(lanes) * 4
+        if shape.ratio == 128:
+            pool_bytes += live * sum(W) * 2 * 4
     return flops, pool_bytes, n_emit * len(lanes), N
+
+
+def carry_bytes(shape, n0, T):
+    """Bytes of the separate ratio-4 frontier carry: kept kv/score rows read and written."""
+    W = [shape.coff * d for d in [shape.d_attn] + ([shape.d_index] if shape.d_index else [])]
+    n = n0 + T
+    c = n % shape.ratio
+    live = (4 if n - c >= 4 else 0) + c
+    return 2 * live * sum(W) * 2 * 4
 
 
 def proj_plan(M: int, N: int, K: int):
@@ -337,16 +350,17 @@ def main():
         # pool is timed.  Warm: it reads the projection output the call's own
         # GEMM has just written.
         L = layers[0]
-        pl_ms, pl_cnt = 0.0, 0
+        pl_ms, pl_cnt, cr_ms, cr_cnt = 0.0, 0, 0.0, 0
         for _ in range(side_steps):
             f = L.frontier
             f.n_tokens = f.n_comp = f.n_index_comp = 0
             L.prefill(x[:1])
-            B.ds4c_profile_enable([B.KCLASS_POOL])
+            B.ds4c_profile_enable([B.KCLASS_POOL, B.KCLASS_CARRY])
             L.prefill(x[1:T])
             m_, c_ = B.ds4c_profile_read()
             B.ds4c_profile_enable(False)
             pl_ms, pl_cnt = pl_ms + m_[B.KCLASS_POOL], pl_cnt + c_[B.KCLASS_POOL]
+            cr_ms, cr_cnt = cr_ms + m_[B.KCLASS_CARRY], cr_cnt + c_[B.KCLASS_CARRY]
         _, pl_bytes, _, _ = layer_algorithmic(w.layer, 1, T - 1)
         pl_avg = pl_ms / max(pl_cnt, 1)
         pl_gbs = pl_bytes / (pl_avg * 1e-3) / 1e9
@@ -355,6 +369,10 @@ def main():
             "kernel": "pool_r4_kernel" if w.layer.ratio == 4 else "pool_r128_partial_kernel + pool_r128_finish_kernel",
             "measured": f"{pl_cnt} calls of {T - 1} tokens from n0 = 1, warm (reads the projection written just before)",
             "avg_ms": pl_avg, "algorithmic_bytes": pl_bytes}
+        if cr_cnt:
+            out["plain_pool_roofline"]["carry"] = {
+                "kernel": "pool_r4_carry_kernel", "avg_ms": cr_ms / cr_cnt,
+                "algorithmic_bytes": carry_bytes(w.layer, 1, T - 1)}
     if not args.no_cpu_baseline:
         n_cpu = min(T, 4096)
         if w.layer is not None:

@@ -21,8 +21,8 @@ DS4C_EFORMAT = -5
 DS4C_EDEVICE = -6
 DS4C_F32 = 0
 DS4C_BF16 = 1
-KCLASS_PROJ, KCLASS_POOL, KCLASS_DECODE, KCLASS_INIT = 0, 1, 2, 3
-PROFILE_ALL = 0xF
+KCLASS_PROJ, KCLASS_POOL, KCLASS_DECODE, KCLASS_INIT, KCLASS_CARRY = 0, 1, 2, 3, 4
+PROFILE_ALL = 0x1F
 
 # Every function the header declares, with (restype, argtypes).
 SIGNATURES = {}
@@ -203,8 +203,8 @@ def ds4c_profile_enable(classes=True) -> None:
 
 
 def ds4c_profile_read():
-    """(ms[4], count[4]) accumulated per kernel class since the last read."""
-    ms = (c_double * 4)()
-    cnt = (c_int64 * 4)()
-    _ok(lib().ds4c_profile_read(ms, cnt, 4), "ds4c_profile_read")
+    """(ms[5], count[5]) accumulated per kernel class since the last read."""
+    ms = (c_double * 5)()
+    cnt = (c_int64 * 5)()
+    _ok(lib().ds4c_profile_read(ms, cnt, 5), "ds4c_profile_read")
     return list(ms), list(cnt)

@@ -424,14 +424,23 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
     st = dev_status(
         timed(DS4C_KCLASS_PROJ, [&](const ds4c::Timing& tm) { return ds4c::launch_proj(pa, layer->in_dtype, hs, tm); }));
     if (st) return st;
+    // The plain ratio-4 path's second launch only carries the frontier; it
+    // is timed as its own class.
+    const int n_pool = ds4c::pool_launches(po);
+    const int n_main = r == 4 && !po.o ? n_pool - 1 : n_pool;
     st = dev_status(timed(DS4C_KCLASS_POOL, [&](const ds4c::Timing& tm) {
-      const int n = ds4c::pool_launches(po);
       hipError_t e = hipSuccess;
-      for (int ph = 0; ph < n && e == hipSuccess; ++ph)
-        e = ds4c::launch_pool(po, ph, hs, ds4c::Timing{ph == 0 ? tm.start : nullptr, ph == n - 1 ? tm.stop : nullptr});
+      for (int ph = 0; ph < n_main && e == hipSuccess; ++ph)
+        e = ds4c::launch_pool(po, ph, hs,
+                              ds4c::Timing{ph == 0 ? tm.start : nullptr, ph == n_main - 1 ? tm.stop : nullptr});
       return e;
     }));
     if (st) return st;
+    if (n_main < n_pool) {
+      st = dev_status(
+          timed(DS4C_KCLASS_CARRY, [&](const ds4c::Timing& tm) { return ds4c::launch_pool(po, n_main, hs, tm); }));
+      if (st) return st;
+    }
     frontier->n_tokens = n;
     frontier->n_comp = k_hi;
     frontier->n_index_comp = r == 4 ? k_hi : 0;
@@ -728,7 +737,7 @@ int ds4c_profile_enable(int class_mask) {
 
 int ds4c_profile_read(double* ms, int64_t* count, int n) {
   try {
-    if (!ms || !count || n < 0 || n > 4) return DS4C_EINVAL;
+    if (!ms || !count || n < 0 || n > 5) return DS4C_EINVAL;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     for (int i = 0; i < n; ++i) {
       ms[i] = 0.0;

@@ -199,7 +199,7 @@ __global__ void __launch_bounds__(kR128Dims * kR128Groups) decode_r128_pool_kern
   if (m != -INFINITY) {
 #pragma unroll
     for (int e = 0; e < kR128Rows; ++e) {
-      const float w = expf(sc[e][0] - m);
+      const float w = pool_exp(sc[e][0] - m);
       den += w;
       num = fmaf(w, kv[e][0], num);
     }
@@ -217,7 +217,7 @@ __global__ void __launch_bounds__(kR128Dims * kR128Groups) decode_r128_pool_kern
 #pragma unroll
     for (int h = 0; h < kR128Groups; ++h) {
       const float mh = s_m[h][dl];
-      const float f = mh == -INFINITY ? 0.f : expf(mh - M);
+      const float f = mh == -INFINITY ? 0.f : pool_exp(mh - M);
       D = fmaf(s_s[h][dl], f, D);
       A = fmaf(s_a[h][dl], f, A);
     }

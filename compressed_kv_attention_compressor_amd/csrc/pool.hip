@@ -235,7 +235,7 @@ __global__ void __launch_bounds__(256) pool_r128_partial_kernel(PoolArgs a) {
     if (m != -INFINITY) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float w = expf(sc[e][i] - m);
+        const float w = pool_exp(sc[e][i] - m);
         den += w;
         num = fmaf(w, kv[e][i], num);
       }
@@ -255,7 +255,7 @@ __global__ void __launch_bounds__(256) pool_r128_partial_kernel(PoolArgs a) {
       for (int g = 0; g < 16; ++g) {
         const float mg = s_m[g][tid];
         if (mg != -INFINITY) {
-          const float f = expf(mg - M);
+          const float f = pool_exp(mg - M);
           den = fmaf(s_s[g][tid], f, den);
           num = fmaf(s_a[g][tid], f, num);
         }
@@ -303,7 +303,7 @@ __global__ void __launch_bounds__(256) pool_r128_finish_kernel(PoolArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           if (m[h][i] == -INFINITY) continue;
-          const float f = expf(m[h][i] - M[i]);
+          const float f = pool_exp(m[h][i] - M[i]);
           den[i] = fmaf(s[h][i], f, den[i]);
           num[i] = fmaf(acc[h][i], f, num[i]);
         }
@@ -347,12 +347,12 @@ __device__ __forceinline__ void fused_pool_dims(const PoolArgs& a, int64_t j, in
     float den = 0.f, num = 0.f;
     if (m != -INFINITY) {
       if (mc[i] != -INFINITY) {
-        const float f = expf(mc[i] - m);
+        const float f = pool_exp(mc[i] - m);
         den = sc[i] * f;
         num = wc[i] * f;
       }
       if (mp[i] != -INFINITY) {
-        const float f = expf(mp[i] - m);
+        const float f = pool_exp(mp[i] - m);
         den = fmaf(sp[i], f, den);
         num = fmaf(wp[i], f, num);
       }

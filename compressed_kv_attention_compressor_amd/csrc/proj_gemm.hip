@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "kernel_args.h"
 #include "launch.h"
 
@@ -95,11 +96,6 @@ __device__ __forceinline__ void load_lds16(const void* base, int bytes, __attrib
 }
 
 
-// Softmax weight e^x for x <= 0 in the pooling epilogues: 2^(x log2 e)
-// through the hardware base-2 exponential.  Rounding x log2 e costs a
-// relative error of at most |x| * 2^-24 * ln 2 in the result (below 1e-6 for
-// |x| < 20) plus the instruction's own error of about one ulp; e^-inf = 0.
-__device__ __forceinline__ float pool_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 
 // LDS index of element (row, col) of a 128 x 128 fp32 tile: rotated by 32
 // columns on odd 4-row groups so that the two half-waves of an accumulator

@@ -228,10 +228,14 @@ const char *ds4c_status_str(int status);
  * (DS4C_KCLASS_*), 0 turns timing off, DS4C_PROFILE_ALL selects every class;
  * other values return DS4C_EINVAL.  ds4c_profile_read waits for the recorded
  * events, writes the accumulated milliseconds and launch counts of each class
- * into ms[n] and count[n] (n <= 4), and clears the record.  Enabling or
- * disabling also clears it. */
-enum { DS4C_KCLASS_PROJ = 0, DS4C_KCLASS_POOL = 1, DS4C_KCLASS_DECODE = 2, DS4C_KCLASS_INIT = 3 };
-enum { DS4C_PROFILE_ALL = 0xF };
+ * into ms[n] and count[n] (n <= 5), and clears the record.  Enabling or
+ * disabling also clears it.  Classes: projection (PROJ; a K-split call's
+ * plane sum included), pooling and row finishing (POOL), the separate
+ * frontier-carry launch of a ratio-4 call that does not start on a window
+ * boundary (CARRY), decode steps (DECODE), frontier init (INIT). */
+enum { DS4C_KCLASS_PROJ = 0, DS4C_KCLASS_POOL = 1, DS4C_KCLASS_DECODE = 2, DS4C_KCLASS_INIT = 3,
+       DS4C_KCLASS_CARRY = 4 };
+enum { DS4C_PROFILE_ALL = 0x1F };
 int ds4c_profile_enable(int class_mask);
 int ds4c_profile_read(double *ms, int64_t *count, int n);
 

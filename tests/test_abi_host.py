@@ -199,10 +199,10 @@ def test_save_rejects_small_buffer():
 def test_profile_read_without_records():
     B.ds4c_profile_enable(True)
     ms, cnt = B.ds4c_profile_read()
-    assert ms == [0.0] * 4 and cnt == [0] * 4
-    B.ds4c_profile_enable([B.KCLASS_PROJ])
+    assert ms == [0.0] * 5 and cnt == [0] * 5
+    B.ds4c_profile_enable([B.KCLASS_PROJ, B.KCLASS_CARRY])
     ms, cnt = B.ds4c_profile_read()
-    assert cnt == [0] * 4
+    assert cnt == [0] * 5
     B.ds4c_profile_enable(False)
 
 
