@@ -9,6 +9,8 @@ Workloads (--workload):
               chunk: a step is one ds4c_compress_stack_prefill call.
   stack32_long the stack over a 65536-token prompt in 16 chunks of 4096, then
               256 ds4c_compress_stack_decode_one steps: a step is all of it.
+  stack32_pro the 32-layer Pro-schedule stack (layers 0-1 ratio 128, then
+              ratio 4 / 128 alternating; 32 compressed layers), one chunk.
 
 Every step starts from position 0 (the frontier counters are reset on the
 host; a call at position 0 reads nothing from the frontier).  Inputs are
@@ -200,7 +202,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0, help="timed steps (default depends on the workload)")
     ap.add_argument("--warmup", type=int, default=-1)
-    ap.add_argument("--workload", default="r4_flash", choices=["r4_flash", "r128_flash", "stack32", "stack32_long"])
+    ap.add_argument("--workload", default="r4_flash", choices=["r4_flash", "r128_flash", "stack32", "stack32_long", "stack32_pro"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0)
     args = ap.parse_args()
@@ -227,7 +229,7 @@ def main():
         shapes = [(0, w.layer)]
         params = {0: synth.layer_params(w.wid, 0, w.layer)}
     else:
-        shapes = [(l, synth.stack_layer_shape(B.ds4c_layer_ratio(0, l))) for l in range(w.n_layers)]
+        shapes = [(l, synth.stack_layer_shape(B.ds4c_layer_ratio(w.variant, l))) for l in range(w.n_layers)]
         params = {l: synth.layer_params(w.wid, l, s) for l, s in shapes if s is not None}
     hidden = 4096 if w.layer is None else w.layer.hidden
     dtype = "bf16" if w.layer is None else w.layer.dtype

@@ -51,9 +51,10 @@ class Workload:
     name: str
     tokens: int                    # prefill tokens
     layer: Optional[LayerShape]    # single-layer workloads
-    n_layers: int = 0              # stack workloads (Flash pattern)
+    n_layers: int = 0              # stack workloads
     chunk: int = 4096
     decode_tokens: int = 0
+    variant: int = 0               # stack schedule: 0 Flash, 1 Pro (Part 3 §1)
 
 
 FLASH_R4 = LayerShape(ratio=4, hidden=4096, d_attn=512, d_index=128, dtype="bf16")
@@ -70,6 +71,10 @@ WORKLOADS: Dict[str, Workload] = {
                         4096, None, n_layers=32),
     "stack32_long": Workload(5, "32-layer Flash stack, 65536 tokens in 16 chunks of 4096, then 256 decode steps",
                              65536, None, n_layers=32, decode_tokens=256),
+    # The Pro schedule: layers 0-1 ratio 128, then ratio 4 on even and 128 on
+    # odd layers (32 compressed layers); the same Flash layer shapes.
+    "stack32_pro": Workload(6, "32-layer Pro-schedule stack, one 4096-token chunk, hidden 4096",
+                            4096, None, n_layers=32, variant=1),
 }
 
 

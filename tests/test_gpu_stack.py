@@ -1,6 +1,7 @@
-"""The Flash-pattern layer stack through the native stack entry points.
+"""The Flash- and Pro-pattern layer stacks through the native stack entry points.
 
-32 layers (0-1 uncompressed, even ratio 4, odd ratio 128), hidden 4096,
+32 layers (Flash: 0-1 uncompressed; Pro: 0-1 ratio 128; then even ratio 4,
+odd ratio 128), hidden 4096,
 head_dim 512 / indexer 128, bf16, independent weights per layer, every layer
 fed the same hidden states.  One 4096-token chunk, and a 65536-token prompt in
 16 chunks of 4096 followed by 256 single-token decode steps, at full size.
@@ -27,8 +28,8 @@ pytestmark = pytest.mark.gpu
 def build_stack(workload, total_tokens):
     layers, specs = [], []
     for l in range(workload.n_layers):
-        r = B.ds4c_layer_ratio(0, l)
-        assert r == oracle.layer_compress_ratio(l, "flash")
+        r = B.ds4c_layer_ratio(workload.variant, l)
+        assert r == oracle.layer_compress_ratio(l, ("flash", "pro")[workload.variant])
         shape = synth.stack_layer_shape(r)
         if shape is None:
             layers.append(None)
@@ -117,4 +118,29 @@ def test_stack32_long_prefill_then_decode():
             ks = [0, 1023, 1024, 1025, 8191, 8192, 16383, 16384, 16400, 16447]
         else:
             ks = [0, 31, 32, 255, 511, 512, 513]
+        check_layer_rows(L, specs[l][0], specs[l][1], x, ks, n)
+
+
+def test_stack32_pro_ragged_prompt_then_decode():
+    """Pro schedule: a 5000-token prompt (chunks of 4096 and 904: the short chunk
+    takes the plain K-split projection on ratio-4 layers and the fused path on
+    ratio-128 layers), then 7 decode steps."""
+    w = synth.WORKLOADS["stack32_pro"]
+    T, Td = 5000, 7
+    print(f"[stack] {w.name}: {T} prompt tokens in chunks of 4096, {Td} decode steps", flush=True)
+    stack, specs = build_stack(w, T + Td)
+    assert all(L is not None for L in stack.layers)
+    x = synth.hidden_states(w.wid, 4096, 0, T + Td, "bf16")
+    xd = torch.from_numpy(x).to("cuda", torch.bfloat16)
+    stack.prefill(xd[:T], chunk_cap=4096)
+    for i in range(Td):
+        stack.decode_one(xd[T + i])
+    torch.cuda.synchronize()
+    n = T + Td
+    for l, L in enumerate(stack.layers):
+        r = L.ratio
+        assert (L.frontier.n_tokens, L.frontier.n_comp, L.frontier.n_index_comp) == (n, n // r, n // 4 if r == 4 else 0)
+        if l not in (0, 1, 2, 3, 30, 31):
+            continue
+        ks = [0, 1, 1023, 1024, 1025, 1249, 1250] if r == 4 else [0, 31, 32, 38]
         check_layer_rows(L, specs[l][0], specs[l][1], x, ks, n)
