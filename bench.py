@@ -346,6 +346,19 @@ def main():
     }
     if cnt[B.KCLASS_DECODE]:
         out["decode_avg_ms"] = ms[B.KCLASS_DECODE] / cnt[B.KCLASS_DECODE]
+    if long_run:
+        # Session snapshot of the whole stack at the end of a step (rows and
+        # frontiers of every layer through pageable host memory), then a
+        # restore into the same buffers; outside the timed region.
+        t_s = time.perf_counter()
+        blob = stack.snapshot()
+        t_m = time.perf_counter()
+        stack.restore(blob)
+        t_e = time.perf_counter()
+        out["snapshot"] = {"bytes": len(blob), "save_ms": (t_m - t_s) * 1e3, "load_ms": (t_e - t_m) * 1e3,
+                           "save_GBs": len(blob) / (t_m - t_s) / 1e9, "load_GBs": len(blob) / (t_e - t_m) / 1e9,
+                           "host_memory": "pageable"}
+        del blob
     if w.layer is not None and T > w.layer.ratio:
         # Calls that start inside a window keep the separate pool launch(es):
         # one token, then the rest of the chunk from n0 = 1; the second call's

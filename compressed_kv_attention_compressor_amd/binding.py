@@ -61,6 +61,11 @@ SIGNATURES.update({
                                             c_size_t, c_void_p]),
     "ds4c_compress_stack_decode_one": (c_int, [_LP, c_int, _FP, c_void_p, POINTER(c_void_p), POINTER(c_int64),
                                                POINTER(c_void_p), POINTER(c_int64), c_void_p]),
+    "ds4c_stack_snapshot_bytes": (c_size_t, [_LP, c_int, c_int64]),
+    "ds4c_stack_snapshot_save": (c_int, [_LP, c_int, _FP, POINTER(c_void_p), POINTER(c_void_p), c_void_p, c_size_t,
+                                         POINTER(c_size_t), c_void_p]),
+    "ds4c_stack_snapshot_load": (c_int, [_LP, c_int, _FP, POINTER(c_void_p), POINTER(c_int64), POINTER(c_void_p),
+                                         POINTER(c_int64), c_void_p, c_size_t, c_void_p]),
     "ds4c_layer_ratio": (c_int, [c_int, c_int]),
     "ds4c_prefill_chunk_cap": (c_int64, [c_int64, c_int64]),
     "ds4c_status_str": (ctypes.c_char_p, [c_int]),
@@ -178,6 +183,39 @@ def ds4c_compress_stack_decode_one(layers, frontiers, x: int, attn_rows, attn_ca
     ar, ac, ir, ic = _ptr_arrays(attn_rows, attn_cap, index_rows, index_cap)
     return _ok(lib().ds4c_compress_stack_decode_one(layers, len(layers), frontiers, x, ar, ac, ir, ic, stream),
                "ds4c_compress_stack_decode_one")
+
+
+def ds4c_stack_snapshot_bytes(layers, n_tokens: int) -> int:
+    return lib().ds4c_stack_snapshot_bytes(layers, len(layers), n_tokens)
+
+
+def _host_ptr(buf):
+    """Address of a bytes or bytearray object's data (the object must outlive the call)."""
+    if isinstance(buf, bytearray):
+        return ctypes.addressof((ctypes.c_char * len(buf)).from_buffer(buf)) if len(buf) else None
+    return ctypes.cast(ctypes.c_char_p(buf), c_void_p).value
+
+
+def ds4c_stack_snapshot_save(layers, frontiers, attn_rows, index_rows, stream: int = 0) -> bytearray:
+    """Snapshot of a stack (all compressed layers at one position), written in place into a bytearray."""
+    n = next((f.n_tokens for L, f in zip(layers, frontiers) if L.ratio), 0)
+    size = ds4c_stack_snapshot_bytes(layers, n)
+    if size == 0:
+        raise DS4CError(DS4C_EINVAL, "ds4c_stack_snapshot_bytes")
+    buf = bytearray(size)
+    written = c_size_t(0)
+    ar = (c_void_p * len(layers))(*[p or None for p in attn_rows])
+    ir = (c_void_p * len(layers))(*[p or None for p in index_rows])
+    _ok(lib().ds4c_stack_snapshot_save(layers, len(layers), frontiers, ar, ir, _host_ptr(buf), size,
+                                       ctypes.byref(written), stream), "ds4c_stack_snapshot_save")
+    return buf
+
+
+def ds4c_stack_snapshot_load(layers, frontiers, blob, attn_rows, attn_cap, index_rows, index_cap,
+                             stream: int = 0) -> int:
+    ar, ac, ir, ic = _ptr_arrays(attn_rows, attn_cap, index_rows, index_cap)
+    return _ok(lib().ds4c_stack_snapshot_load(layers, len(layers), frontiers, ar, ac, ir, ic, _host_ptr(blob),
+                                              len(blob), stream), "ds4c_stack_snapshot_load")
 
 
 def ds4c_layer_ratio(variant: int, layer: int) -> int:

@@ -259,6 +259,84 @@ void put_u64(unsigned char* p, uint64_t v) { std::memcpy(p, &v, 8); }
 uint32_t get_u32(const unsigned char* p) { uint32_t v; std::memcpy(&v, p, 4); return v; }
 uint64_t get_u64(const unsigned char* p) { uint64_t v; std::memcpy(&v, p, 8); return v; }
 
+// ---------------------------------------------------------------------------
+// Stack snapshot: the compressor's sections of a session payload (Part 4 §5:
+// per-layer compressed row counts, compressed attention rows, compressor
+// frontiers, indexer rows, indexer frontiers, in that order; §6: rows 0 .. the
+// live count are contiguous; §7: the frontiers make a reload continue
+// mid-window).  Layout, little-endian:
+//   u32 magic "DS4S", u32 version, u32 n_layers, u32 0, u64 n_tokens,
+//   per layer u32 ratio, D_attn, D_idx, n_rot (0, 0, 0, 0 if uncompressed),
+//   u32[n_layers] attention row counts, u32[n_layers] indexer row counts,
+//   then per compressed layer its rows [count, D_attn] float32, then per
+//   compressed layer its attention frontier kv and score, then per ratio-4
+//   layer its indexer rows [count, D_idx], then per ratio-4 layer its indexer
+//   frontier kv and score.  Frontier rows the recurrence never reads again
+//   are written as kv 0, score -inf.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSnapMagic = 0x53345344u;  // "DS4S" little-endian
+constexpr uint32_t kSnapVersion = 1;
+
+size_t snap_header_bytes(int n_layers) { return 24 + 16 * size_t(n_layers) + 8 * size_t(n_layers); }
+
+// Shapes of the stack's layers (ratio 0 -> uncompressed, shape.ratio = 0).
+int snap_shapes(const ds4c_layer* layers, int n_layers, std::vector<Shape>* shapes) {
+  if (!layers || n_layers <= 0) return DS4C_EINVAL;
+  shapes->assign(size_t(n_layers), Shape{});
+  for (int l = 0; l < n_layers; ++l) {
+    if (layers[l].ratio == 0) continue;
+    const int st = check_layer(&layers[l], &(*shapes)[size_t(l)]);
+    if (st) return st;
+  }
+  return DS4C_OK;
+}
+
+size_t snap_bytes(const std::vector<Shape>& shapes, int64_t n) {
+  size_t b = snap_header_bytes(int(shapes.size()));
+  for (const Shape& s : shapes) {
+    if (!s.ratio) continue;
+    b += size_t(n / s.ratio) * size_t(s.D[0]) * 4 + 2 * s.fr_tensor_bytes[0];
+    if (s.n_lanes > 1) b += size_t(n / 4) * size_t(s.D[1]) * 4 + 2 * s.fr_tensor_bytes[1];
+  }
+  return b;
+}
+
+// Byte offsets of the four body sections' entries of layer l (rows, frontier).
+struct SnapOffsets {
+  std::vector<size_t> attn_rows, attn_fr, idx_rows, idx_fr;
+};
+
+SnapOffsets snap_offsets(const std::vector<Shape>& shapes, int64_t n) {
+  SnapOffsets o;
+  const size_t L = shapes.size();
+  o.attn_rows.assign(L, 0);
+  o.attn_fr.assign(L, 0);
+  o.idx_rows.assign(L, 0);
+  o.idx_fr.assign(L, 0);
+  size_t off = snap_header_bytes(int(L));
+  for (size_t l = 0; l < L; ++l)
+    if (shapes[l].ratio) { o.attn_rows[l] = off; off += size_t(n / shapes[l].ratio) * size_t(shapes[l].D[0]) * 4; }
+  for (size_t l = 0; l < L; ++l)
+    if (shapes[l].ratio) { o.attn_fr[l] = off; off += 2 * shapes[l].fr_tensor_bytes[0]; }
+  for (size_t l = 0; l < L; ++l)
+    if (shapes[l].n_lanes > 1) { o.idx_rows[l] = off; off += size_t(n / 4) * size_t(shapes[l].D[1]) * 4; }
+  for (size_t l = 0; l < L; ++l)
+    if (shapes[l].n_lanes > 1) { o.idx_fr[l] = off; off += 2 * shapes[l].fr_tensor_bytes[1]; }
+  return o;
+}
+
+// Position shared by every compressed layer's frontier, or -1.
+int64_t snap_position(const std::vector<Shape>& shapes, const ds4c_frontier* frontiers) {
+  int64_t n = -1;
+  for (size_t l = 0; l < shapes.size(); ++l) {
+    if (!shapes[l].ratio) continue;
+    if (check_frontier(shapes[l], &frontiers[l])) return -1;
+    if (n >= 0 && frontiers[l].n_tokens != n) return -1;
+    n = frontiers[l].n_tokens;
+  }
+  return n < 0 ? 0 : n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -720,6 +798,164 @@ const char* ds4c_status_str(int status) {
     case DS4C_EFORMAT: return "bad frontier blob";
     case DS4C_EDEVICE: return "HIP runtime error";
     default: return "unknown status";
+  }
+}
+
+size_t ds4c_stack_snapshot_bytes(const ds4c_layer* layers, int n_layers, int64_t n_tokens) {
+  try {
+    std::vector<Shape> shapes;
+    if (snap_shapes(layers, n_layers, &shapes) || n_tokens < 0 || n_tokens > (int64_t(1) << 40)) return 0;
+    return snap_bytes(shapes, n_tokens);
+  } catch (...) {
+    return 0;
+  }
+}
+
+int ds4c_stack_snapshot_save(const ds4c_layer* layers, int n_layers, const ds4c_frontier* frontiers,
+                             const float* const* attn_rows, const float* const* index_rows, void* host_buf,
+                             size_t cap, size_t* written, void* stream) {
+  try {
+    std::vector<Shape> shapes;
+    int st = snap_shapes(layers, n_layers, &shapes);
+    if (st) return st;
+    if (!frontiers || !attn_rows || !index_rows || !host_buf) return DS4C_EINVAL;
+    const int64_t n = snap_position(shapes, frontiers);
+    if (n < 0) return DS4C_EPOS;
+    for (int l = 0; l < n_layers; ++l) {
+      const Shape& sh = shapes[size_t(l)];
+      if (!sh.ratio) continue;
+      if (n / sh.ratio > 0 && !attn_rows[l]) return DS4C_EINVAL;
+      if (sh.n_lanes > 1 && n / 4 > 0 && !index_rows[l]) return DS4C_EINVAL;
+      if (n / sh.ratio > int64_t(UINT32_MAX)) return DS4C_ESHAPE;
+    }
+    const size_t need = snap_bytes(shapes, n);
+    if (cap < need) return DS4C_ECAP;
+    unsigned char* out = static_cast<unsigned char*>(host_buf);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const SnapOffsets o = snap_offsets(shapes, n);
+    for (int l = 0; l < n_layers; ++l) {
+      const Shape& sh = shapes[size_t(l)];
+      if (!sh.ratio) continue;
+      for (int ln = 0; ln < sh.n_lanes; ++ln) {
+        const int64_t cnt = n / (ln ? 4 : sh.ratio);
+        const float* rows = ln ? index_rows[l] : attn_rows[l];
+        unsigned char* dst_rows = out + (ln ? o.idx_rows[size_t(l)] : o.attn_rows[size_t(l)]);
+        if (cnt > 0 && hipMemcpyAsync(dst_rows, rows, size_t(cnt) * size_t(sh.D[ln]) * 4, hipMemcpyDeviceToHost,
+                                      hs) != hipSuccess)
+          return DS4C_EDEVICE;
+        float *kv, *sc;
+        frontier_ptrs(sh, frontiers[l].state, ln, &kv, &sc);
+        unsigned char* dst_fr = out + (ln ? o.idx_fr[size_t(l)] : o.attn_fr[size_t(l)]);
+        if (hipMemcpyAsync(dst_fr, kv, sh.fr_tensor_bytes[ln], hipMemcpyDeviceToHost, hs) != hipSuccess ||
+            hipMemcpyAsync(dst_fr + sh.fr_tensor_bytes[ln], sc, sh.fr_tensor_bytes[ln], hipMemcpyDeviceToHost, hs) !=
+                hipSuccess)
+          return DS4C_EDEVICE;
+      }
+    }
+    if (hipStreamSynchronize(hs) != hipSuccess) return DS4C_EDEVICE;
+    // Header and counts; canonical form of frontier rows never read again.
+    put_u32(out + 0, kSnapMagic);
+    put_u32(out + 4, kSnapVersion);
+    put_u32(out + 8, uint32_t(n_layers));
+    put_u32(out + 12, 0u);
+    put_u64(out + 16, uint64_t(n));
+    for (int l = 0; l < n_layers; ++l) {
+      const Shape& sh = shapes[size_t(l)];
+      unsigned char* d = out + 24 + 16 * size_t(l);
+      put_u32(d + 0, uint32_t(sh.ratio));
+      put_u32(d + 4, uint32_t(sh.ratio ? sh.D[0] : 0));
+      put_u32(d + 8, uint32_t(sh.n_lanes > 1 ? sh.D[1] : 0));
+      put_u32(d + 12, uint32_t(sh.ratio ? layers[l].n_rot : 0));
+      unsigned char* c = out + 24 + 16 * size_t(n_layers) + 4 * size_t(l);
+      put_u32(c, uint32_t(sh.ratio ? n / sh.ratio : 0));
+      put_u32(c + 4 * size_t(n_layers), uint32_t(sh.n_lanes > 1 ? n / 4 : 0));
+      for (int ln = 0; ln < sh.n_lanes; ++ln) {
+        float* kv = reinterpret_cast<float*>(out + (ln ? o.idx_fr[size_t(l)] : o.attn_fr[size_t(l)]));
+        float* sc = kv + sh.fr_tensor_bytes[ln] / 4;
+        for (int row = 0; row < sh.coff * sh.ratio; ++row) {
+          if (row_live(sh.ratio, n, row)) continue;
+          for (int cc = 0; cc < sh.W[ln]; ++cc) {
+            kv[size_t(row) * sh.W[ln] + cc] = 0.f;
+            sc[size_t(row) * sh.W[ln] + cc] = -INFINITY;
+          }
+        }
+      }
+    }
+    if (written) *written = need;
+    return DS4C_OK;
+  } catch (...) {
+    return DS4C_EDEVICE;
+  }
+}
+
+int ds4c_stack_snapshot_load(const ds4c_layer* layers, int n_layers, ds4c_frontier* frontiers,
+                             float* const* attn_rows, const int64_t* attn_cap, float* const* index_rows,
+                             const int64_t* index_cap, const void* host_buf, size_t len, void* stream) {
+  try {
+    std::vector<Shape> shapes;
+    int st = snap_shapes(layers, n_layers, &shapes);
+    if (st) return st;
+    if (!frontiers || !attn_rows || !attn_cap || !index_rows || !index_cap || !host_buf) return DS4C_EINVAL;
+    const unsigned char* in = static_cast<const unsigned char*>(host_buf);
+    if (len < snap_header_bytes(n_layers)) return DS4C_EFORMAT;
+    if (get_u32(in + 0) != kSnapMagic || get_u32(in + 4) != kSnapVersion ||
+        get_u32(in + 8) != uint32_t(n_layers) || get_u32(in + 12) != 0u)
+      return DS4C_EFORMAT;
+    const uint64_t nt = get_u64(in + 16);
+    if (nt > (uint64_t(1) << 40)) return DS4C_EFORMAT;
+    const int64_t n = int64_t(nt);
+    for (int l = 0; l < n_layers; ++l) {
+      const Shape& sh = shapes[size_t(l)];
+      const unsigned char* d = in + 24 + 16 * size_t(l);
+      const unsigned char* c = in + 24 + 16 * size_t(n_layers) + 4 * size_t(l);
+      if (get_u32(d) != uint32_t(sh.ratio) || get_u32(d + 4) != uint32_t(sh.ratio ? sh.D[0] : 0) ||
+          get_u32(d + 8) != uint32_t(sh.n_lanes > 1 ? sh.D[1] : 0) ||
+          get_u32(d + 12) != uint32_t(sh.ratio ? layers[l].n_rot : 0))
+        return DS4C_EFORMAT;
+      if (get_u32(c) != uint32_t(sh.ratio ? n / sh.ratio : 0) ||
+          get_u32(c + 4 * size_t(n_layers)) != uint32_t(sh.n_lanes > 1 ? n / 4 : 0))
+        return DS4C_EFORMAT;
+    }
+    if (len != snap_bytes(shapes, n)) return DS4C_EFORMAT;
+    for (int l = 0; l < n_layers; ++l) {
+      const Shape& sh = shapes[size_t(l)];
+      if (!sh.ratio) continue;
+      if (!frontiers[l].state || !aligned(frontiers[l].state, 256)) return DS4C_EINVAL;
+      if (attn_cap[l] < n / sh.ratio || (n / sh.ratio > 0 && !attn_rows[l])) return DS4C_ECAP;
+      if (sh.n_lanes > 1 && (index_cap[l] < n / 4 || (n / 4 > 0 && !index_rows[l]))) return DS4C_ECAP;
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const SnapOffsets o = snap_offsets(shapes, n);
+    for (int l = 0; l < n_layers; ++l) {
+      const Shape& sh = shapes[size_t(l)];
+      if (!sh.ratio) continue;
+      for (int ln = 0; ln < sh.n_lanes; ++ln) {
+        const int64_t cnt = n / (ln ? 4 : sh.ratio);
+        float* rows = ln ? index_rows[l] : attn_rows[l];
+        const unsigned char* src_rows = in + (ln ? o.idx_rows[size_t(l)] : o.attn_rows[size_t(l)]);
+        if (cnt > 0 && hipMemcpyAsync(rows, src_rows, size_t(cnt) * size_t(sh.D[ln]) * 4, hipMemcpyHostToDevice,
+                                      hs) != hipSuccess)
+          return DS4C_EDEVICE;
+        float *kv, *sc;
+        frontier_ptrs(sh, frontiers[l].state, ln, &kv, &sc);
+        const unsigned char* src_fr = in + (ln ? o.idx_fr[size_t(l)] : o.attn_fr[size_t(l)]);
+        if (hipMemcpyAsync(kv, src_fr, sh.fr_tensor_bytes[ln], hipMemcpyHostToDevice, hs) != hipSuccess ||
+            hipMemcpyAsync(sc, src_fr + sh.fr_tensor_bytes[ln], sh.fr_tensor_bytes[ln], hipMemcpyHostToDevice, hs) !=
+                hipSuccess)
+          return DS4C_EDEVICE;
+      }
+    }
+    if (hipStreamSynchronize(hs) != hipSuccess) return DS4C_EDEVICE;
+    for (int l = 0; l < n_layers; ++l) {
+      const Shape& sh = shapes[size_t(l)];
+      if (!sh.ratio) continue;
+      frontiers[l].n_tokens = n;
+      frontiers[l].n_comp = n / sh.ratio;
+      frontiers[l].n_index_comp = sh.ratio == 4 ? n / 4 : 0;
+    }
+    return DS4C_OK;
+  } catch (...) {
+    return DS4C_EDEVICE;
   }
 }
 

@@ -196,6 +196,21 @@ class CompressorStack:
         finally:
             self._pull()
 
+    def snapshot(self) -> bytearray:
+        """The compressor sections of a session payload for the whole stack."""
+        self._push()
+        ar, _, ir, _ = self._arrays()
+        return B.ds4c_stack_snapshot_save(self.c_layers, self.c_front, ar, ir, CompressorLayer.stream())
+
+    def restore(self, blob) -> None:
+        """Load a snapshot into this stack's existing rows and frontiers."""
+        self._push()
+        ar, ac, ir, ic = self._arrays()
+        try:
+            B.ds4c_stack_snapshot_load(self.c_layers, self.c_front, blob, ar, ac, ir, ic, CompressorLayer.stream())
+        finally:
+            self._pull()
+
     def decode_one(self, x: torch.Tensor) -> None:
         self._push()
         ar, ac, ir, ic = self._arrays()

@@ -209,6 +209,43 @@ int ds4c_compress_stack_decode_one(const ds4c_layer *layers, int n_layers, ds4c_
                                    const void *x, float *const *attn_rows, const int64_t *attn_cap,
                                    float *const *index_rows, const int64_t *index_cap, void *stream);
 
+/* Stack snapshot: the compressor's sections of a session payload (Part 4 §5:
+ * per-layer compressed row counts, the compressed attention rows, the
+ * compressor frontiers, the indexer rows and the indexer frontiers, in that
+ * order; §6: rows 0 .. the live count, which are contiguous; §7: the
+ * frontiers, so a reload continues mid-window).  The payload's other sections
+ * (tokens, logits, raw sliding-window rows) belong to the caller.
+ *
+ * Layout, little-endian: u32 magic "DS4S" (0x53345344), u32 version 1,
+ * u32 n_layers, u32 0, u64 n_tokens; per layer u32 ratio, D_attn, D_index,
+ * n_rot (all 0 for an uncompressed layer); u32[n_layers] attention row
+ * counts; u32[n_layers] indexer row counts; then float32 sections: each
+ * compressed layer's rows [count, D_attn]; each compressed layer's attention
+ * frontier kv then score [coff*ratio, W]; each ratio-4 layer's indexer rows
+ * [count, D_index]; each ratio-4 layer's indexer frontier kv then score.
+ * Frontier rows the recurrence never reads again are written as kv 0,
+ * score -inf, so equal states give equal bytes.
+ *
+ * ds4c_stack_snapshot_bytes: the exact size for a stack at position n_tokens
+ * (0 if a descriptor is invalid).
+ * ds4c_stack_snapshot_save: every compressed layer's frontier must be at the
+ * same position (else DS4C_EPOS); attn_rows[l] / index_rows[l] are the
+ * layers' row buffers (device).  Copies to host_buf (host memory, cap bytes)
+ * and synchronises the stream; *written receives the size.  DS4C_ECAP if cap
+ * is too small.
+ * ds4c_stack_snapshot_load: refuses (DS4C_EFORMAT) a buffer whose magic,
+ * version, layer count, layer shapes, counts or length do not match; DS4C_ECAP
+ * if a row buffer's capacity (rows) is too small.  Copies rows and frontier
+ * tensors into the caller's existing device buffers (Part 4 §12), sets the
+ * counters and synchronises the stream.  Nothing is written on a refusal. */
+size_t ds4c_stack_snapshot_bytes(const ds4c_layer *layers, int n_layers, int64_t n_tokens);
+int ds4c_stack_snapshot_save(const ds4c_layer *layers, int n_layers, const ds4c_frontier *frontiers,
+                             const float *const *attn_rows, const float *const *index_rows, void *host_buf,
+                             size_t cap, size_t *written, void *stream);
+int ds4c_stack_snapshot_load(const ds4c_layer *layers, int n_layers, ds4c_frontier *frontiers,
+                             float *const *attn_rows, const int64_t *attn_cap, float *const *index_rows,
+                             const int64_t *index_cap, const void *host_buf, size_t len, void *stream);
+
 /* Compress ratio of layer `layer` of a 0 = Flash / 1 = Pro model (Part 3
  * §1): Flash layers 0-1 -> 0 (uncompressed), Pro layers 0-1 -> 128; from
  * layer 2 even -> 4, odd -> 128.  -1 for a bad variant or negative layer. */

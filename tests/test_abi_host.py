@@ -48,7 +48,7 @@ def frontier(n=0, ratio=4):
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 19
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B.SIGNATURES), "binding and header disagree"
@@ -270,3 +270,86 @@ def test_stack_rejects_layers_with_different_input_rows():
     layers, fronts = _stack(6)  # ratios 0, 0, 4, 128, 4, 128
     layers[5].hidden = 2048
     assert _stack_call(layers, fronts) == B.DS4C_ESHAPE
+
+
+# --- stack snapshot (the compressor sections of a session payload) -----------
+
+def _snap_header(layers, n):
+    L = len(layers)
+    hdr = struct.pack("<IIIIQ", 0x53345344, 1, L, 0, n)
+    for i in range(L):
+        r = layers[i].ratio
+        hdr += struct.pack("<IIII", r, layers[i].attn.head_dim if r else 0,
+                           layers[i].index.head_dim if r == 4 else 0, layers[i].n_rot if r else 0)
+    hdr += struct.pack(f"<{L}I", *[n // layers[i].ratio if layers[i].ratio else 0 for i in range(L)])
+    hdr += struct.pack(f"<{L}I", *[n // 4 if layers[i].ratio == 4 else 0 for i in range(L)])
+    return hdr
+
+
+def test_snapshot_bytes_is_header_plus_sections():
+    layers, _ = _stack(4)  # ratios 0, 0, 4, 128
+    n = 1000
+    want = 24 + 16 * 4 + 8 * 4
+    want += (n // 4) * 512 * 4 + 2 * 8 * 1024 * 4 + (n // 4) * 128 * 4 + 2 * 8 * 256 * 4  # ratio-4 layer
+    want += (n // 128) * 512 * 4 + 2 * 128 * 512 * 4                                     # ratio-128 layer
+    assert B.ds4c_stack_snapshot_bytes(layers, n) == want
+    assert B.ds4c_stack_snapshot_bytes(layers, -1) == 0
+    layers[3].ratio = 7
+    assert B.ds4c_stack_snapshot_bytes(layers, n) == 0
+
+
+def _snap_arrays(layers, cap=10**6):
+    n = len(layers)
+    ar = (ctypes.c_void_p * n)(*[FAKE + 0x30000000 if layers[i].ratio else 0 for i in range(n)])
+    ac = (ctypes.c_int64 * n)(*[cap if layers[i].ratio else 0 for i in range(n)])
+    ir = (ctypes.c_void_p * n)(*[FAKE + 0x40000000 if layers[i].ratio == 4 else 0 for i in range(n)])
+    ic = (ctypes.c_int64 * n)(*[cap if layers[i].ratio == 4 else 0 for i in range(n)])
+    return ar, ac, ir, ic
+
+
+def test_snapshot_save_refuses_before_copying():
+    layers, fronts = _stack(4)
+    for i in (2, 3):
+        r = layers[i].ratio
+        fronts[i].n_tokens, fronts[i].n_comp = 1000, 1000 // r
+        fronts[i].n_index_comp = 1000 // 4 if r == 4 else 0
+    ar, _, ir, _ = _snap_arrays(layers)
+    size = B.ds4c_stack_snapshot_bytes(layers, 1000)
+    buf = ctypes.create_string_buffer(size)
+    w = ctypes.c_size_t(0)
+    # layers at different positions
+    fronts[3].n_tokens, fronts[3].n_comp = 1128, 1128 // 128
+    assert B.lib().ds4c_stack_snapshot_save(layers, 4, fronts, ar, ir, buf, size, ctypes.byref(w), None) == B.DS4C_EPOS
+    fronts[3].n_tokens, fronts[3].n_comp = 1000, 1000 // 128
+    # inconsistent counters
+    fronts[2].n_comp = 7
+    assert B.lib().ds4c_stack_snapshot_save(layers, 4, fronts, ar, ir, buf, size, ctypes.byref(w), None) == B.DS4C_EPOS
+    fronts[2].n_comp = 250
+    # too small a buffer
+    assert B.lib().ds4c_stack_snapshot_save(layers, 4, fronts, ar, ir, buf, size - 1, ctypes.byref(w), None) == B.DS4C_ECAP
+    assert w.value == 0
+
+
+def test_snapshot_load_refuses_mismatches():
+    layers, fronts = _stack(4)
+    n = 1000
+    size = B.ds4c_stack_snapshot_bytes(layers, n)
+    good = bytearray(_snap_header(layers, n)) + bytes(size - len(_snap_header(layers, n)))
+    ar, ac, ir, ic = _snap_arrays(layers)
+
+    def load(blob, cap=10**6):
+        a, c, i, d = _snap_arrays(layers, cap)
+        return B.lib().ds4c_stack_snapshot_load(layers, 4, fronts, a, c, i, d, bytes(blob), len(blob), None)
+
+    bad = bytearray(good); bad[0] ^= 1
+    assert load(bad) == B.DS4C_EFORMAT                      # magic
+    bad = bytearray(good); bad[4] = 2
+    assert load(bad) == B.DS4C_EFORMAT                      # version
+    bad = bytearray(good); struct.pack_into("<I", bad, 24 + 16 * 2 + 4, 256)
+    assert load(bad) == B.DS4C_EFORMAT                      # head dim of layer 2
+    bad = bytearray(good); struct.pack_into("<I", bad, 24 + 16 * 4 + 4 * 2, 249)
+    assert load(bad) == B.DS4C_EFORMAT                      # row count of layer 2
+    assert load(good[:-4]) == B.DS4C_EFORMAT                # length
+    assert load(good, cap=10) == B.DS4C_ECAP                # row buffer capacity
+    # nothing was written: counters untouched
+    assert [fronts[i].n_tokens for i in range(4)] == [0, 0, 0, 0]
