@@ -67,3 +67,4 @@ from .compressor import (  # noqa: F401
     rows_emitted,
 )
 from .schedule import layer_compress_ratio, prefill_chunk_cap  # noqa: F401
+from . import indexer  # noqa: F401
