@@ -21,8 +21,8 @@ DS4C_EFORMAT = -5
 DS4C_EDEVICE = -6
 DS4C_F32 = 0
 DS4C_BF16 = 1
-KCLASS_PROJ, KCLASS_POOL, KCLASS_DECODE, KCLASS_INIT, KCLASS_CARRY = 0, 1, 2, 3, 4
-PROFILE_ALL = 0x1F
+KCLASS_PROJ, KCLASS_POOL, KCLASS_DECODE, KCLASS_INIT, KCLASS_CARRY, KCLASS_INDEXER = 0, 1, 2, 3, 4, 5
+PROFILE_ALL = 0x3F
 
 # Every function the header declares, with (restype, argtypes).
 SIGNATURES = {}
@@ -66,6 +66,10 @@ SIGNATURES.update({
                                          POINTER(c_size_t), c_void_p]),
     "ds4c_stack_snapshot_load": (c_int, [_LP, c_int, _FP, POINTER(c_void_p), POINTER(c_int64), POINTER(c_void_p),
                                          POINTER(c_int64), c_void_p, c_size_t, c_void_p]),
+    "ds4c_indexer_workspace_bytes": (c_size_t, [c_int64, ctypes.c_int32]),
+    "ds4c_indexer_topk": (c_int, [c_void_p, c_void_p, ctypes.c_int32, ctypes.c_int32, c_void_p, c_int64,
+                                  ctypes.c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                  c_void_p]),
     "ds4c_layer_ratio": (c_int, [c_int, c_int]),
     "ds4c_prefill_chunk_cap": (c_int64, [c_int64, c_int64]),
     "ds4c_status_str": (ctypes.c_char_p, [c_int]),
@@ -218,6 +222,18 @@ def ds4c_stack_snapshot_load(layers, frontiers, blob, attn_rows, attn_cap, index
                                               len(blob), stream), "ds4c_stack_snapshot_load")
 
 
+def ds4c_indexer_workspace_bytes(n_rows: int, k: int) -> int:
+    return lib().ds4c_indexer_workspace_bytes(n_rows, k)
+
+
+def ds4c_indexer_topk(q: int, head_w: int, n_heads: int, head_dim: int, rows: int, n_rows: int, k: int,
+                      out_idx: int, out_score: int, q_hat: int, scores: int, workspace: int, ws_bytes: int,
+                      stream: int = 0) -> int:
+    return _ok(lib().ds4c_indexer_topk(q, head_w, n_heads, head_dim, rows or None, n_rows, k, out_idx, out_score,
+                                       q_hat or None, scores or None, workspace, ws_bytes, stream),
+               "ds4c_indexer_topk")
+
+
 def ds4c_layer_ratio(variant: int, layer: int) -> int:
     return lib().ds4c_layer_ratio(variant, layer)
 
@@ -241,8 +257,8 @@ def ds4c_profile_enable(classes=True) -> None:
 
 
 def ds4c_profile_read():
-    """(ms[5], count[5]) accumulated per kernel class since the last read."""
-    ms = (c_double * 5)()
-    cnt = (c_int64 * 5)()
-    _ok(lib().ds4c_profile_read(ms, cnt, 5), "ds4c_profile_read")
+    """(ms[6], count[6]) accumulated per kernel class since the last read."""
+    ms = (c_double * 6)()
+    cnt = (c_int64 * 6)()
+    _ok(lib().ds4c_profile_read(ms, cnt, 6), "ds4c_profile_read")
     return list(ms), list(cnt)

@@ -959,6 +959,52 @@ int ds4c_stack_snapshot_load(const ds4c_layer* layers, int n_layers, ds4c_fronti
   }
 }
 
+size_t ds4c_indexer_workspace_bytes(int64_t n_rows, int32_t k) {
+  if (n_rows < 0 || k < 1 || k > 512) return 0;
+  const int64_t chunks = (n_rows + ds4c::kIndexerChunk - 1) / ds4c::kIndexerChunk;
+  if (chunks * k > ds4c::kIndexerMaxCand) return 0;
+  return align256(size_t(n_rows) * 4) + align256(size_t(chunks) * size_t(k) * 8) + 256;
+}
+
+int ds4c_indexer_topk(const float* q, const float* head_w, int32_t n_heads, int32_t head_dim,
+                      const float* index_rows, int64_t n_rows, int32_t k, int32_t* out_idx, float* out_score,
+                      float* q_hat, float* scores, void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    if (head_dim != 64 && head_dim != 128) return DS4C_ESHAPE;
+    if (n_heads < 4 || n_heads > 64 || n_heads % 4 != 0) return DS4C_ESHAPE;
+    if (k < 1 || k > 512 || n_rows < 0) return DS4C_EINVAL;
+    const size_t need = ds4c_indexer_workspace_bytes(n_rows, k);
+    if (need == 0) return DS4C_ESHAPE;
+    if (!q || !head_w || !aligned(q, 16) || !aligned(head_w, 4)) return DS4C_EINVAL;
+    if (n_rows > 0 && (!index_rows || !aligned(index_rows, 16))) return DS4C_EINVAL;
+    if (!out_idx || !out_score) return DS4C_EINVAL;
+    if (q_hat && !aligned(q_hat, 16)) return DS4C_EINVAL;
+    if (!workspace || !aligned(workspace, 256)) return DS4C_EINVAL;
+    if (ws_bytes < need) return DS4C_ECAP;
+    if (n_rows == 0) return DS4C_OK;
+    char* ws = static_cast<char*>(workspace);
+    ds4c::IndexerArgs a{};
+    a.q = q;
+    a.head_w = head_w;
+    a.rows = index_rows;
+    a.n = n_rows;
+    a.H = n_heads;
+    a.Dh = head_dim;
+    a.scores = scores ? scores : reinterpret_cast<float*>(ws);
+    a.q_hat = q_hat;
+    a.out_idx = out_idx;
+    a.out_score = out_score;
+    a.k = k;
+    a.cand = reinterpret_cast<uint64_t*>(ws + align256(size_t(n_rows) * 4));
+    a.n_chunks = int((n_rows + ds4c::kIndexerChunk - 1) / ds4c::kIndexerChunk);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return dev_status(
+        timed(DS4C_KCLASS_INDEXER, [&](const ds4c::Timing& tm) { return ds4c::launch_indexer(a, hs, tm); }));
+  } catch (...) {
+    return DS4C_EDEVICE;
+  }
+}
+
 int ds4c_profile_enable(int class_mask) {
   try {
     if (class_mask < 0 || class_mask > DS4C_PROFILE_ALL) return DS4C_EINVAL;
@@ -973,7 +1019,7 @@ int ds4c_profile_enable(int class_mask) {
 
 int ds4c_profile_read(double* ms, int64_t* count, int n) {
   try {
-    if (!ms || !count || n < 0 || n > 5) return DS4C_EINVAL;
+    if (!ms || !count || n < 0 || n > 6) return DS4C_EINVAL;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     for (int i = 0; i < n; ++i) {
       ms[i] = 0.0;

@@ -171,6 +171,46 @@ __device__ __forceinline__ float row_sumsq(const float (&y)[DPL]) {
   return ss;
 }
 
+// Indexer QAT round trip of a D-wide row held by one wave (D == 64 * DPL,
+// lane holds dims lane*DPL ..): the orthonormal Walsh-Hadamard rotation
+// (Sylvester order; butterflies (a, b) -> (a + b, a - b) on index pairs
+// (j, j + h) for h = 1, 2, 4, ...; strides below DPL inside a lane, the rest
+// across lanes), scaled by 1/sqrt(D), then FP4 E2M1 in blocks of 32 dims
+// (32/DPL lanes) with the power-of-two block scale.  The row stays rotated.
+template <int DPL>
+__device__ __forceinline__ void hadamard_fp4(float (&y)[DPL], int D, int lane) {
+#pragma unroll
+  for (int h = 1; h < DPL; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      if ((i & h) == 0) {
+        const float a = y[i], b = y[i + h];
+        y[i] = a + b;
+        y[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const bool low = (lane & m) == 0;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const float p = __shfl_xor(y[i], m, kWave);
+      y[i] = low ? (y[i] + p) : (p - y[i]);
+    }
+  }
+  const float scale = (float)(1.0 / sqrt((double)D));
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) y[i] *= scale;
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) amax = fmaxf(amax, fabsf(y[i]));
+  amax = group_max<32 / DPL>(amax);
+  const int kexp = e2m1_block_exp(amax);
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) y[i] = ldexpf(rne_e2m1(ldexpf(y[i], -kexp)), kexp);
+}
+
 template <int DPL>
 __device__ __forceinline__ void finish_row_part(float (&y)[DPL], const LaneDev& L, float inv, int d0, int n_rot,
                                                 double log2_base, int64_t k, int ratio,
@@ -224,40 +264,7 @@ __device__ __forceinline__ void finish_row_part(float (&y)[DPL], const LaneDev& 
       for (int i = 0; i < DPL; ++i) y[i] = ldexpf(rne_e4m3(ldexpf(y[i], -kexp)), kexp);
     }
   } else {
-    // Orthonormal Walsh-Hadamard rotation (Sylvester order) of the whole row:
-    // butterflies (a, b) -> (a + b, a - b) on index pairs (j, j + h) for
-    // h = 1, 2, 4, ...; strides below DPL inside a lane, the rest across lanes.
-#pragma unroll
-    for (int h = 1; h < DPL; h <<= 1) {
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        if ((i & h) == 0) {
-          const float a = y[i], b = y[i + h];
-          y[i] = a + b;
-          y[i + h] = a - b;
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-      const bool low = (lane & m) == 0;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        const float p = __shfl_xor(y[i], m, kWave);
-        y[i] = low ? (y[i] + p) : (p - y[i]);
-      }
-    }
-    const float scale = (float)(1.0 / sqrt((double)D));
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) y[i] *= scale;
-    // FP4 E2M1 round trip in blocks of 32 dims (32/DPL lanes).
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) amax = fmaxf(amax, fabsf(y[i]));
-    amax = group_max<32 / DPL>(amax);
-    const int kexp = e2m1_block_exp(amax);
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) y[i] = ldexpf(rne_e2m1(ldexpf(y[i], -kexp)), kexp);
+    hadamard_fp4<DPL>(y, D, lane);
   }
 
   store_vec<DPL>(out_row + d0, y);

@@ -115,6 +115,23 @@ struct DecodeArgs {
   LaneDev lane[2];
 };
 
+// Indexer scoring and top-k of one query token.
+struct IndexerArgs {
+  const float* q;       // [H, Dh] query heads (before the QAT round trip)
+  const float* head_w;  // [H] head weights
+  const float* rows;    // [n, Dh] compressed indexer rows (rotated, QAT applied)
+  int64_t n;            // rows
+  int H;                // heads, a multiple of 4, <= 64
+  int Dh;               // 64 or 128
+  float* scores;        // [n] every row's score
+  float* q_hat;         // nullable [H, Dh]: the query after the round trip
+  int32_t* out_idx;     // [min(n, k)] selected rows, descending score
+  float* out_score;     // [min(n, k)] their scores
+  int k;                // 1 .. 512
+  uint64_t* cand;       // [n_chunks * k] sort keys surviving each chunk
+  int n_chunks;         // ceil(n / kIndexerChunk)
+};
+
 struct FillArgs {
   float* kv[2];
   float* sc[2];

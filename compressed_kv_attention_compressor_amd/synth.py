@@ -6,7 +6,9 @@ arithmetic; the GPU path and the CPU oracle both consume what it returns.
 Generator: ``numpy.random.Generator(PCG64(SeedSequence(seed, spawn_key=
 (workload_id, layer, tensor_id, slab))))``.  Tensor ids: 0 = x, 1 = attention
 wkv, 2 = attention wgate, 3 = attention APE, 4 = indexer wkv, 5 = indexer
-wgate, 6 = indexer APE, 7 = attention norm weight, 8 = indexer norm weight.
+wgate, 6 = indexer APE, 7 = attention norm weight, 8 = indexer norm weight,
+9 / 10 / 11 = indexer query heads / head weights / compressed indexer rows
+(indexer scoring inputs).
 Hidden states are drawn per 4096-token slab so that any token range can be
 regenerated without drawing the whole sequence.
 
@@ -75,6 +77,10 @@ WORKLOADS: Dict[str, Workload] = {
     # odd layers (32 compressed layers); the same Flash layer shapes.
     "stack32_pro": Workload(6, "32-layer Pro-schedule stack, one 4096-token chunk, hidden 4096",
                             4096, None, n_layers=32, variant=1),
+    # Indexer scoring + top-512 of one query over the indexer rows a Flash
+    # ratio-4 layer holds after the long prompt (65,792 tokens: 16,448 rows),
+    # 64 heads of 128 dims.
+    "indexer_c5": Workload(7, "indexer top-512 of one query over 16448 rows, 64 heads x 128 dims", 16448, None),
 }
 
 
@@ -138,3 +144,13 @@ def stack_layer_shape(ratio: int) -> Optional[LayerShape]:
     if ratio == 128:
         return FLASH_R128
     return None
+
+
+def indexer_inputs(wid: int, n_rows: int, n_heads: int = 64, head_dim: int = 128, seed: int = 0):
+    """Inputs of one indexer scoring call: query heads q [H, Dh] ~ N(0, 1),
+    head weights [H] ~ N(0, 1/H) and compressed indexer rows [n, Dh] ~ N(0, 1),
+    all float32."""
+    q = _normal(_gen(seed, wid, 0, 9), (n_heads, head_dim), 1.0)
+    w = _normal(_gen(seed, wid, 0, 10), (n_heads,), 1.0 / np.sqrt(n_heads))
+    rows = _normal(_gen(seed, wid, 0, 11), (n_rows, head_dim), 1.0)
+    return q, w, rows

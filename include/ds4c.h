@@ -238,6 +238,31 @@ int ds4c_compress_stack_decode_one(const ds4c_layer *layers, int n_layers, ds4c_
  * if a row buffer's capacity (rows) is too small.  Copies rows and frontier
  * tensors into the caller's existing device buffers (Part 4 §12), sets the
  * counters and synchronises the stream.  Nothing is written on a refusal. */
+/* Indexer scoring and top-k of one query token over a ratio-4 layer's
+ * compressed indexer rows (Part 3 §6: 64 heads of 128 dims, top 512 rows
+ * reach the attention; Part 3 §9: the query passes the same Hadamard + FP4
+ * round trip as the rows).  The score of row j is
+ *   s_j = sum_h head_w[h] * max(0, <qhat_h, row_j>),
+ * qhat_h = the round trip of q[h] (rotation by the orthonormal Hadamard
+ * matrix of size head_dim, FP4 E2M1 in blocks of 32 with a power-of-two
+ * scale; it stays rotated, like the rows).  The k rows with the largest
+ * scores are written to out_idx / out_score (min(n_rows, k) entries) in
+ * descending score order, equal scores to the lower row index.
+ *
+ * q [n_heads, head_dim], head_w [n_heads], index_rows [n_rows, head_dim]
+ * (row-major float32, device; q and index_rows 16-byte aligned): the layer's
+ * rows 0 .. n_index_comp-1 as ds4c_compress_* wrote them.  head_dim 64 or
+ * 128; n_heads a multiple of 4 up to 64; 1 <= k <= 512; rows in chunks of
+ * 4096 with ceil(n_rows / 4096) * k <= 16384 (n_rows up to 131072 at k =
+ * 512), else DS4C_ESHAPE.  q_hat (nullable, [n_heads, head_dim]) receives
+ * the rotated, quantised query; scores (nullable, [n_rows]) every row's
+ * score.  workspace: device, >= ds4c_indexer_workspace_bytes(n_rows, k),
+ * 256-byte aligned.  Asynchronous on stream; n_rows == 0 writes nothing. */
+size_t ds4c_indexer_workspace_bytes(int64_t n_rows, int32_t k);
+int ds4c_indexer_topk(const float *q, const float *head_w, int32_t n_heads, int32_t head_dim,
+                      const float *index_rows, int64_t n_rows, int32_t k, int32_t *out_idx, float *out_score,
+                      float *q_hat, float *scores, void *workspace, size_t ws_bytes, void *stream);
+
 size_t ds4c_stack_snapshot_bytes(const ds4c_layer *layers, int n_layers, int64_t n_tokens);
 int ds4c_stack_snapshot_save(const ds4c_layer *layers, int n_layers, const ds4c_frontier *frontiers,
                              const float *const *attn_rows, const float *const *index_rows, void *host_buf,
@@ -265,14 +290,15 @@ const char *ds4c_status_str(int status);
  * (DS4C_KCLASS_*), 0 turns timing off, DS4C_PROFILE_ALL selects every class;
  * other values return DS4C_EINVAL.  ds4c_profile_read waits for the recorded
  * events, writes the accumulated milliseconds and launch counts of each class
- * into ms[n] and count[n] (n <= 5), and clears the record.  Enabling or
+ * into ms[n] and count[n] (n <= 6), and clears the record.  Enabling or
  * disabling also clears it.  Classes: projection (PROJ; a K-split call's
  * plane sum included), pooling and row finishing (POOL), the separate
  * frontier-carry launch of a ratio-4 call that does not start on a window
- * boundary (CARRY), decode steps (DECODE), frontier init (INIT). */
+ * boundary (CARRY), decode steps (DECODE), frontier init (INIT), indexer
+ * scoring and top-k (INDEXER, the three launches of one call). */
 enum { DS4C_KCLASS_PROJ = 0, DS4C_KCLASS_POOL = 1, DS4C_KCLASS_DECODE = 2, DS4C_KCLASS_INIT = 3,
-       DS4C_KCLASS_CARRY = 4 };
-enum { DS4C_PROFILE_ALL = 0x1F };
+       DS4C_KCLASS_CARRY = 4, DS4C_KCLASS_INDEXER = 5 };
+enum { DS4C_PROFILE_ALL = 0x3F };
 int ds4c_profile_enable(int class_mask);
 int ds4c_profile_read(double *ms, int64_t *count, int n);
 

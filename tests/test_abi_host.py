@@ -48,7 +48,7 @@ def frontier(n=0, ratio=4):
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B.SIGNATURES), "binding and header disagree"
@@ -199,10 +199,10 @@ def test_save_rejects_small_buffer():
 def test_profile_read_without_records():
     B.ds4c_profile_enable(True)
     ms, cnt = B.ds4c_profile_read()
-    assert ms == [0.0] * 5 and cnt == [0] * 5
-    B.ds4c_profile_enable([B.KCLASS_PROJ, B.KCLASS_CARRY])
+    assert ms == [0.0] * 6 and cnt == [0] * 6
+    B.ds4c_profile_enable([B.KCLASS_PROJ, B.KCLASS_CARRY, B.KCLASS_INDEXER])
     ms, cnt = B.ds4c_profile_read()
-    assert cnt == [0] * 5
+    assert cnt == [0] * 6
     B.ds4c_profile_enable(False)
 
 
@@ -353,3 +353,33 @@ def test_snapshot_load_refuses_mismatches():
     assert load(good, cap=10) == B.DS4C_ECAP                # row buffer capacity
     # nothing was written: counters untouched
     assert [fronts[i].n_tokens for i in range(4)] == [0, 0, 0, 0]
+
+
+# --- indexer scoring and top-k -------------------------------------------------
+
+def test_indexer_workspace_bytes():
+    a256 = lambda v: (v + 255) // 256 * 256
+    assert B.ds4c_indexer_workspace_bytes(16448, 512) == a256(16448 * 4) + a256(5 * 512 * 8) + 256
+    assert B.ds4c_indexer_workspace_bytes(0, 512) == 256
+    assert B.ds4c_indexer_workspace_bytes(131072, 512) > 0       # 32 chunks x 512 = 16384 keys
+    assert B.ds4c_indexer_workspace_bytes(131073, 512) == 0      # 33 chunks: too many keys
+    assert B.ds4c_indexer_workspace_bytes(10, 0) == 0
+    assert B.ds4c_indexer_workspace_bytes(10, 513) == 0
+
+
+def test_indexer_validates_before_launching():
+    def call(H=64, Dh=128, n=100, k=16, ws=None, q=FAKE, rows=FAKE + 0x100000, wsp=FAKE + 0x200000):
+        wsb = B.ds4c_indexer_workspace_bytes(n, k) if ws is None else ws
+        return B.lib().ds4c_indexer_topk(q, FAKE + 0x300000, H, Dh, rows, n, k, FAKE + 0x400000, FAKE + 0x500000,
+                                         None, None, wsp, wsb, None)
+    assert call(Dh=96) == B.DS4C_ESHAPE
+    assert call(H=3) == B.DS4C_ESHAPE
+    assert call(H=68) == B.DS4C_ESHAPE
+    assert call(k=0) == B.DS4C_EINVAL
+    assert call(k=513) == B.DS4C_EINVAL
+    assert call(n=131073, k=512) == B.DS4C_ESHAPE
+    assert call(q=FAKE + 4) == B.DS4C_EINVAL                     # q not 16-byte aligned
+    assert call(rows=0) == B.DS4C_EINVAL
+    assert call(wsp=FAKE + 16) == B.DS4C_EINVAL                  # workspace not 256-byte aligned
+    assert call(ws=B.ds4c_indexer_workspace_bytes(100, 16) - 1) == B.DS4C_ECAP
+    assert call(n=0, rows=0) == B.DS4C_OK                        # nothing to score: no launch
