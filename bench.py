@@ -11,6 +11,9 @@ Workloads (--workload):
               256 ds4c_compress_stack_decode_one steps: a step is all of it.
   stack32_pro the 32-layer Pro-schedule stack (layers 0-1 ratio 128, then
               ratio 4 / 128 alternating; 32 compressed layers), one chunk.
+  indexer_c5  indexer scoring + top-512 of one query over the 16,448 indexer
+              rows a ratio-4 layer holds after the long prompt; a step is one
+              ds4c_indexer_topk call (value in queries/s).
 
 Every step starts from position 0 (the frontier counters are reset on the
 host; a call at position 0 reads nothing from the frontier).  Inputs are
@@ -197,12 +200,77 @@ def copy_calibration(mib: int, reps: int = 20) -> None:
           flush=True)
 
 
+def bench_indexer(w, args):
+    """One query's indexer scoring and top-512 over 16,448 rows (64 heads x 128
+    dims): the score launch reads every row once; one select launch follows."""
+    import torch
+
+    from compressed_kv_attention_compressor_amd import binding as B
+    from compressed_kv_attention_compressor_amd import synth
+
+    n, H, Dh, k = w.tokens, 64, 128, 512
+    steps = args.steps or 200
+    warmup = args.warmup if args.warmup >= 0 else 10
+    q_np, w_np, rows_np = synth.indexer_inputs(w.wid, n, H, Dh)
+    q, hw, rows = (torch.from_numpy(a).cuda() for a in (q_np, w_np, rows_np))
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    sc = torch.empty(k, dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.ds4c_indexer_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        B.ds4c_indexer_topk(q.data_ptr(), hw.data_ptr(), H, Dh, rows.data_ptr(), n, k, idx.data_ptr(),
+                            sc.data_ptr(), 0, 0, ws.data_ptr(), ws.numel(), stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    B.ds4c_profile_enable([B.KCLASS_INDEXER])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms, cnt = B.ds4c_profile_read()
+    B.ds4c_profile_enable(False)
+    call_ms = ms[B.KCLASS_INDEXER] / max(cnt[B.KCLASS_INDEXER], 1)
+    # Algorithmic bytes: rows read once, query and head weights, scores written
+    # and read back by the sort, the selected rows and scores written.
+    alg = n * Dh * 4 + H * Dh * 4 + H * 4 + 2 * n * 4 + k * 8
+    gbs = alg / (call_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": steps / el, "unit": "queries/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": el / steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded N(0,1) query heads and rows, N(0,1/64) head weights)",
+        "config": {"workload": w.name, "rows": n, "heads": H, "head_dim": Dh, "top_k": k},
+        "rows_per_s": steps * n / el,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                     "traffic": None, "kernel": "indexer_score_kernel + indexer_select_kernel (one call)",
+                     "avg_ms": call_ms, "algorithmic_bytes": alg},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            oracle.indexer.select(q_np, w_np, rows_np, k)
+            calls += 1
+            el_c = time.perf_counter() - t0
+            if el_c >= 10.0 or calls >= 200:
+                break
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        out["cpu_baseline"] = {"value": calls / el_c, "unit": "queries/s", "cores": threads, "kind": "oracle",
+                               "sample": f"{calls} whole calls ({el_c:.1f} s); float64 NumPy, BLAS threads {threads}"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0, help="timed steps (default depends on the workload)")
     ap.add_argument("--warmup", type=int, default=-1)
-    ap.add_argument("--workload", default="r4_flash", choices=["r4_flash", "r128_flash", "stack32", "stack32_long", "stack32_pro"])
+    ap.add_argument("--workload", default="r4_flash", choices=["r4_flash", "r128_flash", "stack32", "stack32_long", "stack32_pro", "indexer_c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0)
     args = ap.parse_args()
@@ -220,6 +288,9 @@ def main():
     from compressed_kv_attention_compressor_amd.layer import CompressorLayer, CompressorStack
 
     w = synth.WORKLOADS[args.workload]
+    if args.workload == "indexer_c5":
+        bench_indexer(w, args)
+        return
     long_run = args.workload == "stack32_long"
     steps = args.steps or (3 if long_run else 20 if w.layer is None else 50)
     warmup = args.warmup if args.warmup >= 0 else (1 if long_run else 5)

@@ -7,17 +7,15 @@
 // head h's query (rows and query both stay in the rotated basis).  The top-k
 // order is descending score, equal scores to the lower row index.
 //
-// Three launches:
+// Launches:
 //  * indexer_score_kernel: 64 rows per workgroup.  The workgroup rotates and
 //    quantises the query into LDS (each wave a quarter of the heads), stages
-//    its rows in LDS, and thread (row, head group) accumulates the dot
-//    products of its row with heads g, g+4, ...; the four head groups of a
-//    row meet by two shuffles in a fixed order.
-//  * indexer_topk_chunk_kernel: one workgroup per 4096 scores sorts keys
-//    (order-preserving score bits, then the complement of the row index) by
-//    a bitonic network in LDS and keeps the k largest.
-//  * indexer_topk_merge_kernel: one workgroup sorts every chunk's survivors
-//    the same way and writes the k largest as (row, score).
+//    its rows in LDS, and each thread accumulates 4 rows x 4 heads; the 16
+//    head groups of a row meet by butterfly shuffles in a fixed order.
+//  * indexer_select_kernel: the k largest (score, lower row first) by a radix
+//    select over 64-bit keys in one workgroup, each survivor written at its
+//    rank.  Up to kIndexerChunk rows it is one launch; longer calls run
+//    one workgroup per chunk first and a final pass over their survivors.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,6 +29,7 @@ namespace {
 constexpr int kScoreRows = 64;
 constexpr int kScoreThreads = 256;
 constexpr int kSortThreads = 1024;
+constexpr int kSelPerThread = kIndexerChunk / kSortThreads;  // keys per thread in a select pass
 
 // Order-preserving map of float bits to unsigned: larger float, larger key.
 __device__ __forceinline__ uint32_t ord_bits(float f) {
@@ -44,106 +43,222 @@ __device__ __forceinline__ float unord_bits(uint32_t o) {
 template <int DH>
 __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArgs a) {
   constexpr int DPL = DH / 64;
-  constexpr int kLd = DH + 4;  // padded LDS row: consecutive rows start on different banks
+  constexpr int kLd = DH + 4;  // padded LDS row: consecutive rows start 4 banks apart
   __shared__ float s_q[64 * kLd];
   __shared__ float s_k[kScoreRows * kLd];
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int64_t row0 = (int64_t)blockIdx.x * kScoreRows;
 
-  // Rows of this workgroup (zeros past n), 16 bytes per thread and step.
-  constexpr int kVec = DH / 4;  // float4 per row
-  for (int i = t; i < kScoreRows * kVec; i += kScoreThreads) {
-    const int r = i / kVec, c = (i % kVec) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row0 + r < a.n) v = *reinterpret_cast<const float4*>(a.rows + (row0 + r) * DH + c);
-    *reinterpret_cast<float4*>(s_k + r * kLd + c) = v;
-  }
-  // Query heads wave, wave+4, ...: rotation + FP4 round trip into LDS.
-  for (int h = wave; h < a.H; h += kScoreThreads / kWave) {
-    float y[DPL];
-    load_vec<DPL>(y, a.q + h * DH + lane * DPL);
-    hadamard_fp4<DPL>(y, DH, lane);
+  // Every load is issued before any is used: the rows of this workgroup
+  // (zeros past n), 16 bytes per thread and step, and the query heads
+  // wave, wave + 4, ... (zeros past H).
+  constexpr int kVec = DH / 4;                         // float4 per row
+  constexpr int kRowSteps = kScoreRows * kVec / kScoreThreads;
+  float4 kv[kRowSteps];
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) s_q[h * kLd + lane * DPL + i] = y[i];
-    if (a.q_hat && blockIdx.x == 0) store_vec<DPL>(a.q_hat + h * DH + lane * DPL, y);
+  for (int s = 0; s < kRowSteps; ++s) {
+    const int i = t + s * kScoreThreads, r = i / kVec, c = (i % kVec) * 4;
+    kv[s] = row0 + r < a.n ? *reinterpret_cast<const float4*>(a.rows + (row0 + r) * DH + c)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  constexpr int kHeadsPerWave = 64 / (kScoreThreads / kWave);
+  float y[kHeadsPerWave][DPL];
+#pragma unroll
+  for (int j = 0; j < kHeadsPerWave; ++j) {
+    const int h = wave + 4 * j;
+    if (h < a.H) {
+      load_vec<DPL>(y[j], a.q + h * DH + lane * DPL);
+    } else {
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) y[j][i] = 0.f;
+    }
+  }
+  // Rotation + FP4 round trip of each head into LDS (a zero head stays
+  // zero), while the rows are still on their way.
+#pragma unroll
+  for (int j = 0; j < kHeadsPerWave; ++j) {
+    const int h = wave + 4 * j;
+    hadamard_fp4<DPL>(y[j], DH, lane);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) s_q[h * kLd + lane * DPL + i] = y[j][i];
+    if (a.q_hat && blockIdx.x == 0 && h < a.H) store_vec<DPL>(a.q_hat + h * DH + lane * DPL, y[j]);
+  }
+#pragma unroll
+  for (int s = 0; s < kRowSteps; ++s) {
+    const int i = t + s * kScoreThreads, r = i / kVec, c = (i % kVec) * 4;
+    *reinterpret_cast<float4*>(s_k + r * kLd + c) = kv[s];
   }
   __syncthreads();
 
-  const int r = t / 4, g = t % 4;
-  const int nh = a.H / 4;  // heads g, g+4, ... of this thread
-  float acc[16];
+  // Thread (row group rg, head group hg): rows 4rg .. 4rg+3 against heads
+  // hg, hg + 16, hg + 32, hg + 48; per 4 dims 8 LDS reads feed 64 FMAs.
+  const int rg = t / 16, hg = t % 16;
+  float acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[r][i] = 0.f;
   for (int d = 0; d < DH; d += 4) {
-    const float4 k = *reinterpret_cast<const float4*>(s_k + r * kLd + d);
+    float4 k[4], q[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < nh) {
-        const float4 q = *reinterpret_cast<const float4*>(s_q + (g + 4 * i) * kLd + d);
-        float v = acc[i];
-        v = fmaf(k.x, q.x, v);
-        v = fmaf(k.y, q.y, v);
-        v = fmaf(k.z, q.z, v);
-        v = fmaf(k.w, q.w, v);
-        acc[i] = v;
+    for (int r = 0; r < 4; ++r) k[r] = *reinterpret_cast<const float4*>(s_k + (4 * rg + r) * kLd + d);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = *reinterpret_cast<const float4*>(s_q + (hg + 16 * i) * kLd + d);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[r][i];
+        v = fmaf(k[r].x, q[i].x, v);
+        v = fmaf(k[r].y, q[i].y, v);
+        v = fmaf(k[r].z, q[i].z, v);
+        v = fmaf(k[r].w, q[i].w, v);
+        acc[r][i] = v;
       }
-    }
   }
-  float s = 0.f;
+  float w[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (i < nh) s = fmaf(a.head_w[g + 4 * i], fmaxf(acc[i], 0.f), s);
-  // Head groups 0..3 of a row sit in adjacent lanes: (s0 + s1) + (s2 + s3).
-  s += __shfl_xor(s, 1, kWave);
-  s += __shfl_xor(s, 2, kWave);
-  if (g == 0 && row0 + r < a.n) a.scores[row0 + r] = s;
+  for (int i = 0; i < 4; ++i) w[i] = hg + 16 * i < a.H ? a.head_w[hg + 16 * i] : 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = fmaf(w[i], fmaxf(acc[r][i], 0.f), s);
+    // The 16 head groups of a row sit in 16 adjacent lanes; butterfly sums in
+    // a fixed order give every lane the same value.
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, kWave);
+    if (hg == r && row0 + 4 * rg + r < a.n) a.scores[row0 + 4 * rg + r] = s;
+  }
 }
 
-// Bitonic sort of M keys in LDS (M a power of two), descending: merge steps
-// of block size 2, 4, .., M, compare-exchange at strides size/2 .. 1, blocks
-// alternating direction until the last step sorts everything descending.
-template <int THREADS>
-__device__ __forceinline__ void bitonic_desc(uint64_t* keys, int M) {
-  for (int size = 2; size <= M; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int p = threadIdx.x; p < M / 2; p += THREADS) {
-        const int i = 2 * stride * (p / stride) + (p % stride);
-        const int j = i + stride;
-        const uint64_t ki = keys[i], kj = keys[j];
-        const bool desc = (i & size) == 0;
-        if (desc ? (ki < kj) : (ki > kj)) {
-          keys[i] = kj;
-          keys[j] = ki;
+// Adds each distinct digit of the wave's valid lanes to hist once, with the
+// number of lanes holding it (one LDS atomic per distinct digit, however
+// many lanes share it: scores cluster in a few exponent digits).
+__device__ __forceinline__ void count_digits(uint32_t* hist, int digit, bool valid, int lane) {
+  uint64_t active = __ballot(valid);
+  while (active) {
+    const int leader = __ffsll((unsigned long long)active) - 1;
+    const int d0 = __shfl(digit, leader, kWave);
+    const uint64_t same = __ballot(valid && digit == d0);
+    if (lane == leader) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
+    active &= ~same;
+  }
+}
+
+// One workgroup selects the k largest of up to kIndexerChunk unique 64-bit
+// keys (order-preserving score bits, then the complement of the row index):
+// mode 0 builds them from scores[base ..] (base = kIndexerChunk per
+// workgroup), mode 1 reads the surviving keys of every chunk from cand (0 =
+// padding).  A radix select over 8-bit digits, most significant first,
+// narrows the bucket holding the k-th key until the keys still needed are
+// the whole bucket; the keys at or above that bucket's lowest value are then
+// exactly the k largest.  final: each is written as (row, score) at its rank
+// (descending); else they go to cand in any order.
+__global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArgs a, int mode, int final_pass) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t sel[512];
+  __shared__ unsigned long long s_prefix, s_mask, s_thresh;
+  __shared__ int s_need, s_done, s_cnt;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int64_t base = mode == 0 ? (int64_t)blockIdx.x * kIndexerChunk : 0;
+  const int64_t left = a.n - base;
+  const int count = mode == 0 ? (int)(left < kIndexerChunk ? left : kIndexerChunk) : a.n_chunks * a.k;
+  uint64_t key[kSelPerThread];
+#pragma unroll
+  for (int j = 0; j < kSelPerThread; ++j) {
+    const int i = j * kSortThreads + tid;
+    uint64_t v = 0;
+    if (i < count) {
+      if (mode == 0) {
+        const uint32_t row = (uint32_t)(base + i);
+        v = ((uint64_t)ord_bits(a.scores[base + i]) << 32) | (uint64_t)(0xffffffffu - row);
+      } else {
+        v = a.cand[i];
+      }
+    }
+    key[j] = v;
+  }
+  if (tid == 0) {
+    s_prefix = 0ull;
+    s_mask = 0ull;
+    s_need = a.k;
+    s_done = 0;
+  }
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0u;
+    __syncthreads();
+    const uint64_t prefix = s_prefix, mask = s_mask;
+    if (shift == 56) {
+      // First digit: sign and exponent bits, shared by most scores.
+#pragma unroll
+      for (int j = 0; j < kSelPerThread; ++j)
+        count_digits(hist, (int)((key[j] >> shift) & 0xffu), key[j] != 0ull, lane);
+    } else {
+      // Later digits spread over the bins: one atomic per key in the bucket.
+#pragma unroll
+      for (int j = 0; j < kSelPerThread; ++j)
+        if (key[j] != 0ull && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 0xffu], 1u);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      // Lane l holds bins 255-4l .. 252-4l; inclusive counts from the top.
+      uint32_t c[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) c[b] = hist[255 - 4 * lane - b];
+      const uint32_t csum = c[0] + c[1] + c[2] + c[3];
+      uint32_t P = csum;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t t = __shfl_up(P, o, kWave);
+        if (lane >= o) P += t;
+      }
+      const uint32_t E = P - csum;
+      const uint32_t need = (uint32_t)s_need;
+      if (lane == kWave - 1 && P < need) {
+        // Fewer keys than k (only in the first round): take every key.
+        s_thresh = 1ull;
+        s_done = 1;
+      }
+      if (E < need && need <= P) {
+        uint32_t cum = E;
+        int b = 0;
+        while (cum + c[b] < need) cum += c[b++];
+        const int d = 255 - 4 * lane - b;
+        const uint64_t np = prefix | ((uint64_t)d << shift);
+        s_prefix = np;
+        s_mask = mask | (0xffull << shift);
+        s_need = (int)(need - cum);
+        if (need - cum == c[b]) {
+          s_thresh = np;
+          s_done = 1;
         }
       }
-      __syncthreads();
     }
+    __syncthreads();
+    if (s_done) break;
   }
-}
-
-__global__ void __launch_bounds__(kSortThreads) indexer_topk_chunk_kernel(IndexerArgs a) {
-  __shared__ uint64_t keys[kIndexerChunk];
-  const int64_t base = (int64_t)blockIdx.x * kIndexerChunk;
-  for (int i = threadIdx.x; i < kIndexerChunk; i += kSortThreads) {
-    const int64_t j = base + i;
-    keys[i] = j < a.n ? ((uint64_t)ord_bits(a.scores[j]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)j) : 0ull;
+  const uint64_t thresh = s_thresh;
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kSelPerThread; ++j) {
+    if (key[j] != 0ull && key[j] >= thresh) sel[atomicAdd(&s_cnt, 1)] = key[j];
   }
   __syncthreads();
-  bitonic_desc<kSortThreads>(keys, kIndexerChunk);
-  for (int i = threadIdx.x; i < a.k; i += kSortThreads) a.cand[(int64_t)blockIdx.x * a.k + i] = keys[i];
-}
-
-__global__ void __launch_bounds__(kSortThreads) indexer_topk_merge_kernel(IndexerArgs a, int m) {
-  __shared__ uint64_t keys[kIndexerMaxCand];
-  const int count = a.n_chunks * a.k;
-  for (int i = threadIdx.x; i < m; i += kSortThreads) keys[i] = i < count ? a.cand[i] : 0ull;
-  __syncthreads();
-  bitonic_desc<kSortThreads>(keys, m);
-  const int out = a.n < a.k ? (int)a.n : a.k;
-  for (int i = threadIdx.x; i < out; i += kSortThreads) {
-    const uint64_t key = keys[i];
-    a.out_idx[i] = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffu));
-    a.out_score[i] = unord_bits((uint32_t)(key >> 32));
+  const int total = s_cnt;
+  if (!final_pass) {
+    for (int i = tid; i < a.k; i += kSortThreads) a.cand[(int64_t)blockIdx.x * a.k + i] = i < total ? sel[i] : 0ull;
+    return;
+  }
+  // Descending order: a key's position is the number of larger selected
+  // keys (keys are unique, so positions are too).
+  for (int i = tid; i < total; i += kSortThreads) {
+    const uint64_t v = sel[i];
+    int rank = 0;
+    for (int j = 0; j < total; ++j) rank += sel[j] > v ? 1 : 0;
+    a.out_idx[rank] = (int32_t)(0xffffffffu - (uint32_t)(v & 0xffffffffu));
+    a.out_score[rank] = unord_bits((uint32_t)(v >> 32));
   }
 }
 
@@ -152,19 +267,17 @@ __global__ void __launch_bounds__(kSortThreads) indexer_topk_merge_kernel(Indexe
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const Timing& tm) {
   if (a.n <= 0) return hipSuccess;
   const unsigned g_score = (unsigned)((a.n + kScoreRows - 1) / kScoreRows);
-  const Timing t_first{tm.start, nullptr};
   if (a.Dh == 64)
-    hipExtLaunchKernelGGL((indexer_score_kernel<64>), dim3(g_score), dim3(kScoreThreads), 0, stream, t_first.start,
+    hipExtLaunchKernelGGL((indexer_score_kernel<64>), dim3(g_score), dim3(kScoreThreads), 0, stream, tm.start,
                           nullptr, 0, a);
   else
-    hipExtLaunchKernelGGL((indexer_score_kernel<128>), dim3(g_score), dim3(kScoreThreads), 0, stream, t_first.start,
+    hipExtLaunchKernelGGL((indexer_score_kernel<128>), dim3(g_score), dim3(kScoreThreads), 0, stream, tm.start,
                           nullptr, 0, a);
-  hipExtLaunchKernelGGL(indexer_topk_chunk_kernel, dim3((unsigned)a.n_chunks), dim3(kSortThreads), 0, stream, nullptr,
-                        nullptr, 0, a);
-  int m = 1;
-  while (m < a.n_chunks * a.k) m <<= 1;
-  if (m < 2) m = 2;
-  hipExtLaunchKernelGGL(indexer_topk_merge_kernel, dim3(1), dim3(kSortThreads), 0, stream, nullptr, tm.stop, 0, a, m);
+  if (a.n_chunks > 1)
+    hipExtLaunchKernelGGL(indexer_select_kernel, dim3((unsigned)a.n_chunks), dim3(kSortThreads), 0, stream, nullptr,
+                          nullptr, 0, a, 0, 0);
+  hipExtLaunchKernelGGL(indexer_select_kernel, dim3(1), dim3(kSortThreads), 0, stream, nullptr, tm.stop, 0, a,
+                        a.n_chunks > 1 ? 1 : 0, 1);
   return hipGetLastError();
 }
 

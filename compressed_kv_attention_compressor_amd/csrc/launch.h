@@ -43,10 +43,10 @@ int pool_launches(const PoolArgs& a);
 hipError_t launch_pool(const PoolArgs& a, int phase, hipStream_t stream, const Timing& tm);
 hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, const Timing& tm);
 hipError_t launch_fill(const FillArgs& f, hipStream_t stream, const Timing& tm);
-// Indexer: scores per row, then a per-chunk and a final bitonic top-k.  A
-// chunk holds kIndexerChunk scores; the final sort holds at most
-// kIndexerMaxCand keys (n_chunks * k).
-constexpr int kIndexerChunk = 4096;
+// Indexer: scores per row, then a radix top-k.  One select workgroup takes
+// up to kIndexerChunk rows; longer calls select per chunk first, and the
+// final pass takes at most kIndexerMaxCand surviving keys (n_chunks * k).
+constexpr int kIndexerChunk = 32768;
 constexpr int kIndexerMaxCand = 16384;
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const Timing& tm);
 

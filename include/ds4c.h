@@ -253,8 +253,8 @@ int ds4c_compress_stack_decode_one(const ds4c_layer *layers, int n_layers, ds4c_
  * (row-major float32, device; q and index_rows 16-byte aligned): the layer's
  * rows 0 .. n_index_comp-1 as ds4c_compress_* wrote them.  head_dim 64 or
  * 128; n_heads a multiple of 4 up to 64; 1 <= k <= 512; rows in chunks of
- * 4096 with ceil(n_rows / 4096) * k <= 16384 (n_rows up to 131072 at k =
- * 512), else DS4C_ESHAPE.  q_hat (nullable, [n_heads, head_dim]) receives
+ * 32768 with ceil(n_rows / 32768) * k <= 16384 (n_rows up to 1,048,576 at
+ * k = 512), else DS4C_ESHAPE.  q_hat (nullable, [n_heads, head_dim]) receives
  * the rotated, quantised query; scores (nullable, [n_rows]) every row's
  * score.  workspace: device, >= ds4c_indexer_workspace_bytes(n_rows, k),
  * 256-byte aligned.  Asynchronous on stream; n_rows == 0 writes nothing. */

@@ -359,10 +359,11 @@ def test_snapshot_load_refuses_mismatches():
 
 def test_indexer_workspace_bytes():
     a256 = lambda v: (v + 255) // 256 * 256
-    assert B.ds4c_indexer_workspace_bytes(16448, 512) == a256(16448 * 4) + a256(5 * 512 * 8) + 256
+    assert B.ds4c_indexer_workspace_bytes(16448, 512) == a256(16448 * 4) + a256(1 * 512 * 8) + 256
+    assert B.ds4c_indexer_workspace_bytes(40000, 512) == a256(40000 * 4) + a256(2 * 512 * 8) + 256
     assert B.ds4c_indexer_workspace_bytes(0, 512) == 256
-    assert B.ds4c_indexer_workspace_bytes(131072, 512) > 0       # 32 chunks x 512 = 16384 keys
-    assert B.ds4c_indexer_workspace_bytes(131073, 512) == 0      # 33 chunks: too many keys
+    assert B.ds4c_indexer_workspace_bytes(1 << 20, 512) > 0      # 32 chunks of 32768 x 512 = 16384 keys
+    assert B.ds4c_indexer_workspace_bytes((1 << 20) + 1, 512) == 0  # 33 chunks: too many keys
     assert B.ds4c_indexer_workspace_bytes(10, 0) == 0
     assert B.ds4c_indexer_workspace_bytes(10, 513) == 0
 
@@ -377,7 +378,7 @@ def test_indexer_validates_before_launching():
     assert call(H=68) == B.DS4C_ESHAPE
     assert call(k=0) == B.DS4C_EINVAL
     assert call(k=513) == B.DS4C_EINVAL
-    assert call(n=131073, k=512) == B.DS4C_ESHAPE
+    assert call(n=(1 << 20) + 1, k=512) == B.DS4C_ESHAPE
     assert call(q=FAKE + 4) == B.DS4C_EINVAL                     # q not 16-byte aligned
     assert call(rows=0) == B.DS4C_EINVAL
     assert call(wsp=FAKE + 16) == B.DS4C_EINVAL                  # workspace not 256-byte aligned

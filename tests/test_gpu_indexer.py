@@ -80,6 +80,8 @@ CASES = {
     "k_plus_one": (513, 512, 8, 128),
     "two_chunks_odd_k": (4097, 37, 16, 64),
     "many_chunks_small_k": (100000, 64, 32, 128),
+    "two_chunks_k1": (40000, 1, 64, 128),
+    "one_full_chunk": (32768, 512, 64, 128),
     "no_rows": (0, 16, 64, 128),
 }
 
