@@ -171,22 +171,27 @@ __device__ __forceinline__ float row_sumsq(const float (&y)[DPL]) {
   return ss;
 }
 
-// Indexer QAT round trip of a D-wide row held by one wave (D == 64 * DPL,
-// lane holds dims lane*DPL ..): the orthonormal Walsh-Hadamard rotation
-// (Sylvester order; butterflies (a, b) -> (a + b, a - b) on index pairs
-// (j, j + h) for h = 1, 2, 4, ...; strides below DPL inside a lane, the rest
-// across lanes), scaled by 1/sqrt(D), then FP4 E2M1 in blocks of 32 dims
-// (32/DPL lanes) with the power-of-two block scale.  The row stays rotated.
-template <int DPL>
-__device__ __forceinline__ void hadamard_fp4(float (&y)[DPL], int D, int lane) {
+// Indexer QAT round trip of NB independent D-wide rows held by one wave
+// (D == 64 * DPL, lane holds dims lane*DPL .. of each row): the orthonormal
+// Walsh-Hadamard rotation (Sylvester order; butterflies (a, b) -> (a + b,
+// a - b) on index pairs (j, j + h) for h = 1, 2, 4, ...; strides below DPL
+// inside a lane, the rest across lanes), scaled by 1/sqrt(D), then FP4 E2M1
+// in blocks of 32 dims (32/DPL lanes) with the power-of-two block scale.  The
+// rows stay rotated.  Every stage runs over all NB rows before the next, so
+// the rows' cross-lane exchanges overlap.
+template <int DPL, int NB>
+__device__ __forceinline__ void hadamard_fp4_rows(float (&y)[NB][DPL], int D, int lane) {
 #pragma unroll
   for (int h = 1; h < DPL; h <<= 1) {
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      if ((i & h) == 0) {
-        const float a = y[i], b = y[i + h];
-        y[i] = a + b;
-        y[i + h] = a - b;
+    for (int n = 0; n < NB; ++n) {
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        if ((i & h) == 0) {
+          const float a = y[n][i], b = y[n][i + h];
+          y[n][i] = a + b;
+          y[n][i + h] = a - b;
+        }
       }
     }
   }
@@ -194,21 +199,40 @@ __device__ __forceinline__ void hadamard_fp4(float (&y)[DPL], int D, int lane) {
   for (int m = 1; m < kWave; m <<= 1) {
     const bool low = (lane & m) == 0;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      const float p = __shfl_xor(y[i], m, kWave);
-      y[i] = low ? (y[i] + p) : (p - y[i]);
+    for (int n = 0; n < NB; ++n) {
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        const float p = __shfl_xor(y[n][i], m, kWave);
+        y[n][i] = low ? (y[n][i] + p) : (p - y[n][i]);
+      }
     }
   }
   const float scale = (float)(1.0 / sqrt((double)D));
+  float amax[NB];
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) y[i] *= scale;
-  float amax = 0.f;
+  for (int n = 0; n < NB; ++n) {
+    amax[n] = 0.f;
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) amax = fmaxf(amax, fabsf(y[i]));
-  amax = group_max<32 / DPL>(amax);
-  const int kexp = e2m1_block_exp(amax);
+    for (int i = 0; i < DPL; ++i) {
+      y[n][i] *= scale;
+      amax[n] = fmaxf(amax[n], fabsf(y[n][i]));
+    }
+  }
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) y[i] = ldexpf(rne_e2m1(ldexpf(y[i], -kexp)), kexp);
+  for (int o = 32 / DPL / 2; o > 0; o >>= 1)
+#pragma unroll
+    for (int n = 0; n < NB; ++n) amax[n] = fmaxf(amax[n], __shfl_xor(amax[n], o, kWave));
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const int kexp = e2m1_block_exp(amax[n]);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) y[n][i] = ldexpf(rne_e2m1(ldexpf(y[n][i], -kexp)), kexp);
+  }
+}
+
+template <int DPL>
+__device__ __forceinline__ void hadamard_fp4(float (&y)[DPL], int D, int lane) {
+  hadamard_fp4_rows<DPL, 1>(*reinterpret_cast<float (*)[1][DPL]>(&y), D, lane);
 }
 
 template <int DPL>

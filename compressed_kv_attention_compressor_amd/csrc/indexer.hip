@@ -49,36 +49,43 @@ __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArg
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int64_t row0 = (int64_t)blockIdx.x * kScoreRows;
 
-  // Every load is issued before any is used: the rows of this workgroup
-  // (zeros past n), 16 bytes per thread and step, and the query heads
-  // wave, wave + 4, ... (zeros past H).
+  // Every load is issued before any is used, with no branch around a load
+  // (a branch would make the compiler wait for each load before the next):
+  // the rows of this workgroup, 16 bytes per thread and step (rows past n
+  // re-read row n-1 and are zeroed), and the query heads wave, wave + 4, ...
+  // (heads past H re-read head H-1 and are zeroed).
   constexpr int kVec = DH / 4;                         // float4 per row
   constexpr int kRowSteps = kScoreRows * kVec / kScoreThreads;
   float4 kv[kRowSteps];
 #pragma unroll
   for (int s = 0; s < kRowSteps; ++s) {
     const int i = t + s * kScoreThreads, r = i / kVec, c = (i % kVec) * 4;
-    kv[s] = row0 + r < a.n ? *reinterpret_cast<const float4*>(a.rows + (row0 + r) * DH + c)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t row = row0 + r < a.n ? row0 + r : a.n - 1;
+    kv[s] = *reinterpret_cast<const float4*>(a.rows + row * DH + c);
   }
   constexpr int kHeadsPerWave = 64 / (kScoreThreads / kWave);
   float y[kHeadsPerWave][DPL];
 #pragma unroll
   for (int j = 0; j < kHeadsPerWave; ++j) {
     const int h = wave + 4 * j;
-    if (h < a.H) {
-      load_vec<DPL>(y[j], a.q + h * DH + lane * DPL);
-    } else {
+    load_vec<DPL>(y[j], a.q + (h < a.H ? h : a.H - 1) * DH + lane * DPL);
+  }
+#pragma unroll
+  for (int s = 0; s < kRowSteps; ++s) {
+    const int r = (t + s * kScoreThreads) / kVec;
+    if (row0 + r >= a.n) kv[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int j = 0; j < kHeadsPerWave; ++j)
+    if (wave + 4 * j >= a.H)
 #pragma unroll
       for (int i = 0; i < DPL; ++i) y[j][i] = 0.f;
-    }
-  }
-  // Rotation + FP4 round trip of each head into LDS (a zero head stays
-  // zero), while the rows are still on their way.
+  // Rotation + FP4 round trip of the wave's heads into LDS (a zero head
+  // stays zero), while the rows are still on their way.
+  hadamard_fp4_rows<DPL, kHeadsPerWave>(y, DH, lane);
 #pragma unroll
   for (int j = 0; j < kHeadsPerWave; ++j) {
     const int h = wave + 4 * j;
-    hadamard_fp4<DPL>(y[j], DH, lane);
 #pragma unroll
     for (int i = 0; i < DPL; ++i) s_q[h * kLd + lane * DPL + i] = y[j][i];
     if (a.q_hat && blockIdx.x == 0 && h < a.H) store_vec<DPL>(a.q_hat + h * DH + lane * DPL, y[j]);
@@ -132,20 +139,6 @@ __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArg
   }
 }
 
-// Adds each distinct digit of the wave's valid lanes to hist once, with the
-// number of lanes holding it (one LDS atomic per distinct digit, however
-// many lanes share it: scores cluster in a few exponent digits).
-__device__ __forceinline__ void count_digits(uint32_t* hist, int digit, bool valid, int lane) {
-  uint64_t active = __ballot(valid);
-  while (active) {
-    const int leader = __ffsll((unsigned long long)active) - 1;
-    const int d0 = __shfl(digit, leader, kWave);
-    const uint64_t same = __ballot(valid && digit == d0);
-    if (lane == leader) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
-    active &= ~same;
-  }
-}
-
 // One workgroup selects the k largest of up to kIndexerChunk unique 64-bit
 // keys (order-preserving score bits, then the complement of the row index):
 // mode 0 builds them from scores[base ..] (base = kIndexerChunk per
@@ -155,7 +148,9 @@ __device__ __forceinline__ void count_digits(uint32_t* hist, int digit, bool val
 // the whole bucket; the keys at or above that bucket's lowest value are then
 // exactly the k largest.  final: each is written as (row, score) at its rank
 // (descending); else they go to cand in any order.
-__global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArgs a, int mode, int final_pass) {
+template <int MODE>
+__global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArgs a, int final_pass) {
+  constexpr int mode = MODE;
   __shared__ uint32_t hist[256];
   __shared__ uint64_t sel[512];
   __shared__ unsigned long long s_prefix, s_mask, s_thresh;
@@ -164,21 +159,23 @@ __global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArg
   const int64_t base = mode == 0 ? (int64_t)blockIdx.x * kIndexerChunk : 0;
   const int64_t left = a.n - base;
   const int count = mode == 0 ? (int)(left < kIndexerChunk ? left : kIndexerChunk) : a.n_chunks * a.k;
+  // Loads without branches around them (a clamped address past the end,
+  // zeroed afterwards), so all of a thread's loads are in flight at once.
   uint64_t key[kSelPerThread];
 #pragma unroll
   for (int j = 0; j < kSelPerThread; ++j) {
     const int i = j * kSortThreads + tid;
-    uint64_t v = 0;
-    if (i < count) {
-      if (mode == 0) {
-        const uint32_t row = (uint32_t)(base + i);
-        v = ((uint64_t)ord_bits(a.scores[base + i]) << 32) | (uint64_t)(0xffffffffu - row);
-      } else {
-        v = a.cand[i];
-      }
+    const int ic = i < count ? i : count - 1;
+    if constexpr (MODE == 0) {
+      const uint32_t row = (uint32_t)(base + ic);
+      key[j] = ((uint64_t)ord_bits(a.scores[base + ic]) << 32) | (uint64_t)(0xffffffffu - row);
+    } else {
+      key[j] = a.cand[ic];
     }
-    key[j] = v;
   }
+#pragma unroll
+  for (int j = 0; j < kSelPerThread; ++j)
+    if (j * kSortThreads + tid >= count) key[j] = 0ull;
   if (tid == 0) {
     s_prefix = 0ull;
     s_mask = 0ull;
@@ -189,17 +186,12 @@ __global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArg
     if (tid < 256) hist[tid] = 0u;
     __syncthreads();
     const uint64_t prefix = s_prefix, mask = s_mask;
-    if (shift == 56) {
-      // First digit: sign and exponent bits, shared by most scores.
+    // One LDS atomic per key still in the bucket.  (Counting each distinct
+    // digit of a wave once, by ballots, was twice as slow on the first digit,
+    // which most scores share: the ballot loop is serial.)
 #pragma unroll
-      for (int j = 0; j < kSelPerThread; ++j)
-        count_digits(hist, (int)((key[j] >> shift) & 0xffu), key[j] != 0ull, lane);
-    } else {
-      // Later digits spread over the bins: one atomic per key in the bucket.
-#pragma unroll
-      for (int j = 0; j < kSelPerThread; ++j)
-        if (key[j] != 0ull && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 0xffu], 1u);
-    }
+    for (int j = 0; j < kSelPerThread; ++j)
+      if (key[j] != 0ull && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 0xffu], 1u);
     __syncthreads();
     if (tid < kWave) {
       // Lane l holds bins 255-4l .. 252-4l; inclusive counts from the top.
@@ -252,11 +244,21 @@ __global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArg
     return;
   }
   // Descending order: a key's position is the number of larger selected
-  // keys (keys are unique, so positions are too).
+  // keys (keys are unique, so positions are too).  The list is padded with
+  // zeros (below every key) to a multiple of 8 and read 8 keys per step.
+  const int padded = (total + 7) & ~7;
+  for (int i = total + tid; i < padded; i += kSortThreads) sel[i] = 0ull;
+  __syncthreads();
   for (int i = tid; i < total; i += kSortThreads) {
     const uint64_t v = sel[i];
     int rank = 0;
-    for (int j = 0; j < total; ++j) rank += sel[j] > v ? 1 : 0;
+    for (int j = 0; j < padded; j += 8) {
+      uint64_t w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = sel[j + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) rank += w[u] > v ? 1 : 0;
+    }
     a.out_idx[rank] = (int32_t)(0xffffffffu - (uint32_t)(v & 0xffffffffu));
     a.out_score[rank] = unord_bits((uint32_t)(v >> 32));
   }
@@ -273,11 +275,13 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const Timing
   else
     hipExtLaunchKernelGGL((indexer_score_kernel<128>), dim3(g_score), dim3(kScoreThreads), 0, stream, tm.start,
                           nullptr, 0, a);
-  if (a.n_chunks > 1)
-    hipExtLaunchKernelGGL(indexer_select_kernel, dim3((unsigned)a.n_chunks), dim3(kSortThreads), 0, stream, nullptr,
-                          nullptr, 0, a, 0, 0);
-  hipExtLaunchKernelGGL(indexer_select_kernel, dim3(1), dim3(kSortThreads), 0, stream, nullptr, tm.stop, 0, a,
-                        a.n_chunks > 1 ? 1 : 0, 1);
+  if (a.n_chunks > 1) {
+    hipExtLaunchKernelGGL(indexer_select_kernel<0>, dim3((unsigned)a.n_chunks), dim3(kSortThreads), 0, stream,
+                          nullptr, nullptr, 0, a, 0);
+    hipExtLaunchKernelGGL(indexer_select_kernel<1>, dim3(1), dim3(kSortThreads), 0, stream, nullptr, tm.stop, 0, a, 1);
+  } else {
+    hipExtLaunchKernelGGL(indexer_select_kernel<0>, dim3(1), dim3(kSortThreads), 0, stream, nullptr, tm.stop, 0, a, 1);
+  }
   return hipGetLastError();
 }
 
