@@ -136,8 +136,9 @@ def proj_kernel_name(M: int, N: int, K: int) -> str:
     return name + (f" (K split {s})" if s > 1 else "")
 
 
-def read_traffic(workload: str):
-    """HBM bytes per GEMM launch from the committed counter summary, or None.
+def read_traffic(workload: str, key: str = "gemm_hbm_bytes_per_launch"):
+    """HBM bytes per launch (GEMM, or another key of the summary) from the
+    committed counter summary, or None.
 
     The summary names the sha256 of the projection kernel source it was taken
     on; a different source means the counters are stale and none is used.
@@ -154,7 +155,7 @@ def read_traffic(workload: str):
     if kv.get("gemm_source_sha256") != src:
         return None
     try:
-        return float(kv["gemm_hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
 
@@ -454,7 +455,8 @@ def main():
             "bound": "hbm", "achieved": pl_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": pl_gbs / PEAK_HBM_GBS,
             "kernel": "pool_r4_kernel" if w.layer.ratio == 4 else "pool_r128_partial_kernel + pool_r128_finish_kernel",
             "measured": f"{pl_cnt} calls of {T - 1} tokens from n0 = 1, warm (reads the projection written just before)",
-            "avg_ms": pl_avg, "algorithmic_bytes": pl_bytes}
+            "avg_ms": pl_avg, "algorithmic_bytes": pl_bytes,
+            "traffic": read_traffic(args.workload, "plain_pool_hbm_bytes_per_launch")}
         if cr_cnt:
             out["plain_pool_roofline"]["carry"] = {
                 "kernel": "pool_r4_carry_kernel", "avg_ms": cr_ms / cr_cnt,
