@@ -201,8 +201,11 @@ hipEvent_t take_event() {
     g_event_pool.pop_back();
     return e;
   }
+  // Timing-only events: without the system-scope fence a recorded event
+  // does not write back and invalidate the caches, which would otherwise add
+  // to the bracketed interval and slow the work that follows.
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
