@@ -51,9 +51,17 @@ __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArg
 
   // Every load is issued before any is used, with no branch around a load
   // (a branch would make the compiler wait for each load before the next):
-  // the rows of this workgroup, 16 bytes per thread and step (rows past n
-  // re-read row n-1 and are zeroed), and the query heads wave, wave + 4, ...
-  // (heads past H re-read head H-1 and are zeroed).
+  // first the query heads wave, wave + 4, ... (heads past H re-read head H-1
+  // and are zeroed), then the rows of this workgroup, 16 bytes per thread and
+  // step (rows past n re-read row n-1 and are zeroed).  Loads complete in
+  // order, so the query's round trip below waits only for the query.
+  constexpr int kHeadsPerWave = 64 / (kScoreThreads / kWave);
+  float y[kHeadsPerWave][DPL];
+#pragma unroll
+  for (int j = 0; j < kHeadsPerWave; ++j) {
+    const int h = wave + 4 * j;
+    load_vec<DPL>(y[j], a.q + (h < a.H ? h : a.H - 1) * DH + lane * DPL);
+  }
   constexpr int kVec = DH / 4;                         // float4 per row
   constexpr int kRowSteps = kScoreRows * kVec / kScoreThreads;
   float4 kv[kRowSteps];
@@ -62,18 +70,6 @@ __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArg
     const int i = t + s * kScoreThreads, r = i / kVec, c = (i % kVec) * 4;
     const int64_t row = row0 + r < a.n ? row0 + r : a.n - 1;
     kv[s] = *reinterpret_cast<const float4*>(a.rows + row * DH + c);
-  }
-  constexpr int kHeadsPerWave = 64 / (kScoreThreads / kWave);
-  float y[kHeadsPerWave][DPL];
-#pragma unroll
-  for (int j = 0; j < kHeadsPerWave; ++j) {
-    const int h = wave + 4 * j;
-    load_vec<DPL>(y[j], a.q + (h < a.H ? h : a.H - 1) * DH + lane * DPL);
-  }
-#pragma unroll
-  for (int s = 0; s < kRowSteps; ++s) {
-    const int r = (t + s * kScoreThreads) / kVec;
-    if (row0 + r >= a.n) kv[s] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int j = 0; j < kHeadsPerWave; ++j)
@@ -93,7 +89,7 @@ __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArg
 #pragma unroll
   for (int s = 0; s < kRowSteps; ++s) {
     const int i = t + s * kScoreThreads, r = i / kVec, c = (i % kVec) * 4;
-    *reinterpret_cast<float4*>(s_k + r * kLd + c) = kv[s];
+    *reinterpret_cast<float4*>(s_k + r * kLd + c) = row0 + r < a.n ? kv[s] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
 
