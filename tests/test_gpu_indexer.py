@@ -119,3 +119,15 @@ def test_indexer_over_compressor_rows():
     assert rows.shape == (1024, 128)
     q, w, _ = synth.indexer_inputs(51, 0, 64, 128)
     check(q, w, rows, 512, "compressor rows")
+
+
+def test_indexer_is_deterministic():
+    """Survivors are gathered with LDS atomics, then placed by rank: the output
+    is the same on every run."""
+    print("[indexer] determinism", flush=True)
+    q, w, rows = synth.indexer_inputs(52, 100000, 64, 128)
+    a = run_gpu(q, w, rows, 512)
+    b = run_gpu(q, w, rows, 512)
+    for x_, y_ in zip(a, b):
+        assert np.array_equal(x_.view(np.uint32) if x_.dtype == np.float32 else x_,
+                              y_.view(np.uint32) if y_.dtype == np.float32 else y_)

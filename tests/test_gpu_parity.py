@@ -283,6 +283,21 @@ def test_deterministic_and_overwrites_poison():
         assert torch.equal(outs[0][k], outs[1][k])
 
 
+@pytest.mark.parametrize("name", list(FLASH_PLANS))
+def test_short_calls_are_deterministic(name):
+    """The K-split projection adds its planes in a fixed order: two runs of the
+    same ragged plan give bitwise-equal rows and frontiers."""
+    _say(f"[parity] {name} short-call determinism")
+    w, p, x = _workload(name)
+    plan = [1, 3, 64, 127, 256, 600]
+    runs = [run_gpu(w.layer, p, x[:sum(plan)], plan) for _ in range(2)]
+    for k in runs[0]["rows"]:
+        assert np.array_equal(runs[0]["rows"][k], runs[1]["rows"][k])
+        assert np.array_equal(runs[0]["pre"][k], runs[1]["pre"][k])
+        for a_, b_ in zip(runs[0]["frontier"][k], runs[1]["frontier"][k]):
+            assert np.array_equal(a_, b_)
+
+
 def test_row_zero_of_ratio4_pools_current_half_only():
     """Equal scores (zero gate weights and APE) make row 0 the mean of 4 tokens."""
     _say("[parity] equal-score row 0")
