@@ -436,9 +436,11 @@ def main():
         # one token, then the rest of the chunk from n0 = 1; the second call's
         # pool is timed.  Warm: it reads the projection output the call's own
         # GEMM has just written.
+        # One pool interval per call: the median of 21 calls is reported (a
+        # single late dispatch would dominate a mean of a few samples).
         L = layers[0]
-        pl_ms, pl_cnt, cr_ms, cr_cnt = 0.0, 0, 0.0, 0
-        for _ in range(side_steps):
+        pl, cr = [], []
+        for _ in range(21):
             f = L.frontier
             f.n_tokens = f.n_comp = f.n_index_comp = 0
             L.prefill(x[:1])
@@ -446,20 +448,24 @@ def main():
             L.prefill(x[1:T])
             m_, c_ = B.ds4c_profile_read()
             B.ds4c_profile_enable(False)
-            pl_ms, pl_cnt = pl_ms + m_[B.KCLASS_POOL], pl_cnt + c_[B.KCLASS_POOL]
-            cr_ms, cr_cnt = cr_ms + m_[B.KCLASS_CARRY], cr_cnt + c_[B.KCLASS_CARRY]
+            if c_[B.KCLASS_POOL]:
+                pl.append(m_[B.KCLASS_POOL] / c_[B.KCLASS_POOL])
+            if c_[B.KCLASS_CARRY]:
+                cr.append(m_[B.KCLASS_CARRY] / c_[B.KCLASS_CARRY])
+        pl_cnt, cr_cnt = len(pl), len(cr)
         _, pl_bytes, _, _ = layer_algorithmic(w.layer, 1, T - 1)
-        pl_avg = pl_ms / max(pl_cnt, 1)
+        pl_avg = sorted(pl)[len(pl) // 2] if pl else 0.0
         pl_gbs = pl_bytes / (pl_avg * 1e-3) / 1e9
         out["plain_pool_roofline"] = {
             "bound": "hbm", "achieved": pl_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": pl_gbs / PEAK_HBM_GBS,
             "kernel": "pool_r4_kernel" if w.layer.ratio == 4 else "pool_r128_partial_kernel + pool_r128_finish_kernel",
-            "measured": f"{pl_cnt} calls of {T - 1} tokens from n0 = 1, warm (reads the projection written just before)",
+            "measured": f"median of {pl_cnt} calls of {T - 1} tokens from n0 = 1, warm (reads the projection "
+                        f"written just before)",
             "avg_ms": pl_avg, "algorithmic_bytes": pl_bytes,
             "traffic": read_traffic(args.workload, "plain_pool_hbm_bytes_per_launch")}
         if cr_cnt:
             out["plain_pool_roofline"]["carry"] = {
-                "kernel": "pool_r4_carry_kernel", "avg_ms": cr_ms / cr_cnt,
+                "kernel": "pool_r4_carry_kernel", "avg_ms": sorted(cr)[len(cr) // 2],
                 "algorithmic_bytes": carry_bytes(w.layer, 1, T - 1)}
     if not args.no_cpu_baseline:
         n_cpu = min(T, 4096)

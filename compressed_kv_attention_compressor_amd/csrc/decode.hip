@@ -151,7 +151,8 @@ __global__ void __launch_bounds__(64 * (SA + 1)) decode_r4_finish_kernel(DecodeA
   if (wave < SA) {
     const LaneDev& L = a.lane[0];
     const int d0 = wave * (kWave * DPLA) + lane * DPLA;
-    float o[DPLA];
+    float nw[DPLA], o[DPLA];
+    load_vec<DPLA>(nw, L.norm_w + d0);
     r4_pool_and_shift<DPLA>(L, d0, o);
     const float ss = wave_sum(row_sumsq<DPLA>(o));
     if (lane == 0) s_ss[wave] = ss;
@@ -159,15 +160,18 @@ __global__ void __launch_bounds__(64 * (SA + 1)) decode_r4_finish_kernel(DecodeA
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < SA; ++w) tot += s_ss[w];
-    finish_row_part<DPLA>(o, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, L.prequant,
+    finish_row_part<DPLA>(o, nw, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, L.prequant,
                           L.rows + k * L.D, lane);
   } else {
     const LaneDev& L = a.lane[1];
-    float o[DPLI];
-    if (a.n_lanes > 1) r4_pool_and_shift<DPLI>(L, lane * DPLI, o);
+    float nw[DPLI], o[DPLI];
+    if (a.n_lanes > 1) {
+      load_vec<DPLI>(nw, L.norm_w + lane * DPLI);
+      r4_pool_and_shift<DPLI>(L, lane * DPLI, o);
+    }
     __syncthreads();
     if (a.n_lanes > 1)
-      finish_row_wave<DPLI>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, L.prequant, L.rows + k * L.D, lane);
+      finish_row_wave<DPLI>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, L.prequant, L.rows + k * L.D, lane);
   }
 }
 
@@ -234,9 +238,10 @@ __global__ void __launch_bounds__(kWave) decode_r128_finish_kernel(DecodeArgs a)
   const int lane = threadIdx.x;
   const int64_t k = a.pos / 128;
   float* row = L.rows + k * L.D;
-  float o[DPL];
+  float nw[DPL], o[DPL];
+  load_vec<DPL>(nw, L.norm_w + lane * DPL);
   load_vec<DPL>(o, row + lane * DPL);
-  finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, L.prequant, row, lane);
+  finish_row_wave<DPL>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, L.prequant, row, lane);
 }
 
 template <int SA, int DPLA>

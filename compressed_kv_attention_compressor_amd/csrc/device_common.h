@@ -235,14 +235,14 @@ __device__ __forceinline__ void hadamard_fp4(float (&y)[DPL], int D, int lane) {
   hadamard_fp4_rows<DPL, 1>(*reinterpret_cast<float (*)[1][DPL]>(&y), D, lane);
 }
 
+// w holds the norm weights of this lane's dims, loaded by the caller ahead
+// of the row's entries so that no load sits between the pool and the store.
 template <int DPL>
-__device__ __forceinline__ void finish_row_part(float (&y)[DPL], const LaneDev& L, float inv, int d0, int n_rot,
-                                                double log2_base, int64_t k, int ratio,
+__device__ __forceinline__ void finish_row_part(float (&y)[DPL], const float (&w)[DPL], const LaneDev& L, float inv,
+                                                int d0, int n_rot, double log2_base, int64_t k, int ratio,
                                                 float* __restrict__ prequant_row, float* __restrict__ out_row,
                                                 int lane) {
   const int D = L.D;
-  float w[DPL];
-  load_vec<DPL>(w, L.norm_w + d0);
 #pragma unroll
   for (int i = 0; i < DPL; ++i) y[i] = y[i] * w[i] * inv;
 
@@ -300,12 +300,12 @@ __device__ __forceinline__ float rms_inv(float sumsq, int D, float eps) {
 
 // Whole row in one wave (D == 64 * DPL).
 template <int DPL>
-__device__ __forceinline__ void finish_row_wave(float (&y)[DPL], const LaneDev& L, int n_rot, double log2_base,
-                                                float rms_eps, int64_t k, int ratio,
+__device__ __forceinline__ void finish_row_wave(float (&y)[DPL], const float (&w)[DPL], const LaneDev& L, int n_rot,
+                                                double log2_base, float rms_eps, int64_t k, int ratio,
                                                 float* __restrict__ prequant_row, float* __restrict__ out_row,
                                                 int lane) {
   const float inv = rms_inv(wave_sum(row_sumsq<DPL>(y)), L.D, rms_eps);
-  finish_row_part<DPL>(y, L, inv, lane * DPL, n_rot, log2_base, k, ratio, prequant_row, out_row, lane);
+  finish_row_part<DPL>(y, w, L, inv, lane * DPL, n_rot, log2_base, k, ratio, prequant_row, out_row, lane);
 }
 
 }  // namespace ds4c

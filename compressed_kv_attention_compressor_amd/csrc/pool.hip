@@ -171,7 +171,8 @@ __device__ __forceinline__ void r4_window(const PoolArgs& a, int64_t k, float* s
   if (wave < SA) {
     const LaneDev& L = a.lane[0];
     const int d0 = wave * (kWave * DPLA) + lane * DPLA;
-    float o[DPLA];
+    float nw[DPLA], o[DPLA];
+    load_vec<DPLA>(nw, L.norm_w + d0);
     r4_pool<DPLA>(a, L, k, d0, o);
     const float ss = wave_sum(row_sumsq<DPLA>(o));
     if (lane == 0) s_ss[wave] = ss;
@@ -180,15 +181,16 @@ __device__ __forceinline__ void r4_window(const PoolArgs& a, int64_t k, float* s
 #pragma unroll
     for (int s = 0; s < SA; ++s) tot += s_ss[s];
     float* pre = L.prequant ? L.prequant + (k - a.k_lo) * L.D : nullptr;
-    finish_row_part<DPLA>(o, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, pre,
+    finish_row_part<DPLA>(o, nw, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, pre,
                           L.rows + k * L.D, lane);
   } else {
     const LaneDev& L = a.lane[1];
-    float o[DPLI];
+    float nw[DPLI], o[DPLI];
+    load_vec<DPLI>(nw, L.norm_w + lane * DPLI);
     r4_pool<DPLI>(a, L, k, lane * DPLI, o);
     __syncthreads();
     float* pre = L.prequant ? L.prequant + (k - a.k_lo) * L.D : nullptr;
-    finish_row_wave<DPLI>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, pre, L.rows + k * L.D, lane);
+    finish_row_wave<DPLI>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, pre, L.rows + k * L.D, lane);
   }
   __syncthreads();
 }
@@ -283,6 +285,8 @@ __global__ void __launch_bounds__(256) pool_r128_finish_kernel(PoolArgs a) {
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row < a.k_hi - a.k_lo) {
     const int d0 = lane * DPL;
+    float nw[DPL];
+    load_vec<DPL>(nw, L.norm_w + d0);
     float M[DPL], den[DPL], num[DPL];
 #pragma unroll
     for (int i = 0; i < DPL; ++i) { M[i] = -INFINITY; den[i] = 0.f; num[i] = 0.f; }
@@ -312,7 +316,7 @@ __global__ void __launch_bounds__(256) pool_r128_finish_kernel(PoolArgs a) {
     }
     const int64_t k = a.k_lo + row;
     float* pre = L.prequant ? L.prequant + row * L.D : nullptr;
-    finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, pre, L.rows + k * L.D, lane);
+    finish_row_wave<DPL>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, pre, L.rows + k * L.D, lane);
   }
 }
 
@@ -368,7 +372,8 @@ __device__ __forceinline__ void r4_fused_window(const PoolArgs& a, int64_t j, fl
   if (wave < SA) {
     const LaneDev& L = a.lane[0];
     const int d0 = wave * (kWave * DPLA) + lane * DPLA;
-    float o[DPLA];
+    float nw[DPLA], o[DPLA];
+    load_vec<DPLA>(nw, L.norm_w + d0);
     fused_pool_dims<DPLA>(a, j, d0, o);
     const float ss = wave_sum(row_sumsq<DPLA>(o));
     if (lane == 0) s_ss[wave] = ss;
@@ -377,15 +382,16 @@ __device__ __forceinline__ void r4_fused_window(const PoolArgs& a, int64_t j, fl
 #pragma unroll
     for (int s = 0; s < SA; ++s) tot += s_ss[s];
     float* pre = L.prequant ? L.prequant + j * L.D : nullptr;
-    finish_row_part<DPLA>(o, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, pre,
+    finish_row_part<DPLA>(o, nw, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, pre,
                           L.rows + k * L.D, lane);
   } else {
     const LaneDev& L = a.lane[1];
-    float o[DPLI];
+    float nw[DPLI], o[DPLI];
+    load_vec<DPLI>(nw, L.norm_w + lane * DPLI);
     fused_pool_dims<DPLI>(a, j, a.lane[0].D + lane * DPLI, o);
     __syncthreads();
     float* pre = L.prequant ? L.prequant + j * L.D : nullptr;
-    finish_row_wave<DPLI>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, pre, L.rows + k * L.D, lane);
+    finish_row_wave<DPLI>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, pre, L.rows + k * L.D, lane);
   }
 }
 
@@ -443,11 +449,12 @@ __global__ void __launch_bounds__(256) pool_r128_fused_kernel(PoolArgs a) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t j = (int64_t)blockIdx.x * 4 + wave;
     if (j < n_emit) {
-      float o[DPL];
+      float nw[DPL], o[DPL];
+      load_vec<DPL>(nw, L.norm_w + lane * DPL);
       load_vec<DPL>(o, a.o + j * L.D + lane * DPL);
       const int64_t k = a.k_lo + j;
       float* pre = L.prequant ? L.prequant + j * L.D : nullptr;
-      finish_row_wave<DPL>(o, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, pre, L.rows + k * L.D, lane);
+      finish_row_wave<DPL>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, pre, L.rows + k * L.D, lane);
     }
     return;
   }
