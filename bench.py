@@ -43,6 +43,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 GEMM_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", "proj_gemm.hip")
+POOL_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", "pool.hip")
 
 
 def fused_call(shape, n0, T):
@@ -140,8 +141,9 @@ def read_traffic(workload: str, key: str = "gemm_hbm_bytes_per_launch"):
     """HBM bytes per launch (GEMM, or another key of the summary) from the
     committed counter summary, or None.
 
-    The summary names the sha256 of the projection kernel source it was taken
-    on; a different source means the counters are stale and none is used.
+    The summary names the sha256 of the kernel sources it was taken on (the
+    projection's for GEMM figures, the pool's for pool figures); a different
+    source means the counters are stale and none is used.
     """
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
@@ -151,8 +153,9 @@ def read_traffic(workload: str, key: str = "gemm_hbm_bytes_per_launch"):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
-    if kv.get("gemm_source_sha256") != src:
+    pool = "pool" in key
+    src = hashlib.sha256(open(POOL_SOURCE if pool else GEMM_SOURCE, "rb").read()).hexdigest()
+    if kv.get("pool_source_sha256" if pool else "gemm_source_sha256") != src:
         return None
     try:
         return float(kv[key])
