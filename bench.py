@@ -163,7 +163,7 @@ def read_traffic(workload: str, key: str = "gemm_hbm_bytes_per_launch"):
         return None
 
 
-def cpu_baseline(shape, x, params, budget_s=12.0):
+def cpu_baseline(shape, x, params, budget_s=12.0, one_thread=False):
     """The oracle as it is, timed on this host over whole prefill steps of the layer."""
     from threadpoolctl import threadpool_info
 
@@ -179,10 +179,41 @@ def cpu_baseline(shape, x, params, budget_s=12.0):
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= 50:
             break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": steps * len(x) / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{steps} full {len(x)}-token prefill steps of one ratio-{shape.ratio} layer "
-                      f"({el:.1f} s); float64 NumPy, BLAS threads {threads}, recurrence single-threaded"}
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] + [1])
+    blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info
+                             if i.get("user_api") == "blas"})) or "unknown"
+    out = {"value": steps * len(x) / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{steps} full {len(x)}-token prefill steps of one ratio-{shape.ratio} layer "
+                     f"({el:.1f} s); float64 NumPy, BLAS threads {threads}, recurrence single-threaded",
+           "cpu_model": cpu_model(), "blas": blas,
+           "cpus_visible": len(os.sched_getaffinity(0))}
+    if one_thread:
+        # The same oracle with BLAS held to one thread, over a shorter sample.
+        from threadpoolctl import threadpool_limits
+
+        with threadpool_limits(limits=1):
+            n1, t1 = 0, time.perf_counter()
+            while True:
+                st = oracle.new_layer_state(spec)
+                oracle.prefill(spec, st, x)
+                n1 += 1
+                el1 = time.perf_counter() - t1
+                if el1 >= budget_s / 2 or n1 >= 50:
+                    break
+        out["one_thread"] = {"value": n1 * len(x) / el1, "unit": "tokens/s", "cores": 1,
+                             "sample": f"{n1} full {len(x)}-token prefill steps ({el1:.1f} s)"}
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def copy_calibration(mib: int, reps: int = 20) -> None:
@@ -265,7 +296,8 @@ def bench_indexer(w, args):
                 break
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
         out["cpu_baseline"] = {"value": calls / el_c, "unit": "queries/s", "cores": threads, "kind": "oracle",
-                               "sample": f"{calls} whole calls ({el_c:.1f} s); float64 NumPy, BLAS threads {threads}"}
+                               "sample": f"{calls} whole calls ({el_c:.1f} s); float64 NumPy, BLAS threads {threads}",
+                               "cpu_model": cpu_model(), "cpus_visible": len(os.sched_getaffinity(0))}
     print(json.dumps(out), flush=True)
 
 
@@ -455,17 +487,49 @@ def main():
                 pl.append(m_[B.KCLASS_POOL] / c_[B.KCLASS_POOL])
             if c_[B.KCLASS_CARRY]:
                 cr.append(m_[B.KCLASS_CARRY] / c_[B.KCLASS_CARRY])
+        # Cold: the library passes over a 1 GiB scratch buffer between each
+        # call's projection and pool launches (outside the timed interval),
+        # which evicts the projection output from the L2s and the Infinity
+        # Cache.  Read eviction leaves clean lines; write eviction leaves
+        # dirty ones, whose write-back then falls on the pool.
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cold = {}
+        for write in (False, True):
+            B.ds4c_profile_evict(scratch.data_ptr(), scratch.numel(), write=write)
+            ts = []
+            for _ in range(21):
+                f = L.frontier
+                f.n_tokens = f.n_comp = f.n_index_comp = 0
+                L.prefill(x[:1])
+                B.ds4c_profile_enable([B.KCLASS_POOL])
+                L.prefill(x[1:T])
+                m_, c_ = B.ds4c_profile_read()
+                B.ds4c_profile_enable(False)
+                if c_[B.KCLASS_POOL]:
+                    ts.append(m_[B.KCLASS_POOL] / c_[B.KCLASS_POOL])
+            B.ds4c_profile_evict(0, 0)
+            cold[write] = sorted(ts)[len(ts) // 2] if ts else 0.0
+        del scratch
         pl_cnt, cr_cnt = len(pl), len(cr)
         _, pl_bytes, _, _ = layer_algorithmic(w.layer, 1, T - 1)
         pl_avg = sorted(pl)[len(pl) // 2] if pl else 0.0
         pl_gbs = pl_bytes / (pl_avg * 1e-3) / 1e9
+        cold_gbs = {k: pl_bytes / (v * 1e-3) / 1e9 if v else 0.0 for k, v in cold.items()}
         out["plain_pool_roofline"] = {
             "bound": "hbm", "achieved": pl_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": pl_gbs / PEAK_HBM_GBS,
             "kernel": "pool_r4_kernel" if w.layer.ratio == 4 else "pool_r128_partial_kernel + pool_r128_finish_kernel",
             "measured": f"median of {pl_cnt} calls of {T - 1} tokens from n0 = 1, warm (reads the projection "
                         f"written just before)",
             "avg_ms": pl_avg, "algorithmic_bytes": pl_bytes,
-            "traffic": read_traffic(args.workload, "plain_pool_hbm_bytes_per_launch")}
+            "traffic": read_traffic(args.workload, "plain_pool_hbm_bytes_per_launch"),
+            "cold": {"achieved": cold_gbs[False], "frac": cold_gbs[False] / PEAK_HBM_GBS, "avg_ms": cold[False],
+                     "measured": "median of 21 calls, a 1 GiB buffer read between each call's projection and "
+                                 "pool launches (the caches hold clean lines)"},
+            "cold_write_evict": {"achieved": cold_gbs[True], "frac": cold_gbs[True] / PEAK_HBM_GBS,
+                                 "avg_ms": cold[True],
+                                 "measured": "median of 21 calls, a 1 GiB buffer written between each call's "
+                                             "projection and pool launches (the pool also pays the write-back "
+                                             "of the dirty lines it displaces)"}}
         if cr_cnt:
             out["plain_pool_roofline"]["carry"] = {
                 "kernel": "pool_r4_carry_kernel", "avg_ms": sorted(cr)[len(cr) // 2],
@@ -473,7 +537,7 @@ def main():
     if not args.no_cpu_baseline:
         n_cpu = min(T, 4096)
         if w.layer is not None:
-            out["cpu_baseline"] = cpu_baseline(w.layer, x_np[:n_cpu], params[0])
+            out["cpu_baseline"] = cpu_baseline(w.layer, x_np[:n_cpu], params[0], one_thread=True)
         else:
             # Whole-stack rate: time one layer of each ratio on the oracle and
             # weight by how many layers of each ratio the stack has.

@@ -75,6 +75,7 @@ SIGNATURES.update({
     "ds4c_status_str": (ctypes.c_char_p, [c_int]),
     "ds4c_profile_enable": (c_int, [c_int]),
     "ds4c_profile_read": (c_int, [POINTER(c_double), POINTER(c_int64), c_int]),
+    "ds4c_profile_evict": (c_int, [c_void_p, c_size_t, c_int]),
 })
 
 
@@ -262,3 +263,10 @@ def ds4c_profile_read():
     cnt = (c_int64 * 6)()
     _ok(lib().ds4c_profile_read(ms, cnt, 6), "ds4c_profile_read")
     return list(ms), list(cnt)
+
+
+def ds4c_profile_evict(scratch: int = 0, nbytes: int = 0, write: bool = False) -> None:
+    """Cold pool timings: while set (a device pointer and its size), timed
+    prefill calls read (or, with write, overwrite) the buffer between
+    projection and pooling.  (0, 0) turns it off."""
+    _ok(lib().ds4c_profile_evict(scratch or None, nbytes, int(write)), "ds4c_profile_evict")

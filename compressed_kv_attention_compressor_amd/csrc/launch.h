@@ -43,6 +43,8 @@ int pool_launches(const PoolArgs& a);
 hipError_t launch_pool(const PoolArgs& a, int phase, hipStream_t stream, const Timing& tm);
 hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, const Timing& tm);
 hipError_t launch_fill(const FillArgs& f, hipStream_t stream, const Timing& tm);
+// Reads or writes `bytes` (a multiple of 16) of a 16-byte aligned device buffer.
+hipError_t launch_evict(void* p, size_t bytes, bool write, hipStream_t stream);
 // Indexer: scores per row, then a radix top-k.  One select workgroup takes
 // up to kIndexerChunk rows; longer calls select per chunk first, and the
 // final pass takes at most kIndexerMaxCand surviving keys (n_chunks * k).

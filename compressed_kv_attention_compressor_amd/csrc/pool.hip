@@ -547,6 +547,37 @@ hipError_t launch_pool(const PoolArgs& a, int phase, hipStream_t stream, const T
   return hipGetLastError();
 }
 
+// Cache eviction for cold timings: reads (kWrite = false) or writes n16
+// 16-byte words of a caller-owned buffer, displacing whatever the caches
+// held.  Read lines stay clean; written lines are dirty and cost a write-back
+// when the next kernel displaces them.  The read form stores only if the
+// XOR of everything it read equals the word's index, so the loads stay live.
+template <bool kWrite>
+__global__ void __launch_bounds__(256) evict_kernel(uint4* p, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (int64_t i = i0; i < n16; i += stride) {
+    if constexpr (kWrite) {
+      p[i] = make_uint4((uint32_t)i, 0u, 0u, 0u);
+    } else {
+      const uint4 v = p[i];
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+  }
+  if (!kWrite && i0 < n16 && acc == (uint32_t)i0 + 0x9e3779b9u) p[i0].x = acc;
+}
+
+hipError_t launch_evict(void* p, size_t bytes, bool write, hipStream_t stream) {
+  if (write)
+    hipLaunchKernelGGL(evict_kernel<true>, dim3(2048), dim3(256), 0, stream, static_cast<uint4*>(p),
+                       (int64_t)(bytes / 16));
+  else
+    hipLaunchKernelGGL(evict_kernel<false>, dim3(2048), dim3(256), 0, stream, static_cast<uint4*>(p),
+                       (int64_t)(bytes / 16));
+  return hipGetLastError();
+}
+
 hipError_t launch_fill(const FillArgs& f, hipStream_t stream, const Timing& tm) {
   hipExtLaunchKernelGGL(frontier_fill_kernel, dim3(64), dim3(256), 0, stream, tm.start, tm.stop, 0, f);
   return hipGetLastError();

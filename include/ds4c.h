@@ -302,6 +302,20 @@ enum { DS4C_PROFILE_ALL = 0x3F };
 int ds4c_profile_enable(int class_mask);
 int ds4c_profile_read(double *ms, int64_t *count, int n);
 
+/* Cold pool timings (measurement only).  While `scratch` is set and the
+ * POOL class is being timed, every prefill call passes once over `bytes` of
+ * `scratch` (a caller-owned device buffer, 16-byte aligned, bytes a multiple
+ * of 16; 1 GiB exceeds the L2s and the 256 MiB Infinity Cache) between its
+ * projection and its pooling launches, outside the timed interval, so the
+ * pooling reads the projection output from HBM.  write = 0 reads the
+ * buffer (the caches are left holding clean lines); write = 1 overwrites it
+ * (the caches are left holding dirty lines, whose write-back then falls on
+ * the pooling).  The buffer must stay allocated while set; its contents may
+ * be overwritten in either mode.  (NULL, 0, 0) turns it off.  A NULL pointer
+ * with nonzero bytes, a nonzero pointer with zero bytes, a misaligned
+ * pointer or size, or write outside {0, 1} returns DS4C_EINVAL. */
+int ds4c_profile_evict(void *scratch, size_t bytes, int write);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,7 +48,7 @@ def frontier(n=0, ratio=4):
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B.SIGNATURES), "binding and header disagree"
@@ -210,6 +210,19 @@ def test_profile_mask_out_of_range():
     assert B.lib().ds4c_profile_enable(-1) == B.DS4C_EINVAL
     assert B.lib().ds4c_profile_enable(B.PROFILE_ALL + 1) == B.DS4C_EINVAL
     assert B.lib().ds4c_profile_enable(0) == B.DS4C_OK
+
+
+def test_profile_evict_validation():
+    """Only the pointer and size are stored; no device call is made."""
+    f = B.lib().ds4c_profile_evict
+    assert f(None, 16, 0) == B.DS4C_EINVAL
+    assert f(ctypes.c_void_p(4096), 0, 0) == B.DS4C_EINVAL
+    assert f(ctypes.c_void_p(4104), 4096, 0) == B.DS4C_EINVAL
+    assert f(ctypes.c_void_p(4096), 4100, 1) == B.DS4C_EINVAL
+    assert f(ctypes.c_void_p(4096), 4096, 2) == B.DS4C_EINVAL
+    assert f(ctypes.c_void_p(4096), 1 << 20, 0) == B.DS4C_OK
+    assert f(ctypes.c_void_p(4096), 1 << 20, 1) == B.DS4C_OK
+    assert f(None, 0, 0) == B.DS4C_OK
 
 
 def _stack(n=4):
