@@ -81,6 +81,11 @@ WORKLOADS: Dict[str, Workload] = {
     # ratio-4 layer holds after the long prompt (65,792 tokens: 16,448 rows),
     # 64 heads of 128 dims.
     "indexer_c5": Workload(7, "indexer top-512 of one query over 16448 rows, 64 heads x 128 dims", 16448, None),
+    # Ratio-4 mixed attention of one decode query over the same layer: the
+    # 128-token raw sliding window plus the top 512 of its 16,448 compressed
+    # attention rows (512 dims), 64 query heads.
+    "mixed_attn_c5": Workload(8, "ratio-4 mixed attention of one decode query, 64 heads x 512 dims, 128 raw rows "
+                                 "+ top 512 of 16448 compressed rows", 16448, None),
 }
 
 
@@ -154,3 +159,16 @@ def indexer_inputs(wid: int, n_rows: int, n_heads: int = 64, head_dim: int = 128
     w = _normal(_gen(seed, wid, 0, 10), (n_heads,), 1.0 / np.sqrt(n_heads))
     rows = _normal(_gen(seed, wid, 0, 11), (n_rows, head_dim), 1.0)
     return q, w, rows
+
+
+def mixed_attention_inputs(wid: int, n_comp: int, n_heads: int = 64, head_dim: int = 512, ring_cap: int = 128,
+                           k: int = 512, seed: int = 0):
+    """Inputs of one mixed-attention call: query heads q [H, D], the raw
+    sliding-window ring [ring_cap, D] and compressed attention rows
+    [n_comp, D], all ~ N(0, 1) float32, and a top-k list of min(k, n_comp)
+    distinct row indices in random order (int32)."""
+    q = _normal(_gen(seed, wid, 0, 12), (n_heads, head_dim), 1.0)
+    ring = _normal(_gen(seed, wid, 0, 13), (ring_cap, head_dim), 1.0)
+    comp = _normal(_gen(seed, wid, 0, 14), (max(n_comp, 1), head_dim), 1.0)[:n_comp]
+    topk = _gen(seed, wid, 0, 15).choice(max(n_comp, 1), size=min(k, n_comp), replace=False).astype(np.int32)
+    return q, ring, comp, topk

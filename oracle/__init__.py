@@ -68,3 +68,4 @@ from .compressor import (  # noqa: F401
 )
 from .schedule import layer_compress_ratio, prefill_chunk_cap  # noqa: F401
 from . import indexer  # noqa: F401
+from . import mixed_attention  # noqa: F401
