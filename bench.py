@@ -301,12 +301,82 @@ def bench_indexer(w, args):
     print(json.dumps(out), flush=True)
 
 
+def bench_mixed_attention(w, args):
+    """One decode query's ratio-4 mixed attention: 64 heads x 512 dims over
+    the 128 raw window rows and the top 512 of 16,448 compressed rows."""
+    import torch
+
+    from compressed_kv_attention_compressor_amd import binding as B
+    from compressed_kv_attention_compressor_amd import synth
+
+    n, H, D, ring_cap, k = w.tokens, 64, 512, 128, 512
+    qpos = 4 * n - 1                       # the last token of the prompt whose rows are all emitted
+    first = qpos + 1 - ring_cap
+    steps = args.steps or 200
+    warmup = args.warmup if args.warmup >= 0 else 10
+    q_np, ring_np, comp_np, topk_np = synth.mixed_attention_inputs(w.wid, n, H, D, ring_cap, k)
+    q, ring, comp = (torch.from_numpy(a).cuda() for a in (q_np, ring_np, comp_np))
+    topk = torch.from_numpy(topk_np).cuda()
+    out = torch.empty(H, D, dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.ds4c_mixed_attention_workspace_bytes(H, D, ring_cap, k), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        B.ds4c_mixed_attention(q, ring, first, qpos, ring_cap, comp, topk, qpos, 4, out, ws, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    B.ds4c_profile_enable([B.KCLASS_ATTENTION])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms, cnt = B.ds4c_profile_read()
+    B.ds4c_profile_enable(False)
+    call_ms = ms[B.KCLASS_ATTENTION] / max(cnt[B.KCLASS_ATTENTION], 1)
+    # Algorithmic bytes: each attended row read once, the query read, the
+    # output written, the list read.
+    rows = ring_cap + k
+    alg = rows * D * 4 + 2 * H * D * 4 + k * 4
+    flops = 2 * 2 * H * rows * D           # logits and weighted rows
+    gbs = alg / (call_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": steps / el, "unit": "queries/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": el / steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded N(0,1) query heads, raw and compressed rows; a random top-512)",
+        "config": {"workload": w.name, "compressed_rows": n, "heads": H, "head_dim": D, "raw_rows": ring_cap,
+                   "top_k": k, "qpos": qpos},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                     "traffic": None, "kernel": "mixed_attn_part_kernel + mixed_attn_merge_kernel (one call)",
+                     "avg_ms": call_ms, "algorithmic_bytes": alg, "algorithmic_flops": flops},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            oracle.mixed_attention.mixed_attention(q_np, ring_np, first, qpos, ring_cap, comp_np, topk_np, qpos, 4)
+            calls += 1
+            el_c = time.perf_counter() - t0
+            if el_c >= 10.0 or calls >= 2000:
+                break
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        res["cpu_baseline"] = {"value": calls / el_c, "unit": "queries/s", "cores": threads, "kind": "oracle",
+                               "sample": f"{calls} whole calls ({el_c:.1f} s); float64 NumPy, BLAS threads {threads}",
+                               "cpu_model": cpu_model(), "cpus_visible": len(os.sched_getaffinity(0))}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0, help="timed steps (default depends on the workload)")
     ap.add_argument("--warmup", type=int, default=-1)
-    ap.add_argument("--workload", default="r4_flash", choices=["r4_flash", "r128_flash", "stack32", "stack32_long", "stack32_pro", "indexer_c5"])
+    ap.add_argument("--workload", default="r4_flash", choices=["r4_flash", "r128_flash", "stack32", "stack32_long", "stack32_pro", "indexer_c5",
+                                                     "mixed_attn_c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0)
     args = ap.parse_args()
@@ -326,6 +396,9 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.workload == "indexer_c5":
         bench_indexer(w, args)
+        return
+    if args.workload == "mixed_attn_c5":
+        bench_mixed_attention(w, args)
         return
     long_run = args.workload == "stack32_long"
     steps = args.steps or (3 if long_run else 20 if w.layer is None else 50)

@@ -21,8 +21,8 @@ DS4C_EFORMAT = -5
 DS4C_EDEVICE = -6
 DS4C_F32 = 0
 DS4C_BF16 = 1
-KCLASS_PROJ, KCLASS_POOL, KCLASS_DECODE, KCLASS_INIT, KCLASS_CARRY, KCLASS_INDEXER = 0, 1, 2, 3, 4, 5
-PROFILE_ALL = 0x3F
+KCLASS_PROJ, KCLASS_POOL, KCLASS_DECODE, KCLASS_INIT, KCLASS_CARRY, KCLASS_INDEXER, KCLASS_ATTENTION = 0, 1, 2, 3, 4, 5, 6
+PROFILE_ALL = 0x7F
 
 # Every function the header declares, with (restype, argtypes).
 SIGNATURES = {}
@@ -70,6 +70,10 @@ SIGNATURES.update({
     "ds4c_indexer_topk": (c_int, [c_void_p, c_void_p, ctypes.c_int32, ctypes.c_int32, c_void_p, c_int64,
                                   ctypes.c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                   c_void_p]),
+    "ds4c_mixed_attention_workspace_bytes": (c_size_t, [ctypes.c_int32, ctypes.c_int32, c_int64, ctypes.c_int32]),
+    "ds4c_mixed_attention": (c_int, [c_void_p, ctypes.c_int32, ctypes.c_int32, c_void_p, c_int64, c_int64, c_int64,
+                                     c_int64, c_void_p, c_int64, c_void_p, ctypes.c_int32, c_int64, ctypes.c_int32,
+                                     c_void_p, c_void_p, c_size_t, c_void_p]),
     "ds4c_layer_ratio": (c_int, [c_int, c_int]),
     "ds4c_prefill_chunk_cap": (c_int64, [c_int64, c_int64]),
     "ds4c_status_str": (ctypes.c_char_p, [c_int]),
@@ -258,10 +262,10 @@ def ds4c_profile_enable(classes=True) -> None:
 
 
 def ds4c_profile_read():
-    """(ms[6], count[6]) accumulated per kernel class since the last read."""
-    ms = (c_double * 6)()
-    cnt = (c_int64 * 6)()
-    _ok(lib().ds4c_profile_read(ms, cnt, 6), "ds4c_profile_read")
+    """(ms[7], count[7]) accumulated per kernel class since the last read."""
+    ms = (c_double * 7)()
+    cnt = (c_int64 * 7)()
+    _ok(lib().ds4c_profile_read(ms, cnt, 7), "ds4c_profile_read")
     return list(ms), list(cnt)
 
 
@@ -270,3 +274,22 @@ def ds4c_profile_evict(scratch: int = 0, nbytes: int = 0, write: bool = False) -
     prefill calls read (or, with write, overwrite) the buffer between
     projection and pooling.  (0, 0) turns it off."""
     _ok(lib().ds4c_profile_evict(scratch or None, nbytes, int(write)), "ds4c_profile_evict")
+
+
+def ds4c_mixed_attention_workspace_bytes(n_heads: int, head_dim: int, ring_cap: int, k: int) -> int:
+    return lib().ds4c_mixed_attention_workspace_bytes(n_heads, head_dim, ring_cap, k)
+
+
+def ds4c_mixed_attention(q, raw_ring, first_raw_pos: int, raw_last_pos: int, window: int, comp_rows, topk,
+                         qpos: int, ratio: int, out, workspace, stream: int = 0) -> None:
+    """Ratio-4 indexed mixed attention of one decode query (Part 3 §7).
+    q [H, D], raw_ring [ring_cap, D], comp_rows [n, D], out [H, D]: float32
+    device tensors; topk int32 device tensor [k]; workspace uint8 device
+    tensor of ds4c_mixed_attention_workspace_bytes bytes."""
+    H, D = q.shape
+    _ok(lib().ds4c_mixed_attention(q.data_ptr(), H, D, raw_ring.data_ptr(), raw_ring.shape[0], first_raw_pos,
+                                   raw_last_pos, window, comp_rows.data_ptr() if comp_rows.numel() else None,
+                                   comp_rows.shape[0], topk.data_ptr() if topk.numel() else None, topk.numel(),
+                                   qpos, ratio, out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                   stream or None),
+        "ds4c_mixed_attention")

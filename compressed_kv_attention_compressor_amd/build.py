@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libds4c.so")
-SOURCES = ["api.cpp", "proj_gemm.hip", "pool.hip", "decode.hip", "indexer.hip"]
+SOURCES = ["api.cpp", "proj_gemm.hip", "pool.hip", "decode.hip", "indexer.hip", "attention.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -25,6 +25,8 @@ using ds4c::ProjArgs;
 
 constexpr size_t kCtrlBytes = 256;
 constexpr int64_t kMaxTokensPerCall = int64_t(1) << 22;
+constexpr int64_t kMaxRing = 4096;  // mixed attention: raw ring rows
+constexpr int32_t kMaxTopk = 4096;  // mixed attention: list entries
 constexpr uint32_t kBlobMagic = 0x46345344u;  // "DS4F" little-endian
 constexpr uint32_t kBlobVersion = 1;
 constexpr size_t kBlobHeader = 8 * 4 + 3 * 8;
@@ -1019,6 +1021,65 @@ int ds4c_indexer_topk(const float* q, const float* head_w, int32_t n_heads, int3
   }
 }
 
+size_t ds4c_mixed_attention_workspace_bytes(int32_t n_heads, int32_t head_dim, int64_t ring_cap, int32_t k) {
+  if (n_heads < 8 || n_heads > 128 || n_heads % 8 != 0) return 0;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512) return 0;
+  if (ring_cap < 0 || ring_cap > kMaxRing || k < 0 || k > kMaxTopk) return 0;
+  const size_t splits = size_t(ds4c::mixed_attn_splits(int(ring_cap + k)));
+  return align256(splits * n_heads * head_dim * 4) + 2 * align256(splits * n_heads * 4);
+}
+
+int ds4c_mixed_attention(const float* q, int32_t n_heads, int32_t head_dim, const float* raw_ring, int64_t ring_cap,
+                         int64_t first_raw_pos, int64_t raw_last_pos, int64_t window, const float* comp_rows,
+                         int64_t n_comp, const int32_t* topk, int32_t k, int64_t qpos, int32_t ratio, float* out,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    const size_t need = ds4c_mixed_attention_workspace_bytes(n_heads, head_dim, ring_cap, k);
+    if (need == 0) return DS4C_ESHAPE;
+    if (ratio < 1 || qpos < 0 || window < 0 || n_comp < 0 || first_raw_pos < 0) return DS4C_EINVAL;
+    if (!q || !aligned(q, 16) || !out || !aligned(out, 16)) return DS4C_EINVAL;
+    // The ring holds positions first_raw_pos .. raw_last_pos (none when
+    // raw_last_pos < first_raw_pos), at most ring_cap of them.
+    if (raw_last_pos >= first_raw_pos && raw_last_pos - first_raw_pos + 1 > ring_cap) return DS4C_EINVAL;
+    const int64_t window_first = (window != 0 && qpos + 1 > window) ? qpos + 1 - window : 0;
+    const int64_t first = std::max(first_raw_pos, window_first), last = std::min(qpos, raw_last_pos);
+    const int64_t n_raw = last >= first ? last - first + 1 : 0;
+    if (n_raw > 0 && (!raw_ring || !aligned(raw_ring, 16))) return DS4C_EINVAL;
+    const int64_t visible = (qpos + 1) / ratio;
+    if (visible > n_comp) return DS4C_ECAP;
+    if (visible > 0 && (!comp_rows || !aligned(comp_rows, 16))) return DS4C_EINVAL;
+    if (k > 0 && (!topk || !aligned(topk, 4))) return DS4C_EINVAL;
+    if (!workspace || !aligned(workspace, 256)) return DS4C_EINVAL;
+    if (ws_bytes < need) return DS4C_ECAP;
+    char* ws = static_cast<char*>(workspace);
+    ds4c::MixedAttnArgs a{};
+    a.q = q;
+    a.ring = raw_ring;
+    a.comp = comp_rows;
+    a.topk = topk;
+    a.H = n_heads;
+    a.D = head_dim;
+    a.ring_cap = int(ring_cap);
+    a.ring_row0 = ring_cap > 0 ? int(first % ring_cap) : 0;
+    a.k = k;
+    a.n_raw = int(n_raw);
+    a.visible = visible;
+    a.n_split = ds4c::mixed_attn_splits(int(n_raw + k));
+    a.scale = float(1.0 / std::sqrt(double(head_dim)));
+    const size_t o_bytes = align256(size_t(a.n_split) * n_heads * head_dim * 4);
+    const size_t ml_bytes = align256(size_t(a.n_split) * n_heads * 4);
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_m = reinterpret_cast<float*>(ws + o_bytes);
+    a.part_l = reinterpret_cast<float*>(ws + o_bytes + ml_bytes);
+    a.out = out;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return dev_status(timed(DS4C_KCLASS_ATTENTION,
+                            [&](const ds4c::Timing& tm) { return ds4c::launch_mixed_attention(a, hs, tm); }));
+  } catch (...) {
+    return DS4C_EDEVICE;
+  }
+}
+
 int ds4c_profile_enable(int class_mask) {
   try {
     if (class_mask < 0 || class_mask > DS4C_PROFILE_ALL) return DS4C_EINVAL;
@@ -1047,7 +1108,7 @@ int ds4c_profile_evict(void* scratch, size_t bytes, int write) {
 
 int ds4c_profile_read(double* ms, int64_t* count, int n) {
   try {
-    if (!ms || !count || n < 0 || n > 6) return DS4C_EINVAL;
+    if (!ms || !count || n < 0 || n > 7) return DS4C_EINVAL;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     for (int i = 0; i < n; ++i) {
       ms[i] = 0.0;

@@ -132,6 +132,26 @@ struct IndexerArgs {
   int n_chunks;         // ceil(n / kIndexerChunk)
 };
 
+struct MixedAttnArgs {
+  const float* q;        // [H, D] query heads
+  const float* ring;     // [ring_cap, D] raw sliding-window rows, position p at row p % ring_cap
+  const float* comp;     // [n_comp, D] compressed attention rows
+  const int32_t* topk;   // [k] selected compressed rows (negative: skipped)
+  float* part_o;         // [n_split, H, D] weighted rows per split (workspace)
+  float* part_m;         // [n_split, H] max logit per split
+  float* part_l;         // [n_split, H] softmax sum per split
+  float* out;            // [H, D]
+  int H;                 // heads, a multiple of 8
+  int D;                 // 64, 128, 256 or 512
+  int ring_cap;
+  int ring_row0;         // ring row of the first attended raw position
+  int k;
+  int n_split;
+  int n_raw;             // attended raw rows, ring rows ring_row0 .. ring_row0 + n_raw - 1 (wrapped)
+  int64_t visible;       // compressed rows visible to the query
+  float scale;           // 1 / sqrt(D)
+};
+
 struct FillArgs {
   float* kv[2];
   float* sc[2];

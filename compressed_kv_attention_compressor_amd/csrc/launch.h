@@ -51,5 +51,9 @@ hipError_t launch_evict(void* p, size_t bytes, bool write, hipStream_t stream);
 constexpr int kIndexerChunk = 32768;
 constexpr int kIndexerMaxCand = 16384;
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const Timing& tm);
+// Mixed attention: a partial launch over (item chunks of 32, head groups of
+// 8), then a merge launch per head.
+int mixed_attn_splits(int n_items);
+hipError_t launch_mixed_attention(const MixedAttnArgs& a, hipStream_t stream, const Timing& tm);
 
 }  // namespace ds4c

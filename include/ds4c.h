@@ -271,6 +271,36 @@ int ds4c_stack_snapshot_load(const ds4c_layer *layers, int n_layers, ds4c_fronti
                              float *const *attn_rows, const int64_t *attn_cap, float *const *index_rows,
                              const int64_t *index_cap, const void *host_buf, size_t len, void *stream);
 
+/* Ratio-4 indexed mixed attention of one decode query (Part 3 §7).  The
+ * query's n_heads heads attend, in one softmax, two sets of rows of
+ * head_dim floats, each row serving as key and value for every head, with
+ * logits <q_h, row> / sqrt(head_dim):
+ *  - raw sliding-window rows: positions max(first_raw_pos, w0) ..
+ *    min(qpos, raw_last_pos), where w0 = qpos + 1 - window when window > 0
+ *    and qpos + 1 > window, else 0; position p is row p % ring_cap of
+ *    raw_ring, which holds positions first_raw_pos .. raw_last_pos (none
+ *    when raw_last_pos < first_raw_pos);
+ *  - compressed rows: topk[0 .. k) walked in order, negative entries
+ *    skipped, the walk ending at the first entry >= visible =
+ *    (qpos + 1) / ratio (the rows the compressor has emitted by then); an
+ *    entry listed twice is attended twice.
+ * out[h] = sum_j softmax_j * row_j, or zeros when no row is attended.
+ * Layout: q [n_heads, head_dim], raw_ring [ring_cap, head_dim], comp_rows
+ * [n_comp, head_dim], out [n_heads, head_dim], all float32 row-major device
+ * buffers, 16-byte aligned; topk int32 [k] (device).  n_heads a multiple of 8
+ * in 8..128, head_dim 64/128/256/512 (else DS4C_ESHAPE, as for ring_cap or
+ * k outside 0..4096); ratio >= 1, qpos >= 0, window >= 0, first_raw_pos >= 0
+ * and at most ring_cap held positions (else DS4C_EINVAL); visible > n_comp
+ * returns DS4C_ECAP.  The workspace (256-byte aligned, caller-owned,
+ * ds4c_mixed_attention_workspace_bytes for the same n_heads, head_dim,
+ * ring_cap and k) holds per-split partials.  Asynchronous on `stream`: two
+ * launches, no allocation.  Timed as DS4C_KCLASS_ATTENTION. */
+size_t ds4c_mixed_attention_workspace_bytes(int32_t n_heads, int32_t head_dim, int64_t ring_cap, int32_t k);
+int ds4c_mixed_attention(const float *q, int32_t n_heads, int32_t head_dim, const float *raw_ring,
+                         int64_t ring_cap, int64_t first_raw_pos, int64_t raw_last_pos, int64_t window,
+                         const float *comp_rows, int64_t n_comp, const int32_t *topk, int32_t k, int64_t qpos,
+                         int32_t ratio, float *out, void *workspace, size_t ws_bytes, void *stream);
+
 /* Compress ratio of layer `layer` of a 0 = Flash / 1 = Pro model (Part 3
  * §1): Flash layers 0-1 -> 0 (uncompressed), Pro layers 0-1 -> 128; from
  * layer 2 even -> 4, odd -> 128.  -1 for a bad variant or negative layer. */
@@ -290,15 +320,16 @@ const char *ds4c_status_str(int status);
  * (DS4C_KCLASS_*), 0 turns timing off, DS4C_PROFILE_ALL selects every class;
  * other values return DS4C_EINVAL.  ds4c_profile_read waits for the recorded
  * events, writes the accumulated milliseconds and launch counts of each class
- * into ms[n] and count[n] (n <= 6), and clears the record.  Enabling or
+ * into ms[n] and count[n] (n <= 7), and clears the record.  Enabling or
  * disabling also clears it.  Classes: projection (PROJ; a K-split call's
  * plane sum included), pooling and row finishing (POOL), the separate
  * frontier-carry launch of a ratio-4 call that does not start on a window
  * boundary (CARRY), decode steps (DECODE), frontier init (INIT), indexer
- * scoring and top-k (INDEXER, the three launches of one call). */
+ * scoring and top-k (INDEXER, the three launches of one call), mixed
+ * attention (ATTENTION, the two launches of one call). */
 enum { DS4C_KCLASS_PROJ = 0, DS4C_KCLASS_POOL = 1, DS4C_KCLASS_DECODE = 2, DS4C_KCLASS_INIT = 3,
-       DS4C_KCLASS_CARRY = 4, DS4C_KCLASS_INDEXER = 5 };
-enum { DS4C_PROFILE_ALL = 0x3F };
+       DS4C_KCLASS_CARRY = 4, DS4C_KCLASS_INDEXER = 5, DS4C_KCLASS_ATTENTION = 6 };
+enum { DS4C_PROFILE_ALL = 0x7F };
 int ds4c_profile_enable(int class_mask);
 int ds4c_profile_read(double *ms, int64_t *count, int n);
 

@@ -48,7 +48,7 @@ def frontier(n=0, ratio=4):
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 24
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B.SIGNATURES), "binding and header disagree"
@@ -199,10 +199,10 @@ def test_save_rejects_small_buffer():
 def test_profile_read_without_records():
     B.ds4c_profile_enable(True)
     ms, cnt = B.ds4c_profile_read()
-    assert ms == [0.0] * 6 and cnt == [0] * 6
+    assert ms == [0.0] * 7 and cnt == [0] * 7
     B.ds4c_profile_enable([B.KCLASS_PROJ, B.KCLASS_CARRY, B.KCLASS_INDEXER])
     ms, cnt = B.ds4c_profile_read()
-    assert cnt == [0] * 6
+    assert cnt == [0] * 7
     B.ds4c_profile_enable(False)
 
 
@@ -223,6 +223,43 @@ def test_profile_evict_validation():
     assert f(ctypes.c_void_p(4096), 1 << 20, 0) == B.DS4C_OK
     assert f(ctypes.c_void_p(4096), 1 << 20, 1) == B.DS4C_OK
     assert f(None, 0, 0) == B.DS4C_OK
+
+
+def test_mixed_attention_workspace_and_validation():
+    """Host-side refusals of the mixed-attention call (no device work)."""
+    ws = B.ds4c_mixed_attention_workspace_bytes
+    # ceil((128 + 512) / 32) = 20 splits of 64 heads x 512 dims, plus max and sum.
+    assert ws(64, 512, 128, 512) == 20 * 64 * 512 * 4 + 2 * 5120
+    assert ws(64, 512, 0, 0) > 0
+    for bad in [(4, 512, 128, 512), (12, 512, 128, 512), (136, 512, 128, 512), (64, 96, 128, 512),
+                (64, 512, -1, 512), (64, 512, 128, 4097), (64, 512, 4097, 8)]:
+        assert ws(*bad) == 0, bad
+    f = B.lib().ds4c_mixed_attention
+    P = ctypes.c_void_p(1 << 20)  # aligned stand-in; every call below is refused before use
+    W = ctypes.c_void_p(1 << 24)
+    need = ws(64, 512, 128, 512)
+
+    def call(**kw):
+        a = dict(q=P, H=64, D=512, ring=P, ring_cap=128, first=0, last=99, window=128, comp=P, n_comp=25,
+                 topk=P, k=512, qpos=99, ratio=4, out=P, ws=W, ws_bytes=need)
+        a.update(kw)
+        return f(a["q"], a["H"], a["D"], a["ring"], a["ring_cap"], a["first"], a["last"], a["window"], a["comp"],
+                 a["n_comp"], a["topk"], a["k"], a["qpos"], a["ratio"], a["out"], a["ws"], a["ws_bytes"], None)
+
+    assert call(H=60) == B.DS4C_ESHAPE
+    assert call(D=320) == B.DS4C_ESHAPE
+    assert call(ratio=0) == B.DS4C_EINVAL
+    assert call(qpos=-1) == B.DS4C_EINVAL
+    assert call(window=-1) == B.DS4C_EINVAL
+    assert call(q=None) == B.DS4C_EINVAL
+    assert call(q=ctypes.c_void_p((1 << 20) + 4)) == B.DS4C_EINVAL
+    assert call(last=128) == B.DS4C_EINVAL           # 129 held positions in a ring of 128
+    assert call(ring=None) == B.DS4C_EINVAL          # raw rows are attended
+    assert call(n_comp=24) == B.DS4C_ECAP            # 25 rows visible at qpos 99
+    assert call(comp=None) == B.DS4C_EINVAL
+    assert call(topk=None) == B.DS4C_EINVAL
+    assert call(ws=None) == B.DS4C_EINVAL
+    assert call(ws_bytes=need - 1) == B.DS4C_ECAP
 
 
 def _stack(n=4):
