@@ -18,6 +18,7 @@
 //    works out where the walk ends, so a call costs two memory round trips.
 //  * mixed_attn_merge_kernel, one wave per head: rescales the splits'
 //    partials to a common max, adds them in split order and normalises.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>

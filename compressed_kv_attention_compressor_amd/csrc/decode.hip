@@ -11,6 +11,7 @@
 // Each of these reads all of its entries at once, so a boundary costs about
 // one memory round trip per launch.
 // The launch boundary orders the pool after every column store.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

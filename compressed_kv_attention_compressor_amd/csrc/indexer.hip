@@ -16,6 +16,7 @@
 //    select over 64-bit keys in one workgroup, each survivor written at its
 //    rank.  Up to kIndexerChunk rows it is one launch; longer calls run
 //    one workgroup per chunk first and a final pass over their survivors.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -1,8 +1,7 @@
 // Host-side launchers of the compressor kernels (enqueue only).
 #pragma once
 
-#include <hip/hip_ext.h>
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include "kernel_args.h"
 

@@ -20,6 +20,7 @@
 // merges the partials, normalises, rotates and quantises each row while
 // extra workgroups carry the frontier.  In both, a launch boundary orders the
 // carry after every read of the incoming frontier.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"

@@ -32,6 +32,7 @@
 // proj_mfma_kernel (128 x 128 and 64 x 64 tiles, plain output): four waves,
 // 32-column K stages (64-byte rows) in a 6-stage ring, loads issued five
 // stages ahead.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
