@@ -120,3 +120,48 @@ def test_repeated_calls_are_bitwise_equal():
     a = run_gpu(q, ring, 65664, 65791, 128, comp, topk, 65791)
     b = run_gpu(q, ring, 65664, 65791, 128, comp, topk, 65791)
     assert np.array_equal(a, b)
+
+
+def test_chain_compressor_indexer_attention():
+    """The three calls in sequence with every intermediate left on the device:
+    a Flash ratio-4 layer compresses a 4096-token chunk (1024 rows per lane),
+    the indexer selects 512 of its indexer rows for a query, and the
+    query at position 4095 attends the 128 raw window rows plus the selected
+    attention rows.  The selection is checked against the oracle's on the
+    GPU's own scores, the attention against the oracle on the same rows."""
+    from oracle import indexer
+
+    print("[mixed] chain: r4_flash prefill -> indexer top-512 -> mixed attention", flush=True)
+    w_ = synth.WORKLOADS["r4_flash"]
+    shape = w_.layer
+    p = synth.layer_params(w_.wid, 0, shape)
+    x = synth.hidden_states(w_.wid, shape.hidden, 0, w_.tokens, shape.dtype)
+    from compressed_kv_attention_compressor_amd.layer import CompressorLayer
+    layer = CompressorLayer(shape.ratio, shape.hidden, p, dtype=shape.dtype, max_tokens=w_.tokens)
+    layer.prefill(torch.from_numpy(x).to("cuda", torch.bfloat16))
+    n = layer.frontier.n_index_comp
+    assert n == 1024 and layer.frontier.n_comp == 1024
+    dev = "cuda"
+    # Indexer over the layer's indexer rows, straight from the row buffer.
+    qi, wi, _ = synth.indexer_inputs(52, 0, 64, 128)
+    qid, wid = torch.from_numpy(qi).to(dev), torch.from_numpy(wi).to(dev)
+    k = 512
+    idx = torch.empty(k, dtype=torch.int32, device=dev)
+    isc = torch.empty(k, dtype=torch.float32, device=dev)
+    scores = torch.empty(n, dtype=torch.float32, device=dev)
+    iws = torch.empty(B.ds4c_indexer_workspace_bytes(n, k), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    B.ds4c_indexer_topk(qid.data_ptr(), wid.data_ptr(), 64, 128, layer.rows["index"].data_ptr(), n, k,
+                        idx.data_ptr(), isc.data_ptr(), 0, scores.data_ptr(), iws.data_ptr(), iws.numel(), stream)
+    # Mixed attention over the layer's attention rows with that selection.
+    q, ring, _, _ = synth.mixed_attention_inputs(53, 1, n_heads=64, head_dim=512, ring_cap=128, k=1)
+    qd, rd = torch.from_numpy(q).to(dev), torch.from_numpy(ring).to(dev)
+    comp = layer.rows["attn"][:1024]
+    out = torch.full((64, 512), float("nan"), dtype=torch.float32, device=dev)
+    aws = torch.empty(B.ds4c_mixed_attention_workspace_bytes(64, 512, 128, k), dtype=torch.uint8, device=dev)
+    B.ds4c_mixed_attention(qd, rd, 3968, 4095, 128, comp, idx, 4095, 4, out, aws, stream)
+    torch.cuda.synchronize()
+    g_idx, g_scores = idx.cpu().numpy(), scores.cpu().numpy()
+    assert np.array_equal(g_idx.astype(np.int64), indexer.topk(g_scores, k))
+    ref = MA.mixed_attention(q, ring, 3968, 4095, 128, comp.cpu().numpy(), g_idx, 4095, 4)
+    np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=RTOL, atol=ATOL)
