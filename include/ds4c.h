@@ -15,7 +15,10 @@
  * row is RMS-normalised, its last n_rot dims are rotated (tail RoPE with
  * the compression base), and it goes through the FP8 E4M3 round trip
  * (attention lane, non-RoPE dims) or the Hadamard + FP4 E2M1 round trip
- * (indexer lane).  Part 3 §4, §5, §8, §9.
+ * (indexer lane).  Part 3 §4, §5, §8, §9.  Beside the compressor, its two
+ * consumers on ratio-4 layers: the indexer's top-k over the compressed
+ * indexer rows (Part 3 §6) and the indexed mixed attention over the raw
+ * window and the selected compressed rows (Part 3 §7).
  *
  * Conventions for every call:
  *   - Pointers are device pointers unless the name starts with host_.
