@@ -16,8 +16,9 @@
 //    LDS, in a fixed order, and one partial per (split, head) goes to the
 //    workspace.  The list entries and rows are requested before the wave
 //    works out where the walk ends, so a call costs two memory round trips.
-//  * mixed_attn_merge_kernel, one wave per head: rescales the splits'
-//    partials to a common max, adds them in split order and normalises.
+//  * mixed_attn_merge_kernel, one wave per (head, 128 dims): rescales the
+//    splits' partials to a common max, adds them in split order and
+//    normalises.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -224,52 +225,52 @@ __global__ void __launch_bounds__(kAttnWaves * kWave) mixed_attn_part_kernel(Mix
   }
 }
 
+// Merge, one wave per (head, 64*DPL-dim chunk of the row), 32 splits per
+// pass: lane i < 32 loads split i's (max, sum) while every lane loads its
+// dims of the 32 splits' weighted rows, all issued before any is used (one
+// memory round trip per pass).  Passes merge online: the running max, sum
+// and weighted row are rescaled when a pass raises the max.  Splits are
+// added in order, so the result does not depend on timing.
 template <int DPL>
 __global__ void __launch_bounds__(kWave) mixed_attn_merge_kernel(MixedAttnArgs a) {
-  constexpr int D = DPL * kWave;
+  constexpr int kPass = 32;
   const int h = blockIdx.x, lane = threadIdx.x;
-  // Splits' (max, sum) across the lanes, 64 splits per pass; the common max
-  // and each split's rescale factor, then the weighted rows 8 splits at a
-  // time with every load of a batch issued first.  Splits are added in
-  // order, so the result does not depend on timing.
-  float mx = -INFINITY;
-  for (int s0 = 0; s0 < a.n_split; s0 += kWave) {
-    const int s = s0 + lane;
-    if (s < a.n_split) mx = fmaxf(mx, a.part_m[(int64_t)s * a.H + h]);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-  float o[DPL], sum = 0.f;
+  const int64_t d0 = (int64_t)blockIdx.y * kWave * DPL + lane * DPL;
+  float mx = -INFINITY, sum = 0.f, o[DPL];
 #pragma unroll
   for (int d = 0; d < DPL; ++d) o[d] = 0.f;
-  if (mx != -INFINITY) {
-    for (int s0 = 0; s0 < a.n_split; s0 += kWave) {
-      const int s = s0 + lane;
-      const float f = s < a.n_split ? pool_exp(a.part_m[(int64_t)s * a.H + h] - mx) : 0.f;
-      const float l = s < a.n_split ? a.part_l[(int64_t)s * a.H + h] : 0.f;
-      sum += wave_sum(l * f);
-      const int n = min(kWave, a.n_split - s0);
-      for (int b = 0; b < n; b += 8) {
-        float t[8][DPL], fb[8];
+  for (int s0 = 0; s0 < a.n_split; s0 += kPass) {
+    const int s = min(s0 + (lane % kPass), a.n_split - 1);
+    const bool mine = lane < kPass && s0 + lane < a.n_split;
+    const float ms = a.part_m[(int64_t)s * a.H + h], ls = a.part_l[(int64_t)s * a.H + h];
+    float t[kPass][DPL];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int si = min(s0 + b + i, a.n_split - 1);
-          load_vec<DPL>(t[i], a.part_o + ((int64_t)si * a.H + h) * D + lane * DPL);
-          fb[i] = __shfl(f, b + i, kWave);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float w = b + i < n ? fb[i] : 0.f;
-#pragma unroll
-          for (int d = 0; d < DPL; ++d) o[d] = fmaf(t[i][d], w, o[d]);
-        }
-      }
+    for (int i = 0; i < kPass; ++i) {
+      const int si = min(s0 + i, a.n_split - 1);
+      load_vec<DPL>(t[i], a.part_o + ((int64_t)si * a.H + h) * a.D + d0);
     }
+    float mp = mine ? ms : -INFINITY;
+#pragma unroll
+    for (int k = 32; k > 0; k >>= 1) mp = fmaxf(mp, __shfl_xor(mp, k, kWave));
+    const float mn = fmaxf(mx, mp);
+    if (mn == -INFINITY) continue;  // nothing attended so far (uniform)
+    const float r = mx == -INFINITY ? 0.f : pool_exp(mx - mn);
+    const float f = mine && ms != -INFINITY ? pool_exp(ms - mn) : 0.f;
+    sum = sum * r + wave_sum(mine ? ls * f : 0.f);
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) o[d] *= r;
+#pragma unroll
+    for (int i = 0; i < kPass; ++i) {
+      const float w = __shfl(f, i, kWave);  // 0 for splits past the end
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) o[d] = fmaf(t[i][d], w, o[d]);
+    }
+    mx = mn;
   }
   const float inv = sum > 0.f ? 1.f / sum : 0.f;
 #pragma unroll
   for (int d = 0; d < DPL; ++d) o[d] *= inv;
-  store_vec<DPL>(a.out + (int64_t)h * D + lane * DPL, o);
+  store_vec<DPL>(a.out + (int64_t)h * a.D + d0, o);
 }
 
 template <int DPL>
@@ -277,7 +278,9 @@ void launch_attn(const MixedAttnArgs& a, hipStream_t stream, const Timing& tm) {
   const dim3 g1(a.n_split, a.H / kHeadsPerGroup);
   hipExtLaunchKernelGGL(mixed_attn_part_kernel<DPL>, g1, dim3(kAttnWaves * kWave), 0, stream, tm.start, nullptr, 0,
                         a);
-  hipExtLaunchKernelGGL(mixed_attn_merge_kernel<DPL>, dim3(a.H), dim3(kWave), 0, stream, nullptr, tm.stop, 0, a);
+  constexpr int kMergeDpl = DPL < 2 ? DPL : 2;
+  hipExtLaunchKernelGGL(mixed_attn_merge_kernel<kMergeDpl>, dim3(a.H, DPL / kMergeDpl), dim3(kWave), 0, stream,
+                        nullptr, tm.stop, 0, a);
 }
 
 }  // namespace

@@ -84,8 +84,9 @@ def test_walk_rules_on_the_device():
 
 
 def test_long_list_ends_past_the_first_scan_pass():
-    """1200 entries: the end of the walk (entry 900) lies in the second pass
-    of 512 entries; 1 + 900 + 10 items over 29 splits."""
+    """1200 entries: the end of the walk (entry 900) lies in the second scan
+    pass of 512 entries; 10 raw + 1200 listed items make 38 splits, so the
+    merge takes two passes of 32."""
     print("[mixed] k 1200, walk ends at entry 900", flush=True)
     q, ring, comp, topk = synth.mixed_attention_inputs(64, 1900, n_heads=8, head_dim=64, ring_cap=16, k=1200)
     lst = topk.copy()
