@@ -312,6 +312,14 @@ __device__ __forceinline__ int tile_ix(int row, int col) {
   return row * 160 + (c < 160 ? c : c - 160);
 }
 
+// e^(s - m) as 2^(s*log2(e) - m*log2(e)) with ml = m*log2(e): one FMA and
+// the hardware base-2 exponential per weight (the epilogue's pool is bound
+// by VALU issue, so the subtraction is folded into the scaling).
+constexpr float kLog2e = 1.44269504088896341f;
+__device__ __forceinline__ float exp_shifted(float s, float ml) {
+  return __builtin_amdgcn_exp2f(fmaf(s, kLog2e, -ml));
+}
+
 // (max, sum, weighted sum) of four entries of one dim, without branches: an
 // all-empty half (every score -inf) gives (-inf, 0, 0).
 struct Part3 {
@@ -320,12 +328,12 @@ struct Part3 {
 __device__ __forceinline__ Part3 half_pool(const float (&kv)[4], const float (&sc)[4]) {
   Part3 p;
   p.m = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-  const float ms = p.m == -INFINITY ? 0.f : p.m;
+  const float ml = (p.m == -INFINITY ? 0.f : p.m) * kLog2e;
   p.s = 0.f;
   p.w = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float x = pool_exp(sc[e] - ms);
+    const float x = exp_shifted(sc[e], ml);
     p.s += x;
     p.w = fmaf(x, kv[e], p.w);
   }
@@ -333,26 +341,28 @@ __device__ __forceinline__ Part3 half_pool(const float (&kv)[4], const float (&s
 }
 
 // Softmax pool of one dim over a whole window: previous half (kp, sp) and
-// current half (kc, sc).  An all-empty window gives 0.
+// current half (kc, sc).  An all-empty window gives 0.  The quotient uses
+// the hardware reciprocal (about 1 ulp), well inside the pooled values'
+// tolerance and below the FP8 grid the row is rounded to afterwards.
 __device__ __forceinline__ float window_pool(const float (&kp)[4], const float (&sp)[4], const float (&kc)[4],
                                              const float (&sc)[4]) {
   const float m =
       fmaxf(fmaxf(fmaxf(sp[0], sp[1]), fmaxf(sp[2], sp[3])), fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-  const float ms = m == -INFINITY ? 0.f : m;
+  const float ml = (m == -INFINITY ? 0.f : m) * kLog2e;
   float den = 0.f, num = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float x = pool_exp(sp[e] - ms);
+    const float x = exp_shifted(sp[e], ml);
     den += x;
     num = fmaf(x, kp[e], num);
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float x = pool_exp(sc[e] - ms);
+    const float x = exp_shifted(sc[e], ml);
     den += x;
     num = fmaf(x, kc[e], num);
   }
-  return den > 0.f ? num / den : 0.f;
+  return den > 0.f ? num * __builtin_amdgcn_rcpf(den) : 0.f;
 }
 
 template <int WM, int FN>
