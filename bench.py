@@ -491,6 +491,11 @@ def main():
     pool_gbs = pool_bytes_per_launch / (pool_ms * 1e-3) / 1e9
     peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
     traffic = read_traffic(args.workload)
+    # MFMA pipes busy over the GEMM's run, from the committed counter summary
+    # (SQ_VALU_MFMA_BUSY_CYCLES summed over the 1024 SIMDs against
+    # GRBM_GUI_ACTIVE summed over the 8 XCDs); None when stale or absent.
+    busy, active = (read_traffic(args.workload, k) for k in ("gemm_mfma_busy_cycles", "gemm_grbm_gui_active"))
+    mfma_busy = busy / 1024 / (active / 8) if busy and active else None
 
     cfg = {"workload": w.name, "tokens": T, "decode_tokens": Td, "hidden": hidden, "chunk": chunk,
            "layers": sum(1 for s in shapes if s[1] is not None), "dtype": dtype}
@@ -512,7 +517,7 @@ def main():
         "config": cfg,
         "rows_per_s": steps * rows / el,
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": gemm_tflops / peak, "traffic": traffic, "kernel": gemm_kernel,
+                     "frac": gemm_tflops / peak, "traffic": traffic, "mfma_busy": mfma_busy, "kernel": gemm_kernel,
                      "avg_ms": gemm_ms, "algorithmic_flops": flops_per_launch},
         "pool_roofline": {"bound": "hbm", "achieved": pool_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": pool_gbs / PEAK_HBM_GBS,
