@@ -1,0 +1,41 @@
+"""bench.py's algorithmic work per call against the per-unit figures the
+measurement plan fixes for the Flash ratio-4 and ratio-128 layers (4096-token
+chunks): GEMM flops 2*T*N*H, and the pool's bytes (every projected kv/score
+element read once, the APE table, the rows written, the live frontier rows
+written).  The achieved GB/s and TFLOP/s in the bench line are these figures
+over measured times, so a mistake here would misstate every roofline."""
+
+import bench
+from compressed_kv_attention_compressor_amd import synth
+
+R4, R128 = synth.FLASH_R4, synth.FLASH_R128
+
+
+def test_gemm_flops():
+    assert bench.layer_algorithmic(R4, 0, 4096)[0] == 85_899_345_920
+    assert bench.layer_algorithmic(R128, 0, 4096)[0] == 34_359_738_368
+    assert bench.layer_algorithmic(R4, 0, 4096)[3] == 2560
+    assert bench.layer_algorithmic(R128, 0, 4096)[3] == 1024
+
+
+def test_pool_bytes_of_the_plain_path():
+    # 4096 tokens from position 0 read 41,943,040 B of projection, 20,480 B of
+    # APE, write 2,621,440 B of rows and 40,960 B of live frontier (ratio 4);
+    # the bench's plain-path call covers tokens 1..4095 (one token's 10,240 B
+    # fewer) and counts the ratio-4 frontier write in the separate carry
+    # launch (read and written there).
+    _, pb, rows, N = bench.layer_algorithmic(R4, 1, 4095)
+    assert rows == 2048
+    assert pb + N * 4 + bench.carry_bytes(R4, 1, 4095) // 2 == 44_625_920
+    # Ratio 128: 16,777,216 + 262,144 + 65,536 B, no live frontier after 4096 tokens.
+    _, pb, rows, N = bench.layer_algorithmic(R128, 1, 4095)
+    assert rows == 32
+    assert pb + N * 4 == 17_104_896
+
+
+def test_fused_finisher_bytes():
+    # Fused ratio-4 call: pooled rows read once and rows written (1024 rows x
+    # 640 dims x 4 B, twice), plus the frontier tokens it writes from the
+    # staged tokens (4 kept tokens x 1280 columns x 2 tensors, read and written).
+    _, pb, _, _ = bench.layer_algorithmic(R4, 0, 4096)
+    assert pb == 1024 * 640 * 4 * 2 + 4 * 1280 * 2 * 4 * 2 == 5_324_800
