@@ -2,11 +2,17 @@
 
 * Values before any codec (pre-quant rows, the attention RoPE tail, live
   frontier kv/score): |g - o| <= 2e-3 * max(|o|, rms(o over the row)).
-* Values after a codec: each block's power-of-two exponent is recomputed from
-  both sides' pre-codec values.  Same exponent: the ordered code distance
-  must be <= 1.  Different exponents are accepted only when the oracle's
-  block maximum lies within 2e-3 (relative) of the boundary between them;
-  then the values must agree to one step of the coarser grid.
+* Values after a codec: first, every GPU block must be a codec output -- each
+  value a point of the format's grid times the block's power of two 2^kg, none
+  beyond the format's maximum.  kg comes from the GPU's pre-codec block, or,
+  without it, from the GPU block's own maximum.  A value that skipped the
+  round trip is off the grid and fails here.  Where the GPU's attention-lane
+  pre-codec rows are at hand (they are exactly what the kernel quantised), its
+  FP8 output must equal their round trip bit for bit.  Then each block's exponent is
+  recomputed from both sides' pre-codec values.  Same exponent: the ordered
+  code distance must be <= 1.  Different exponents are accepted only when the
+  oracle's block maximum lies within 2e-3 (relative) of the boundary between
+  them; then the values must agree to one step of the coarser grid.
 """
 
 from __future__ import annotations
@@ -50,33 +56,76 @@ def _grid_step(v: np.ndarray, k: int, mbits: int, emin: int) -> np.ndarray:
     return 2.0 ** (e - mbits + k)
 
 
+def _on_grid(v: np.ndarray, k: int, qmax: float, enc, dec) -> np.ndarray:
+    """True where v is exactly a finite grid value of the format times 2**k
+    and |v| <= qmax * 2**k (a value that skipped the codec fails)."""
+    a = np.ldexp(np.asarray(v, np.float64), -k)          # exact: a power of two
+    inside = np.abs(a) <= qmax
+    back = dec(enc(np.where(inside, a, 0.0)))
+    return inside & (back == a)
+
+
+def check_codec_outputs(g_final: np.ndarray, g_pre, block: int, fmt: str, what: str) -> None:
+    """Every GPU block must be a codec output (see the module docstring)."""
+    if fmt == "e4m3":
+        qmax, enc, dec = codecs.E4M3_MAX, codecs.e4m3_encode, codecs.e4m3_decode
+    else:
+        qmax, enc, dec = codecs.E2M1_MAX, codecs.e2m1_encode, codecs.e2m1_decode
+    g_final = np.asarray(g_final, np.float64)
+    if not np.all(np.isfinite(g_final)):
+        raise AssertionError(f"{what}: non-finite codec output")
+    for r in range(g_final.shape[0]):
+        for b0 in range(0, g_final.shape[1], block):
+            sl = slice(b0, b0 + block)
+            gv = g_final[r, sl]
+            if g_pre is not None:
+                # The pre-codec values the test holds may differ from the
+                # kernel's own in the last bits (the indexer rows' rotation is
+                # recomputed here in float64), so a maximum within 1e-5 of an
+                # exponent boundary admits either neighbour.
+                amax_pre = float(np.max(np.abs(np.asarray(g_pre[r, sl], np.float32))))
+                k0 = codecs.pow2_block_exponent(amax_pre, qmax)
+                cands = [k0] + [kk for kk in (k0 - 1, k0 + 1)
+                                if amax_pre > 0 and abs(amax_pre - math.ldexp(qmax, min(kk, k0)))
+                                <= 1e-5 * math.ldexp(qmax, min(kk, k0))]
+            else:
+                cands = [codecs.pow2_block_exponent(float(np.max(np.abs(gv))), qmax)]
+            oks = [_on_grid(gv, kk, qmax, enc, dec) for kk in cands]
+            if not any(np.all(ok) for ok in oks):
+                j = int(np.argmin(oks[0]))
+                raise AssertionError(f"{what}: row {r} block {b0 // block} dim {j}: gpu value {gv[j]!r} is not "
+                                     f"a {fmt} value times 2^{cands[0]} (no codec round trip)")
+
+
 def check_codec_blocks(g_final: np.ndarray, o_final: np.ndarray, g_pre: np.ndarray, o_pre: np.ndarray,
                        block: int, fmt: str, what: str) -> int:
-    """Compare codec outputs block by block; returns the number of straddle blocks."""
+    """Check that the GPU blocks are codec outputs, then compare them with the
+    oracle's block by block; returns the number of straddle blocks."""
+    check_codec_outputs(g_final, g_pre, block, fmt, what)
     if fmt == "e4m3":
-        qmax, enc, sign, mbits, emin = codecs.E4M3_MAX, codecs.e4m3_encode, 0x80, 3, -6
+        qmax, enc, dec, sign, mbits, emin = codecs.E4M3_MAX, codecs.e4m3_encode, codecs.e4m3_decode, 0x80, 3, -6
     else:
-        qmax, enc, sign, mbits, emin = codecs.E2M1_MAX, codecs.e2m1_encode, 0x8, 1, 0
+        qmax, enc, dec, sign, mbits, emin = codecs.E2M1_MAX, codecs.e2m1_encode, codecs.e2m1_decode, 0x8, 1, 0
     g_final = np.asarray(g_final, np.float64)
     o_final = np.asarray(o_final, np.float64)
     straddles = 0
     for r in range(o_final.shape[0]):
         for b0 in range(0, o_final.shape[1], block):
             sl = slice(b0, b0 + block)
+            gv, ov = g_final[r, sl], o_final[r, sl]
             amax_o = float(np.max(np.abs(np.asarray(o_pre[r, sl], np.float32))))
             ko = codecs.pow2_block_exponent(amax_o, qmax)
             if g_pre is not None:
                 amax_g = float(np.max(np.abs(np.asarray(g_pre[r, sl], np.float32))))
                 kg = codecs.pow2_block_exponent(amax_g, qmax)
             else:
-                # No GPU pre-codec values: the GPU exponent is taken to be the
-                # oracle's unless the block sits within tolerance of a boundary.
-                kg = ko
-                for kk in (ko - 1, ko + 1):
-                    edge = math.ldexp(qmax, min(kk, ko))
-                    if abs(amax_o - edge) <= REL_TOL * edge:
-                        kg = kk
-            gv, ov = g_final[r, sl], o_final[r, sl]
+                # No GPU pre-codec values: the block's scale is 2^kg or 2^(kg+1)
+                # with kg from its own maximum (a maximum that rounded down to
+                # half the format's range reads one lower).  The oracle's
+                # exponent is the GPU's when the GPU block lies on its grid.
+                kg = codecs.pow2_block_exponent(float(np.max(np.abs(gv))), qmax)
+                if ko in (kg, kg + 1) and np.all(_on_grid(gv, ko, qmax, enc, dec)):
+                    kg = ko
             if ko == kg:
                 dg = _ordered(enc(np.ldexp(gv, -ko)), sign)
                 do = _ordered(enc(np.ldexp(ov, -ko)), sign)
@@ -104,6 +153,17 @@ def check_attn_rows(g_final, o_final, g_pre, o_pre, n_rot: int, what: str = "att
     if nq == 0:
         return 0
     gp = None if g_pre is None else g_pre[:, :nq]
+    if gp is not None:
+        # The attention lane's pre-codec rows are exactly the values the kernel
+        # quantised, so its FP8 output must be their round trip, bit for bit:
+        # this pins the scale rule and the rounding, not only the grid.
+        want = np.stack([codecs.fp8_row_roundtrip(row, nq) for row in np.asarray(gp, np.float64)]) \
+            if len(gp) else np.zeros((0, nq))
+        got = np.asarray(g_final[:, :nq], np.float64)
+        if not np.array_equal(got, want):
+            r, j = np.argwhere(got != want)[0]
+            raise AssertionError(f"{what}: row {r} dim {j}: gpu {got[r, j]!r} is not the FP8 round trip "
+                                 f"{want[r, j]!r} of its own pre-codec value {float(gp[r, j])!r}")
     return check_codec_blocks(g_final[:, :nq], o_final[:, :nq], gp, o_pre[:, :nq], 64, "e4m3", what)
 
 

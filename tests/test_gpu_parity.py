@@ -89,9 +89,10 @@ def compare_all(shape, g, spec, st, n):
         assert g["rows"][k].shape == o_rows.shape
         check_prequant(g["pre"][k], o_pre, f"{k} prequant")
         if k == "attn":
-            check_attn_rows(g["rows"][k], o_rows, g["pre"][k], o_pre, shape.n_rot)
+            nst = check_attn_rows(g["rows"][k], o_rows, g["pre"][k], o_pre, shape.n_rot)
         else:
-            check_index_rows(g["rows"][k], o_rows, g["pre"][k], o_pre)
+            nst = check_index_rows(g["rows"][k], o_rows, g["pre"][k], o_pre)
+        _say(f"[straddle] {k}: {nst} of {o_rows.size // (64 if k == 'attn' else 32)} codec blocks")
         # live frontier rows, pre-quant tolerance; -inf positions exact
         kv_g, sc_g = g["frontier"][k]
         for row, _tok in oracle.compressor.live_frontier_rows(r, n):

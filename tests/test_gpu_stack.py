@@ -65,9 +65,11 @@ def check_layer_rows(L, shape, spec, x, ks, n):
         pre, fin = oracle.window_rows(spec, lane, kv[k_name], sc[k_name], ks)
         got = L.rows[k_name][torch.tensor(ks, device=L.rows[k_name].device)].cpu().numpy()
         if k_name == "attn":
-            check_attn_rows(got, fin, None, pre, shape.n_rot, f"attn rows {ks}")
+            nst = check_attn_rows(got, fin, None, pre, shape.n_rot, f"attn rows {ks}")
         else:
-            check_index_rows(got, fin, None, pre, f"index rows {ks}")
+            nst = check_index_rows(got, fin, None, pre, f"index rows {ks}")
+        if nst:
+            print(f"[straddle] {k_name}: {nst} codec blocks in {len(ks)} rows", flush=True)
     closed = oracle.frontier_from_tokens(spec, n, kv, sc)
     views = L.frontier_views()
     for lane in spec.lanes():

@@ -6,6 +6,8 @@ linearity in the head weights, rotation invariance without the codec),
 a library sort for the selection, and idempotence of the query codec.
 """
 
+import math
+
 import numpy as np
 import pytest
 
@@ -36,6 +38,55 @@ def test_brute_force_tiny():
     s32 = s.astype(np.float32)
     best = sorted(range(n), key=lambda j: (-float(s32[j]), j))[:k]
     assert list(top) == best
+
+
+def _brute_qat(q_row):
+    """Pure-Python QAT of one head row, independent of oracle/codecs.py: the
+    Sylvester Hadamard entry by entry, H[i][j] = (-1)**popcount(i & j)
+    (the closed form of the H_2m = [[H, H], [H, -H]] recursion), scaled by
+    1/sqrt(n); then E2M1 in blocks of 32, each scaled by the smallest power of
+    two that fits its largest magnitude into 6, rounded to the nearest of
+    0, .5, 1, 1.5, 2, 3, 4, 6 with ties to the even code."""
+    n = len(q_row)
+    z = []
+    for i in range(n):
+        acc = 0.0
+        for j in range(n):
+            acc += (-1.0 if bin(i & j).count("1") % 2 else 1.0) * float(q_row[j])
+        z.append(float(np.float32(acc / math.sqrt(n))))
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    out = []
+    for b in range(0, n, 32):
+        blk = z[b:b + 32]
+        amax = max(abs(v) for v in blk)
+        k = 0
+        if amax > 0:
+            k = -300
+            while amax > 6.0 * 2.0 ** k:
+                k += 1
+        for v in blk:
+            a = abs(v) / 2.0 ** k
+            best = min(range(8), key=lambda c: (abs(a - grid[c]), c % 2))
+            out.append(math.copysign(grid[best] * 2.0 ** k, v))
+    return out
+
+
+@pytest.mark.parametrize("dh", [32, 64, 128])
+def test_qat_query_matches_brute_force(dh):
+    """Pins the query's rotation and FP4 round trip (Part 3 §9): a dropped
+    rotation, a wrong Hadamard order or scale, or a wrong codec fails here."""
+    g = _rng(11)
+    q = g.standard_normal((3, dh)).astype(np.float32)
+    q_hat = indexer.qat_query(q)
+    for h in range(3):
+        want = _brute_qat(q[h])
+        # the oracle rounds the rotated value to float32 before its decision,
+        # as the brute force does; the float64 rotations differ only in the
+        # last bits, so the codes agree except at an exact tie (none here)
+        assert np.array_equal(q_hat[h], np.array(want)), (h, np.flatnonzero(q_hat[h] != np.array(want)))
+    # planted mistake: the query quantised without its rotation
+    unrot = np.stack([oracle.fp4_row_roundtrip(q[h]) for h in range(3)])
+    assert not np.array_equal(unrot[0], np.array(_brute_qat(q[0])))
 
 
 def test_one_head_unit_weight_is_relu_dot():
