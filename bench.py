@@ -1,14 +1,17 @@
 """Throughput of the compressed-KV compressor on one MI355X.
 
 Workloads (--workload):
-  r4_flash    (default) one Flash ratio-4 layer, one 4096-token chunk, hidden 4096,
+  stack32_long (default) the 32-layer Flash stack (30 compressed layers, hidden
+              4096, head_dim 512, indexer head_dim 128, bf16) over a 65536-token
+              prompt in 16 chunks of 4096, then 256 single-token decode steps:
+              a step is one ds4c_compress_stack_prefill call and one
+              ds4c_compress_stack_decode call (256 steps looped in the library).
+  r4_flash    one Flash ratio-4 layer, one 4096-token chunk, hidden 4096,
               head_dim 512, indexer head_dim 128, bf16.  A step is one
               ds4c_compress_prefill call: projection GEMM + fused pool kernel.
   r128_flash  the same for a ratio-128 layer (head_dim 512).
   stack32     the 32-layer Flash stack (30 compressed layers), one 4096-token
               chunk: a step is one ds4c_compress_stack_prefill call.
-  stack32_long the stack over a 65536-token prompt in 16 chunks of 4096, then
-              256 ds4c_compress_stack_decode_one steps: a step is all of it.
   stack32_pro the 32-layer Pro-schedule stack (layers 0-1 ratio 128, then
               ratio 4 / 128 alternating; 32 compressed layers), one chunk.
   indexer_c5  indexer scoring + top-512 of one query over the 16,448 indexer
@@ -19,7 +22,9 @@ Every step starts from position 0 (the frontier counters are reset on the
 host; a call at position 0 reads nothing from the frontier).  Inputs are
 resident in HBM before timing.  Kernel times come from events the dispatch
 itself records around each kernel (the library's timing mode), over the
-timed region.  Prints one JSON line.
+timed region; `roofline` describes the kernel class that takes the most time
+there (the decode GEMV for stack32_long), the other of the two is given
+beside it.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME]
   python bench.py --copy-mib N     plain device copy of N MiB (counter calibration)
@@ -44,6 +49,7 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 GEMM_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", "proj_gemm.hip")
 POOL_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", "pool.hip")
+DECODE_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", "decode.hip")
 
 
 def fused_call(shape, n0, T):
@@ -96,6 +102,20 @@ def layer_algorithmic(shape, n0, T):
     return flops, pool_bytes, n_emit * len(lanes), N
 
 
+def decode_gemv_bytes(shapes) -> float:
+    """Weight bytes one decode token streams through every compressed layer
+    of a stack (each layer's projection weights read once; x, the frontier
+    row and the APE row are under 0.1 % and not counted)."""
+    tot = 0.0
+    for _, s in shapes:
+        if s is None:
+            continue
+        lanes = [s.d_attn] + ([s.d_index] if s.d_index else [])
+        N = 2 * sum(s.coff * d for d in lanes)
+        tot += N * s.hidden * (2 if s.dtype == "bf16" else 4)
+    return tot
+
+
 def carry_bytes(shape, n0, T):
     """Bytes of the separate ratio-4 frontier carry: kept kv/score rows read and written."""
     W = [shape.coff * d for d in [shape.d_attn] + ([shape.d_index] if shape.d_index else [])]
@@ -142,8 +162,9 @@ def read_traffic(workload: str, key: str = "gemm_hbm_bytes_per_launch"):
     committed counter summary, or None.
 
     The summary names the sha256 of the kernel sources it was taken on (the
-    projection's for GEMM figures, the pool's for pool figures); a different
-    source means the counters are stale and none is used.
+    projection's for GEMM figures, the pool's for pool figures, the decode
+    source's for decode figures); a different source means the counters are
+    stale and none is used.
     """
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
@@ -153,9 +174,10 @@ def read_traffic(workload: str, key: str = "gemm_hbm_bytes_per_launch"):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    pool = "pool" in key
-    src = hashlib.sha256(open(POOL_SOURCE if pool else GEMM_SOURCE, "rb").read()).hexdigest()
-    if kv.get("pool_source_sha256" if pool else "gemm_source_sha256") != src:
+    kind = "decode" if key.startswith("decode") else "pool" if "pool" in key else "gemm"
+    source = {"decode": DECODE_SOURCE, "pool": POOL_SOURCE, "gemm": GEMM_SOURCE}[kind]
+    src = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    if kv.get(f"{kind}_source_sha256") != src:
         return None
     try:
         return float(kv[key])
@@ -444,8 +466,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0, help="timed steps (default depends on the workload)")
     ap.add_argument("--warmup", type=int, default=-1)
-    ap.add_argument("--workload", default="r4_flash", choices=["r4_flash", "r128_flash", "stack32", "stack32_long", "stack32_pro", "indexer_c5",
-                                                     "mixed_attn_c5"])
+    ap.add_argument("--workload", default="stack32_long",
+                    choices=["r4_flash", "r128_flash", "stack32", "stack32_long", "stack32_pro", "indexer_c5",
+                             "mixed_attn_c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0)
     args = ap.parse_args()
@@ -525,8 +548,8 @@ def main():
 
         def work():
             stack.prefill(x[:T], chunk_cap=chunk)
-            for i in range(Td):
-                stack.decode_one(x[T + i])
+            if Td:
+                stack.decode(x[T:T + Td])   # Td single-token steps, looped in the library
 
     def step():
         reinit()
@@ -536,9 +559,11 @@ def main():
         step()
     torch.cuda.synchronize()
     # Timed region: each step's calls between two events on the library's
-    # stream (the re-initialisation stays outside them); the projection GEMM
-    # (the dominant kernel) is also bracketed by dispatch-recorded events.
-    B.ds4c_profile_enable([B.KCLASS_PROJ])
+    # stream (the re-initialisation stays outside them); the projection GEMMs
+    # and, with decode steps, the decode GEMVs (the two largest kernel
+    # classes) are also bracketed by dispatch-recorded events.
+    timed_classes = [B.KCLASS_PROJ] + ([B.KCLASS_DECODE] if Td else [])
+    B.ds4c_profile_enable(timed_classes)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -555,15 +580,16 @@ def main():
     el_graph = graph_timing(w, L if w.layer is not None else None, reinit, work, step, steps) \
         if w.layer is not None else None
     el = el_graph if el_graph is not None else el_eager
-    # A separate pass times the pool and decode kernels.
+    # A separate pass times the pool kernels (and the decode boundary launches).
     side_steps = max(1, min(steps, 10))
-    B.ds4c_profile_enable([B.KCLASS_POOL, B.KCLASS_DECODE])
+    side = [B.KCLASS_POOL, B.KCLASS_DECODE_POOL] + ([] if Td else [B.KCLASS_DECODE])
+    B.ds4c_profile_enable(side)
     for _ in range(side_steps):
         step()
     torch.cuda.synchronize()
     ms2, cnt2 = B.ds4c_profile_read()
     B.ds4c_profile_enable(False)
-    for c in (B.KCLASS_POOL, B.KCLASS_DECODE):
+    for c in side:
         ms[c], cnt[c] = ms2[c], cnt2[c]
 
     gemm_ms = ms[B.KCLASS_PROJ] / max(cnt[B.KCLASS_PROJ], 1)
@@ -584,6 +610,30 @@ def main():
     # GRBM_GUI_ACTIVE summed over the 8 XCDs); None when stale or absent.
     busy, active = (read_traffic(args.workload, k) for k in ("gemm_mfma_busy_cycles", "gemm_grbm_gui_active"))
     mfma_busy = busy / 1024 / (active / 8) if busy and active else None
+    gemm_roofline = {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": gemm_tflops / peak, "traffic": traffic, "mfma_busy": mfma_busy, "kernel": gemm_kernel,
+                     "avg_ms": gemm_ms, "launches": cnt[B.KCLASS_PROJ], "total_ms": ms[B.KCLASS_PROJ],
+                     "algorithmic_flops": flops_per_launch}
+    decode_roofline = None
+    if Td:
+        # Decode GEMV: every layer's projection weights stream once per token
+        # (the per-token figure of the measurement plan); the launches of the
+        # ratio-4 and ratio-128 layers are averaged together, as one kernel.
+        gemv_ms = ms[B.KCLASS_DECODE] / max(cnt[B.KCLASS_DECODE], 1)
+        gemv_bytes = decode_gemv_bytes(shapes) / max(sum(1 for _, s in shapes if s is not None), 1)
+        gemv_gbs = gemv_bytes / (gemv_ms * 1e-3) / 1e9
+        decode_roofline = {"bound": "hbm", "achieved": gemv_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": gemv_gbs / PEAK_HBM_GBS,
+                           "traffic": read_traffic(args.workload, "decode_gemv_hbm_bytes_per_launch"),
+                           "kernel": "decode_gemv_kernel (ratio-4 and ratio-128 layers)", "avg_ms": gemv_ms,
+                           "launches": cnt[B.KCLASS_DECODE], "total_ms": ms[B.KCLASS_DECODE],
+                           "algorithmic_bytes": gemv_bytes}
+    # The roofline reported is the one of the kernel class that takes the most
+    # time in the timed region; the other is given beside it.
+    if decode_roofline is not None and ms[B.KCLASS_DECODE] > ms[B.KCLASS_PROJ]:
+        roofline, other = decode_roofline, ("mfma_roofline", gemm_roofline)
+    else:
+        roofline, other = gemm_roofline, ("decode_roofline", decode_roofline)
 
     cfg = {"workload": w.name, "tokens": T, "decode_tokens": Td, "hidden": hidden, "chunk": chunk,
            "layers": sum(1 for s in shapes if s[1] is not None), "dtype": dtype}
@@ -612,9 +662,8 @@ def main():
         "data": "synthetic (seeded N(0,1) hidden states, N(0,0.02) weights, N(0,0.1) APE)",
         "config": cfg,
         "rows_per_s": steps * rows / el,
-        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": gemm_tflops / peak, "traffic": traffic, "mfma_busy": mfma_busy, "kernel": gemm_kernel,
-                     "avg_ms": gemm_ms, "algorithmic_flops": flops_per_launch},
+        "roofline": roofline,
+        **({other[0]: other[1]} if other[1] is not None else {}),
         "pool_roofline": {"bound": "hbm", "achieved": pool_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": pool_gbs / PEAK_HBM_GBS,
                           "kernel": "pool (all launches of one call)" if not all_fused else
@@ -623,10 +672,14 @@ def main():
                           "avg_ms": pool_ms, "algorithmic_bytes": pool_bytes_per_launch},
         "kernel_launches": {"proj (timed region)": cnt[B.KCLASS_PROJ],
                             f"pool (pass of {side_steps} steps)": cnt[B.KCLASS_POOL],
-                            f"decode (pass of {side_steps} steps)": cnt[B.KCLASS_DECODE]},
+                            ("decode GEMV (timed region)" if Td else f"decode GEMV (pass of {side_steps} steps)"):
+                                cnt[B.KCLASS_DECODE],
+                            f"decode boundary (pass of {side_steps} steps)": cnt[B.KCLASS_DECODE_POOL]},
     }
     if cnt[B.KCLASS_DECODE]:
         out["decode_avg_ms"] = ms[B.KCLASS_DECODE] / cnt[B.KCLASS_DECODE]
+    if cnt[B.KCLASS_DECODE_POOL]:
+        out["decode_boundary_avg_ms"] = ms[B.KCLASS_DECODE_POOL] / cnt[B.KCLASS_DECODE_POOL]
     if long_run:
         # Session snapshot of the whole stack at the end of a step (rows and
         # frontiers of every layer through pageable host memory), then a
@@ -711,19 +764,40 @@ def main():
         if w.layer is not None:
             out["cpu_baseline"] = cpu_baseline(w.layer, x_np[:n_cpu], params[0], one_thread=True)
         else:
-            # Whole-stack rate: time one layer of each ratio on the oracle and
-            # weight by how many layers of each ratio the stack has.
-            per_token_s, parts = 0.0, []
+            # Whole-stack rate: time one layer of each ratio on the oracle
+            # (prefill over a 4096-token sample; with decode steps, also a
+            # sample of single-token steps after it, two ratio-4 window
+            # boundaries included) and weight by how many layers of each
+            # ratio the stack has and how many tokens of each kind a step has.
+            import oracle
+            from tests._helpers import oracle_spec
+
+            step_s, parts = 0.0, []
             for r in (4, 128):
                 l_r = next(l for l, s in shapes if s is not None and s.ratio == r)
                 n_r = sum(1 for _, s in shapes if s is not None and s.ratio == r)
                 b = cpu_baseline(shapes[l_r][1], x_np[:n_cpu], params[l_r], budget_s=6.0)
-                per_token_s += n_r / b["value"]
-                parts.append(f"ratio {r}: {b['value']:.0f} tokens/s per layer x {n_r} layers")
-            out["cpu_baseline"] = {"value": 1.0 / per_token_s, "unit": "tokens/s", "cores": b["cores"],
+                step_s += n_r * T / b["value"]
+                part = f"ratio {r}: prefill {b['value']:.0f} tokens/s per layer"
+                if Td:
+                    spec = oracle_spec(shapes[l_r][1], params[l_r])
+                    st = oracle.new_layer_state(spec)
+                    oracle.prefill(spec, st, x_np[:n_cpu])
+                    nd, td0 = 8, time.perf_counter()
+                    for i in range(nd):
+                        oracle.decode_one(spec, st, x_np[T + i])
+                    dec_s = (time.perf_counter() - td0) / nd
+                    step_s += n_r * Td * dec_s
+                    part += f", decode {dec_s * 1e3:.1f} ms per token per layer ({nd} steps)"
+                parts.append(part + f", x {n_r} layers")
+            out["cpu_baseline"] = {"value": (T + Td) / step_s, "unit": "tokens/s", "cores": b["cores"],
                                    "kind": "oracle",
                                    "sample": f"{n_cpu}-token prefill steps of one layer of each ratio, about 6 s "
-                                             f"each, combined over the stack ({'; '.join(parts)}); float64 NumPy"}
+                                             f"each{', then single-token decode steps' if Td else ''}, combined "
+                                             f"over the stack and a step's {T} prefill + {Td} decode tokens "
+                                             f"({'; '.join(parts)}); float64 NumPy",
+                                   "cpu_model": b.get("cpu_model"), "blas": b.get("blas"),
+                                   "cpus_visible": b.get("cpus_visible")}
     print(json.dumps(out), flush=True)
 
 

@@ -22,7 +22,9 @@ DS4C_EDEVICE = -6
 DS4C_F32 = 0
 DS4C_BF16 = 1
 KCLASS_PROJ, KCLASS_POOL, KCLASS_DECODE, KCLASS_INIT, KCLASS_CARRY, KCLASS_INDEXER, KCLASS_ATTENTION = 0, 1, 2, 3, 4, 5, 6
-PROFILE_ALL = 0x7F
+KCLASS_DECODE_POOL = 7
+KCLASS_COUNT = 8
+PROFILE_ALL = 0xFF
 
 # Every function the header declares, with (restype, argtypes).
 SIGNATURES = {}
@@ -61,6 +63,8 @@ SIGNATURES.update({
                                             c_size_t, c_void_p]),
     "ds4c_compress_stack_decode_one": (c_int, [_LP, c_int, _FP, c_void_p, POINTER(c_void_p), POINTER(c_int64),
                                                POINTER(c_void_p), POINTER(c_int64), c_void_p]),
+    "ds4c_compress_stack_decode": (c_int, [_LP, c_int, _FP, c_void_p, c_int64, POINTER(c_void_p), POINTER(c_int64),
+                                           POINTER(c_void_p), POINTER(c_int64), c_void_p]),
     "ds4c_stack_snapshot_bytes": (c_size_t, [_LP, c_int, c_int64]),
     "ds4c_stack_snapshot_save": (c_int, [_LP, c_int, _FP, POINTER(c_void_p), POINTER(c_void_p), c_void_p, c_size_t,
                                          POINTER(c_size_t), c_void_p]),
@@ -194,6 +198,14 @@ def ds4c_compress_stack_decode_one(layers, frontiers, x: int, attn_rows, attn_ca
                "ds4c_compress_stack_decode_one")
 
 
+def ds4c_compress_stack_decode(layers, frontiers, x: int, n_tokens: int, attn_rows, attn_cap, index_rows,
+                               index_cap, stream: int = 0) -> int:
+    """n_tokens decode steps; x points at [n_tokens, hidden]."""
+    ar, ac, ir, ic = _ptr_arrays(attn_rows, attn_cap, index_rows, index_cap)
+    return _ok(lib().ds4c_compress_stack_decode(layers, len(layers), frontiers, x, n_tokens, ar, ac, ir, ic, stream),
+               "ds4c_compress_stack_decode")
+
+
 def ds4c_stack_snapshot_bytes(layers, n_tokens: int) -> int:
     return lib().ds4c_stack_snapshot_bytes(layers, len(layers), n_tokens)
 
@@ -262,10 +274,10 @@ def ds4c_profile_enable(classes=True) -> None:
 
 
 def ds4c_profile_read():
-    """(ms[7], count[7]) accumulated per kernel class since the last read."""
-    ms = (c_double * 7)()
-    cnt = (c_int64 * 7)()
-    _ok(lib().ds4c_profile_read(ms, cnt, 7), "ds4c_profile_read")
+    """(ms[KCLASS_COUNT], count[KCLASS_COUNT]) accumulated per kernel class since the last read."""
+    ms = (c_double * KCLASS_COUNT)()
+    cnt = (c_int64 * KCLASS_COUNT)()
+    _ok(lib().ds4c_profile_read(ms, cnt, KCLASS_COUNT), "ds4c_profile_read")
     return list(ms), list(cnt)
 
 

@@ -239,6 +239,26 @@ hipError_t timed(int cls, F&& launch) {
   return hipSuccess;
 }
 
+// As timed(), for a launch sequence with two timed parts: the first under
+// class `cls`, the second (present only when `has_second`) under `cls2`.
+template <class F>
+hipError_t timed2(int cls, int cls2, bool has_second, F&& launch) {
+  std::unique_lock<std::mutex> lk(g_prof_mu);
+  const bool on1 = g_prof_mask & (1 << cls), on2 = has_second && (g_prof_mask & (1 << cls2));
+  if (!on1 && !on2) {
+    lk.unlock();
+    return launch(ds4c::Timing{}, ds4c::Timing{});
+  }
+  ds4c::Timing t1, t2;
+  if (on1 && (!(t1.start = take_event()) || !(t1.stop = take_event()))) return hipErrorOutOfMemory;
+  if (on2 && (!(t2.start = take_event()) || !(t2.stop = take_event()))) return hipErrorOutOfMemory;
+  const hipError_t e = launch(t1, t2);
+  if (e != hipSuccess) return e;
+  if (on1) g_prof.push_back({cls, t1.start, t1.stop});
+  if (on2) g_prof.push_back({cls2, t2.start, t2.stop});
+  return hipSuccess;
+}
+
 int dev_status(hipError_t e) { return e == hipSuccess ? DS4C_OK : DS4C_EDEVICE; }
 
 void fill_proj_segments(const ds4c_layer& L, const Shape& s, ds4c::ProjSeg* seg, int* n_seg) {
@@ -576,8 +596,11 @@ int ds4c_compress_decode_one(const ds4c_layer* layer, ds4c_frontier* frontier, c
     if (s.n_lanes > 1) d.lane[1] = lane_dev(s, *layer, frontier->state, 1, index_rows, index_prequant);
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    st = dev_status(timed(DS4C_KCLASS_DECODE,
-                          [&](const ds4c::Timing& tm) { return ds4c::launch_decode(d, layer->in_dtype, hs, tm); }));
+    const bool boundary = (pos + 1) % r == 0;
+    st = dev_status(timed2(DS4C_KCLASS_DECODE, DS4C_KCLASS_DECODE_POOL, boundary,
+                           [&](const ds4c::Timing& tm, const ds4c::Timing& tp) {
+                             return ds4c::launch_decode(d, layer->in_dtype, hs, tm, tp);
+                           }));
     if (st) return st;
     frontier->n_tokens = pos + 1;
     frontier->n_comp = k_hi;
@@ -757,13 +780,15 @@ int ds4c_compress_stack_prefill(const ds4c_layer* layers, int n_layers, ds4c_fro
   }
 }
 
-int ds4c_compress_stack_decode_one(const ds4c_layer* layers, int n_layers, ds4c_frontier* frontiers,
-                                   const void* x, float* const* attn_rows, const int64_t* attn_cap,
-                                   float* const* index_rows, const int64_t* index_cap, void* stream) {
+int ds4c_compress_stack_decode(const ds4c_layer* layers, int n_layers, ds4c_frontier* frontiers, const void* x,
+                               int64_t n_tokens, float* const* attn_rows, const int64_t* attn_cap,
+                               float* const* index_rows, const int64_t* index_cap, void* stream) {
   try {
     if (!layers || !frontiers || n_layers <= 0 || !attn_rows || !attn_cap || !index_rows || !index_cap)
       return DS4C_EINVAL;
+    if (n_tokens < 0 || n_tokens > kMaxTokensPerCall) return DS4C_EINVAL;
     int64_t n0 = -1;
+    size_t row_bytes = 0;
     for (int l = 0; l < n_layers; ++l) {
       if (layers[l].ratio == 0) continue;
       Shape s;
@@ -773,23 +798,37 @@ int ds4c_compress_stack_decode_one(const ds4c_layer* layers, int n_layers, ds4c_
       if (st) return st;
       if (n0 < 0) n0 = frontiers[l].n_tokens;
       if (frontiers[l].n_tokens != n0) return DS4C_EPOS;
-      const int64_t k_hi = (n0 + 1) / s.ratio;
+      const int64_t k_hi = (n0 + n_tokens) / s.ratio;
       st = check_rows(s, k_hi, k_hi - n0 / s.ratio, attn_rows[l], attn_cap[l], index_rows[l], index_cap[l],
                       nullptr, nullptr);
       if (st) return st;
+      // All layers read the same x rows: one row size for the stack.
+      const size_t b = size_t(layers[l].hidden) * (layers[l].in_dtype == DS4C_BF16 ? 2 : 4);
+      if (row_bytes == 0) row_bytes = b;
+      if (b != row_bytes) return DS4C_ESHAPE;
     }
-    if (n0 < 0) return DS4C_OK;
+    if (n0 < 0 || n_tokens == 0) return DS4C_OK;
     if (!x || !aligned(x, 16)) return DS4C_EINVAL;
-    for (int l = 0; l < n_layers; ++l) {
-      if (layers[l].ratio == 0) continue;
-      const int st = ds4c_compress_decode_one(&layers[l], &frontiers[l], x, attn_rows[l], attn_cap[l],
-                                              index_rows[l], index_cap[l], nullptr, nullptr, stream);
-      if (st) return st;
+    for (int64_t t = 0; t < n_tokens; ++t) {
+      const void* xt = static_cast<const char*>(x) + size_t(t) * row_bytes;
+      for (int l = 0; l < n_layers; ++l) {
+        if (layers[l].ratio == 0) continue;
+        const int st = ds4c_compress_decode_one(&layers[l], &frontiers[l], xt, attn_rows[l], attn_cap[l],
+                                                index_rows[l], index_cap[l], nullptr, nullptr, stream);
+        if (st) return st;  // only a HIP failure can get here
+      }
     }
     return DS4C_OK;
   } catch (...) {
     return DS4C_EDEVICE;
   }
+}
+
+int ds4c_compress_stack_decode_one(const ds4c_layer* layers, int n_layers, ds4c_frontier* frontiers,
+                                   const void* x, float* const* attn_rows, const int64_t* attn_cap,
+                                   float* const* index_rows, const int64_t* index_cap, void* stream) {
+  return ds4c_compress_stack_decode(layers, n_layers, frontiers, x, 1, attn_rows, attn_cap, index_rows, index_cap,
+                                    stream);
 }
 
 int ds4c_layer_ratio(int variant, int layer) {
@@ -1108,7 +1147,7 @@ int ds4c_profile_evict(void* scratch, size_t bytes, int write) {
 
 int ds4c_profile_read(double* ms, int64_t* count, int n) {
   try {
-    if (!ms || !count || n < 0 || n > 7) return DS4C_EINVAL;
+    if (!ms || !count || n < 0 || n > DS4C_KCLASS_COUNT) return DS4C_EINVAL;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     for (int i = 0; i < n; ++i) {
       ms[i] = 0.0;

@@ -1,7 +1,7 @@
 // One decode token through a compressed layer (Part 3 §4,
 // compressor_decode_one; Part 3 §5, the ratio-4 frontier).
 //
-// Every token: a GEMV launch in which each wave computes two projected
+// Every token: a GEMV launch in which each workgroup computes two projected
 // columns (dot products of weight rows with x) and stores them straight into
 // frontier row (coff-1)*ratio + pos%ratio, adding APE[pos%ratio] to scores.
 // Only when (pos+1) % ratio == 0 the frontier is pooled into row pos/ratio
@@ -22,16 +22,18 @@ namespace ds4c {
 
 namespace {
 
-// One wave per workgroup: the grid (N/2 workgroups) then spreads evenly over the CUs.
-constexpr int kDecThreads = 64;
+// Four waves per workgroup, two projected columns per workgroup: wave w
+// takes the w-th quarter of K for both columns, and the four partial sums
+// meet in LDS in a fixed order.  The grid (N/2 workgroups) spreads evenly
+// over the CUs; against one wave per pair of columns over all of K this cut
+// a 30-layer token (15 ratio-4 + 15 ratio-128 GEMVs, weights streamed from
+// HBM) from 154 to 144 us on one MI355X.
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kColsPerBlock = 2;
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-
-constexpr int kColsPerWave = 2;
-// 16-byte steps a lane issues before it computes: with K up to 4096 bf16
-// (2048 fp32) values, a wave has both weight rows and x in flight at once.
-constexpr int kDotUnroll = 8;
 
 // acc += dot(w, x) over one 16-byte step.
 __device__ __forceinline__ float dot16(uint4 w, uint4 x, float acc, uint16_t) {
@@ -49,28 +51,30 @@ __device__ __forceinline__ float dot16(uint4 w, uint4 x, float acc, float) {
   return acc;
 }
 
-// Two dot products of K-long weight rows with x, one wave.  Lane l takes
-// 16-byte step l of every 64-step span; a chunk of kDotUnroll spans is
+// Two dot products over k in [k0, k0 + kr) of weight rows w0, w1 with x,
+// one wave.  Lane l takes 16-byte step l of every 64-step span; U spans are
 // loaded (x straight from global memory, where it stays cache-resident for
-// the whole grid) before any of it is used.  Steps past K load a clamped
-// in-bounds address and are zeroed, so the body has no branches.
-template <typename Tin>
+// the whole grid) before any of them is used.  Steps past the range load a
+// clamped in-range address and are zeroed, so the body has no branches.
+template <typename Tin, int U>
 __device__ __forceinline__ void wave_dot2(const Tin* __restrict__ w0, const Tin* __restrict__ w1,
-                                          const Tin* __restrict__ x, int K, int lane, float* d0, float* d1) {
+                                          const Tin* __restrict__ x, int k0, int kr, int lane, float* d0,
+                                          float* d1) {
   constexpr int kVec = 16 / (int)sizeof(Tin), kSpan = kWave * kVec;
+  const int kend = k0 + kr;
   float a0 = 0.f, a1 = 0.f;
-  for (int k0 = 0; k0 < K; k0 += kSpan * kDotUnroll) {
-    uint4 xv[kDotUnroll], u[kDotUnroll], v[kDotUnroll];
+  for (int kb = k0; kb < kend; kb += kSpan * U) {
+    uint4 xv[U], u[U], v[U];
 #pragma unroll
-    for (int i = 0; i < kDotUnroll; ++i) {
-      const int k = min(k0 + i * kSpan + lane * kVec, K - kVec);
+    for (int i = 0; i < U; ++i) {
+      const int k = min(kb + i * kSpan + lane * kVec, kend - kVec);
       xv[i] = *reinterpret_cast<const uint4*>(x + k);
       u[i] = *reinterpret_cast<const uint4*>(w0 + k);
       v[i] = *reinterpret_cast<const uint4*>(w1 + k);
     }
 #pragma unroll
-    for (int i = 0; i < kDotUnroll; ++i) {
-      const bool in = k0 + i * kSpan + lane * kVec < K;
+    for (int i = 0; i < U; ++i) {
+      const bool in = kb + i * kSpan + lane * kVec < kend;
       const uint4 z = {0u, 0u, 0u, 0u};
       const uint4 xi = in ? xv[i] : z;
       a0 = dot16(in ? u[i] : z, xi, a0, Tin{});
@@ -83,14 +87,15 @@ __device__ __forceinline__ void wave_dot2(const Tin* __restrict__ w0, const Tin*
 
 // Projection of one token into its frontier row.  Workgroup b covers
 // columns [2b, 2b+2); both lie in one column block (blocks have even sizes).
-template <typename Tin>
+template <typename Tin, int U>
 __global__ void __launch_bounds__(kDecThreads) decode_gemv_kernel(DecodeArgs a) {
+  __shared__ float s_part[kDecWaves][kColsPerBlock];
   const int tid = threadIdx.x;
   // Wave-uniform column index: the block selection and the argument fields
   // it reads stay scalar, so the weight loads start after one round of
   // argument loads.
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
-  const int c0 = (blockIdx.x * (kDecThreads / kWave) + wave) * kColsPerWave;
+  const int c0 = blockIdx.x * kColsPerBlock;
   if (c0 >= a.N) return;  // N is a multiple of 64: both columns exist
   int sg = 0;
   if (a.n_seg > 1 && c0 >= a.tgt[1].col0) sg = 1;
@@ -104,10 +109,34 @@ __global__ void __launch_bounds__(kDecThreads) decode_gemv_kernel(DecodeArgs a) 
   // the weight loads issue.
   int zero;
   asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-  const float2 add = G.ape ? *reinterpret_cast<const float2*>(G.ape + j + zero) : float2{0.f, 0.f};
+  const float2 add = (G.ape && wave == 0) ? *reinterpret_cast<const float2*>(G.ape + j + zero) : float2{0.f, 0.f};
+  const int kr = a.K / kDecWaves;  // K is a multiple of 64, so kr is a whole number of 16-byte steps
   float v0, v1;
-  wave_dot2<Tin>(w0, w0 + a.K, reinterpret_cast<const Tin*>(a.x), a.K, lane, &v0, &v1);
-  if (lane == 0) *reinterpret_cast<float2*>(G.dst + j) = float2{v0 + add.x, v1 + add.y};
+  wave_dot2<Tin, U>(w0, w0 + a.K, reinterpret_cast<const Tin*>(a.x), wave * kr, kr, lane, &v0, &v1);
+  if (lane == 0) {
+    s_part[wave][0] = v0;
+    s_part[wave][1] = v1;
+  }
+  __syncthreads();
+  if (tid < kColsPerBlock) {
+    float v = s_part[0][tid];
+#pragma unroll
+    for (int w = 1; w < kDecWaves; ++w) v += s_part[w][tid];
+    G.dst[j + tid] = v + (tid == 0 ? add.x : add.y);
+  }
+}
+
+template <typename Tin>
+void launch_gemv(const DecodeArgs& g, unsigned grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  // Spans of 64 16-byte steps in a wave's quarter of K, all loaded at once
+  // (up to 8; longer quarters loop).
+  constexpr int kSpan = kWave * (16 / (int)sizeof(Tin));
+  const int spans = (g.K / kDecWaves + kSpan - 1) / kSpan;
+  const dim3 gr(grid), bl(kDecThreads);
+  if (spans <= 1) hipExtLaunchKernelGGL((decode_gemv_kernel<Tin, 1>), gr, bl, 0, s, start, stop, 0, g);
+  else if (spans <= 2) hipExtLaunchKernelGGL((decode_gemv_kernel<Tin, 2>), gr, bl, 0, s, start, stop, 0, g);
+  else if (spans <= 4) hipExtLaunchKernelGGL((decode_gemv_kernel<Tin, 4>), gr, bl, 0, s, start, stop, 0, g);
+  else hipExtLaunchKernelGGL((decode_gemv_kernel<Tin, 8>), gr, bl, 0, s, start, stop, 0, g);
 }
 
 // One thread's share of a ratio-4 boundary for dims [d0, d0+DPL) of lane L:
@@ -249,20 +278,19 @@ template <int SA, int DPLA>
 void launch_r4_fin(const DecodeArgs& a, int dpli, hipStream_t s, const Timing& tm) {
   const dim3 g(1), b(64 * (SA + 1));
   switch (dpli) {
-    case 1: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 1>), g, b, 0, s, nullptr, tm.stop, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 2>), g, b, 0, s, nullptr, tm.stop, 0, a); break;
-    case 4: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 4>), g, b, 0, s, nullptr, tm.stop, 0, a); break;
-    default: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 8>), g, b, 0, s, nullptr, tm.stop, 0, a); break;
+    case 1: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 1>), g, b, 0, s, tm.start, tm.stop, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 2>), g, b, 0, s, tm.start, tm.stop, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 4>), g, b, 0, s, tm.start, tm.stop, 0, a); break;
+    default: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 8>), g, b, 0, s, tm.start, tm.stop, 0, a); break;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, const Timing& tm) {
+hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, const Timing& tm,
+                         const Timing& tm_pool) {
   const bool boundary = (a.pos + 1) % a.ratio == 0;
-  constexpr int kColsPerBlock = kColsPerWave * (kDecThreads / kWave);
   const unsigned grid = (unsigned)((a.N + kColsPerBlock - 1) / kColsPerBlock);
-  hipEvent_t stop = boundary ? nullptr : tm.stop;
   DecodeArgs g = a;
   const int pr = (int)(a.pos % a.ratio), slot = (a.ratio == 4 ? 4 : 0) + pr;
   for (int s = 0; s < a.n_seg; ++s) {
@@ -274,11 +302,9 @@ hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, 
     g.tgt[s].col0 = a.seg[s].col0;
   }
   if (in_dtype == 1)
-    hipExtLaunchKernelGGL(decode_gemv_kernel<uint16_t>, dim3(grid), dim3(kDecThreads), 0, stream, tm.start,
-                          stop, 0, g);
+    launch_gemv<uint16_t>(g, grid, stream, tm.start, tm.stop);
   else
-    hipExtLaunchKernelGGL(decode_gemv_kernel<float>, dim3(grid), dim3(kDecThreads), 0, stream, tm.start,
-                          stop, 0, g);
+    launch_gemv<float>(g, grid, stream, tm.start, tm.stop);
   if (boundary) {
     if (a.ratio == 4) {
       // Attention rows split over waves as in prefill: two waves of 256 dims
@@ -286,20 +312,20 @@ hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, 
       // launch), 128 dims at D = 128 / 256, 64 at D = 64.
       const int dpli = a.n_lanes > 1 ? a.lane[1].D / 64 : 1;
       switch (a.lane[0].D) {
-        case 64: launch_r4_fin<1, 1>(a, dpli, stream, tm); break;
-        case 128: launch_r4_fin<1, 2>(a, dpli, stream, tm); break;
-        case 256: launch_r4_fin<2, 2>(a, dpli, stream, tm); break;
-        default: launch_r4_fin<2, 4>(a, dpli, stream, tm); break;
+        case 64: launch_r4_fin<1, 1>(a, dpli, stream, tm_pool); break;
+        case 128: launch_r4_fin<1, 2>(a, dpli, stream, tm_pool); break;
+        case 256: launch_r4_fin<2, 2>(a, dpli, stream, tm_pool); break;
+        default: launch_r4_fin<2, 4>(a, dpli, stream, tm_pool); break;
       }
     } else {
       hipExtLaunchKernelGGL(decode_r128_pool_kernel, dim3(a.lane[0].D / kR128Dims), dim3(kR128Dims * kR128Groups), 0,
-                            stream, nullptr, nullptr, 0, a);
+                            stream, tm_pool.start, nullptr, 0, a);
       const dim3 g(1), b(kWave);
       switch (a.lane[0].D / 64) {
-        case 1: hipExtLaunchKernelGGL((decode_r128_finish_kernel<1>), g, b, 0, stream, nullptr, tm.stop, 0, a); break;
-        case 2: hipExtLaunchKernelGGL((decode_r128_finish_kernel<2>), g, b, 0, stream, nullptr, tm.stop, 0, a); break;
-        case 4: hipExtLaunchKernelGGL((decode_r128_finish_kernel<4>), g, b, 0, stream, nullptr, tm.stop, 0, a); break;
-        default: hipExtLaunchKernelGGL((decode_r128_finish_kernel<8>), g, b, 0, stream, nullptr, tm.stop, 0, a); break;
+        case 1: hipExtLaunchKernelGGL((decode_r128_finish_kernel<1>), g, b, 0, stream, nullptr, tm_pool.stop, 0, a); break;
+        case 2: hipExtLaunchKernelGGL((decode_r128_finish_kernel<2>), g, b, 0, stream, nullptr, tm_pool.stop, 0, a); break;
+        case 4: hipExtLaunchKernelGGL((decode_r128_finish_kernel<4>), g, b, 0, stream, nullptr, tm_pool.stop, 0, a); break;
+        default: hipExtLaunchKernelGGL((decode_r128_finish_kernel<8>), g, b, 0, stream, nullptr, tm_pool.stop, 0, a); break;
       }
     }
   }

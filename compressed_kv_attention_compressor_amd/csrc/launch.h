@@ -40,7 +40,9 @@ hipError_t launch_proj(const ProjArgs& a, int in_dtype, hipStream_t stream, cons
 // two (phase 0: partial pools, phase 1: merge, finish and frontier carry).
 int pool_launches(const PoolArgs& a);
 hipError_t launch_pool(const PoolArgs& a, int phase, hipStream_t stream, const Timing& tm);
-hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, const Timing& tm);
+// The GEMV launch is timed by `tm`, the window-boundary launches (if any) by `tm_pool`.
+hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, const Timing& tm,
+                         const Timing& tm_pool);
 hipError_t launch_fill(const FillArgs& f, hipStream_t stream, const Timing& tm);
 // Reads or writes `bytes` (a multiple of 16) of a 16-byte aligned device buffer.
 hipError_t launch_evict(void* p, size_t bytes, bool write, hipStream_t stream);

@@ -219,3 +219,14 @@ class CompressorStack:
                                              CompressorLayer.stream())
         finally:
             self._pull()
+
+    def decode(self, x: torch.Tensor) -> None:
+        """x [n, hidden]: n single-token decode steps through the stack, in the library."""
+        assert x.dim() == 2 and x.is_contiguous()
+        self._push()
+        ar, ac, ir, ic = self._arrays()
+        try:
+            B.ds4c_compress_stack_decode(self.c_layers, self.c_front, x.data_ptr(), x.shape[0], ar, ac, ir, ic,
+                                         CompressorLayer.stream())
+        finally:
+            self._pull()

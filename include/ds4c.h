@@ -201,7 +201,15 @@ int ds4c_frontier_load(const ds4c_layer *layer, ds4c_frontier *frontier,
  * ds4c_compress_prefill; the frontiers must all be at the same position,
  * else DS4C_EPOS).  Asynchronous on `stream`.
  *
- * ds4c_compress_stack_decode_one: one token x [hidden] through every layer. */
+ * ds4c_compress_stack_decode_one: one token x [hidden] through every layer.
+ *
+ * ds4c_compress_stack_decode: n_tokens single-token decode steps, token
+ * after token, each through every layer in order (Part 3 §4: the decode
+ * path stores one token per call and pools at each window boundary); x is
+ * [n_tokens, hidden], row t the input of step t.  Equivalent to n_tokens
+ * calls of ds4c_compress_stack_decode_one, with the whole run validated
+ * (positions, row capacity at the last step) before anything is enqueued.
+ * Asynchronous on `stream`. */
 size_t ds4c_stack_workspace_bytes(const ds4c_layer *layers, int n_layers, int64_t chunk_cap);
 int ds4c_compress_stack_prefill(const ds4c_layer *layers, int n_layers, ds4c_frontier *frontiers,
                                 const void *x, int64_t T, int64_t chunk_cap,
@@ -211,6 +219,10 @@ int ds4c_compress_stack_prefill(const ds4c_layer *layers, int n_layers, ds4c_fro
 int ds4c_compress_stack_decode_one(const ds4c_layer *layers, int n_layers, ds4c_frontier *frontiers,
                                    const void *x, float *const *attn_rows, const int64_t *attn_cap,
                                    float *const *index_rows, const int64_t *index_cap, void *stream);
+int ds4c_compress_stack_decode(const ds4c_layer *layers, int n_layers, ds4c_frontier *frontiers,
+                               const void *x, int64_t n_tokens, float *const *attn_rows,
+                               const int64_t *attn_cap, float *const *index_rows,
+                               const int64_t *index_cap, void *stream);
 
 /* Stack snapshot: the compressor's sections of a session payload (Part 4 §5:
  * per-layer compressed row counts, the compressed attention rows, the
@@ -323,16 +335,19 @@ const char *ds4c_status_str(int status);
  * (DS4C_KCLASS_*), 0 turns timing off, DS4C_PROFILE_ALL selects every class;
  * other values return DS4C_EINVAL.  ds4c_profile_read waits for the recorded
  * events, writes the accumulated milliseconds and launch counts of each class
- * into ms[n] and count[n] (n <= 7), and clears the record.  Enabling or
- * disabling also clears it.  Classes: projection (PROJ; a K-split call's
- * plane sum included), pooling and row finishing (POOL), the separate
- * frontier-carry launch of a ratio-4 call that does not start on a window
- * boundary (CARRY), decode steps (DECODE), frontier init (INIT), indexer
+ * into ms[n] and count[n] (n <= DS4C_KCLASS_COUNT), and clears the record.
+ * Enabling or disabling also clears it.  Classes: projection (PROJ; a
+ * K-split call's plane sum included), pooling and row finishing (POOL), the
+ * separate frontier-carry launch of a ratio-4 call that does not start on a
+ * window boundary (CARRY), a decode step's projection (DECODE: the GEMV
+ * launch) and its window-boundary pool (DECODE_POOL: the launches that pool,
+ * finish and shift, only at a boundary), frontier init (INIT), indexer
  * scoring and top-k (INDEXER, the three launches of one call), mixed
  * attention (ATTENTION, the two launches of one call). */
 enum { DS4C_KCLASS_PROJ = 0, DS4C_KCLASS_POOL = 1, DS4C_KCLASS_DECODE = 2, DS4C_KCLASS_INIT = 3,
-       DS4C_KCLASS_CARRY = 4, DS4C_KCLASS_INDEXER = 5, DS4C_KCLASS_ATTENTION = 6 };
-enum { DS4C_PROFILE_ALL = 0x7F };
+       DS4C_KCLASS_CARRY = 4, DS4C_KCLASS_INDEXER = 5, DS4C_KCLASS_ATTENTION = 6,
+       DS4C_KCLASS_DECODE_POOL = 7, DS4C_KCLASS_COUNT = 8 };
+enum { DS4C_PROFILE_ALL = 0xFF };
 int ds4c_profile_enable(int class_mask);
 int ds4c_profile_read(double *ms, int64_t *count, int n);
 

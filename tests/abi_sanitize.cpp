@@ -194,8 +194,13 @@ void check_stack() {
   CHECK(ds4c_compress_stack_prefill(layers, 4, fr, dev(0x2000000), 64, 0, ar, ac, ir, ic, dev(0x5000000),
                                     ds4c_stack_workspace_bytes(layers, 4, 4096), nullptr) == DS4C_EPOS);
   CHECK(ds4c_compress_stack_decode_one(layers, 4, fr, dev(0x2000000), ar, ac, ir, ic, nullptr) == DS4C_EPOS);
+  CHECK(ds4c_compress_stack_decode(layers, 4, fr, dev(0x2000000), 16, ar, ac, ir, ic, nullptr) == DS4C_EPOS);
   fr[3].n_tokens = 0;
   fr[3].n_comp = 0;
+  // 4004 decode steps from position 0 need 1001 ratio-4 rows; capacity is 1000.
+  CHECK(ds4c_compress_stack_decode(layers, 4, fr, dev(0x2000000), 4004, ar, ac, ir, ic, nullptr) == DS4C_ECAP);
+  CHECK(ds4c_compress_stack_decode(layers, 4, fr, dev(0x2000000), -1, ar, ac, ir, ic, nullptr) == DS4C_EINVAL);
+  CHECK(ds4c_compress_stack_decode(layers, 4, fr, dev(0x2000000), 0, ar, ac, ir, ic, nullptr) == DS4C_OK);
   CHECK(ds4c_compress_stack_prefill(layers, 4, fr, dev(0x2000000), 64, 0, nullptr, ac, ir, ic, dev(0x5000000),
                                     ds4c_stack_workspace_bytes(layers, 4, 4096), nullptr) != DS4C_OK);
   // Snapshot headers: a consistent header for 1000 tokens over a blob that
@@ -261,11 +266,11 @@ void check_next_rows_and_helpers() {
   CHECK(ds4c_prefill_chunk_cap(10000, 0) == 4096 && ds4c_prefill_chunk_cap(100, 0) == 100);
   CHECK(ds4c_prefill_chunk_cap(0, 0) == 1 && ds4c_prefill_chunk_cap(10000, 512) == 512);
   CHECK(ds4c_profile_enable(-1) == DS4C_EINVAL && ds4c_profile_enable(DS4C_PROFILE_ALL + 1) == DS4C_EINVAL);
-  double ms[8];
-  int64_t cnt[8];
-  CHECK(ds4c_profile_read(ms, cnt, 8) == DS4C_EINVAL);
-  CHECK(ds4c_profile_read(nullptr, cnt, 7) == DS4C_EINVAL);
-  CHECK(ds4c_profile_read(ms, cnt, 7) == DS4C_OK);
+  double ms[DS4C_KCLASS_COUNT + 1];
+  int64_t cnt[DS4C_KCLASS_COUNT + 1];
+  CHECK(ds4c_profile_read(ms, cnt, DS4C_KCLASS_COUNT + 1) == DS4C_EINVAL);
+  CHECK(ds4c_profile_read(nullptr, cnt, DS4C_KCLASS_COUNT) == DS4C_EINVAL);
+  CHECK(ds4c_profile_read(ms, cnt, DS4C_KCLASS_COUNT) == DS4C_OK);
   CHECK(ds4c_profile_evict(nullptr, 16, 0) == DS4C_EINVAL && ds4c_profile_evict(dev(0x1008), 64, 0) == DS4C_EINVAL);
   CHECK(ds4c_profile_evict(dev(0x1000), 64, 3) == DS4C_EINVAL && ds4c_profile_evict(nullptr, 0, 0) == DS4C_OK);
 }

@@ -48,7 +48,7 @@ def frontier(n=0, ratio=4):
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B.SIGNATURES), "binding and header disagree"
@@ -199,10 +199,10 @@ def test_save_rejects_small_buffer():
 def test_profile_read_without_records():
     B.ds4c_profile_enable(True)
     ms, cnt = B.ds4c_profile_read()
-    assert ms == [0.0] * 7 and cnt == [0] * 7
+    assert ms == [0.0] * B.KCLASS_COUNT and cnt == [0] * B.KCLASS_COUNT
     B.ds4c_profile_enable([B.KCLASS_PROJ, B.KCLASS_CARRY, B.KCLASS_INDEXER])
     ms, cnt = B.ds4c_profile_read()
-    assert cnt == [0] * 7
+    assert cnt == [0] * B.KCLASS_COUNT
     B.ds4c_profile_enable(False)
 
 
@@ -320,6 +320,32 @@ def test_stack_rejects_layers_with_different_input_rows():
     layers, fronts = _stack(6)  # ratios 0, 0, 4, 128, 4, 128
     layers[5].hidden = 2048
     assert _stack_call(layers, fronts) == B.DS4C_ESHAPE
+
+
+def _stack_decode(layers, fronts, n_tok=8, cap=10**6, x=FAKE + 0x20000000):
+    n = len(layers)
+    ar = (ctypes.c_void_p * n)(*[FAKE + 0x30000000 if layers[i].ratio else 0 for i in range(n)])
+    ac = (ctypes.c_int64 * n)(*[cap] * n)
+    ir = (ctypes.c_void_p * n)(*[FAKE + 0x40000000 if layers[i].ratio == 4 else 0 for i in range(n)])
+    ic = (ctypes.c_int64 * n)(*[cap if layers[i].ratio == 4 else 0 for i in range(n)])
+    return B.lib().ds4c_compress_stack_decode(layers, n, fronts, x, n_tok, ar, ac, ir, ic, None)
+
+
+def test_stack_decode_validates_the_whole_run_first():
+    layers, fronts = _stack(6)  # ratios 0, 0, 4, 128, 4, 128
+    fronts[4].n_tokens = 4
+    fronts[4].n_comp = fronts[4].n_index_comp = 1
+    assert _stack_decode(layers, fronts) == B.DS4C_EPOS
+    layers, fronts = _stack(6)
+    # 400 steps from position 0 emit 100 rows on the ratio-4 layers
+    assert _stack_decode(layers, fronts, n_tok=400, cap=99) == B.DS4C_ECAP
+    assert _stack_decode(layers, fronts, n_tok=-1) == B.DS4C_EINVAL
+    assert _stack_decode(layers, fronts, n_tok=0) == B.DS4C_OK
+    assert _stack_decode(layers, fronts, x=FAKE + 0x20000004) == B.DS4C_EINVAL  # x not 16-byte aligned
+    layers[5].hidden = 2048
+    assert _stack_decode(layers, fronts) == B.DS4C_ESHAPE
+    for i in range(6):
+        assert fronts[i].n_tokens == 0
 
 
 # --- stack snapshot (the compressor sections of a session payload) -----------

@@ -39,3 +39,14 @@ def test_fused_finisher_bytes():
     # staged tokens (4 kept tokens x 1280 columns x 2 tensors, read and written).
     _, pb, _, _ = bench.layer_algorithmic(R4, 0, 4096)
     assert pb == 1024 * 640 * 4 * 2 + 4 * 1280 * 2 * 4 * 2 == 5_324_800
+
+
+def test_decode_gemv_bytes_per_token():
+    # The measurement plan's per-token decode figure for the 30 compressed
+    # layers of the Flash stack: 440,401,920 B of bf16 weights (15 ratio-4
+    # layers of 2560 x 4096 and 15 ratio-128 layers of 1024 x 4096).
+    shapes = [(l, synth.stack_layer_shape(r)) for l, r in
+              enumerate([0, 0] + [4 if l % 2 == 0 else 128 for l in range(2, 32)])]
+    assert bench.decode_gemv_bytes(shapes) == 440_401_920
+    assert bench.decode_gemv_bytes([(0, R4)]) == 20_971_520
+    assert bench.decode_gemv_bytes([(0, R128)]) == 8_388_608

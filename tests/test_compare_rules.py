@@ -127,3 +127,27 @@ def test_straddle_block_is_counted():
     g_fin = codecs.fp8_row_roundtrip(g_pre[0], 64)[None, :]
     n = compare.check_codec_blocks(g_fin, o_fin, g_pre, pre, 64, "e4m3", "straddle")
     assert n == 1
+
+
+def test_tiny_values_follow_the_pre_codec_tolerance():
+    """A value far below its row's scale sits where the block's FP8 grid is
+    finer than the pre-codec tolerance: a code that quantising a value within
+    that tolerance gives is accepted, one beyond it is not."""
+    rng = np.random.default_rng(9)
+    pre = rng.normal(0, 1, (1, 64))
+    pre[0, 0] = 3.0                  # block maximum: exponent -7, codes near 2e-4 are ~2e-6 apart
+    pre[0, 7] = -2.0e-4
+    o_fin = codecs.fp8_row_roundtrip(pre[0], 64)[None, :]
+    k = codecs.pow2_block_exponent(float(np.max(np.abs(pre[0].astype(np.float32)))), codecs.E4M3_MAX)
+    rms = float(np.sqrt(np.mean(pre[0] ** 2)))
+    for shift, ok in ((0.5e-3 * rms, True), (3e-3 * rms, False)):
+        g_pre = pre.copy()
+        g_pre[0, 7] += shift
+        g_fin = codecs.fp8_row_roundtrip(g_pre[0], 64)[None, :]
+        dist = abs(int(codecs.e4m3_encode(np.ldexp(g_fin[0, 7], -k))) - int(codecs.e4m3_encode(np.ldexp(o_fin[0, 7], -k))))
+        assert dist > 1                  # more than one code apart either way
+        if ok:
+            compare.check_codec_blocks(g_fin, o_fin, None, pre, 64, "e4m3", "tiny")
+        else:
+            with pytest.raises(AssertionError, match="more than one e4m3 code"):
+                compare.check_codec_blocks(g_fin, o_fin, None, pre, 64, "e4m3", "tiny")

@@ -311,3 +311,53 @@ def test_row_zero_of_ratio4_pools_current_half_only():
     g = run_gpu(shape, p, x, [12])
     spec, st = run_oracle(shape, p, x)
     compare_all(shape, g, spec, st, 12)
+
+
+# Score edge cases through every path (fused and plain prefill of both
+# ratios, decode steps): every score of every window shifted by +-1000 (the
+# pool's max subtraction; e^1000 overflows without it), and one entry per
+# window planted 60 above the rest (the pool then returns that entry's kv).
+# The oracle's pins hold both cases to closed forms; here the GPU must match
+# the oracle on the same extreme inputs.
+EDGE_PLANS = {"ragged": PLANS["ragged"], "decode_mix": PLANS["decode_mix"], "aligned_long": PLANS["aligned_long"]}
+
+
+def _edge_params(shape, p, mode):
+    p = {k: {kk: (vv.copy() if isinstance(vv, np.ndarray) else vv) for kk, vv in v.items()} for k, v in p.items()}
+    for kind, lane in p.items():
+        d = lane["head_dim"]
+        if mode == "shift+1000":
+            lane["ape"] += np.float32(1000.0)
+        elif mode == "shift-1000":
+            lane["ape"] -= np.float32(1000.0)
+        else:
+            # ratio 4: the current half's token at p % 4 == 2 (columns [D, 2D));
+            # ratio 128: the token at p % 128 == 5
+            row = 2 if shape.ratio == 4 else 5
+            c0 = d if shape.ratio == 4 else 0
+            lane["ape"][row, c0:c0 + d] += np.float32(60.0)
+    return p
+
+
+@pytest.mark.parametrize("mode", ["shift+1000", "shift-1000", "argmax+60"])
+@pytest.mark.parametrize("plan", list(EDGE_PLANS))
+@pytest.mark.parametrize("name", ["r4_d512_bf16", "r128_d512"])
+def test_score_extremes(name, plan, mode):
+    n = sum(abs(s) for s in EDGE_PLANS[plan])
+    _say(f"[parity] {name} plan {plan} scores {mode} n={n}")
+    shape, p, x = _small(name, n, seed=7)
+    p = _edge_params(shape, p, mode)
+    g = run_gpu(shape, p, x, EDGE_PLANS[plan])
+    spec, st = run_oracle(shape, p, x)
+    compare_all(shape, g, spec, st, n)
+    if mode == "argmax+60":
+        # the planted entry dominates: the pooled value (before the norm) of
+        # every full window is that token's kv to within e^-60 of the rest
+        lane = spec.attn
+        pooled = np.array(st.lanes["attn"].pooled)
+        kv_all, _ = oracle.project(lane, x)
+        d, r = lane.head_dim, shape.ratio
+        for k in range(1, len(pooled)):
+            t = 4 * k + 2 if r == 4 else 128 * k + 5
+            want = kv_all[t][d:2 * d] if r == 4 else kv_all[t][:d]
+            assert np.allclose(pooled[k], want, rtol=1e-12, atol=1e-12)
