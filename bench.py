@@ -461,6 +461,82 @@ def graph_timing(w, L, reinit, work, step, steps):
     return (t_full - t_init) * steps
 
 
+def decode_graph_timing(stack, layers, x, T, Td, chunk, reinit, steps):
+    """Seconds for `steps` steps of a stack workload with decode steps, the
+    decode part replayed from a captured HIP graph.
+
+    The Td decode steps are thousands of small launches whose host-side
+    enqueueing (tens of microseconds per launch with Python and the library's
+    validation) outruns their GPU time; captured once (after a prefill, at
+    the positions every step decodes) and replayed, they run back to back on
+    the GPU.  Each timed step is: re-initialisation (not timed), the prefill
+    calls (eager) and one replay, between two events.  None when capture is
+    not available or a replay does not reproduce the eager run's rows and
+    frontiers bit for bit (checked after the first and the last timed step).
+    """
+    import torch
+
+    def snapshot_state():
+        # rows a step emits (the host counters do not follow graph replays)
+        # and the frontier tensors
+        out = []
+        for L in layers:
+            if L is None:
+                continue
+            out += [v[:(T + Td) // L.ratio].clone() for v in L.rows.values()]
+            out += [t.clone() for pair in L.frontier_views().values() for t in pair]
+        return out
+
+    def same(ref):
+        cur = snapshot_state()
+        return len(cur) == len(ref) and all(torch.equal(a, b) for a, b in zip(cur, ref))
+
+    try:
+        reinit()
+        stack.prefill(x[:T], chunk_cap=chunk)
+        stack.decode(x[T:T + Td])
+        torch.cuda.synchronize()
+        ref = snapshot_state()
+        reinit()
+        stack.prefill(x[:T], chunk_cap=chunk)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            stack.decode(x[T:T + Td])        # enqueued into the graph, not run
+        for L in layers:
+            if L is not None:
+                for v in L.rows.values():
+                    v.fill_(float("nan"))
+        reinit()
+        stack.prefill(x[:T], chunk_cap=chunk)
+        g.replay()
+        torch.cuda.synchronize()
+        if not same(ref):
+            print("decode graph replay differs from the eager steps; eager timing kept", file=sys.stderr)
+            return None
+    except Exception as e:  # capture not supported here: keep the eager timing
+        torch.cuda.synchronize()
+        print(f"graph capture unavailable ({e}); eager timing kept", file=sys.stderr)
+        return None
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for ev_a, ev_b in evs:
+        reinit()
+        ev_a.record()
+        stack.prefill(x[:T], chunk_cap=chunk)
+        g.replay()
+        ev_b.record()
+    torch.cuda.synchronize()
+    ok = same(ref)
+    el = sum(a.elapsed_time(b) for a, b in evs) * 1e-3
+    reinit()
+    torch.cuda.synchronize()
+    if not ok:
+        print("timed decode graph replays differ from the eager steps; eager timing kept", file=sys.stderr)
+        return None
+    GRAPH_FIGURES.update({"graph_decode_steps": Td, "graph_ms_per_step": el / steps * 1e3})
+    return el
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -577,8 +653,12 @@ def main():
     el_eager = sum(a.elapsed_time(b) for a, b in evs) * 1e-3
     ms, cnt = B.ds4c_profile_read()
     B.ds4c_profile_enable(False)
-    el_graph = graph_timing(w, L if w.layer is not None else None, reinit, work, step, steps) \
-        if w.layer is not None else None
+    if w.layer is not None:
+        el_graph = graph_timing(w, L, reinit, work, step, steps)
+    elif Td:
+        el_graph = decode_graph_timing(stack, layers, x, T, Td, chunk, reinit, steps)
+    else:
+        el_graph = None
     el = el_graph if el_graph is not None else el_eager
     # A separate pass times the pool kernels (and the decode boundary launches).
     side_steps = max(1, min(steps, 10))
@@ -649,8 +729,12 @@ def main():
         "ms_per_step": el / steps * 1e3,
         "timing": ("replays of a captured HIP graph of 10 steps (frontier re-initialisation + the step's calls, "
                    "ten times) minus replays of a graph of the 10 re-initialisations alone; the first and the last "
-                   "replay were checked to write the eager run's rows" if el_graph is not None else
-                   "sum of per-step event intervals on the library's stream; the frontier re-initialisation "
+                   "replay were checked to write the eager run's rows" if el_graph is not None and w.layer is not None
+                   else "sum of per-step event intervals on the library's stream, each step the prefill calls "
+                   "(eager) and one replay of a HIP graph holding the step's decode launches (captured once; "
+                   "rows and frontiers of the first and last timed step checked bitwise against the eager run); "
+                   "the frontier re-initialisation between steps is outside the intervals" if el_graph is not None
+                   else "sum of per-step event intervals on the library's stream; the frontier re-initialisation "
                    "between steps is outside them"),
         **GRAPH_FIGURES,
         "eager_ms_per_step": el_eager / steps * 1e3,

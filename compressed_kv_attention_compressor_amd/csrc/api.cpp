@@ -564,6 +564,44 @@ int ds4c_compress_prefill(const ds4c_layer* layer, ds4c_frontier* frontier, cons
   }
 }
 
+namespace {
+
+// Arguments of one decode step of a validated layer; the caller sets d.x and
+// d.pos per token (everything else stays fixed for a layer).
+DecodeArgs decode_args(const Shape& s, const ds4c_layer& layer, void* state, float* attn_rows, float* index_rows,
+                       float* attn_prequant, float* index_prequant) {
+  DecodeArgs d{};
+  d.K = layer.hidden;
+  d.N = s.N;
+  fill_proj_segments(layer, s, d.seg, &d.n_seg);
+  d.ratio = s.ratio;
+  d.n_rot = layer.n_rot;
+  d.n_lanes = s.n_lanes;
+  d.log2_base = std::log2((double)layer.rope_base);
+  d.rms_eps = layer.rms_eps;
+  d.lane[0] = lane_dev(s, layer, state, 0, attn_rows, attn_prequant);
+  if (s.n_lanes > 1) d.lane[1] = lane_dev(s, layer, state, 1, index_rows, index_prequant);
+  return d;
+}
+
+// Enqueues the step at d.pos and advances the frontier's counters.
+int enqueue_decode(const DecodeArgs& d, int in_dtype, ds4c_frontier* frontier, hipStream_t hs) {
+  const int r = d.ratio;
+  const int64_t pos = d.pos, k_hi = (pos + 1) / r;
+  const bool boundary = (pos + 1) % r == 0;
+  const int st = dev_status(timed2(DS4C_KCLASS_DECODE, DS4C_KCLASS_DECODE_POOL, boundary,
+                                   [&](const ds4c::Timing& tm, const ds4c::Timing& tp) {
+                                     return ds4c::launch_decode(d, in_dtype, hs, tm, tp);
+                                   }));
+  if (st) return st;
+  frontier->n_tokens = pos + 1;
+  frontier->n_comp = k_hi;
+  frontier->n_index_comp = r == 4 ? k_hi : 0;
+  return DS4C_OK;
+}
+
+}  // namespace
+
 int ds4c_compress_decode_one(const ds4c_layer* layer, ds4c_frontier* frontier, const void* x,
                              float* attn_rows, int64_t attn_cap, float* index_rows, int64_t index_cap,
                              float* attn_prequant, float* index_prequant, void* stream) {
@@ -580,32 +618,10 @@ int ds4c_compress_decode_one(const ds4c_layer* layer, ds4c_frontier* frontier, c
                     index_prequant);
     if (st) return st;
     if (!x || !aligned(x, 16)) return DS4C_EINVAL;
-
-    DecodeArgs d{};
+    DecodeArgs d = decode_args(s, *layer, frontier->state, attn_rows, index_rows, attn_prequant, index_prequant);
     d.x = x;
-    d.K = layer->hidden;
-    d.N = s.N;
-    fill_proj_segments(*layer, s, d.seg, &d.n_seg);
     d.pos = pos;
-    d.ratio = r;
-    d.n_rot = layer->n_rot;
-    d.n_lanes = s.n_lanes;
-    d.log2_base = std::log2((double)layer->rope_base);
-    d.rms_eps = layer->rms_eps;
-    d.lane[0] = lane_dev(s, *layer, frontier->state, 0, attn_rows, attn_prequant);
-    if (s.n_lanes > 1) d.lane[1] = lane_dev(s, *layer, frontier->state, 1, index_rows, index_prequant);
-
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    const bool boundary = (pos + 1) % r == 0;
-    st = dev_status(timed2(DS4C_KCLASS_DECODE, DS4C_KCLASS_DECODE_POOL, boundary,
-                           [&](const ds4c::Timing& tm, const ds4c::Timing& tp) {
-                             return ds4c::launch_decode(d, layer->in_dtype, hs, tm, tp);
-                           }));
-    if (st) return st;
-    frontier->n_tokens = pos + 1;
-    frontier->n_comp = k_hi;
-    frontier->n_index_comp = r == 4 ? k_hi : 0;
-    return DS4C_OK;
+    return enqueue_decode(d, layer->in_dtype, frontier, static_cast<hipStream_t>(stream));
   } catch (...) {
     return DS4C_EDEVICE;
   }
@@ -809,12 +825,23 @@ int ds4c_compress_stack_decode(const ds4c_layer* layers, int n_layers, ds4c_fron
     }
     if (n0 < 0 || n_tokens == 0) return DS4C_OK;
     if (!x || !aligned(x, 16)) return DS4C_EINVAL;
+    // Everything is validated: build each layer's arguments once, then
+    // enqueue token after token, each through every layer in order.
+    std::vector<DecodeArgs> args(n_layers);
+    for (int l = 0; l < n_layers; ++l) {
+      if (layers[l].ratio == 0) continue;
+      Shape s;
+      check_layer(&layers[l], &s);
+      args[l] = decode_args(s, layers[l], frontiers[l].state, attn_rows[l], index_rows[l], nullptr, nullptr);
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
     for (int64_t t = 0; t < n_tokens; ++t) {
       const void* xt = static_cast<const char*>(x) + size_t(t) * row_bytes;
       for (int l = 0; l < n_layers; ++l) {
         if (layers[l].ratio == 0) continue;
-        const int st = ds4c_compress_decode_one(&layers[l], &frontiers[l], xt, attn_rows[l], attn_cap[l],
-                                                index_rows[l], index_cap[l], nullptr, nullptr, stream);
+        args[l].x = xt;
+        args[l].pos = n0 + t;
+        const int st = enqueue_decode(args[l], layers[l].in_dtype, &frontiers[l], hs);
         if (st) return st;  // only a HIP failure can get here
       }
     }
