@@ -74,6 +74,8 @@ SIGNATURES.update({
     "ds4c_indexer_topk": (c_int, [c_void_p, c_void_p, ctypes.c_int32, ctypes.c_int32, c_void_p, c_int64,
                                   ctypes.c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                   c_void_p]),
+    "ds4c_indexer_topk_noalloc": (c_int, [c_void_p, c_void_p, ctypes.c_int32, ctypes.c_int32, c_void_p, c_int64,
+                                          ctypes.c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "ds4c_mixed_attention_workspace_bytes": (c_size_t, [ctypes.c_int32, ctypes.c_int32, c_int64, ctypes.c_int32]),
     "ds4c_mixed_attention": (c_int, [c_void_p, ctypes.c_int32, ctypes.c_int32, c_void_p, c_int64, c_int64, c_int64,
                                      c_int64, c_void_p, c_int64, c_void_p, ctypes.c_int32, c_int64, ctypes.c_int32,
@@ -249,6 +251,14 @@ def ds4c_indexer_topk(q: int, head_w: int, n_heads: int, head_dim: int, rows: in
     return _ok(lib().ds4c_indexer_topk(q, head_w, n_heads, head_dim, rows or None, n_rows, k, out_idx, out_score,
                                        q_hat or None, scores or None, workspace, ws_bytes, stream),
                "ds4c_indexer_topk")
+
+
+def ds4c_indexer_topk_noalloc(q: int, head_w: int, n_heads: int, head_dim: int, rows: int, n_rows: int, k: int,
+                              out_idx: int, out_score: int, q_hat: int, scores: int, stream: int = 0) -> int:
+    """ds4c_indexer_topk on the library's fixed per-device scratch (no workspace)."""
+    return _ok(lib().ds4c_indexer_topk_noalloc(q, head_w, n_heads, head_dim, rows or None, n_rows, k, out_idx,
+                                               out_score, q_hat or None, scores or None, stream),
+               "ds4c_indexer_topk_noalloc")
 
 
 def ds4c_layer_ratio(variant: int, layer: int) -> int:

@@ -1048,40 +1048,82 @@ size_t ds4c_indexer_workspace_bytes(int64_t n_rows, int32_t k) {
   return align256(size_t(n_rows) * 4) + align256(size_t(chunks) * size_t(k) * 8) + 256;
 }
 
+namespace {
+
+// Validates an indexer call (everything but the workspace) and fills its
+// arguments; the scores default to the workspace's first section.
+int indexer_args(const float* q, const float* head_w, int32_t n_heads, int32_t head_dim, const float* index_rows,
+                 int64_t n_rows, int32_t k, int32_t* out_idx, float* out_score, float* q_hat, float* scores,
+                 size_t* need, ds4c::IndexerArgs* a) {
+  if (head_dim != 64 && head_dim != 128) return DS4C_ESHAPE;
+  if (n_heads < 4 || n_heads > 64 || n_heads % 4 != 0) return DS4C_ESHAPE;
+  if (k < 1 || k > 512 || n_rows < 0) return DS4C_EINVAL;
+  *need = ds4c_indexer_workspace_bytes(n_rows, k);
+  if (*need == 0) return DS4C_ESHAPE;
+  if (!q || !head_w || !aligned(q, 16) || !aligned(head_w, 4)) return DS4C_EINVAL;
+  if (n_rows > 0 && (!index_rows || !aligned(index_rows, 16))) return DS4C_EINVAL;
+  if (!out_idx || !out_score) return DS4C_EINVAL;
+  if (q_hat && !aligned(q_hat, 16)) return DS4C_EINVAL;
+  *a = ds4c::IndexerArgs{};
+  a->q = q;
+  a->head_w = head_w;
+  a->rows = index_rows;
+  a->n = n_rows;
+  a->H = n_heads;
+  a->Dh = head_dim;
+  a->scores = scores;
+  a->q_hat = q_hat;
+  a->out_idx = out_idx;
+  a->out_score = out_score;
+  a->k = k;
+  a->n_chunks = int((n_rows + ds4c::kIndexerChunk - 1) / ds4c::kIndexerChunk);
+  return DS4C_OK;
+}
+
+void indexer_workspace(ds4c::IndexerArgs* a, char* ws) {
+  if (!a->scores) a->scores = reinterpret_cast<float*>(ws);
+  a->cand = reinterpret_cast<uint64_t*>(ws + align256(size_t(a->n) * 4));
+}
+
+}  // namespace
+
 int ds4c_indexer_topk(const float* q, const float* head_w, int32_t n_heads, int32_t head_dim,
                       const float* index_rows, int64_t n_rows, int32_t k, int32_t* out_idx, float* out_score,
                       float* q_hat, float* scores, void* workspace, size_t ws_bytes, void* stream) {
   try {
-    if (head_dim != 64 && head_dim != 128) return DS4C_ESHAPE;
-    if (n_heads < 4 || n_heads > 64 || n_heads % 4 != 0) return DS4C_ESHAPE;
-    if (k < 1 || k > 512 || n_rows < 0) return DS4C_EINVAL;
-    const size_t need = ds4c_indexer_workspace_bytes(n_rows, k);
-    if (need == 0) return DS4C_ESHAPE;
-    if (!q || !head_w || !aligned(q, 16) || !aligned(head_w, 4)) return DS4C_EINVAL;
-    if (n_rows > 0 && (!index_rows || !aligned(index_rows, 16))) return DS4C_EINVAL;
-    if (!out_idx || !out_score) return DS4C_EINVAL;
-    if (q_hat && !aligned(q_hat, 16)) return DS4C_EINVAL;
+    size_t need = 0;
+    ds4c::IndexerArgs a;
+    const int st = indexer_args(q, head_w, n_heads, head_dim, index_rows, n_rows, k, out_idx, out_score, q_hat,
+                                scores, &need, &a);
+    if (st) return st;
     if (!workspace || !aligned(workspace, 256)) return DS4C_EINVAL;
     if (ws_bytes < need) return DS4C_ECAP;
     if (n_rows == 0) return DS4C_OK;
-    char* ws = static_cast<char*>(workspace);
-    ds4c::IndexerArgs a{};
-    a.q = q;
-    a.head_w = head_w;
-    a.rows = index_rows;
-    a.n = n_rows;
-    a.H = n_heads;
-    a.Dh = head_dim;
-    a.scores = scores ? scores : reinterpret_cast<float*>(ws);
-    a.q_hat = q_hat;
-    a.out_idx = out_idx;
-    a.out_score = out_score;
-    a.k = k;
-    a.cand = reinterpret_cast<uint64_t*>(ws + align256(size_t(n_rows) * 4));
-    a.n_chunks = int((n_rows + ds4c::kIndexerChunk - 1) / ds4c::kIndexerChunk);
+    indexer_workspace(&a, static_cast<char*>(workspace));
     hipStream_t hs = static_cast<hipStream_t>(stream);
     return dev_status(
         timed(DS4C_KCLASS_INDEXER, [&](const ds4c::Timing& tm) { return ds4c::launch_indexer(a, hs, tm); }));
+  } catch (...) {
+    return DS4C_EDEVICE;
+  }
+}
+
+int ds4c_indexer_topk_noalloc(const float* q, const float* head_w, int32_t n_heads, int32_t head_dim,
+                              const float* index_rows, int64_t n_rows, int32_t k, int32_t* out_idx,
+                              float* out_score, float* q_hat, float* scores, void* stream) {
+  try {
+    size_t need = 0;
+    ds4c::IndexerArgs a;
+    const int st = indexer_args(q, head_w, n_heads, head_dim, index_rows, n_rows, k, out_idx, out_score, q_hat,
+                                scores, &need, &a);
+    if (st) return st;
+    if (need > ds4c::kIndexerScratchBytes) return DS4C_ECAP;
+    if (n_rows == 0) return DS4C_OK;
+    void* ws = nullptr;
+    if (ds4c::indexer_scratch(&ws) != hipSuccess) return DS4C_EDEVICE;
+    indexer_workspace(&a, static_cast<char*>(ws));
+    // Untimed: the timing mode may create events, which this entry point must not.
+    return dev_status(ds4c::launch_indexer(a, static_cast<hipStream_t>(stream), ds4c::Timing{}));
   } catch (...) {
     return DS4C_EDEVICE;
   }

@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -262,6 +264,40 @@ __global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArg
 }
 
 }  // namespace
+
+// Scratch of the allocation-free indexer entry point: the row scores and the
+// per-chunk candidate keys of the largest call the indexer accepts
+// (1,048,576 rows at k = 512: 4 MiB of scores, 128 KiB of keys).  Each
+// device holds its own copy until the process ends; every call on a device
+// shares it.
+static __device__ __align__(256) unsigned char scratch[kIndexerScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+}  // namespace
+
+hipError_t indexer_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    // The array's host-side name is only a handle: its device address comes
+    // from the runtime, once per device, with that device current.
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *ptr = g_scratch_addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const Timing& tm) {
   if (a.n <= 0) return hipSuccess;

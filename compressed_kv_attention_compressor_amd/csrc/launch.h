@@ -52,6 +52,11 @@ hipError_t launch_evict(void* p, size_t bytes, bool write, hipStream_t stream);
 constexpr int kIndexerChunk = 32768;
 constexpr int kIndexerMaxCand = 16384;
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const Timing& tm);
+// Allocation-free indexer calls use a fixed device array of this many bytes
+// (the workspace of the largest call the indexer accepts); indexer_scratch
+// returns the current device's copy (looked up once per device).
+constexpr size_t kIndexerScratchBytes = 4456448;
+hipError_t indexer_scratch(void** ptr);
 // Mixed attention: a partial launch over (item chunks of 32, head groups of
 // 8), then a merge launch per head.
 int mixed_attn_splits(int n_items);

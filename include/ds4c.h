@@ -278,6 +278,21 @@ int ds4c_indexer_topk(const float *q, const float *head_w, int32_t n_heads, int3
                       const float *index_rows, int64_t n_rows, int32_t k, int32_t *out_idx, float *out_score,
                       float *q_hat, float *scores, void *workspace, size_t ws_bytes, void *stream);
 
+/* ds4c_indexer_topk without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and errors as
+ * ds4c_indexer_topk; the scratch is a fixed array in the library, 4,456,448
+ * bytes per device (every call ds4c_indexer_topk accepts fits), held by each
+ * device the library runs on until the process ends.  Calls whose
+ * ds4c_indexer_workspace_bytes(n_rows, k) exceeds it return DS4C_ECAP.  The
+ * call allocates nothing (no hipMalloc, no events; kernel timing does not
+ * cover it).  Every call on a device shares that device's array: calls that
+ * overlap on one device (other streams, other threads) race and must be
+ * serialised by the caller.  The stream must belong to the current device. */
+int ds4c_indexer_topk_noalloc(const float *q, const float *head_w, int32_t n_heads, int32_t head_dim,
+                              const float *index_rows, int64_t n_rows, int32_t k, int32_t *out_idx,
+                              float *out_score, float *q_hat, float *scores, void *stream);
+
 size_t ds4c_stack_snapshot_bytes(const ds4c_layer *layers, int n_layers, int64_t n_tokens);
 int ds4c_stack_snapshot_save(const ds4c_layer *layers, int n_layers, const ds4c_frontier *frontiers,
                              const float *const *attn_rows, const float *const *index_rows, void *host_buf,

@@ -248,6 +248,9 @@ void check_next_rows_and_helpers() {
   CHECK(ds4c_indexer_topk(q, q, 64, 128, q, 100, 0, oi, os, nullptr, nullptr, ws, 1 << 20, nullptr) ==
         DS4C_EINVAL);
   CHECK(ds4c_indexer_topk(q, q, 64, 128, q, 100, 8, oi, os, nullptr, nullptr, ws, 16, nullptr) == DS4C_ECAP);
+  CHECK(ds4c_indexer_topk_noalloc(q, q, 64, 96, q, 100, 8, oi, os, nullptr, nullptr, nullptr) == DS4C_ESHAPE);
+  CHECK(ds4c_indexer_topk_noalloc(q, q, 64, 128, q, 2000000, 1, oi, os, nullptr, nullptr, nullptr) == DS4C_ECAP);
+  CHECK(ds4c_indexer_topk_noalloc(q, q, 64, 128, q, 0, 8, oi, os, nullptr, nullptr, nullptr) == DS4C_OK);
   CHECK(ds4c_mixed_attention_workspace_bytes(64, 512, 128, 512) > 0);
   CHECK(ds4c_mixed_attention_workspace_bytes(60, 512, 128, 512) == 0);
   const size_t mw = ds4c_mixed_attention_workspace_bytes(64, 512, 128, 512);

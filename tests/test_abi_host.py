@@ -48,7 +48,7 @@ def frontier(n=0, ratio=4):
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = declared_functions()
-    assert len(names) == 25
+    assert len(names) == 26
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B.SIGNATURES), "binding and header disagree"
@@ -460,3 +460,24 @@ def test_indexer_validates_before_launching():
     assert call(wsp=FAKE + 16) == B.DS4C_EINVAL                  # workspace not 256-byte aligned
     assert call(ws=B.ds4c_indexer_workspace_bytes(100, 16) - 1) == B.DS4C_ECAP
     assert call(n=0, rows=0) == B.DS4C_OK                        # nothing to score: no launch
+
+
+def test_indexer_noalloc_validates_before_launching():
+    """The allocation-free indexer refuses what ds4c_indexer_topk refuses, and
+    calls whose workspace would exceed its fixed scratch (DS4C_ECAP), before
+    any device call."""
+    def call(H=64, Dh=128, n=100, k=16, q=FAKE, rows=FAKE + 0x100000):
+        return B.lib().ds4c_indexer_topk_noalloc(q, FAKE + 0x300000, H, Dh, rows, n, k, FAKE + 0x400000,
+                                                 FAKE + 0x500000, None, None, None)
+    assert call(Dh=96) == B.DS4C_ESHAPE
+    assert call(H=68) == B.DS4C_ESHAPE
+    assert call(k=0) == B.DS4C_EINVAL
+    assert call(n=(1 << 20) + 1, k=512) == B.DS4C_ESHAPE
+    assert call(q=FAKE + 4) == B.DS4C_EINVAL
+    assert call(rows=0) == B.DS4C_EINVAL
+    assert call(n=0, rows=0) == B.DS4C_OK
+    # every call the workspace variant accepts at k = 512 fits the scratch ...
+    assert B.ds4c_indexer_workspace_bytes(1 << 20, 512) <= 4456448
+    # ... a longer call at a small k does not: 2,000,000 rows need 8 MB of scores
+    assert B.ds4c_indexer_workspace_bytes(2_000_000, 1) > 4456448
+    assert call(n=2_000_000, k=1) == B.DS4C_ECAP
