@@ -824,16 +824,20 @@ def main():
         pl_avg = sorted(pl)[len(pl) // 2] if pl else 0.0
         pl_gbs = pl_bytes / (pl_avg * 1e-3) / 1e9
         cold_gbs = {k: pl_bytes / (v * 1e-3) / 1e9 if v else 0.0 for k, v in cold.items()}
+        # The HBM fraction is the cold figure (the projection output read from
+        # HBM); the warm figure, whose reads partly hit the caches, is given
+        # beside it as such.
         out["plain_pool_roofline"] = {
-            "bound": "hbm", "achieved": pl_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": pl_gbs / PEAK_HBM_GBS,
+            "bound": "hbm", "achieved": cold_gbs[False], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": cold_gbs[False] / PEAK_HBM_GBS,
             "kernel": "pool_r4_kernel" if w.layer.ratio == 4 else "pool_r128_partial_kernel + pool_r128_finish_kernel",
-            "measured": f"median of {pl_cnt} calls of {T - 1} tokens from n0 = 1, warm (reads the projection "
-                        f"written just before)",
-            "avg_ms": pl_avg, "algorithmic_bytes": pl_bytes,
+            "measured": f"median of 21 calls of {T - 1} tokens from n0 = 1, cold: a 1 GiB buffer read between each "
+                        f"call's projection and pool launches (the caches hold clean lines)",
+            "avg_ms": cold[False], "algorithmic_bytes": pl_bytes,
             "traffic": read_traffic(args.workload, "plain_pool_hbm_bytes_per_launch"),
-            "cold": {"achieved": cold_gbs[False], "frac": cold_gbs[False] / PEAK_HBM_GBS, "avg_ms": cold[False],
-                     "measured": "median of 21 calls, a 1 GiB buffer read between each call's projection and "
-                                 "pool launches (the caches hold clean lines)"},
+            "cache_warm": {"achieved": pl_gbs, "avg_ms": pl_avg,
+                           "measured": f"median of {pl_cnt} calls, warm: the pool reads the projection written just "
+                                       f"before, partly from the caches (not an HBM figure)"},
             "cold_write_evict": {"achieved": cold_gbs[True], "frac": cold_gbs[True] / PEAK_HBM_GBS,
                                  "avg_ms": cold[True],
                                  "measured": "median of 21 calls, a 1 GiB buffer written between each call's "
