@@ -97,23 +97,37 @@ typedef struct ds4c_frontier {
   void *state;
 } ds4c_frontier;
 
-/* Bytes of device memory a layer's frontier needs: a 256-byte block reserved
- * for the library then, per lane, kv and score tensors of [coff*ratio, W]
- * float32. 0 if the layer descriptor is invalid. */
+/* Bytes of device memory a layer's frontier needs (Part 3 §2: the layer
+ * cache keeps attn_state_kv / attn_state_score and index_state_kv /
+ * index_state_score; Part 3 §5: a ratio-4 lane's state is 8 rows of width
+ * 2 * head_dim, a ratio-128 lane's 128 rows of head_dim): a 256-byte block
+ * reserved for the library then, per lane, kv and score tensors of
+ * [coff*ratio, W] float32.  0 if the layer descriptor is invalid. */
 size_t ds4c_frontier_bytes(const ds4c_layer *layer);
 
 /* Bytes of device workspace ds4c_compress_prefill needs for calls of up to
- * max_tokens tokens: the [T, N] float32 projection (N = 2 * sum of lane
- * widths; a short call that splits K over several ranges keeps up to
- * min(1024, 16 T) rows of partial sums, so T rows become max(T, min(1024,
- * 16 T))) plus per-row pooling scratch on ratio-128 layers.  0 if invalid. */
+ * max_tokens tokens (Part 3 §4: the kv and score projections of every token
+ * of the chunk, pooled per window): the [T, N] float32 projection (N = 2 *
+ * sum of lane widths; a short call that splits K over several ranges keeps
+ * up to min(1024, 16 T) rows of partial sums, so T rows become max(T,
+ * min(1024, 16 T))) plus per-row pooling scratch on ratio-128 layers, or the
+ * pooled rows and kept tokens of a call that pools in the projection, if
+ * larger.  0 if invalid.  Pure function of its arguments; no device call. */
 size_t ds4c_workspace_bytes(const ds4c_layer *layer, int64_t max_tokens);
 
-/* Bytes of the host blob ds4c_frontier_save writes for this layer. */
+/* Bytes of the host blob ds4c_frontier_save writes for this layer (Part 4
+ * §5-§7: the frontier tensors are saved with the counters so a restored
+ * session continues mid-window): the 56-byte header, then each lane's kv and
+ * score tensors.  0 if the layer descriptor is invalid. */
 size_t ds4c_frontier_blob_bytes(const ds4c_layer *layer);
 
-/* Empty state (every kv 0, every score -inf, control block 0) and counters
- * 0.  Enqueued on `stream` as a fill kernel (no memset). */
+/* Empty state and counters 0 (Part 3 §4: the pool weighs entries by
+ * exp(score - max) and returns 0 when the weights sum to 0, so an empty row
+ * is kv 0 with score -inf: it takes no weight, and a window with no token
+ * yet pools to 0): every kv 0, every score -inf, the control block 0.
+ * Enqueued on `stream` as a fill kernel (no memset).  DS4C_EINVAL for a bad
+ * descriptor or frontier (nothing enqueued), DS4C_EDEVICE on a launch
+ * failure.  Call it once before a frontier's first use. */
 int ds4c_frontier_init(const ds4c_layer *layer, ds4c_frontier *frontier, void *stream);
 
 /* Compress a chunk of T tokens x [T, hidden] (in_dtype, row-major) at
@@ -340,7 +354,10 @@ int ds4c_layer_ratio(int variant, int layer);
  * prompt is longer than 4096 tokens, else the prompt length (at least 1). */
 int64_t ds4c_prefill_chunk_cap(int64_t prompt_len, int64_t override_cap);
 
-/* Static description of a status code; never NULL. */
+/* Static description of a status code (Part 3 §1: the engine refuses to run
+ * with a shape or layout it does not expect rather than guess; the codes name
+ * which check refused a call); never NULL, also for codes the library does
+ * not define. */
 const char *ds4c_status_str(int status);
 
 /* Kernel timing.  While enabled, every kernel of a selected class that the
