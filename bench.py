@@ -26,7 +26,7 @@ timed region; `roofline` describes the kernel class that takes the most time
 there (the decode GEMV for stack32_long), the other of the two is given
 beside it.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
   python bench.py --copy-mib N     plain device copy of N MiB (counter calibration)
 """
 
@@ -546,6 +546,8 @@ def main():
                     choices=["r4_flash", "r128_flash", "stack32", "stack32_long", "stack32_pro", "indexer_c5",
                              "mixed_attn_c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time every step eagerly, without HIP graph capture (for profiler counter passes)")
     ap.add_argument("--copy-mib", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -653,7 +655,9 @@ def main():
     el_eager = sum(a.elapsed_time(b) for a, b in evs) * 1e-3
     ms, cnt = B.ds4c_profile_read()
     B.ds4c_profile_enable(False)
-    if w.layer is not None:
+    if args.eager:
+        el_graph = None
+    elif w.layer is not None:
         el_graph = graph_timing(w, L, reinit, work, step, steps)
     elif Td:
         el_graph = decode_graph_timing(stack, layers, x, T, Td, chunk, reinit, steps)
