@@ -518,22 +518,26 @@ def decode_graph_timing(stack, layers, x, T, Td, chunk, reinit, steps):
         torch.cuda.synchronize()
         print(f"graph capture unavailable ({e}); eager timing kept", file=sys.stderr)
         return None
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for ev_a, ev_b in evs:
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    for ev_a, ev_m, ev_b in evs:
         reinit()
         ev_a.record()
         stack.prefill(x[:T], chunk_cap=chunk)
+        ev_m.record()
         g.replay()
         ev_b.record()
     torch.cuda.synchronize()
     ok = same(ref)
-    el = sum(a.elapsed_time(b) for a, b in evs) * 1e-3
+    el = sum(a.elapsed_time(b) for a, _, b in evs) * 1e-3
+    el_pre = sum(a.elapsed_time(m) for a, m, _ in evs) * 1e-3
     reinit()
     torch.cuda.synchronize()
     if not ok:
         print("timed decode graph replays differ from the eager steps; eager timing kept", file=sys.stderr)
         return None
-    GRAPH_FIGURES.update({"graph_decode_steps": Td, "graph_ms_per_step": el / steps * 1e3})
+    GRAPH_FIGURES.update({"graph_decode_steps": Td, "graph_ms_per_step": el / steps * 1e3,
+                          "prefill_ms_per_step": el_pre / steps * 1e3,
+                          "decode_us_per_token": (el - el_pre) / steps / Td * 1e6})
     return el
 
 

@@ -88,6 +88,26 @@ __device__ __forceinline__ void load_vec(float (&v)[DPL], const float* __restric
   }
 }
 
+// The same load with the nontemporal hint, for data read exactly once (the
+// projection rows a plain pool consumes).
+template <int DPL>
+__device__ __forceinline__ void load_vec_stream(float (&v)[DPL], const float* __restrict__ p) {
+  if constexpr (DPL == 1) {
+    v[0] = __builtin_nontemporal_load(p);
+  } else if constexpr (DPL == 2) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 t = __builtin_nontemporal_load(reinterpret_cast<const f2*>(p));
+    v[0] = t.x; v[1] = t.y;
+  } else {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < DPL; i += 4) {
+      const f4 t = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p + i));
+      v[i] = t.x; v[i + 1] = t.y; v[i + 2] = t.z; v[i + 3] = t.w;
+    }
+  }
+}
+
 template <int DPL>
 __device__ __forceinline__ void store_vec(float* __restrict__ p, const float (&v)[DPL]) {
   if constexpr (DPL == 1) {

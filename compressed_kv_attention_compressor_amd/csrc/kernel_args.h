@@ -97,15 +97,22 @@ struct GemvTarget {
   int col0;             // first output column of the block
 };
 
+// The decode GEMV's own arguments: the token's column blocks resolved on the
+// host (blocks are ordered attention kv, attention score, indexer kv, indexer
+// score; unused blocks have col0 = N).
+struct GemvArgs {
+  const void* x;        // [K]
+  int K;
+  int N;
+  GemvTarget tgt[4];
+};
+
 struct DecodeArgs {
   const void* x;        // [K]
   int K;
   int N;
   int n_seg;
   ProjSeg seg[4];
-  // Column block s resolved for this token on the host (blocks are ordered
-  // attention kv, attention score, indexer kv, indexer score):
-  GemvTarget tgt[4];
   int64_t pos;
   int ratio;
   int n_rot;

@@ -49,8 +49,8 @@ __device__ __forceinline__ void fetch_token(const PoolArgs& a, const LaneDev& L,
     return;
   }
   const float* src = a.proj + (p - a.n0) * a.ld;
-  load_vec<DPL>(kv, src + L.kv_col + c);
-  load_vec<DPL>(sc, src + L.sc_col + c);
+  load_vec_stream<DPL>(kv, src + L.kv_col + c);
+  load_vec_stream<DPL>(sc, src + L.sc_col + c);
   float ape[DPL];
   load_vec<DPL>(ape, L.ape + pr * L.W + c);
 #pragma unroll
