@@ -29,9 +29,15 @@ COMMON = [
 ]
 
 
+# Per-source flags.  decode.hip: leading scalar kernel arguments (up to 16
+# dwords) are preloaded into scalar registers by the dispatch, so a decode
+# GEMV starts its weight loads without an argument load from memory.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+
+
 def _compile(src: str, obj_dir: str) -> str:
     obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -14,6 +14,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <climits>
+#include <cstddef>
 
 #include "device_common.h"
 #include "launch.h"
@@ -82,14 +84,15 @@ __device__ __forceinline__ uint4 load_global(const Tin* p) {
 // loaded (x straight from global memory, where it stays cache-resident for
 // the whole grid) before any of them is used.  Steps past the range load a
 // clamped in-range address and are zeroed, so the body has no branches.
-template <typename Tin, int U>
+// mid() runs after the first loads are issued and before any is used.
+template <typename Tin, int U, typename Mid>
 __device__ __forceinline__ void wave_dot2(const Tin* __restrict__ w0, const Tin* __restrict__ w1,
                                           const Tin* __restrict__ x, int k0, int kr, int lane, float* d0,
-                                          float* d1) {
+                                          float* d1, Mid&& mid) {
   constexpr int kVec = 16 / (int)sizeof(Tin), kSpan = kWave * kVec;
   const int kend = k0 + kr;
   float a0 = 0.f, a1 = 0.f;
-  if (kr == kSpan * U) {  // the usual case (hidden 4096 bf16): one pass, nothing to mask
+  if (kr == kSpan * U) {  // the usual shape (hidden 4096 bf16): one pass, nothing to mask
     uint4 xv[U], u[U], v[U];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
@@ -98,6 +101,9 @@ __device__ __forceinline__ void wave_dot2(const Tin* __restrict__ w0, const Tin*
       u[i] = load_stream(w0 + k);
       v[i] = load_stream(w1 + k);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    mid();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       a0 = dot16(u[i], xv[i], a0, Tin{});
@@ -107,6 +113,7 @@ __device__ __forceinline__ void wave_dot2(const Tin* __restrict__ w0, const Tin*
     *d1 = wave_sum(a1);
     return;
   }
+  mid();
   for (int kb = k0; kb < kend; kb += kSpan * U) {
     uint4 xv[U], u[U], v[U];
 #pragma unroll
@@ -129,58 +136,64 @@ __device__ __forceinline__ void wave_dot2(const Tin* __restrict__ w0, const Tin*
   *d1 = wave_sum(a1);
 }
 
+// The decode GEMV's argument segment, laid out as its parameter list (the
+// kernel reads the store targets from it by offset).
+struct GemvKernargs {
+  const void* x;
+  const void* w[4];
+  const float* ape_a;
+  unsigned kc;
+  int ape_i_off;
+  GemvStore st;
+};
+
 // Projection of one token into its frontier row.  Workgroup b covers
 // columns [2b, 2b+2); both lie in one column block (blocks have even sizes).
-// Every argument field is loaded in one round and the block chosen by
-// selects: the weight loads start after a single argument round trip.
-template <typename Tin, int U>
-__global__ void __launch_bounds__(kDecThreads) decode_gemv_kernel(GemvArgs a) {
+// Every argument before `st` (14 dwords) arrives preloaded in scalar
+// registers: the workgroup picks its block with scalar selects and issues
+// its weight, x and APE loads at once, without waiting on memory for an
+// argument; the frontier row it stores to is read from `st` meanwhile.
+// kc = K/64 | c1/64 << 10 | c2/64 << 17 | c3/64 << 24: block s starts at
+// output column c_s (c_0 = 0; unused blocks start at N).  ape_a: the
+// attention lane's APE row for this token (score block 1); the indexer
+// lane's (score block 3) is ape_a + ape_i_off, or st.ape_i in the FAR form
+// (used when the two rows are not within 2^31 floats of each other).
+template <typename Tin, int U, bool FAR>
+__global__ void __launch_bounds__(kDecThreads)
+    decode_gemv_kernel(const void* x_, const void* w0_, const void* w1_, const void* w2_, const void* w3_,
+                       const float* ape_a, unsigned kc, int ape_i_off, GemvStore st) {
   __shared__ float s_part[kDecWaves][kColsPerBlock];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int K = (int)(kc & 1023u) * 64, c1 = (int)((kc >> 10) & 127u) * 64, c2 = (int)((kc >> 17) & 127u) * 64,
+            c3 = (int)(kc >> 24) * 64;
   const int c0 = blockIdx.x * kColsPerBlock;  // the grid covers N exactly
-  int K = a.K;
-  const Tin* x = reinterpret_cast<const Tin*>(a.x);
-  const void* w[4];
-  float* dst[4];
-  const float* ape[4];
-  int col0[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    w[s] = a.tgt[s].w;
-    dst[s] = a.tgt[s].dst;
-    ape[s] = a.tgt[s].ape;
-    col0[s] = a.tgt[s].col0;
-  }
-  // One empty statement that takes every field in scalar registers: the
-  // fields are loaded together before it, and the selects below stay
-  // selects instead of becoming dependent argument loads.
-  asm volatile(""
-               : "+s"(K), "+s"(x), "+s"(w[0]), "+s"(w[1]), "+s"(w[2]), "+s"(w[3]), "+s"(dst[0]), "+s"(dst[1]),
-                 "+s"(dst[2]), "+s"(dst[3]), "+s"(ape[0]), "+s"(ape[1]), "+s"(ape[2]), "+s"(ape[3]), "+s"(col0[0]),
-                 "+s"(col0[1]), "+s"(col0[2]), "+s"(col0[3]));
-  int sg = 0;
-#pragma unroll
-  for (int s = 1; s < 4; ++s) sg = c0 >= col0[s] ? s : sg;
-  const void* ws = w[0];
-  float* ds = dst[0];
-  const float* as = ape[0];
-  int cs = col0[0];
-#pragma unroll
-  for (int s = 1; s < 4; ++s)
-    if (sg == s) { ws = w[s]; ds = dst[s]; as = ape[s]; cs = col0[s]; }
-  const int j = c0 - cs;
+  const int sg = c0 >= c3 ? 3 : c0 >= c2 ? 2 : c0 >= c1 ? 1 : 0;
+  const void* ws = sg == 3 ? w3_ : sg == 2 ? w2_ : sg == 1 ? w1_ : w0_;
+  const int j = c0 - (sg == 3 ? c3 : sg == 2 ? c2 : sg == 1 ? c1 : 0);
+  const float* as = sg == 1 ? ape_a : sg == 3 ? (FAR ? st.ape_i : ape_a + ape_i_off) : nullptr;
   const Tin* w0 = reinterpret_cast<const Tin*>(ws) + (int64_t)j * K;
+  const Tin* x = reinterpret_cast<const Tin*>(x_);
+  const int kr = K / kDecWaves;  // K is a multiple of 64, so kr is a whole number of 16-byte steps
   // The APE pair is read with a vector load (a zero offset the compiler
-  // cannot see through), so no scalar load waits on global memory before
-  // the weight loads issue.
+  // cannot see through), issued with the weight loads.
+  typedef float f2 __attribute__((ext_vector_type(2)));
   int zero;
   asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-  typedef float f2 __attribute__((ext_vector_type(2)));
   const f2 add = (as && wave == 0) ? *gptr<f2>(as + j + zero) : f2{0.f, 0.f};
-  const int kr = K / kDecWaves;  // K is a multiple of 64, so kr is a whole number of 16-byte steps
+  // The store target is read from the argument segment after the weight
+  // loads are issued and waited for there, while they are in flight: the
+  // scalar load and its wait sit in one statement, so the compiler can
+  // neither hoist the load nor place its wait ahead of the weight loads.
+  float* ds = nullptr;
+  auto mid = [&]() {
+    const __attribute__((address_space(4))) char* p =
+        (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr() +
+        offsetof(GemvKernargs, st) + offsetof(GemvStore, dst) + sizeof(float*) * sg;
+    asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(ds) : "s"(p) : "memory");
+  };
   float v0, v1;
-  wave_dot2<Tin, U>(w0, w0 + K, x, wave * kr, kr, lane, &v0, &v1);
+  wave_dot2<Tin, U>(w0, w0 + K, x, wave * kr, kr, lane, &v0, &v1, mid);
   if (lane == 0) {
     s_part[wave][0] = v0;
     s_part[wave][1] = v1;
@@ -194,17 +207,33 @@ __global__ void __launch_bounds__(kDecThreads) decode_gemv_kernel(GemvArgs a) {
   }
 }
 
+struct GemvLaunch {
+  const void* x;
+  const void* w[4];
+  unsigned kc;
+  const float* ape_a;
+  int ape_i_off;
+  bool far;  // the indexer APE row is read from st (not within 2^31 floats of the attention row)
+  GemvStore st;
+};
+
 template <typename Tin>
-void launch_gemv(const GemvArgs& g, unsigned grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+void launch_gemv(const GemvLaunch& g, int K, unsigned grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   // Spans of 64 16-byte steps in a wave's quarter of K, all loaded at once
   // (up to 8; longer quarters loop).
   constexpr int kSpan = kWave * (16 / (int)sizeof(Tin));
-  const int spans = (g.K / kDecWaves + kSpan - 1) / kSpan;
+  const int spans = (K / kDecWaves + kSpan - 1) / kSpan;
   const dim3 gr(grid), bl(kDecThreads);
-  if (spans <= 1) hipExtLaunchKernelGGL((decode_gemv_kernel<Tin, 1>), gr, bl, 0, s, start, stop, 0, g);
-  else if (spans <= 2) hipExtLaunchKernelGGL((decode_gemv_kernel<Tin, 2>), gr, bl, 0, s, start, stop, 0, g);
-  else if (spans <= 4) hipExtLaunchKernelGGL((decode_gemv_kernel<Tin, 4>), gr, bl, 0, s, start, stop, 0, g);
-  else hipExtLaunchKernelGGL((decode_gemv_kernel<Tin, 8>), gr, bl, 0, s, start, stop, 0, g);
+#define DS4C_GEMV(U)                                                                                        \
+  (g.far ? hipExtLaunchKernelGGL((decode_gemv_kernel<Tin, U, true>), gr, bl, 0, s, start, stop, 0, g.x, g.w[0],  \
+                                 g.w[1], g.w[2], g.w[3], g.ape_a, g.kc, g.ape_i_off, g.st)                   \
+         : hipExtLaunchKernelGGL((decode_gemv_kernel<Tin, U, false>), gr, bl, 0, s, start, stop, 0, g.x, g.w[0], \
+                                 g.w[1], g.w[2], g.w[3], g.ape_a, g.kc, g.ape_i_off, g.st))
+  if (spans <= 1) DS4C_GEMV(1);
+  else if (spans <= 2) DS4C_GEMV(2);
+  else if (spans <= 4) DS4C_GEMV(4);
+  else DS4C_GEMV(8);
+#undef DS4C_GEMV
 }
 
 // One thread's share of a ratio-4 boundary for dims [d0, d0+DPL) of lane L:
@@ -360,28 +389,37 @@ hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, 
                          const Timing& tm_pool) {
   const bool boundary = (a.pos + 1) % a.ratio == 0;
   const unsigned grid = (unsigned)((a.N + kColsPerBlock - 1) / kColsPerBlock);
-  GemvArgs g{};
+  // The packed argument holds K/64 in 10 bits and each block's first
+  // column/64 in 7 bits (K and the block sizes are multiples of 64).
+  if (a.K % 64 || a.K / 64 > 1023 || a.N % 64 || a.N / 64 > 127) return hipErrorInvalidValue;
+  GemvLaunch g{};
   g.x = a.x;
-  g.K = a.K;
-  g.N = a.N;
   const int pr = (int)(a.pos % a.ratio), slot = (a.ratio == 4 ? 4 : 0) + pr;
+  unsigned c[4] = {0u, (unsigned)a.N, (unsigned)a.N, (unsigned)a.N};  // unused blocks start at N
+  const float* ape[2] = {nullptr, nullptr};
   for (int s = 0; s < 4; ++s) {
-    if (s >= a.n_seg) {  // unused block: never selected (c0 < N = col0)
-      g.tgt[s] = g.tgt[0];
-      g.tgt[s].col0 = a.N;
+    if (s >= a.n_seg) {  // unused block: never selected
+      g.w[s] = a.seg[0].w;
       continue;
     }
     const LaneDev& L = a.lane[s >> 1];
-    const bool score = (s & 1) != 0;
-    g.tgt[s].w = a.seg[s].w;
-    g.tgt[s].dst = (score ? L.fr_sc : L.fr_kv) + (int64_t)slot * L.W;
-    g.tgt[s].ape = score ? L.ape + (int64_t)pr * L.W : nullptr;
-    g.tgt[s].col0 = a.seg[s].col0;
+    g.w[s] = a.seg[s].w;
+    c[s] = (unsigned)a.seg[s].col0;
+    g.st.dst[s] = ((s & 1) ? L.fr_sc : L.fr_kv) + (int64_t)slot * L.W;
+    if (s & 1) ape[s >> 1] = L.ape + (int64_t)pr * L.W;
+  }
+  g.kc = (unsigned)a.K / 64 | c[1] / 64 << 10 | c[2] / 64 << 17 | c[3] / 64 << 24;
+  g.ape_a = ape[0];
+  g.st.ape_i = ape[1];
+  if (ape[1]) {
+    const int64_t off = ape[1] - ape[0];
+    g.far = off < INT_MIN || off > INT_MAX;
+    g.ape_i_off = g.far ? 0 : (int)off;
   }
   if (in_dtype == 1)
-    launch_gemv<uint16_t>(g, grid, stream, tm.start, tm.stop);
+    launch_gemv<uint16_t>(g, a.K, grid, stream, tm.start, tm.stop);
   else
-    launch_gemv<float>(g, grid, stream, tm.start, tm.stop);
+    launch_gemv<float>(g, a.K, grid, stream, tm.start, tm.stop);
   if (boundary) {
     if (a.ratio == 4) {
       // Attention rows split over waves as in prefill: two waves of 256 dims

@@ -89,22 +89,16 @@ struct PoolArgs {
   int64_t carry_lo;
 };
 
-// Where a decode column block goes for the current token.
-struct GemvTarget {
-  const void* w;        // weights [n, K] of the block
-  float* dst;           // frontier row (coff-1)*ratio + pos%ratio, at the block's first dim
-  const float* ape;     // APE row pos%ratio at the block's first dim (score blocks), else null
-  int col0;             // first output column of the block
-};
-
-// The decode GEMV's own arguments: the token's column blocks resolved on the
-// host (blocks are ordered attention kv, attention score, indexer kv, indexer
-// score; unused blocks have col0 = N).
-struct GemvArgs {
-  const void* x;        // [K]
-  int K;
-  int N;
-  GemvTarget tgt[4];
+// The decode GEMV's arguments.  What a workgroup needs before its loads is
+// passed as leading scalar kernel arguments, which the dispatch preloads
+// into scalar registers (no argument load from memory before the weight
+// loads); the frontier rows the results go to are read from this struct
+// while the weights stream.  The token's column blocks are resolved on the
+// host (blocks are ordered attention kv, attention score, indexer kv,
+// indexer score).
+struct GemvStore {
+  float* dst[4];        // frontier row (coff-1)*ratio + pos%ratio, at the block's first dim
+  const float* ape_i;   // indexer lane's APE row, used when it is not within 2^31 floats of the attention lane's
 };
 
 struct DecodeArgs {
