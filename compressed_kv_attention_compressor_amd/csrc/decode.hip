@@ -269,19 +269,29 @@ __device__ __forceinline__ void r4_pool_and_shift(const LaneDev& L, int d0, floa
 // Ratio-4 window boundary on one workgroup of SA + 1 waves: SA attention
 // waves (DPLA dims per lane) and one indexer wave (DPLI per lane) pool and
 // shift their dims in one pass of loads, then finish the row (the attention
-// row's sum of squares meets in LDS).
+// row's sum of squares meets in LDS).  The frontier and norm pointers and
+// dims = D_attn | D_index << 16 (0 without an indexer lane) arrive
+// preloaded in scalar registers, so the frontier loads issue at once; the
+// rest of the token's arguments (row outputs, position, constants) is read
+// from `a` meanwhile.
 template <int SA, int DPLA, int DPLI>
-__global__ void __launch_bounds__(64 * (SA + 1)) decode_r4_finish_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(64 * (SA + 1))
+    decode_r4_finish_kernel(float* kv0, float* sc0, float* kv1, float* sc1, const float* nw0, const float* nw1,
+                            unsigned dims, DecodeArgs a) {
   __shared__ float s_ss[SA];
-  // Wave-uniform lane selection: each wave reads its lane's fields in the
-  // same round of argument loads as the rest.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-  const LaneDev& L = a.lane[wave < SA ? 0 : 1];
-  const int64_t k = a.pos / 4;
-  if (wave < SA) {
+  const bool att = wave < SA;
+  const int d_idx = (int)(dims >> 16);
+  LaneDev L{};  // the fields the pool and the finish read
+  L.fr_kv = att ? kv0 : kv1;
+  L.fr_sc = att ? sc0 : sc1;
+  L.D = att ? (int)(dims & 0xffffu) : d_idx;
+  L.W = 2 * L.D;
+  L.is_index = att ? 0 : 1;
+  if (att) {
     const int d0 = wave * (kWave * DPLA) + lane * DPLA;
     float nw[DPLA], o[DPLA];
-    load_vec<DPLA>(nw, L.norm_w + d0);
+    load_vec<DPLA>(nw, nw0 + d0);
     r4_pool_and_shift<DPLA>(L, d0, o);
     const float ss = wave_sum(row_sumsq<DPLA>(o));
     if (lane == 0) s_ss[wave] = ss;
@@ -289,17 +299,21 @@ __global__ void __launch_bounds__(64 * (SA + 1)) decode_r4_finish_kernel(DecodeA
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < SA; ++w) tot += s_ss[w];
-    finish_row_part<DPLA>(o, nw, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, L.prequant,
-                          L.rows + k * L.D, lane);
+    const int64_t k = a.pos / 4;
+    finish_row_part<DPLA>(o, nw, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, a.lane[0].prequant,
+                          a.lane[0].rows + k * L.D, lane);
   } else {
     float nw[DPLI], o[DPLI];
-    if (a.n_lanes > 1) {
-      load_vec<DPLI>(nw, L.norm_w + lane * DPLI);
+    if (d_idx > 0) {
+      load_vec<DPLI>(nw, nw1 + lane * DPLI);
       r4_pool_and_shift<DPLI>(L, lane * DPLI, o);
     }
     __syncthreads();
-    if (a.n_lanes > 1)
-      finish_row_wave<DPLI>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, L.prequant, L.rows + k * L.D, lane);
+    if (d_idx > 0) {
+      const int64_t k = a.pos / 4;
+      finish_row_wave<DPLI>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, a.lane[1].prequant,
+                            a.lane[1].rows + k * L.D, lane);
+    }
   }
 }
 
@@ -375,12 +389,20 @@ __global__ void __launch_bounds__(kWave) decode_r128_finish_kernel(DecodeArgs a)
 template <int SA, int DPLA>
 void launch_r4_fin(const DecodeArgs& a, int dpli, hipStream_t s, const Timing& tm) {
   const dim3 g(1), b(64 * (SA + 1));
+  const LaneDev& A = a.lane[0];
+  const bool idx = a.n_lanes > 1;
+  const LaneDev& I = a.lane[idx ? 1 : 0];
+  const unsigned dims = (unsigned)A.D | (idx ? (unsigned)I.D << 16 : 0u);
+#define DS4C_R4FIN(P)                                                                                          \
+  hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, P>), g, b, 0, s, tm.start, tm.stop, 0, A.fr_kv, A.fr_sc, \
+                        I.fr_kv, I.fr_sc, A.norm_w, I.norm_w, dims, a)
   switch (dpli) {
-    case 1: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 1>), g, b, 0, s, tm.start, tm.stop, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 2>), g, b, 0, s, tm.start, tm.stop, 0, a); break;
-    case 4: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 4>), g, b, 0, s, tm.start, tm.stop, 0, a); break;
-    default: hipExtLaunchKernelGGL((decode_r4_finish_kernel<SA, DPLA, 8>), g, b, 0, s, tm.start, tm.stop, 0, a); break;
+    case 1: DS4C_R4FIN(1); break;
+    case 2: DS4C_R4FIN(2); break;
+    case 4: DS4C_R4FIN(4); break;
+    default: DS4C_R4FIN(8); break;
   }
+#undef DS4C_R4FIN
 }
 
 }  // namespace
