@@ -412,7 +412,9 @@ hipError_t launch_decode(const DecodeArgs& a, int in_dtype, hipStream_t stream, 
   const bool boundary = (a.pos + 1) % a.ratio == 0;
   const unsigned grid = (unsigned)((a.N + kColsPerBlock - 1) / kColsPerBlock);
   // The packed argument holds K/64 in 10 bits and each block's first
-  // column/64 in 7 bits (K and the block sizes are multiples of 64).
+  // column/64 in 7 bits (K and the block sizes are multiples of 64).  Layers
+  // that pass the descriptor checks (hidden <= 16384, head_dim <= 512, so
+  // N <= 4096) are always inside these limits; this is a guard only.
   if (a.K % 64 || a.K / 64 > 1023 || a.N % 64 || a.N / 64 > 127) return hipErrorInvalidValue;
   GemvLaunch g{};
   g.x = a.x;
