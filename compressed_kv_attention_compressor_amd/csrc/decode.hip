@@ -84,7 +84,8 @@ __device__ __forceinline__ uint4 load_global(const Tin* p) {
 // loaded (x straight from global memory, where it stays cache-resident for
 // the whole grid) before any of them is used.  Steps past the range load a
 // clamped in-range address and are zeroed, so the body has no branches.
-// mid() runs after the first loads are issued and before any is used.
+// mid() runs before any load is used: in the single-pass form after all of
+// the loads are issued, in the looped form before the loop.
 template <typename Tin, int U, typename Mid>
 __device__ __forceinline__ void wave_dot2(const Tin* __restrict__ w0, const Tin* __restrict__ w1,
                                           const Tin* __restrict__ x, int k0, int kr, int lane, float* d0,
