@@ -160,6 +160,12 @@ class CompressorStack:
         self._ws: Optional[torch.Tensor] = None
         self._ws_chunk = 0
 
+    def _check_x(self, x: torch.Tensor, n: int) -> None:
+        """The library reads x as n rows of the layers' input dtype and width."""
+        L0 = next(L for L in self.layers if L is not None)
+        assert x.dtype == L0.tdtype and x.is_contiguous() and x.device == L0.device, "x: dtype, layout or device"
+        assert x.numel() == n * L0.hidden, "x: shape"
+
     def _arrays(self):
         ar = [L.rows["attn"].data_ptr() if L else 0 for L in self.layers]
         ac = [L.cap if L else 0 for L in self.layers]
@@ -186,6 +192,7 @@ class CompressorStack:
 
     def prefill(self, x: torch.Tensor, chunk_cap: int = 0) -> None:
         T = x.shape[0]
+        self._check_x(x, T)
         chunk = chunk_cap if chunk_cap > 0 else B.ds4c_prefill_chunk_cap(T, 0)
         self.reserve(min(chunk, max(T, 1)))
         self._push()
@@ -212,6 +219,7 @@ class CompressorStack:
             self._pull()
 
     def decode_one(self, x: torch.Tensor) -> None:
+        self._check_x(x, 1)
         self._push()
         ar, ac, ir, ic = self._arrays()
         try:
@@ -222,7 +230,8 @@ class CompressorStack:
 
     def decode(self, x: torch.Tensor) -> None:
         """x [n, hidden]: n single-token decode steps through the stack, in the library."""
-        assert x.dim() == 2 and x.is_contiguous()
+        assert x.dim() == 2
+        self._check_x(x, x.shape[0])
         self._push()
         ar, ac, ir, ic = self._arrays()
         try:
