@@ -163,7 +163,8 @@ class CompressorStack:
     def _check_x(self, x: torch.Tensor, n: int) -> None:
         """The library reads x as n rows of the layers' input dtype and width."""
         L0 = next(L for L in self.layers if L is not None)
-        assert x.dtype == L0.tdtype and x.is_contiguous() and x.device == L0.device, "x: dtype, layout or device"
+        assert x.dtype == L0.tdtype and x.is_contiguous() and x.device.type == L0.device.type, \
+            "x: dtype, layout or device"
         assert x.numel() == n * L0.hidden, "x: shape"
 
     def _arrays(self):
