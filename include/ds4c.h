@@ -37,10 +37,10 @@
  *     enqueue kernel launches only (no memset or copy nodes), so with kernel
  *     timing and cache eviction off (ds4c_profile_enable(0), no
  *     ds4c_profile_evict buffer) they may be recorded under HIP stream
- *     capture.  A captured sequence replays at the
- *     positions and buffers it was recorded with: the host counters advance
- *     at capture, not at replay, so before each replay the caller puts the
- *     frontier's device state back where it stood at capture.
+ *     capture.  A captured sequence replays at the positions and buffers
+ *     it was recorded with: the host counters advance at capture, not at
+ *     replay, so before each replay the caller puts the frontier's device
+ *     state back where it stood at capture.
  *   - Little-endian hosts only (the frontier blob is little-endian).
  *   - No C++ exception crosses this interface.
  */
