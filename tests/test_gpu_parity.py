@@ -157,6 +157,38 @@ def test_chunked_and_decode(name, plan):
     compare_all(shape, g, spec, st, n)
 
 
+def random_plan(seed, n_calls=10):
+    """A seeded mix of call kinds: short prefills (1-7 tokens), ragged ones
+    (8-599), runs of single decode steps, and window-multiple lengths (4,
+    128, 256, 1100: on a window boundary these take the fused paths, which
+    need more than 1024 tokens at ratio 4 and more than 256 at ratio 128)."""
+    rng = np.random.default_rng(seed)
+    plan = []
+    for _ in range(n_calls):
+        kind = int(rng.integers(0, 4))
+        if kind == 0:
+            plan.append(int(rng.integers(1, 8)))
+        elif kind == 1:
+            plan.append(int(rng.integers(8, 600)))
+        elif kind == 2:
+            plan.append(-int(rng.integers(1, 10)))
+        else:
+            plan.append(int(rng.choice([4, 128, 256, 1100])))
+    return plan
+
+
+@pytest.mark.parametrize("seed", [11, 12, 13])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_random_chunk_plans(name, seed):
+    plan = random_plan(1000 * list(SMALL).index(name) + seed)
+    n = sum(abs(s) for s in plan)
+    _say(f"[parity] {name} random plan {plan} n={n}")
+    shape, p, x = _small(name, n, seed=seed)
+    g = run_gpu(shape, p, x, plan)
+    spec, st = run_oracle(shape, p, x)
+    compare_all(shape, g, spec, st, n)
+
+
 # The largest hidden size the boundary accepts (16384), and fp32 at 4096:
 # decode dot products then run over several unrolled chunks, the prefill
 # GEMM over its longest K loop.
