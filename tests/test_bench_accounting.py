@@ -50,3 +50,14 @@ def test_decode_gemv_bytes_per_token():
     assert bench.decode_gemv_bytes(shapes) == 440_401_920
     assert bench.decode_gemv_bytes([(0, R4)]) == 20_971_520
     assert bench.decode_gemv_bytes([(0, R128)]) == 8_388_608
+
+
+def test_more_than_one_gpu_is_refused():
+    # One GPU is measured; asking for more exits non-zero with a message and
+    # prints no result line.
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
+    assert '"metric"' not in r.stdout
