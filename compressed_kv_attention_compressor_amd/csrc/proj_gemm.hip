@@ -47,6 +47,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
+typedef float f32x4 __attribute__((ext_vector_type(4)));     // four fp32 partial sums
 
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
@@ -98,11 +99,15 @@ __device__ __forceinline__ void load_lds16(const void* base, int bytes, __attrib
 
 
 
-// LDS index of element (row, col) of a 128 x 128 fp32 tile: rotated by 32
-// columns on odd 4-row groups so that the two half-waves of an accumulator
-// store (rows r and r + 4) hit different banks.
+// LDS index of element (row, col) of a 128 x 128 fp32 tile, column-major:
+// a column's 128 rows are 32 groups of 4 consecutive rows (16 bytes), group
+// G at slot (G & 16) | ((G ^ 2 col ^ col / 8 ^ G / 16) mod 16).  Both the
+// accumulator stores (one group of 16 consecutive columns) and the pool's
+// reads (8 groups of 2 adjacent columns) then touch 16 different bank groups
+// per 16 lanes.
 __device__ __forceinline__ int tile128_ix(int row, int col) {
-  return row * 128 + ((col + (((row >> 2) & 1) << 5)) & 127);
+  const int g = row >> 2;
+  return col * 128 + (((g ^ (col << 1) ^ (col >> 3) ^ (g >> 4)) & 15) | (g & 16)) * 4 + (row & 3);
 }
 
 template <typename Tin, int BM, int BN, int WM, int WN>
@@ -298,18 +303,22 @@ __global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int til
 // ---------------------------------------------------------------------------
 // Fused ratio-4 epilogue (Part 3 §4-§5) of a 256-token x 40-dim tile (see
 // FuseArgs for the column runs).  The two wave groups' partial sums meet in
-// an LDS copy of the tile; then each (window, dim) of the tile is pooled:
+// an LDS copy of the tile (column-major, below); then each (window, dim) of
+// the tile is pooled:
 // window g >= 1 of the tile from its own rows as one 8-entry softmax, window
 // 0's current half and the next tile's window 0 previous half as (max, sum,
 // weighted sum) partials.  The tokens the frontier keeps are staged in the
 // plain column layout with APE added to their scores.
 // ---------------------------------------------------------------------------
-// LDS index of tile element (row, col): 160-float rows, rotated by 32
-// columns on odd 4-row groups so that the two half-waves of an accumulator
-// store (rows r and r + 4) hit different banks.
+// LDS index of tile element (row, col), column-major: a column's 256 rows
+// are 64 groups of 4 consecutive rows (16 bytes each); group G sits at slot
+// G with its low four bits XORed with col % 16.  An accumulator store (one
+// 4-row group of 16 consecutive columns per 16 lanes) then touches 16
+// different bank groups, and the pool's reads (one group of each of its
+// dims' columns) at most two lanes per bank group; both move 16 bytes per
+// lane per instruction.
 __device__ __forceinline__ int tile_ix(int row, int col) {
-  const int c = col + (((row >> 2) & 1) << 5);
-  return row * 160 + (c < 160 ? c : c - 160);
+  return col * 256 + ((((row >> 2) ^ col) & 15) | ((row >> 2) & ~15)) * 4 + (row & 3);
 }
 
 // e^(s - m) as 2^(s*log2(e) - m*log2(e)) with ml = m*log2(e): one FMA and
@@ -391,7 +400,9 @@ __device__ __forceinline__ void fused_r4_epilogue(const ProjArgs& a, f32x16 (&ac
   // block into the tile.  Each element takes exactly one addition, so the
   // result does not depend on which group owns it.
   // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4.
-  constexpr int kPark = 4 * FN * 16 * 64;  // floats parked per group
+  // Parked in 16-byte chunks (four consecutive v), lane-major.
+  f32x4* tile4 = reinterpret_cast<f32x4*>(tile);
+  constexpr int kPark4 = 4 * FN * 4 * 64;  // chunks parked per group
   asm volatile("s_barrier" ::: "memory");  // every wave is done with the ring the tile overlaps
 #pragma unroll
   for (int fm = 0; fm < 2; ++fm) {
@@ -399,7 +410,9 @@ __device__ __forceinline__ void fused_r4_epilogue(const ProjArgs& a, f32x16 (&ac
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) tile[grp * kPark + ((wq * FN + fn) * 16 + v) * 64 + lane] = acc[fm][fn][v];
+      for (int j = 0; j < 4; ++j)
+        tile4[grp * kPark4 + ((wq * FN + fn) * 4 + j) * 64 + lane] =
+            f32x4{acc[fm][fn][4 * j], acc[fm][fn][4 * j + 1], acc[fm][fn][4 * j + 2], acc[fm][fn][4 * j + 3]};
   }
   __syncthreads();
 #pragma unroll
@@ -408,17 +421,25 @@ __device__ __forceinline__ void fused_r4_epilogue(const ProjArgs& a, f32x16 (&ac
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[fm][fn][v] += tile[(1 - grp) * kPark + ((wq * FN + fn) * 16 + v) * 64 + lane];
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 p = tile4[(1 - grp) * kPark4 + ((wq * FN + fn) * 4 + j) * 64 + lane];
+        acc[fm][fn][4 * j] += p.x;
+        acc[fm][fn][4 * j + 1] += p.y;
+        acc[fm][fn][4 * j + 2] += p.z;
+        acc[fm][fn][4 * j + 3] += p.w;
+      }
   }
   __syncthreads();
+  // Rows 8j + 4h .. 8j + 4h + 3 of a 32-row block are one 4-row group.
 #pragma unroll
   for (int fm = 0; fm < 2; ++fm) {
     if (fm != grp) continue;
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        tile[tile_ix(wq * 64 + fm * 32 + 8 * (v >> 2) + 4 * h + (v & 3), fn * 32 + r32)] = acc[fm][fn][v];
+      for (int j = 0; j < 4; ++j)
+        tile4[tile_ix(wq * 64 + fm * 32 + 8 * j + 4 * h, fn * 32 + r32) >> 2] =
+            f32x4{acc[fm][fn][4 * j], acc[fm][fn][4 * j + 1], acc[fm][fn][4 * j + 2], acc[fm][fn][4 * j + 3]};
   }
   __syncthreads();
 
@@ -433,22 +454,26 @@ __device__ __forceinline__ void fused_r4_epilogue(const ProjArgs& a, f32x16 (&ac
     const int g_lo = rg * 64 / 12, g_hi = (rg + 1) * 64 / 12;
     float kp[4], sp[4];  // previous half of the next window
     if (g_lo > 0) {
+      const f32x4 k4 = tile4[tile_ix(4 * (g_lo - 1), dd) >> 2];
+      const f32x4 s4 = tile4[tile_ix(4 * (g_lo - 1), 80 + dd) >> 2];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kp[e] = tile[tile_ix(4 * (g_lo - 1) + e, dd)];
-        sp[e] = tile[tile_ix(4 * (g_lo - 1) + e, 80 + dd)] + ape_p[e];
+        kp[e] = k4[e];
+        sp[e] = s4[e] + ape_p[e];
       }
     } else {
       // Window j0: its previous half lies in the previous tile (or, for
       // tile 0, in rows 0..3 of the incoming frontier, whose scores already
       // hold their APE), so both halves are written as partials.
       float kc[4], sc[4];
+      const f32x4 kc4 = tile4[tile_ix(0, 40 + dd) >> 2], sc4 = tile4[tile_ix(0, 120 + dd) >> 2];
+      const f32x4 kp4 = tile4[tile_ix(0, dd) >> 2], sp4 = tile4[tile_ix(0, 80 + dd) >> 2];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kc[e] = tile[tile_ix(e, 40 + dd)];
-        sc[e] = tile[tile_ix(e, 120 + dd)] + ape_c[e];
-        kp[e] = tile[tile_ix(e, dd)];
-        sp[e] = tile[tile_ix(e, 80 + dd)] + ape_p[e];
+        kc[e] = kc4[e];
+        sc[e] = sc4[e] + ape_c[e];
+        kp[e] = kp4[e];
+        sp[e] = sp4[e] + ape_p[e];
       }
       if (j0 < f.n_emit) {
         const Part3 pc = half_pool(kc, sc);
@@ -473,12 +498,14 @@ __device__ __forceinline__ void fused_r4_epilogue(const ProjArgs& a, f32x16 (&ac
     }
     for (int g = g_lo > 0 ? g_lo : 1; g < g_hi; ++g) {
       float kc[4], sc[4], kq[4], sq[4];
+      const f32x4 kc4 = tile4[tile_ix(4 * g, 40 + dd) >> 2], sc4 = tile4[tile_ix(4 * g, 120 + dd) >> 2];
+      const f32x4 kq4 = tile4[tile_ix(4 * g, dd) >> 2], sq4 = tile4[tile_ix(4 * g, 80 + dd) >> 2];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kc[e] = tile[tile_ix(4 * g + e, 40 + dd)];
-        sc[e] = tile[tile_ix(4 * g + e, 120 + dd)] + ape_c[e];
-        kq[e] = tile[tile_ix(4 * g + e, dd)];
-        sq[e] = tile[tile_ix(4 * g + e, 80 + dd)] + ape_p[e];
+        kc[e] = kc4[e];
+        sc[e] = sc4[e] + ape_c[e];
+        kq[e] = kq4[e];
+        sq[e] = sq4[e] + ape_p[e];
       }
       const int64_t jw = j0 + g;
       if (jw < f.n_emit) f.o[jw * f.d_tot + dim] = window_pool(kp, sp, kc, sc);
@@ -967,57 +994,69 @@ __global__ void __launch_bounds__(512) proj_r128_splitk4_kernel(ProjArgs a, int 
 #pragma unroll
   for (int e = 0; e < 16; ++e) ape[e] = f.ape[0][(qq * 16 + e) * D + dim];
   float* tile = reinterpret_cast<float*>(smem);
-  constexpr int kPark = FM * FN * 16 * 64;  // floats of one wave's partial sums
+  f32x4* tile4 = reinterpret_cast<f32x4*>(smem);
+  // Partial sums park in 16-byte chunks (four consecutive v), lane-major.
+  constexpr int kPark4 = FM * FN * 4 * 64;  // chunks of one wave's partial sums
   asm volatile("s_barrier" ::: "memory");  // every wave is done with the ring
-  // Round 1: splits 2 and 3 park lane-major, splits 0 and 1 add them.
-  if (ks >= 2) {
+  auto park = [&](int slot) {
 #pragma unroll
     for (int i = 0; i < FM * FN; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) tile[((ks - 2) * 2 + wn) * kPark + (i * 16 + v) * 64 + lane] = acc[i / FN][i % FN][v];
-  }
+      for (int j = 0; j < 4; ++j) {
+        const f32x16& s = acc[i / FN][i % FN];
+        tile4[slot * kPark4 + (i * 4 + j) * 64 + lane] = f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
+      }
+  };
+  auto add = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < FM * FN; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 p = tile4[slot * kPark4 + (i * 4 + j) * 64 + lane];
+        f32x16& s = acc[i / FN][i % FN];
+        s[4 * j] += p.x;
+        s[4 * j + 1] += p.y;
+        s[4 * j + 2] += p.z;
+        s[4 * j + 3] += p.w;
+      }
+  };
+  // Round 1: splits 2 and 3 park, splits 0 and 1 add them.
+  if (ks >= 2) park((ks - 2) * 2 + wn);
   __syncthreads();
-  if (ks < 2) {
-#pragma unroll
-    for (int i = 0; i < FM * FN; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i / FN][i % FN][v] += tile[(ks * 2 + wn) * kPark + (i * 16 + v) * 64 + lane];
-  }
+  if (ks < 2) add(ks * 2 + wn);
   __syncthreads();
   // Round 2: split 1 parks, split 0 adds.
-  if (ks == 1) {
-#pragma unroll
-    for (int i = 0; i < FM * FN; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) tile[wn * kPark + (i * 16 + v) * 64 + lane] = acc[i / FN][i % FN][v];
-  }
+  if (ks == 1) park(wn);
   __syncthreads();
-  if (ks == 0) {
-#pragma unroll
-    for (int i = 0; i < FM * FN; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i / FN][i % FN][v] += tile[wn * kPark + (i * 16 + v) * 64 + lane];
-  }
+  if (ks == 0) add(wn);
   __syncthreads();
-  // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4.
+  // 32x32 accumulator layout: lane holds column r32, rows 8*(v/4) + 4*h + v%4;
+  // rows 8j + 4h .. 8j + 4h + 3 are one 4-row group.
   if (ks == 0) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          tile[tile128_ix(fm * 32 + 8 * (v >> 2) + 4 * h + (v & 3), wn * 64 + fn * 32 + r32)] = acc[fm][fn][v];
+        for (int j = 0; j < 4; ++j) {
+          const f32x16& s = acc[fm][fn];
+          tile4[tile128_ix(fm * 32 + 8 * j + 4 * h, wn * 64 + fn * 32 + r32) >> 2] =
+              f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
+        }
   }
   __syncthreads();
   // Eight lanes per dim pool 16 tokens each and merge by shuffles.
   if (jw < f.n_emit) {
     float kv[16], sc[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = qq * 16 + e;
-      kv[e] = tile[tile128_ix(row, dd)];
-      sc[e] = tile[tile128_ix(row, 64 + dd)] + ape[e];
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 k4 = tile4[tile128_ix(qq * 16 + 4 * i, dd) >> 2];
+      const f32x4 s4 = tile4[tile128_ix(qq * 16 + 4 * i, 64 + dd) >> 2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kv[4 * i + e] = k4[e];
+        sc[4 * i + e] = s4[e] + ape[4 * i + e];
+      }
     }
     float m = sc[0];
 #pragma unroll
