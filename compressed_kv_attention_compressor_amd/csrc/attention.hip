@@ -46,7 +46,7 @@ __device__ __forceinline__ float transpose_reduce32(const float (&v)[32], int la
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const float mine = hi ? v[16 + t] : v[t], other = hi ? v[t] : v[16 + t];
-      a[t] = mine + __shfl_xor(other, 32, kWave);
+      a[t] = mine + lane_xor(other, 32);
     }
   }
   {
@@ -54,7 +54,7 @@ __device__ __forceinline__ float transpose_reduce32(const float (&v)[32], int la
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float mine = hi ? a[8 + t] : a[t], other = hi ? a[t] : a[8 + t];
-      b[t] = mine + __shfl_xor(other, 16, kWave);
+      b[t] = mine + lane_xor(other, 16);
     }
   }
   {
@@ -62,7 +62,7 @@ __device__ __forceinline__ float transpose_reduce32(const float (&v)[32], int la
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const float mine = hi ? b[4 + t] : b[t], other = hi ? b[t] : b[4 + t];
-      c[t] = mine + __shfl_xor(other, 8, kWave);
+      c[t] = mine + lane_xor(other, 8);
     }
   }
   {
@@ -70,13 +70,13 @@ __device__ __forceinline__ float transpose_reduce32(const float (&v)[32], int la
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const float mine = hi ? c[2 + t] : c[t], other = hi ? c[t] : c[2 + t];
-      d[t] = mine + __shfl_xor(other, 4, kWave);
+      d[t] = mine + lane_xor(other, 4);
     }
   }
   const bool hi = (lane & 2) != 0;
   const float mine = hi ? d[1] : d[0], other = hi ? d[0] : d[1];
-  const float e = mine + __shfl_xor(other, 2, kWave);
-  return e + __shfl_xor(e, 1, kWave);
+  const float e = mine + lane_xor(other, 2);
+  return e + lane_xor(e, 1);
 }
 
 template <int DPL>
@@ -142,8 +142,12 @@ __global__ void __launch_bounds__(kAttnWaves * kWave) mixed_attn_part_kernel(Mix
       if (i < a.k && e[r] >= a.visible) cut = min(cut, i);
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) cut = min(cut, __shfl_xor(cut, o, kWave));
+  cut = min(cut, lane_xor(cut, 32));
+  cut = min(cut, lane_xor(cut, 16));
+  cut = min(cut, lane_xor(cut, 8));
+  cut = min(cut, lane_xor(cut, 4));
+  cut = min(cut, lane_xor(cut, 2));
+  cut = min(cut, lane_xor(cut, 1));
   unsigned valid = 0;
 #pragma unroll
   for (int j = 0; j < kItemsPerWave; ++j) {
@@ -168,14 +172,14 @@ __global__ void __launch_bounds__(kAttnWaves * kWave) mixed_attn_part_kernel(Mix
   const float s = (valid >> (pair / kHeadsPerGroup)) & 1u ? logit * a.scale : -INFINITY;
   // Per head over the wave's 8 items (lanes that differ in bits 3-5).
   float m = s;
-  m = fmaxf(m, __shfl_xor(m, 8, kWave));
-  m = fmaxf(m, __shfl_xor(m, 16, kWave));
-  m = fmaxf(m, __shfl_xor(m, 32, kWave));
+  m = fmaxf(m, lane_xor(m, 8));
+  m = fmaxf(m, lane_xor(m, 16));
+  m = fmaxf(m, lane_xor(m, 32));
   const float p = m == -INFINITY ? 0.f : pool_exp(s - m);
   float l = p;
-  l += __shfl_xor(l, 8, kWave);
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
+  l += lane_xor(l, 8);
+  l += lane_xor(l, 16);
+  l += lane_xor(l, 32);
   if ((lane & 1) == 0) s_p[wave][pair] = p;
   if ((lane & 1) == 0 && pair < kHeadsPerGroup) {
     s_m[wave][pair] = m;
@@ -251,7 +255,7 @@ __global__ void __launch_bounds__(kWave) mixed_attn_merge_kernel(MixedAttnArgs a
     }
     float mp = mine ? ms : -INFINITY;
 #pragma unroll
-    for (int k = 32; k > 0; k >>= 1) mp = fmaxf(mp, __shfl_xor(mp, k, kWave));
+    for (int k = 32; k > 0; k >>= 1) mp = fmaxf(mp, lane_xor(mp, k));
     const float mn = fmaxf(mx, mp);
     if (mn == -INFINITY) continue;  // nothing attended so far (uniform)
     const float r = mx == -INFINITY ? 0.f : pool_exp(mx - mn);
@@ -261,7 +265,7 @@ __global__ void __launch_bounds__(kWave) mixed_attn_merge_kernel(MixedAttnArgs a
     for (int d = 0; d < DPL; ++d) o[d] *= r;
 #pragma unroll
     for (int i = 0; i < kPass; ++i) {
-      const float w = __shfl(f, i, kWave);  // 0 for splits past the end
+      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), i));  // 0 for splits past the end
 #pragma unroll
       for (int d = 0; d < DPL; ++d) o[d] = fmaf(t[i][d], w, o[d]);
     }

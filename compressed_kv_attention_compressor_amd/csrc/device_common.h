@@ -3,7 +3,7 @@
 // The row epilogue (RMS norm, tail RoPE, FP8 or Hadamard+FP4 round trip)
 // runs on one wavefront holding one D-wide row, DPL = D/64 consecutive dims
 // per lane.  Reductions over the row or over a codec block are xor-butterfly
-// shuffles, so every lane ends with bitwise the same value.
+// exchanges (lane_xor), so every lane ends with bitwise the same value.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,9 +15,43 @@ namespace ds4c {
 
 constexpr int kWave = 64;
 
+// The value that lane (lane ^ m) holds, for the whole wave (every lane
+// active).  Once loops are unrolled m is a constant and the switch folds:
+// distances 1 and 2 are DPP quad permutes; 4 and 8 two DPP mirrors each
+// (the half-row mirror is lane ^ 7, the row mirror lane ^ 15, so ^7 then ^3
+// gives ^4 and ^15 then ^7 gives ^8); 16 and 32 are the row-pair and
+// half-wave swaps (v_permlane16_swap / v_permlane32_swap, with the source
+// itself as both operands: a lane in the upper row or half reads the first
+// result, a lane in the lower one the second).  All of these are VALU
+// operations; a general distance falls back to the LDS permute.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int lane_xor(int v, int m) {
+  switch (m) {
+    case 1: return dpp_mov<0xB1>(v);                  // quad_perm [1,0,3,2]
+    case 2: return dpp_mov<0x4E>(v);                  // quad_perm [2,3,0,1]
+    case 4: return dpp_mov<0x1B>(dpp_mov<0x141>(v));  // half-row mirror, quad_perm [3,2,1,0]
+    case 8: return dpp_mov<0x141>(dpp_mov<0x140>(v));  // row mirror, half-row mirror
+    case 16: {
+      const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (__lane_id() & 16) ? r[0] : r[1];
+    }
+    case 32: {
+      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (__lane_id() & 32) ? r[0] : r[1];
+    }
+    default: return __shfl_xor(v, m, kWave);
+  }
+}
+__device__ __forceinline__ float lane_xor(float v, int m) {
+  return __builtin_bit_cast(float, lane_xor(__builtin_bit_cast(int, v), m));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  for (int o = 32; o > 0; o >>= 1) v += lane_xor(v, o);
   return v;
 }
 
@@ -25,7 +59,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
 #pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, lane_xor(v, o));
   return v;
 }
 
@@ -222,7 +256,7 @@ __device__ __forceinline__ void hadamard_fp4_rows(float (&y)[NB][DPL], int D, in
     for (int n = 0; n < NB; ++n) {
 #pragma unroll
       for (int i = 0; i < DPL; ++i) {
-        const float p = __shfl_xor(y[n][i], m, kWave);
+        const float p = lane_xor(y[n][i], m);
         y[n][i] = low ? (y[n][i] + p) : (p - y[n][i]);
       }
     }
@@ -241,7 +275,7 @@ __device__ __forceinline__ void hadamard_fp4_rows(float (&y)[NB][DPL], int D, in
 #pragma unroll
   for (int o = 32 / DPL / 2; o > 0; o >>= 1)
 #pragma unroll
-    for (int n = 0; n < NB; ++n) amax[n] = fmaxf(amax[n], __shfl_xor(amax[n], o, kWave));
+    for (int n = 0; n < NB; ++n) amax[n] = fmaxf(amax[n], lane_xor(amax[n], o));
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
     const int kexp = e2m1_block_exp(amax[n]);
@@ -283,7 +317,7 @@ __device__ __forceinline__ void finish_row_part(float (&y)[DPL], const float (&w
     }
   } else {
     // One dim per lane: the pair partner is the neighbouring lane.
-    const float other = __shfl_xor(y[0], 1, kWave);
+    const float other = lane_xor(y[0], 1);
     if (d0 >= n_nope) {
       float sf, cf;
       rope_sincos(pos, (d0 - n_nope) >> 1, n_rot, log2_base, &sf, &cf);

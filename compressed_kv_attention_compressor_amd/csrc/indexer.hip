@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArg
     // The 16 head groups of a row sit in 16 adjacent lanes; butterfly sums in
     // a fixed order give every lane the same value.
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, kWave);
+    for (int o = 1; o < 16; o <<= 1) s += lane_xor(s, o);
     if (hg == r && row0 + 4 * rg + r < a.n) a.scores[row0 + 4 * rg + r] = s;
   }
 }

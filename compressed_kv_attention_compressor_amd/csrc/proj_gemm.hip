@@ -1071,7 +1071,7 @@ __global__ void __launch_bounds__(512) proj_r128_splitk4_kernel(ProjArgs a, int 
     }
 #pragma unroll
     for (int o = 1; o < 8; o <<= 1) {
-      const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64), w2 = __shfl_xor(w, o, 64);
+      const float m2 = lane_xor(m, o), s2 = lane_xor(s, o), w2 = lane_xor(w, o);
       const float mm = fmaxf(m, m2);
       const float mms = mm == -INFINITY ? 0.f : mm;
       const float f1 = pool_exp(m - mms), f2 = pool_exp(m2 - mms);
