@@ -157,14 +157,29 @@ def proj_kernel_name(M: int, N: int, K: int) -> str:
     return name + (f" (K split {s})" if s > 1 else "")
 
 
+# What a kernel source compiles with besides itself: the shared device
+# helpers and argument structs, and the build script that holds the flags.
+SHARED_SOURCES = [os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", f)
+                  for f in ("device_common.h", "kernel_args.h", "launch.h")] + \
+                 [os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "build.py")]
+
+
+def source_digest(source: str) -> str:
+    """sha256 over a kernel source followed by SHARED_SOURCES, in that order."""
+    h = hashlib.sha256()
+    for path in [source] + SHARED_SOURCES:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
 def read_traffic(workload: str, key: str = "gemm_hbm_bytes_per_launch"):
     """HBM bytes per launch (GEMM, or another key of the summary) from the
     committed counter summary, or None.
 
-    The summary names the sha256 of the kernel sources it was taken on (the
-    projection's for GEMM figures, the pool's for pool figures, the decode
-    source's for decode figures); a different source means the counters are
-    stale and none is used.
+    The summary names the digest (source_digest) of the kernel sources it
+    was taken on (the projection's for GEMM figures, the pool's for pool
+    figures, the decode source's for decode figures); a different digest
+    means the counters are stale and none is used.
     """
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
@@ -176,8 +191,7 @@ def read_traffic(workload: str, key: str = "gemm_hbm_bytes_per_launch"):
             kv[k.strip()] = v.strip()
     kind = "decode" if key.startswith("decode") else "pool" if "pool" in key else "gemm"
     source = {"decode": DECODE_SOURCE, "pool": POOL_SOURCE, "gemm": GEMM_SOURCE}[kind]
-    src = hashlib.sha256(open(source, "rb").read()).hexdigest()
-    if kv.get(f"{kind}_source_sha256") != src:
+    if kv.get(f"{kind}_sources_sha256") != source_digest(source):
         return None
     try:
         return float(kv[key])
