@@ -243,8 +243,8 @@ void launch_gemv(const GemvLaunch& g, int K, unsigned grid, hipStream_t s, hipEv
 // o, and apply the half shift to the same columns (rows 0..3 <- rows 4..7 on
 // both halves).  The thread writes only addresses it has read itself, so
 // the shift needs no synchronisation with other threads.
-template <int DPL>
-__device__ __forceinline__ void r4_pool_and_shift(const LaneDev& L, int d0, float (&o)[DPL]) {
+template <int DPL, typename Mid>
+__device__ __forceinline__ void r4_pool_and_shift(const LaneDev& L, int d0, float (&o)[DPL], Mid&& mid) {
   float kv[8][DPL], sc[8][DPL], kvs[4][DPL], scs[4][DPL];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -257,6 +257,10 @@ __device__ __forceinline__ void r4_pool_and_shift(const LaneDev& L, int d0, floa
     load_vec<DPL>(kvs[e], L.fr_kv + (e + 4) * L.W + d0);
     load_vec<DPL>(scs[e], L.fr_sc + (e + 4) * L.W + d0);
   }
+  // Work that needs none of the loads runs while they are in flight.
+  __builtin_amdgcn_sched_barrier(0);
+  mid();
+  __builtin_amdgcn_sched_barrier(0);
   pool_entries<8, DPL>(kv, sc, o);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -291,30 +295,31 @@ __global__ void __launch_bounds__(64 * (SA + 1))
   L.is_index = att ? 0 : 1;
   if (att) {
     const int d0 = wave * (kWave * DPLA) + lane * DPLA;
+    const int64_t k = a.pos / 4;
     float nw[DPLA], o[DPLA];
     load_vec<DPLA>(nw, nw0 + d0);
-    r4_pool_and_shift<DPLA>(L, d0, o);
+    RowConsts<DPLA> rc;
+    r4_pool_and_shift<DPLA>(L, d0, o, [&] { rc = row_consts<DPLA>(d0, L.D, a.n_rot, a.log2_base, k, 4); });
     const float ss = wave_sum(row_sumsq<DPLA>(o));
     if (lane == 0) s_ss[wave] = ss;
     __syncthreads();
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < SA; ++w) tot += s_ss[w];
-    const int64_t k = a.pos / 4;
-    finish_row_part<DPLA>(o, nw, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, a.lane[0].prequant,
+    finish_row_part<DPLA>(o, nw, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, rc, a.lane[0].prequant,
                           a.lane[0].rows + k * L.D, lane);
   } else {
+    const int64_t k = a.pos / 4;
     float nw[DPLI], o[DPLI];
+    RowConsts<DPLI> rc;
     if (d_idx > 0) {
       load_vec<DPLI>(nw, nw1 + lane * DPLI);
-      r4_pool_and_shift<DPLI>(L, lane * DPLI, o);
+      r4_pool_and_shift<DPLI>(L, lane * DPLI, o,
+                              [&] { rc = row_consts<DPLI>(lane * DPLI, L.D, a.n_rot, a.log2_base, k, 4); });
     }
     __syncthreads();
-    if (d_idx > 0) {
-      const int64_t k = a.pos / 4;
-      finish_row_wave<DPLI>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, a.lane[1].prequant,
-                            a.lane[1].rows + k * L.D, lane);
-    }
+    if (d_idx > 0)
+      finish_row_wave<DPLI>(o, nw, L, a.n_rot, a.rms_eps, rc, a.lane[1].prequant, a.lane[1].rows + k * L.D, lane);
   }
 }
 
@@ -384,7 +389,10 @@ __global__ void __launch_bounds__(kWave) decode_r128_finish_kernel(DecodeArgs a)
   float nw[DPL], o[DPL];
   load_vec<DPL>(nw, L.norm_w + lane * DPL);
   load_vec<DPL>(o, row + lane * DPL);
-  finish_row_wave<DPL>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, L.prequant, row, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  const RowConsts<DPL> rc = row_consts<DPL>(lane * DPL, L.D, a.n_rot, a.log2_base, k, 128);  // while the row loads
+  __builtin_amdgcn_sched_barrier(0);
+  finish_row_wave<DPL>(o, nw, L, a.n_rot, a.rms_eps, rc, L.prequant, row, lane);
 }
 
 template <int SA, int DPLA>

@@ -234,7 +234,7 @@ __device__ __forceinline__ float row_sumsq(const float (&y)[DPL]) {
 // rows stay rotated.  Every stage runs over all NB rows before the next, so
 // the rows' cross-lane exchanges overlap.
 template <int DPL, int NB>
-__device__ __forceinline__ void hadamard_fp4_rows(float (&y)[NB][DPL], int D, int lane) {
+__device__ __forceinline__ void hadamard_fp4_rows(float (&y)[NB][DPL], float scale, int lane) {
 #pragma unroll
   for (int h = 1; h < DPL; h <<= 1) {
 #pragma unroll
@@ -261,7 +261,6 @@ __device__ __forceinline__ void hadamard_fp4_rows(float (&y)[NB][DPL], int D, in
       }
     }
   }
-  const float scale = (float)(1.0 / sqrt((double)D));
   float amax[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
@@ -285,15 +284,52 @@ __device__ __forceinline__ void hadamard_fp4_rows(float (&y)[NB][DPL], int D, in
 }
 
 template <int DPL>
-__device__ __forceinline__ void hadamard_fp4(float (&y)[DPL], int D, int lane) {
-  hadamard_fp4_rows<DPL, 1>(*reinterpret_cast<float (*)[1][DPL]>(&y), D, lane);
+__device__ __forceinline__ void hadamard_fp4(float (&y)[DPL], float scale, int lane) {
+  hadamard_fp4_rows<DPL, 1>(*reinterpret_cast<float (*)[1][DPL]>(&y), scale, lane);
+}
+
+// The rotation's scale 1/sqrt(D), rounded once to float.
+__device__ __forceinline__ float hadamard_scale(int D) { return (float)(1.0 / sqrt((double)D)); }
+
+// Per-row constants of the finish that need none of the row's data: the RoPE
+// sin/cos of the pairs this lane rotates (with DPL >= 2, pairs (d0 + 2p,
+// d0 + 2p + 1) for p < DPL/2; with DPL == 1, the pair of dim d0 and its
+// neighbouring lane) and the indexer rotation's scale.  They depend on the
+// position and the dims only, so a caller computes them between issuing its
+// loads and using the data, where the fp64 arithmetic overlaps the memory
+// round trip.  Every lane computes them (a lane outside the tail takes pair
+// 0 and never uses it).
+template <int DPL>
+struct RowConsts {
+  static constexpr int kPairs = DPL >= 2 ? DPL / 2 : 1;
+  float s[kPairs], c[kPairs];
+  float hscale;
+};
+template <int DPL>
+__device__ __forceinline__ RowConsts<DPL> row_consts(int d0, int D, int n_rot, double log2_base, int64_t k,
+                                                     int ratio) {
+  RowConsts<DPL> r;
+  const int n_nope = D - n_rot;
+  const double pos = (double)k * (double)ratio;
+#pragma unroll
+  for (int p = 0; p < RowConsts<DPL>::kPairs; ++p) {
+    const int i = (DPL >= 2 ? d0 + 2 * p - n_nope : d0 - n_nope) >> 1;
+    rope_sincos(pos, i > 0 ? i : 0, n_rot, log2_base, &r.s[p], &r.c[p]);
+    // An empty asm that takes the values keeps the compiler from sinking
+    // their computation to the later point of use.
+    asm volatile("" : "+v"(r.s[p]), "+v"(r.c[p]));
+  }
+  r.hscale = hadamard_scale(D);
+  asm volatile("" : "+v"(r.hscale));
+  return r;
 }
 
 // w holds the norm weights of this lane's dims, loaded by the caller ahead
-// of the row's entries so that no load sits between the pool and the store.
+// of the row's entries so that no load sits between the pool and the store;
+// rc holds the row's constants (row_consts).
 template <int DPL>
 __device__ __forceinline__ void finish_row_part(float (&y)[DPL], const float (&w)[DPL], const LaneDev& L, float inv,
-                                                int d0, int n_rot, double log2_base, int64_t k, int ratio,
+                                                int d0, int n_rot, const RowConsts<DPL>& rc,
                                                 float* __restrict__ prequant_row, float* __restrict__ out_row,
                                                 int lane) {
   const int D = L.D;
@@ -303,13 +339,11 @@ __device__ __forceinline__ void finish_row_part(float (&y)[DPL], const float (&w
   // Tail RoPE: the last n_rot dims, adjacent pairs (2i, 2i+1), rotated by
   // (k * ratio) * base^(-2i/n_rot) radians.
   const int n_nope = D - n_rot;
-  const double pos = (double)k * (double)ratio;
   if constexpr (DPL >= 2) {
     if (d0 >= n_nope) {
 #pragma unroll
       for (int i = 0; i < DPL; i += 2) {
-        float sf, cf;
-        rope_sincos(pos, (d0 + i - n_nope) >> 1, n_rot, log2_base, &sf, &cf);
+        const float sf = rc.s[i / 2], cf = rc.c[i / 2];
         const float a = y[i], b = y[i + 1];
         y[i] = a * cf - b * sf;
         y[i + 1] = a * sf + b * cf;
@@ -319,8 +353,7 @@ __device__ __forceinline__ void finish_row_part(float (&y)[DPL], const float (&w
     // One dim per lane: the pair partner is the neighbouring lane.
     const float other = lane_xor(y[0], 1);
     if (d0 >= n_nope) {
-      float sf, cf;
-      rope_sincos(pos, (d0 - n_nope) >> 1, n_rot, log2_base, &sf, &cf);
+      const float sf = rc.s[0], cf = rc.c[0];
       if ((lane & 1) == 0)
         y[0] = y[0] * cf - other * sf;  // a' = a cos - b sin
       else
@@ -342,7 +375,7 @@ __device__ __forceinline__ void finish_row_part(float (&y)[DPL], const float (&w
       for (int i = 0; i < DPL; ++i) y[i] = ldexpf(rne_e4m3(ldexpf(y[i], -kexp)), kexp);
     }
   } else {
-    hadamard_fp4<DPL>(y, D, lane);
+    hadamard_fp4<DPL>(y, rc.hscale, lane);
   }
 
   store_vec<DPL>(out_row + d0, y);
@@ -355,11 +388,10 @@ __device__ __forceinline__ float rms_inv(float sumsq, int D, float eps) {
 // Whole row in one wave (D == 64 * DPL).
 template <int DPL>
 __device__ __forceinline__ void finish_row_wave(float (&y)[DPL], const float (&w)[DPL], const LaneDev& L, int n_rot,
-                                                double log2_base, float rms_eps, int64_t k, int ratio,
-                                                float* __restrict__ prequant_row, float* __restrict__ out_row,
-                                                int lane) {
+                                                float rms_eps, const RowConsts<DPL>& rc, float* __restrict__ prequant_row,
+                                                float* __restrict__ out_row, int lane) {
   const float inv = rms_inv(wave_sum(row_sumsq<DPL>(y)), L.D, rms_eps);
-  finish_row_part<DPL>(y, w, L, inv, lane * DPL, n_rot, log2_base, k, ratio, prequant_row, out_row, lane);
+  finish_row_part<DPL>(y, w, L, inv, lane * DPL, n_rot, rc, prequant_row, out_row, lane);
 }
 
 }  // namespace ds4c

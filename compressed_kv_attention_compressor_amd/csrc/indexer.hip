@@ -81,7 +81,7 @@ __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArg
       for (int i = 0; i < DPL; ++i) y[j][i] = 0.f;
   // Rotation + FP4 round trip of the wave's heads into LDS (a zero head
   // stays zero), while the rows are still on their way.
-  hadamard_fp4_rows<DPL, kHeadsPerWave>(y, DH, lane);
+  hadamard_fp4_rows<DPL, kHeadsPerWave>(y, hadamard_scale(DH), lane);
 #pragma unroll
   for (int j = 0; j < kHeadsPerWave; ++j) {
     const int h = wave + 4 * j;

@@ -182,8 +182,8 @@ __device__ __forceinline__ void r4_window(const PoolArgs& a, int64_t k, float* s
 #pragma unroll
     for (int s = 0; s < SA; ++s) tot += s_ss[s];
     float* pre = L.prequant ? L.prequant + (k - a.k_lo) * L.D : nullptr;
-    finish_row_part<DPLA>(o, nw, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, pre,
-                          L.rows + k * L.D, lane);
+    const RowConsts<DPLA> rc = row_consts<DPLA>(d0, L.D, a.n_rot, a.log2_base, k, 4);
+    finish_row_part<DPLA>(o, nw, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, rc, pre, L.rows + k * L.D, lane);
   } else {
     const LaneDev& L = a.lane[1];
     float nw[DPLI], o[DPLI];
@@ -191,7 +191,8 @@ __device__ __forceinline__ void r4_window(const PoolArgs& a, int64_t k, float* s
     r4_pool<DPLI>(a, L, k, lane * DPLI, o);
     __syncthreads();
     float* pre = L.prequant ? L.prequant + (k - a.k_lo) * L.D : nullptr;
-    finish_row_wave<DPLI>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, pre, L.rows + k * L.D, lane);
+    const RowConsts<DPLI> rc = row_consts<DPLI>(lane * DPLI, L.D, a.n_rot, a.log2_base, k, 4);
+    finish_row_wave<DPLI>(o, nw, L, a.n_rot, a.rms_eps, rc, pre, L.rows + k * L.D, lane);
   }
   __syncthreads();
 }
@@ -317,7 +318,8 @@ __global__ void __launch_bounds__(256) pool_r128_finish_kernel(PoolArgs a) {
     }
     const int64_t k = a.k_lo + row;
     float* pre = L.prequant ? L.prequant + row * L.D : nullptr;
-    finish_row_wave<DPL>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, pre, L.rows + k * L.D, lane);
+    const RowConsts<DPL> rc = row_consts<DPL>(d0, L.D, a.n_rot, a.log2_base, k, 128);
+    finish_row_wave<DPL>(o, nw, L, a.n_rot, a.rms_eps, rc, pre, L.rows + k * L.D, lane);
   }
 }
 
@@ -330,10 +332,14 @@ __global__ void __launch_bounds__(256) pool_r128_finish_kernel(PoolArgs a) {
 // part[j/64][1] (window 0's previous half comes from the incoming frontier,
 // read by the projection launch).
 // ---------------------------------------------------------------------------
-template <int DPL>
-__device__ __forceinline__ void fused_pool_dims(const PoolArgs& a, int64_t j, int dg, float (&o)[DPL]) {
+// mid() runs once the loads are issued and before their data is used.
+template <int DPL, typename Mid>
+__device__ __forceinline__ void fused_pool_dims(const PoolArgs& a, int64_t j, int dg, float (&o)[DPL], Mid&& mid) {
   if (j % 64 != 0) {
     load_vec<DPL>(o, a.o + j * a.d_tot + dg);
+    __builtin_amdgcn_sched_barrier(0);
+    mid();
+    __builtin_amdgcn_sched_barrier(0);
     return;
   }
   const int64_t tm = j / 64;
@@ -346,6 +352,9 @@ __device__ __forceinline__ void fused_pool_dims(const PoolArgs& a, int64_t j, in
   load_vec<DPL>(mp, pp);
   load_vec<DPL>(sp, pp + a.d_tot);
   load_vec<DPL>(wp, pp + 2 * a.d_tot);
+  __builtin_amdgcn_sched_barrier(0);
+  mid();
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < DPL; ++i) {
     const float m = fmaxf(mc[i], mp[i]);
@@ -375,7 +384,9 @@ __device__ __forceinline__ void r4_fused_window(const PoolArgs& a, int64_t j, fl
     const int d0 = wave * (kWave * DPLA) + lane * DPLA;
     float nw[DPLA], o[DPLA];
     load_vec<DPLA>(nw, L.norm_w + d0);
-    fused_pool_dims<DPLA>(a, j, d0, o);
+    // The row constants need none of the loads: computed while they are in flight.
+    RowConsts<DPLA> rc;
+    fused_pool_dims<DPLA>(a, j, d0, o, [&] { rc = row_consts<DPLA>(d0, L.D, a.n_rot, a.log2_base, k, 4); });
     const float ss = wave_sum(row_sumsq<DPLA>(o));
     if (lane == 0) s_ss[wave] = ss;
     __syncthreads();
@@ -383,16 +394,17 @@ __device__ __forceinline__ void r4_fused_window(const PoolArgs& a, int64_t j, fl
 #pragma unroll
     for (int s = 0; s < SA; ++s) tot += s_ss[s];
     float* pre = L.prequant ? L.prequant + j * L.D : nullptr;
-    finish_row_part<DPLA>(o, nw, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, a.log2_base, k, 4, pre,
-                          L.rows + k * L.D, lane);
+    finish_row_part<DPLA>(o, nw, L, rms_inv(tot, L.D, a.rms_eps), d0, a.n_rot, rc, pre, L.rows + k * L.D, lane);
   } else {
     const LaneDev& L = a.lane[1];
     float nw[DPLI], o[DPLI];
     load_vec<DPLI>(nw, L.norm_w + lane * DPLI);
-    fused_pool_dims<DPLI>(a, j, a.lane[0].D + lane * DPLI, o);
+    RowConsts<DPLI> rc;
+    fused_pool_dims<DPLI>(a, j, a.lane[0].D + lane * DPLI, o,
+                          [&] { rc = row_consts<DPLI>(lane * DPLI, L.D, a.n_rot, a.log2_base, k, 4); });
     __syncthreads();
     float* pre = L.prequant ? L.prequant + j * L.D : nullptr;
-    finish_row_wave<DPLI>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 4, pre, L.rows + k * L.D, lane);
+    finish_row_wave<DPLI>(o, nw, L, a.n_rot, a.rms_eps, rc, pre, L.rows + k * L.D, lane);
   }
 }
 
@@ -454,8 +466,11 @@ __global__ void __launch_bounds__(256) pool_r128_fused_kernel(PoolArgs a) {
       load_vec<DPL>(nw, L.norm_w + lane * DPL);
       load_vec<DPL>(o, a.o + j * L.D + lane * DPL);
       const int64_t k = a.k_lo + j;
+      __builtin_amdgcn_sched_barrier(0);
+      const RowConsts<DPL> rc = row_consts<DPL>(lane * DPL, L.D, a.n_rot, a.log2_base, k, 128);  // while the row loads
+      __builtin_amdgcn_sched_barrier(0);
       float* pre = L.prequant ? L.prequant + j * L.D : nullptr;
-      finish_row_wave<DPL>(o, nw, L, a.n_rot, a.log2_base, a.rms_eps, k, 128, pre, L.rows + k * L.D, lane);
+      finish_row_wave<DPL>(o, nw, L, a.n_rot, a.rms_eps, rc, pre, L.rows + k * L.D, lane);
     }
     return;
   }
