@@ -198,11 +198,14 @@ __global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArg
 #pragma unroll
       for (int b = 0; b < 4; ++b) c[b] = hist[255 - 4 * lane - b];
       const uint32_t csum = c[0] + c[1] + c[2] + c[3];
-      uint32_t P = csum;
+      // Inclusive scan over the lanes as a butterfly: a lane in the upper
+      // half of each pair of blocks adds the lower block's total.
+      uint32_t P = csum, tot = csum;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t t = __shfl_up(P, o, kWave);
-        if (lane >= o) P += t;
+        const uint32_t t = (uint32_t)lane_xor((int)tot, o);
+        if (lane & o) P += t;
+        tot += t;
       }
       const uint32_t E = P - csum;
       const uint32_t need = (uint32_t)s_need;
