@@ -245,24 +245,41 @@ __global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArg
     for (int i = tid; i < a.k; i += kSortThreads) a.cand[(int64_t)blockIdx.x * a.k + i] = i < total ? sel[i] : 0ull;
     return;
   }
-  // Descending order: a key's position is the number of larger selected
-  // keys (keys are unique, so positions are too).  The list is padded with
-  // zeros (below every key) to a multiple of 8 and read 8 keys per step.
-  const int padded = (total + 7) & ~7;
-  for (int i = total + tid; i < padded; i += kSortThreads) sel[i] = 0ull;
-  __syncthreads();
-  for (int i = tid; i < total; i += kSortThreads) {
-    const uint64_t v = sel[i];
-    int rank = 0;
-    for (int j = 0; j < padded; j += 8) {
-      uint64_t w[8];
+  // Descending order by a bitonic sort of the selected keys (padded with
+  // zeros, below every key, to 512), one key per thread of the first eight
+  // waves: 45 compare-exchange steps, the 39 between lanes of one wave by
+  // lane exchanges, the 6 across waves through LDS.  Keys are unique, so the
+  // order is.
+  static_assert(kSortThreads >= 512, "one key per thread");
+  const bool sorter = tid < 512;  // whole waves
+  uint64_t v = sorter && tid < total ? sel[tid] : 0ull;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) w[u] = sel[j + u];
+  for (int size = 2; size <= 512; size <<= 1) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) rank += w[u] > v ? 1 : 0;
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      uint64_t w = 0ull;
+      if (stride >= kWave) {
+        __syncthreads();  // every read of the previous step is done
+        if (sorter) sel[tid] = v;
+        __syncthreads();
+        if (sorter) w = sel[tid ^ stride];
+      } else if (sorter) {
+        const uint32_t lo = (uint32_t)lane_xor((int)(uint32_t)v, stride);
+        const uint32_t hi = (uint32_t)lane_xor((int)(uint32_t)(v >> 32), stride);
+        w = ((uint64_t)hi << 32) | lo;
+      }
+      // Blocks of `size` alternate direction so that the last merge sorts
+      // descending; within a pair the lower index keeps the larger key in a
+      // descending block.
+      const bool desc = (tid & size) == 0;
+      const bool lower = (tid & stride) == 0;
+      const uint64_t hi_k = v > w ? v : w, lo_k = v > w ? w : v;
+      v = lower == desc ? hi_k : lo_k;
     }
-    a.out_idx[rank] = (int32_t)(0xffffffffu - (uint32_t)(v & 0xffffffffu));
-    a.out_score[rank] = unord_bits((uint32_t)(v >> 32));
+  }
+  if (sorter && tid < total) {
+    a.out_idx[tid] = (int32_t)(0xffffffffu - (uint32_t)(v & 0xffffffffu));
+    a.out_score[tid] = unord_bits((uint32_t)(v >> 32));
   }
 }
 
