@@ -11,10 +11,10 @@
 //  * indexer_score_kernel: 64 rows per workgroup.  The workgroup rotates and
 //    quantises the query into LDS (each wave a quarter of the heads), stages
 //    its rows in LDS, and each thread accumulates 4 rows x 4 heads; the 16
-//    head groups of a row meet by butterfly shuffles in a fixed order.
+//    head groups of a row meet by butterfly exchanges in a fixed order.
 //  * indexer_select_kernel: the k largest (score, lower row first) by a radix
-//    select over 64-bit keys in one workgroup, each survivor written at its
-//    rank.  Up to kIndexerChunk rows it is one launch; longer calls run
+//    select over 64-bit keys in one workgroup, the survivors then sorted
+//    descending.  Up to kIndexerChunk rows it is one launch; longer calls run
 //    one workgroup per chunk first and a final pass over their survivors.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -145,8 +145,8 @@ __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArg
 // padding).  A radix select over 8-bit digits, most significant first,
 // narrows the bucket holding the k-th key until the keys still needed are
 // the whole bucket; the keys at or above that bucket's lowest value are then
-// exactly the k largest.  final: each is written as (row, score) at its rank
-// (descending); else they go to cand in any order.
+// exactly the k largest.  final: they are sorted and written as (row,
+// score), descending; else they go to cand in any order.
 template <int MODE>
 __global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArgs a, int final_pass) {
   constexpr int mode = MODE;
