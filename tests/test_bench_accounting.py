@@ -61,3 +61,27 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
     assert '"metric"' not in r.stdout
+
+
+def test_counter_summaries_go_stale_with_any_source_they_depend_on(tmp_path, monkeypatch):
+    # A summary's counters are used only while its digest matches the kernel
+    # source and the shared headers and build script it compiles with.
+    import os
+    import shutil
+    csrc = tmp_path / "compressed_kv_attention_compressor_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    for f in ("proj_gemm.hip", "device_common.h", "kernel_args.h", "launch.h"):
+        shutil.copy(os.path.join(bench.ROOT, "compressed_kv_attention_compressor_amd", "csrc", f), csrc / f)
+    shutil.copy(os.path.join(bench.ROOT, "compressed_kv_attention_compressor_amd", "build.py"),
+                tmp_path / "compressed_kv_attention_compressor_amd" / "build.py")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "GEMM_SOURCE", str(csrc / "proj_gemm.hip"))
+    monkeypatch.setattr(bench, "SHARED_SOURCES", [str(csrc / f) for f in ("device_common.h", "kernel_args.h", "launch.h")]
+                        + [str(tmp_path / "compressed_kv_attention_compressor_amd" / "build.py")])
+    digest = bench.source_digest(bench.GEMM_SOURCE)
+    (tmp_path / "profiles" / "traffic_w.txt").write_text(
+        f"# comment = ignored\ngemm_hbm_bytes_per_launch = 123\ngemm_sources_sha256 = {digest}\n")
+    assert bench.read_traffic("w") == 123.0
+    (csrc / "device_common.h").write_text((csrc / "device_common.h").read_text() + "\n// edit\n")
+    assert bench.read_traffic("w") is None
