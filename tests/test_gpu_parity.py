@@ -143,6 +143,11 @@ PLANS = {
     "aligned": [256, 256, 188],
     # calls on window boundaries spanning several 256-token tiles, short tails
     "aligned_long": [4, 600, 64, 5, 3],
+    # fused calls over several 256-token tiles whose length leaves 7 tokens for
+    # the ratio-4 frontier (T % 4 == 3) in a 3-token last tile, the second
+    # starting from the frontier the decode steps left; at ratio 128 the first
+    # leaves 3 tokens of an open window
+    "fused_ragged": [1027, -5, 1031, 2],
 }
 
 
