@@ -225,16 +225,21 @@ __device__ __forceinline__ float row_sumsq(const float (&y)[DPL]) {
   return ss;
 }
 
-// Indexer QAT round trip of NB independent D-wide rows held by one wave
-// (D == 64 * DPL, lane holds dims lane*DPL .. of each row): the orthonormal
+// Indexer QAT round trip of NB independent D-wide rows, each held by LANES
+// consecutive lanes of one wave (D == LANES * DPL; the lane at position c of
+// its group holds dims c*DPL .. of each of its rows): the orthonormal
 // Walsh-Hadamard rotation (Sylvester order; butterflies (a, b) -> (a + b,
 // a - b) on index pairs (j, j + h) for h = 1, 2, 4, ...; strides below DPL
 // inside a lane, the rest across lanes), scaled by 1/sqrt(D), then FP4 E2M1
 // in blocks of 32 dims (32/DPL lanes) with the power-of-two block scale.  The
 // rows stay rotated.  Every stage runs over all NB rows before the next, so
-// the rows' cross-lane exchanges overlap.
-template <int DPL, int NB>
+// the rows' cross-lane exchanges overlap.  Across lanes the butterfly is one
+// fma with a weight of +1 (lower lane: b + a) or -1 (upper lane: a - b),
+// exact in the product, so each output is the same single rounding of a + b
+// or a - b as inside a lane.
+template <int DPL, int NB, int LANES = kWave>
 __device__ __forceinline__ void hadamard_fp4_rows(float (&y)[NB][DPL], float scale, int lane) {
+  static_assert(LANES >= 1 && LANES <= kWave && (LANES & (LANES - 1)) == 0, "lanes per row");
 #pragma unroll
   for (int h = 1; h < DPL; h <<= 1) {
 #pragma unroll
@@ -250,15 +255,12 @@ __device__ __forceinline__ void hadamard_fp4_rows(float (&y)[NB][DPL], float sca
     }
   }
 #pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
-    const bool low = (lane & m) == 0;
+  for (int m = 1; m < LANES; m <<= 1) {
+    const float sgn = (lane & m) ? -1.f : 1.f;
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        const float p = lane_xor(y[n][i], m);
-        y[n][i] = low ? (y[n][i] + p) : (p - y[n][i]);
-      }
+      for (int i = 0; i < DPL; ++i) y[n][i] = fmaf(sgn, y[n][i], lane_xor(y[n][i], m));
     }
   }
   float amax[NB];

@@ -9,9 +9,9 @@
 //
 // Launches:
 //  * indexer_score_kernel: 64 rows per workgroup.  The workgroup rotates and
-//    quantises the query into LDS (each wave a quarter of the heads), stages
-//    its rows in LDS, and each thread accumulates 4 rows x 4 heads; the 16
-//    head groups of a row meet by butterfly exchanges in a fixed order.
+//    quantises the query into LDS (each wave a quarter of the heads) while
+//    its rows load; the dot products run on fp32 MFMA tiles of 32 rows x 32
+//    heads, one per wave, and the heads' weighted sum meets in a fixed order.
 //  * indexer_select_kernel: the k largest (score, lower row first) by a radix
 //    select over 64-bit keys in one workgroup, the survivors then sorted
 //    descending.  Up to kIndexerChunk rows it is one launch; longer calls run
@@ -43,99 +43,107 @@ __device__ __forceinline__ float unord_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// The heads' dot products with the rows are a [heads x Dh] x [Dh x rows]
+// product: wave w takes rows 32 (w & 1) .. +31 against heads 32 (w >> 1) ..
+// +31 as one 32 x 32 fp32 MFMA tile (v_mfma_f32_32x32x2_f32; its result
+// holds, in lane l, row l % 32 against heads 8 (v / 4) + 4 (l / 32) + v % 4
+// of the tile, v = 0..15).  The sum runs over the dims in an order of the
+// kernel's choosing, the same on both operands: lane half h = l / 32 takes
+// dims Dh/2 * h .. +Dh/2 - 1, so each lane reads one contiguous half row
+// from memory straight into its operand registers, and its query operands
+// come from LDS four steps per 16-byte read.
 template <int DH>
 __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArgs a) {
-  constexpr int DPL = DH / 64;
-  constexpr int kLd = DH + 4;  // padded LDS row: consecutive rows start 4 banks apart
-  __shared__ float s_q[64 * kLd];
-  __shared__ float s_k[kScoreRows * kLd];
+  constexpr int kLd = DH + 4;   // padded LDS row: consecutive heads start 4 banks apart
+  constexpr int kHalf = DH / 2; // dims per lane half
+  constexpr int kV = kHalf / 4; // float4 per lane
+  __shared__ __attribute__((aligned(16))) float s_q[64 * kLd];
+  __shared__ float s_part[2][kScoreRows];
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int rb = 32 * (wave & 1), hb = 32 * (wave >> 1);
   const int64_t row0 = (int64_t)blockIdx.x * kScoreRows;
 
   // Every load is issued before any is used, with no branch around a load
   // (a branch would make the compiler wait for each load before the next):
-  // first the query heads wave, wave + 4, ... (heads past H re-read head H-1
-  // and are zeroed), then the rows of this workgroup, 16 bytes per thread and
-  // step (rows past n re-read row n-1 and are zeroed).  Loads complete in
-  // order, so the query's round trip below waits only for the query.
-  constexpr int kHeadsPerWave = 64 / (kScoreThreads / kWave);
-  float y[kHeadsPerWave][DPL];
+  // first the wave's query heads wave + 4m (m = 0..15; heads past H re-read
+  // head H-1 and are zeroed), then this lane's half row (rows past n re-read
+  // row n-1; their scores are not written) and the weights of its 16 heads.
+  // Loads complete in order, so the query's round trip below waits only for
+  // the query.  For the round trip a head spans kLH lanes of 8 dims each, so
+  // three of its butterfly stages stay inside a lane.
+  constexpr int kLH = DH / 8;            // lanes per head
+  constexpr int kHPass = kWave / kLH;    // heads side by side in the wave
+  constexpr int kSlots = 16 / kHPass;    // heads per lane
+  const int hgrp = lane / kLH, dcol = 8 * (lane % kLH);
+  float y[kSlots][8];
 #pragma unroll
-  for (int j = 0; j < kHeadsPerWave; ++j) {
-    const int h = wave + 4 * j;
-    load_vec<DPL>(y[j], a.q + (h < a.H ? h : a.H - 1) * DH + lane * DPL);
+  for (int j = 0; j < kSlots; ++j) {
+    const int hq = wave + 4 * (kHPass * j + hgrp);
+    load_vec<8>(y[j], a.q + (hq < a.H ? hq : a.H - 1) * DH + dcol);
   }
-  constexpr int kVec = DH / 4;                         // float4 per row
-  constexpr int kRowSteps = kScoreRows * kVec / kScoreThreads;
-  float4 kv[kRowSteps];
+  const int64_t row = row0 + rb + r32 < a.n ? row0 + rb + r32 : a.n - 1;
+  float4 kv[kV];
 #pragma unroll
-  for (int s = 0; s < kRowSteps; ++s) {
-    const int i = t + s * kScoreThreads, r = i / kVec, c = (i % kVec) * 4;
-    const int64_t row = row0 + r < a.n ? row0 + r : a.n - 1;
-    kv[s] = *reinterpret_cast<const float4*>(a.rows + row * DH + c);
+  for (int u = 0; u < kV; ++u) kv[u] = *reinterpret_cast<const float4*>(a.rows + row * DH + kHalf * h + 4 * u);
+  float w[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int hd = hb + 8 * (v / 4) + 4 * h + v % 4;
+    w[v] = a.head_w[hd < a.H ? hd : a.H - 1];
   }
+  // Keeps the compiler from moving the row loads down to their first use,
+  // past the query's round trip.
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = 0; j < kHeadsPerWave; ++j)
-    if (wave + 4 * j >= a.H)
+  for (int j = 0; j < kSlots; ++j)
+    if (wave + 4 * (kHPass * j + hgrp) >= a.H)
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) y[j][i] = 0.f;
+      for (int i = 0; i < 8; ++i) y[j][i] = 0.f;
   // Rotation + FP4 round trip of the wave's heads into LDS (a zero head
   // stays zero), while the rows are still on their way.
-  hadamard_fp4_rows<DPL, kHeadsPerWave>(y, hadamard_scale(DH), lane);
+  hadamard_fp4_rows<8, kSlots, kLH>(y, hadamard_scale(DH), lane);
 #pragma unroll
-  for (int j = 0; j < kHeadsPerWave; ++j) {
-    const int h = wave + 4 * j;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) s_q[h * kLd + lane * DPL + i] = y[j][i];
-    if (a.q_hat && blockIdx.x == 0 && h < a.H) store_vec<DPL>(a.q_hat + h * DH + lane * DPL, y[j]);
+  for (int j = 0; j < kSlots; ++j) {
+    const int hq = wave + 4 * (kHPass * j + hgrp);
+    store_vec<8>(s_q + hq * kLd + dcol, y[j]);
+    if (a.q_hat && blockIdx.x == 0 && hq < a.H) store_vec<8>(a.q_hat + hq * DH + dcol, y[j]);
   }
 #pragma unroll
-  for (int s = 0; s < kRowSteps; ++s) {
-    const int i = t + s * kScoreThreads, r = i / kVec, c = (i % kVec) * 4;
-    *reinterpret_cast<float4*>(s_k + r * kLd + c) = row0 + r < a.n ? kv[s] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  for (int v = 0; v < 16; ++v)
+    if (hb + 8 * (v / 4) + 4 * h + v % 4 >= a.H) w[v] = 0.f;
   __syncthreads();
 
-  // Thread (row group rg, head group hg): rows 4rg .. 4rg+3 against heads
-  // hg, hg + 16, hg + 32, hg + 48; per 4 dims 8 LDS reads feed 64 FMAs.
-  const int rg = t / 16, hg = t % 16;
-  float acc[4][4];
+  // Two accumulators (even and odd groups of four dims) keep consecutive
+  // MFMAs independent; they are added once at the end.
+  f32x16 acc0 = {}, acc1 = {};
+  auto four = [](f32x16& acc, const float4& q4, const float4& k4) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(q4.x, k4.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(q4.y, k4.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(q4.z, k4.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(q4.w, k4.w, acc, 0, 0, 0);
+  };
+  const float* qrow = s_q + (hb + r32) * kLd + kHalf * h;
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[r][i] = 0.f;
-  for (int d = 0; d < DH; d += 4) {
-    float4 k[4], q[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) k[r] = *reinterpret_cast<const float4*>(s_k + (4 * rg + r) * kLd + d);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = *reinterpret_cast<const float4*>(s_q + (hg + 16 * i) * kLd + d);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = acc[r][i];
-        v = fmaf(k[r].x, q[i].x, v);
-        v = fmaf(k[r].y, q[i].y, v);
-        v = fmaf(k[r].z, q[i].z, v);
-        v = fmaf(k[r].w, q[i].w, v);
-        acc[r][i] = v;
-      }
+  for (int u = 0; u < kV; ++u) {
+    const float4 q4 = *reinterpret_cast<const float4*>(qrow + 4 * u);
+    if (u & 1)
+      four(acc1, q4, kv[u]);
+    else
+      four(acc0, q4, kv[u]);
   }
-  float w[4];
+  // Weighted ReLU sum over the lane's 16 heads, then over the other lane half
+  // (the tile's other 16 heads), then over the two head tiles in LDS, each in
+  // a fixed order.
+  float sc = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = hg + 16 * i < a.H ? a.head_w[hg + 16 * i] : 0.f;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s = fmaf(w[i], fmaxf(acc[r][i], 0.f), s);
-    // The 16 head groups of a row sit in 16 adjacent lanes; butterfly sums in
-    // a fixed order give every lane the same value.
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) s += lane_xor(s, o);
-    if (hg == r && row0 + 4 * rg + r < a.n) a.scores[row0 + 4 * rg + r] = s;
-  }
+  for (int v = 0; v < 16; ++v) sc = fmaf(w[v], fmaxf(acc0[v] + acc1[v], 0.f), sc);
+  sc += lane_xor(sc, 32);
+  if (h == 0) s_part[wave >> 1][rb + r32] = sc;
+  __syncthreads();
+  if (t < kScoreRows && row0 + t < a.n) a.scores[row0 + t] = s_part[0][t] + s_part[1][t];
 }
 
 // One workgroup selects the k largest of up to kIndexerChunk unique 64-bit
