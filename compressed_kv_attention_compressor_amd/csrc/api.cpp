@@ -1045,7 +1045,8 @@ size_t ds4c_indexer_workspace_bytes(int64_t n_rows, int32_t k) {
   if (n_rows < 0 || k < 1 || k > 512) return 0;
   const int64_t chunks = (n_rows + ds4c::kIndexerChunk - 1) / ds4c::kIndexerChunk;
   if (chunks * k > ds4c::kIndexerMaxCand) return 0;
-  return align256(size_t(n_rows) * 4) + align256(size_t(chunks) * size_t(k) * 8) + 256;
+  const size_t hist_words = size_t((n_rows + 63) / 64) * 64;  // 64 words per 64-row score workgroup
+  return align256(size_t(n_rows) * 4) + align256(size_t(chunks) * size_t(k) * 8) + align256(hist_words * 4) + 256;
 }
 
 namespace {
@@ -1082,7 +1083,9 @@ int indexer_args(const float* q, const float* head_w, int32_t n_heads, int32_t h
 
 void indexer_workspace(ds4c::IndexerArgs* a, char* ws) {
   if (!a->scores) a->scores = reinterpret_cast<float*>(ws);
-  a->cand = reinterpret_cast<uint64_t*>(ws + align256(size_t(a->n) * 4));
+  const size_t cand_off = align256(size_t(a->n) * 4);
+  a->cand = reinterpret_cast<uint64_t*>(ws + cand_off);
+  a->hist = reinterpret_cast<uint32_t*>(ws + cand_off + align256(size_t(a->n_chunks) * size_t(a->k) * 8));
 }
 
 }  // namespace

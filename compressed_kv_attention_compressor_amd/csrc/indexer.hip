@@ -30,7 +30,9 @@ namespace ds4c {
 namespace {
 
 constexpr int kScoreRows = 64;
-constexpr int kScoreThreads = 256;
+constexpr int kScoreThreads = 256;  // also one thread per first-digit bin
+constexpr int kHistGroups = 16;     // select threads summing one word of the chunk's counts
+constexpr int kHistPerThread = kIndexerChunk / kScoreRows / kHistGroups;
 constexpr int kSortThreads = 1024;
 constexpr int kSelPerThread = kIndexerChunk / kSortThreads;  // keys per thread in a select pass
 
@@ -61,6 +63,7 @@ __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArg
   constexpr int kV = kHalf / 4; // float4 per lane
   __shared__ __attribute__((aligned(16))) float s_q[64 * kLd];
   __shared__ float s_part[2][kScoreRows];
+  __shared__ uint32_t s_hist[256];
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int h = lane >> 5, r32 = lane & 31;
   const int rb = 32 * (wave & 1), hb = 32 * (wave >> 1);
@@ -114,6 +117,7 @@ __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArg
 #pragma unroll
   for (int v = 0; v < 16; ++v)
     if (hb + 8 * (v / 4) + 4 * h + v % 4 >= a.H) w[v] = 0.f;
+  s_hist[t] = 0u;
   __syncthreads();
 
   // Two accumulators (even and odd groups of four dims) keep consecutive
@@ -143,7 +147,19 @@ __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArg
   sc += lane_xor(sc, 32);
   if (h == 0) s_part[wave >> 1][rb + r32] = sc;
   __syncthreads();
-  if (t < kScoreRows && row0 + t < a.n) a.scores[row0 + t] = s_part[0][t] + s_part[1][t];
+  // The select's first radix digit is the top byte of a key, which is the
+  // top byte of the score's order-preserving bits: the workgroup counts its
+  // rows per byte value here, where the counting is spread over every score
+  // workgroup, and writes the 256 counts (at most 64, one byte each).
+  if (t < kScoreRows && row0 + t < a.n) {
+    const float score = s_part[0][t] + s_part[1][t];
+    a.scores[row0 + t] = score;
+    atomicAdd(&s_hist[ord_bits(score) >> 24], 1u);
+  }
+  __syncthreads();
+  if (t < 64)
+    a.hist[(int64_t)blockIdx.x * 64 + t] =
+        s_hist[4 * t] | (s_hist[4 * t + 1] << 8) | (s_hist[4 * t + 2] << 16) | (s_hist[4 * t + 3] << 24);
 }
 
 // One workgroup selects the k largest of up to kIndexerChunk unique 64-bit
@@ -159,6 +175,7 @@ template <int MODE>
 __global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArgs a, int final_pass) {
   constexpr int mode = MODE;
   __shared__ uint32_t hist[256];
+  __shared__ uint32_t part[MODE == 0 ? kHistGroups : 1][256];
   __shared__ uint64_t sel[512];
   __shared__ unsigned long long s_prefix, s_mask, s_thresh;
   __shared__ int s_need, s_done, s_cnt;
@@ -168,21 +185,66 @@ __global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArg
   const int count = mode == 0 ? (int)(left < kIndexerChunk ? left : kIndexerChunk) : a.n_chunks * a.k;
   // Loads without branches around them (a clamped address past the end,
   // zeroed afterwards), so all of a thread's loads are in flight at once.
+  // Mode 0: the raw score bits (the keys are formed after every load is
+  // issued); mode 1: the keys themselves.
   uint64_t key[kSelPerThread];
+  uint32_t raw[MODE == 0 ? kSelPerThread : 1];
 #pragma unroll
   for (int j = 0; j < kSelPerThread; ++j) {
     const int i = j * kSortThreads + tid;
     const int ic = i < count ? i : count - 1;
-    if constexpr (MODE == 0) {
-      const uint32_t row = (uint32_t)(base + ic);
-      key[j] = ((uint64_t)ord_bits(a.scores[base + ic]) << 32) | (uint64_t)(0xffffffffu - row);
-    } else {
+    if constexpr (MODE == 0)
+      raw[j] = __float_as_uint(a.scores[base + ic]);
+    else
       key[j] = a.cand[ic];
+  }
+  // Mode 0: the first digit's counts come from the chunk's score workgroups.
+  // Thread (word q, group g) adds word q of workgroups g, g + 16, ... in two
+  // registers of 16-bit fields (even and odd bins; at most 32 * 64 per
+  // field).
+  uint32_t hw[kHistPerThread];
+  const int hq = tid % 64, hg = tid / 64;
+  const int n_hw = (count + kScoreRows - 1) / kScoreRows;
+  if constexpr (MODE == 0) {
+    const int64_t w0 = base / kScoreRows;
+#pragma unroll
+    for (int i = 0; i < kHistPerThread; ++i) {
+      const int wi = hg + kHistGroups * i;
+      hw[i] = a.hist[(w0 + (wi < n_hw ? wi : n_hw - 1)) * 64 + hq];
+    }
+  }
+  // Every load above is in flight before the first is used.
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (MODE == 0) {
+#pragma unroll
+    for (int j = 0; j < kSelPerThread; ++j) {
+      const uint32_t row = (uint32_t)(base + j * kSortThreads + tid);
+      key[j] = ((uint64_t)ord_bits(__uint_as_float(raw[j])) << 32) | (uint64_t)(0xffffffffu - row);
     }
   }
 #pragma unroll
   for (int j = 0; j < kSelPerThread; ++j)
     if (j * kSortThreads + tid >= count) key[j] = 0ull;
+  if constexpr (MODE == 0) {
+    uint32_t ev = 0u, od = 0u;
+#pragma unroll
+    for (int i = 0; i < kHistPerThread; ++i) {
+      const uint32_t x = hg + kHistGroups * i < n_hw ? hw[i] : 0u;
+      ev += x & 0x00ff00ffu;
+      od += (x >> 8) & 0x00ff00ffu;
+    }
+    part[hg][4 * hq] = ev & 0xffffu;
+    part[hg][4 * hq + 1] = od & 0xffffu;
+    part[hg][4 * hq + 2] = ev >> 16;
+    part[hg][4 * hq + 3] = od >> 16;
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t c = 0u;
+#pragma unroll
+      for (int g = 0; g < kHistGroups; ++g) c += part[g][tid];
+      hist[tid] = c;
+    }
+  }
   if (tid == 0) {
     s_prefix = 0ull;
     s_mask = 0ull;
@@ -190,15 +252,19 @@ __global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArg
     s_done = 0;
   }
   for (int shift = 56; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0u;
+    // In mode 0 the first digit's counts are already in hist.
+    const bool counted = MODE == 0 && shift == 56;
+    if (!counted && tid < 256) hist[tid] = 0u;
     __syncthreads();
     const uint64_t prefix = s_prefix, mask = s_mask;
     // One LDS atomic per key still in the bucket.  (Counting each distinct
     // digit of a wave once, by ballots, was twice as slow on the first digit,
     // which most scores share: the ballot loop is serial.)
+    if (!counted) {
 #pragma unroll
-    for (int j = 0; j < kSelPerThread; ++j)
-      if (key[j] != 0ull && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 0xffu], 1u);
+      for (int j = 0; j < kSelPerThread; ++j)
+        if (key[j] != 0ull && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 0xffu], 1u);
+    }
     __syncthreads();
     if (tid < kWave) {
       // Lane l holds bins 255-4l .. 252-4l; inclusive counts from the top.
@@ -293,9 +359,10 @@ __global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArg
 
 }  // namespace
 
-// Scratch of the allocation-free indexer entry point: the row scores and the
-// per-chunk candidate keys of the largest call the indexer accepts
-// (1,048,576 rows at k = 512: 4 MiB of scores, 128 KiB of keys).  Each
+// Scratch of the allocation-free indexer entry point: the row scores, the
+// per-chunk candidate keys and the score workgroups' first-digit counts of
+// the largest call the indexer accepts (1,048,576 rows at k = 512: 4 MiB of
+// scores, 128 KiB of keys, 4 MiB of counts).  Each
 // device holds its own copy until the process ends; every call on a device
 // shares it.
 static __device__ __align__(256) unsigned char scratch[kIndexerScratchBytes];

@@ -53,9 +53,10 @@ constexpr int kIndexerChunk = 32768;
 constexpr int kIndexerMaxCand = 16384;
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const Timing& tm);
 // Allocation-free indexer calls use a fixed device array of this many bytes
-// (the workspace of the largest call the indexer accepts); indexer_scratch
-// returns the current device's copy (looked up once per device).
-constexpr size_t kIndexerScratchBytes = 4456448;
+// (the workspace of a call of 1,048,576 rows at k = 512, the largest of any
+// call up to that many rows); indexer_scratch returns the current device's
+// copy (looked up once per device).
+constexpr size_t kIndexerScratchBytes = 8519936;
 hipError_t indexer_scratch(void** ptr);
 // Mixed attention: a partial launch over (item chunks of 32, head groups of
 // 8), then a merge launch per head.

@@ -303,8 +303,8 @@ int ds4c_indexer_topk(const float *q, const float *head_w, int32_t n_heads, int3
 /* ds4c_indexer_topk without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  Same arguments, results and errors as
- * ds4c_indexer_topk; the scratch is a fixed array in the library, 4,456,448
- * bytes per device (every call ds4c_indexer_topk accepts fits), held by each
+ * ds4c_indexer_topk; the scratch is a fixed array in the library, 8,519,936
+ * bytes per device (every call of up to 1,048,576 rows fits), held by each
  * device the library runs on until the process ends.  Calls whose
  * ds4c_indexer_workspace_bytes(n_rows, k) exceeds it return DS4C_ECAP.  The
  * call allocates nothing (no hipMalloc, no events; kernel timing does not

@@ -435,8 +435,9 @@ def test_snapshot_load_refuses_mismatches():
 
 def test_indexer_workspace_bytes():
     a256 = lambda v: (v + 255) // 256 * 256
-    assert B.ds4c_indexer_workspace_bytes(16448, 512) == a256(16448 * 4) + a256(1 * 512 * 8) + 256
-    assert B.ds4c_indexer_workspace_bytes(40000, 512) == a256(40000 * 4) + a256(2 * 512 * 8) + 256
+    # scores, candidate keys, then 256 bytes of first-digit counts per 64-row score workgroup
+    assert B.ds4c_indexer_workspace_bytes(16448, 512) == a256(16448 * 4) + a256(1 * 512 * 8) + 257 * 256 + 256
+    assert B.ds4c_indexer_workspace_bytes(40000, 512) == a256(40000 * 4) + a256(2 * 512 * 8) + 625 * 256 + 256
     assert B.ds4c_indexer_workspace_bytes(0, 512) == 256
     assert B.ds4c_indexer_workspace_bytes(1 << 20, 512) > 0      # 32 chunks of 32768 x 512 = 16384 keys
     assert B.ds4c_indexer_workspace_bytes((1 << 20) + 1, 512) == 0  # 33 chunks: too many keys
@@ -477,7 +478,7 @@ def test_indexer_noalloc_validates_before_launching():
     assert call(rows=0) == B.DS4C_EINVAL
     assert call(n=0, rows=0) == B.DS4C_OK
     # every call the workspace variant accepts at k = 512 fits the scratch ...
-    assert B.ds4c_indexer_workspace_bytes(1 << 20, 512) <= 4456448
-    # ... a longer call at a small k does not: 2,000,000 rows need 8 MB of scores
-    assert B.ds4c_indexer_workspace_bytes(2_000_000, 1) > 4456448
+    assert B.ds4c_indexer_workspace_bytes(1 << 20, 512) <= 8519936
+    # ... a longer call at a small k does not: 2,000,000 rows need 8 MB of scores and 8 MB of counts
+    assert B.ds4c_indexer_workspace_bytes(2_000_000, 1) > 8519936
     assert call(n=2_000_000, k=1) == B.DS4C_ECAP
