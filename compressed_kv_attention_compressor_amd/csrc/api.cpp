@@ -1045,7 +1045,7 @@ size_t ds4c_indexer_workspace_bytes(int64_t n_rows, int32_t k) {
   if (n_rows < 0 || k < 1 || k > 512) return 0;
   const int64_t chunks = (n_rows + ds4c::kIndexerChunk - 1) / ds4c::kIndexerChunk;
   if (chunks * k > ds4c::kIndexerMaxCand) return 0;
-  const size_t hist_words = size_t((n_rows + 63) / 64) * 64;  // 64 words per 64-row score workgroup
+  const size_t hist_words = size_t((n_rows + 63) / 64) * 64;  // 64 words of first-digit counts per 64-row block
   return align256(size_t(n_rows) * 4) + align256(size_t(chunks) * size_t(k) * 8) + align256(hist_words * 4) + 256;
 }
 

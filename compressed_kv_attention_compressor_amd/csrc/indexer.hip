@@ -8,10 +8,12 @@
 // order is descending score, equal scores to the lower row index.
 //
 // Launches:
-//  * indexer_score_kernel: 64 rows per workgroup.  The workgroup rotates and
-//    quantises the query into LDS (each wave a quarter of the heads) while
-//    its rows load; the dot products run on fp32 MFMA tiles of 32 rows x 32
-//    heads, one per wave, and the heads' weighted sum meets in a fixed order.
+//  * indexer_score_kernel: at most one workgroup per CU, each taking 64-row
+//    blocks in turn.  The workgroup rotates and quantises the query into LDS
+//    (each wave a quarter of the heads) while its first rows load; the dot
+//    products run on bf16 MFMA tiles of 32 rows x 32 heads, one per wave, the
+//    rows split into two bf16 parts, and the heads' weighted sum meets in a
+//    fixed order.
 //  * indexer_select_kernel: the k largest (score, lower row first) by a radix
 //    select over 64-bit keys in one workgroup, the survivors then sorted
 //    descending.  Up to kIndexerChunk rows it is one launch; longer calls run
@@ -31,7 +33,8 @@ namespace {
 
 constexpr int kScoreRows = 64;
 constexpr int kScoreThreads = 256;  // also one thread per first-digit bin
-constexpr int kHistGroups = 16;     // select threads summing one word of the chunk's counts
+constexpr int kScoreGrid = 256;     // score workgroups at most: one per CU
+constexpr int kHistGroups = 16;     // select threads summing one word of a chunk's block counts
 constexpr int kHistPerThread = kIndexerChunk / kScoreRows / kHistGroups;
 constexpr int kSortThreads = 1024;
 constexpr int kSelPerThread = kIndexerChunk / kSortThreads;  // keys per thread in a select pass
@@ -46,37 +49,67 @@ __device__ __forceinline__ float unord_bits(uint32_t o) {
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Eight floats as bf16 rounded to nearest even (hi) and their remainders,
+// which are exact in float, rounded to bf16 again (lo): x = hi + lo to
+// within 2^-18 |x|, and exactly when x has at most 8 significant bits (as
+// every value of an FP4 row with its power-of-two scale has).
+__device__ __forceinline__ void split_bf16(const float4& a, const float4& b, bf16x8& hi, bf16x8& lo) {
+  const f32x8 x = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  hi = __builtin_convertvector(x, bf16x8);
+  lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x8), bf16x8);
+}
 
 // The heads' dot products with the rows are a [heads x Dh] x [Dh x rows]
-// product: wave w takes rows 32 (w & 1) .. +31 against heads 32 (w >> 1) ..
-// +31 as one 32 x 32 fp32 MFMA tile (v_mfma_f32_32x32x2_f32; its result
-// holds, in lane l, row l % 32 against heads 8 (v / 4) + 4 (l / 32) + v % 4
-// of the tile, v = 0..15).  The sum runs over the dims in an order of the
-// kernel's choosing, the same on both operands: lane half h = l / 32 takes
-// dims Dh/2 * h .. +Dh/2 - 1, so each lane reads one contiguous half row
-// from memory straight into its operand registers, and its query operands
-// come from LDS four steps per 16-byte read.
+// product: wave w takes rows 32 (w & 1) .. +31 of a 64-row block against
+// heads 32 (w >> 1) .. +31 as one 32 x 32 tile of bf16 MFMAs with float
+// accumulation (v_mfma_f32_32x32x16_bf16; its result holds, in lane l, row
+// l % 32 against heads 8 (v / 4) + 4 (l / 32) + v % 4 of the tile, v =
+// 0..15).  The query after its FP4 round trip is exact in bf16; each row
+// value is split into two bf16 parts (split_bf16), multiplied separately and
+// summed in float, so a score differs from a float dot product only by the
+// split's 2^-18 and the order of the float additions (FP4 rows, which the
+// compressor writes, split exactly).  The sum runs over the dims in an order
+// of the kernel's choosing, the same on both operands: lane half h = l / 32
+// takes dims Dh/2 * h .. +Dh/2 - 1, eight per MFMA, so each lane reads one
+// contiguous half row from memory straight into its operand registers, and
+// its query operands come from LDS eight dims per 16-byte read.  A
+// workgroup rotates the query once and then takes the 64-row blocks
+// blockIdx.x, blockIdx.x + gridDim.x, ... (the grid is at most one
+// workgroup per CU), loading each block's rows while the previous block's
+// MFMAs run.
 template <int DH>
 __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArgs a) {
-  constexpr int kLd = DH + 4;   // padded LDS row: consecutive heads start 4 banks apart
+  constexpr int kLd = DH + 8;   // padded bf16 LDS row: consecutive heads start 4 banks apart
   constexpr int kHalf = DH / 2; // dims per lane half
   constexpr int kV = kHalf / 4; // float4 per lane
-  __shared__ __attribute__((aligned(16))) float s_q[64 * kLd];
+  __shared__ __attribute__((aligned(16))) __bf16 s_q[64 * kLd];
   __shared__ float s_part[2][kScoreRows];
-  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_hist[2][256];  // by block parity
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int h = lane >> 5, r32 = lane & 31;
   const int rb = 32 * (wave & 1), hb = 32 * (wave >> 1);
-  const int64_t row0 = (int64_t)blockIdx.x * kScoreRows;
+  const int64_t n_blocks = (a.n + kScoreRows - 1) / kScoreRows;
+
+  // This lane's half row of the block's row rb + r32 (rows past n re-read
+  // row n-1; their scores are not written).
+  auto load_rows = [&](float4 (&kv)[kV], int64_t blk) {
+    const int64_t r = blk * kScoreRows + rb + r32;
+    const int64_t row = r < a.n ? r : a.n - 1;
+#pragma unroll
+    for (int u = 0; u < kV; ++u) kv[u] = *reinterpret_cast<const float4*>(a.rows + row * DH + kHalf * h + 4 * u);
+  };
 
   // Every load is issued before any is used, with no branch around a load
   // (a branch would make the compiler wait for each load before the next):
   // first the wave's query heads wave + 4m (m = 0..15; heads past H re-read
-  // head H-1 and are zeroed), then this lane's half row (rows past n re-read
-  // row n-1; their scores are not written) and the weights of its 16 heads.
-  // Loads complete in order, so the query's round trip below waits only for
-  // the query.  For the round trip a head spans kLH lanes of 8 dims each, so
-  // three of its butterfly stages stay inside a lane.
+  // head H-1 and are zeroed), then the first block's rows and the weights of
+  // this lane's 16 heads.  Loads complete in order, so the query's round trip
+  // below waits only for the query.  For the round trip a head spans kLH
+  // lanes of 8 dims each, so three of its butterfly stages stay inside a
+  // lane.
   constexpr int kLH = DH / 8;            // lanes per head
   constexpr int kHPass = kWave / kLH;    // heads side by side in the wave
   constexpr int kSlots = 16 / kHPass;    // heads per lane
@@ -87,10 +120,8 @@ __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArg
     const int hq = wave + 4 * (kHPass * j + hgrp);
     load_vec<8>(y[j], a.q + (hq < a.H ? hq : a.H - 1) * DH + dcol);
   }
-  const int64_t row = row0 + rb + r32 < a.n ? row0 + rb + r32 : a.n - 1;
   float4 kv[kV];
-#pragma unroll
-  for (int u = 0; u < kV; ++u) kv[u] = *reinterpret_cast<const float4*>(a.rows + row * DH + kHalf * h + 4 * u);
+  load_rows(kv, blockIdx.x);
   float w[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -111,55 +142,64 @@ __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArg
 #pragma unroll
   for (int j = 0; j < kSlots; ++j) {
     const int hq = wave + 4 * (kHPass * j + hgrp);
-    store_vec<8>(s_q + hq * kLd + dcol, y[j]);
+    const f32x8 yv = {y[j][0], y[j][1], y[j][2], y[j][3], y[j][4], y[j][5], y[j][6], y[j][7]};
+    *reinterpret_cast<bf16x8*>(s_q + hq * kLd + dcol) = __builtin_convertvector(yv, bf16x8);  // exact
     if (a.q_hat && blockIdx.x == 0 && hq < a.H) store_vec<8>(a.q_hat + hq * DH + dcol, y[j]);
   }
 #pragma unroll
   for (int v = 0; v < 16; ++v)
     if (hb + 8 * (v / 4) + 4 * h + v % 4 >= a.H) w[v] = 0.f;
-  s_hist[t] = 0u;
+  s_hist[0][t] = 0u;
   __syncthreads();
 
-  // Two accumulators (even and odd groups of four dims) keep consecutive
-  // MFMAs independent; they are added once at the end.
-  f32x16 acc0 = {}, acc1 = {};
-  auto four = [](f32x16& acc, const float4& q4, const float4& k4) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(q4.x, k4.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(q4.y, k4.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(q4.z, k4.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(q4.w, k4.w, acc, 0, 0, 0);
-  };
-  const float* qrow = s_q + (hb + r32) * kLd + kHalf * h;
+  const __bf16* qrow = s_q + (hb + r32) * kLd + kHalf * h;
+  int par = 0;
+  for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x, par ^= 1) {
+    // The next block's rows load while this block's MFMAs run.
+    const bool has_next = blk + gridDim.x < n_blocks;
+    float4 kv_next[kV];
+    if (has_next) load_rows(kv_next, blk + gridDim.x);
+    // The rows' two bf16 parts accumulate apart (which also keeps
+    // consecutive MFMAs independent) and are added once at the end.
+    f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
-  for (int u = 0; u < kV; ++u) {
-    const float4 q4 = *reinterpret_cast<const float4*>(qrow + 4 * u);
-    if (u & 1)
-      four(acc1, q4, kv[u]);
-    else
-      four(acc0, q4, kv[u]);
-  }
-  // Weighted ReLU sum over the lane's 16 heads, then over the other lane half
-  // (the tile's other 16 heads), then over the two head tiles in LDS, each in
-  // a fixed order.
-  float sc = 0.f;
+    for (int st = 0; st < kV / 2; ++st) {
+      const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(qrow + 8 * st);
+      bf16x8 khi, klo;
+      split_bf16(kv[2 * st], kv[2 * st + 1], khi, klo);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q8, khi, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q8, klo, acc1, 0, 0, 0);
+    }
+    // Weighted ReLU sum over the lane's 16 heads, then over the other lane
+    // half (the tile's other 16 heads), then over the two head tiles in
+    // LDS, each in a fixed order.
+    float sc = 0.f;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) sc = fmaf(w[v], fmaxf(acc0[v] + acc1[v], 0.f), sc);
-  sc += lane_xor(sc, 32);
-  if (h == 0) s_part[wave >> 1][rb + r32] = sc;
-  __syncthreads();
-  // The select's first radix digit is the top byte of a key, which is the
-  // top byte of the score's order-preserving bits: the workgroup counts its
-  // rows per byte value here, where the counting is spread over every score
-  // workgroup, and writes the 256 counts (at most 64, one byte each).
-  if (t < kScoreRows && row0 + t < a.n) {
-    const float score = s_part[0][t] + s_part[1][t];
-    a.scores[row0 + t] = score;
-    atomicAdd(&s_hist[ord_bits(score) >> 24], 1u);
+    for (int v = 0; v < 16; ++v) sc = fmaf(w[v], fmaxf(acc0[v] + acc1[v], 0.f), sc);
+    sc += lane_xor(sc, 32);
+    if (h == 0) s_part[wave >> 1][rb + r32] = sc;
+    __syncthreads();
+    // The select's first radix digit is the top byte of a key, which is the
+    // top byte of the score's order-preserving bits: each block's rows are
+    // counted per byte value here, where the counting is spread over every
+    // score workgroup, and the block's 256 counts (at most 64, one byte
+    // each) are written.  The other parity's counts are cleared for the
+    // next block (their last reads were before the barrier above).
+    s_hist[par ^ 1][t] = 0u;
+    const int64_t row0 = blk * kScoreRows;
+    if (t < kScoreRows && row0 + t < a.n) {
+      const float score = s_part[0][t] + s_part[1][t];
+      a.scores[row0 + t] = score;
+      atomicAdd(&s_hist[par][ord_bits(score) >> 24], 1u);
+    }
+    __syncthreads();
+    if (t < 64)
+      a.hist[blk * 64 + t] = s_hist[par][4 * t] | (s_hist[par][4 * t + 1] << 8) | (s_hist[par][4 * t + 2] << 16) |
+                             (s_hist[par][4 * t + 3] << 24);
+    if (has_next)
+#pragma unroll
+      for (int u = 0; u < kV; ++u) kv[u] = kv_next[u];
   }
-  __syncthreads();
-  if (t < 64)
-    a.hist[(int64_t)blockIdx.x * 64 + t] =
-        s_hist[4 * t] | (s_hist[4 * t + 1] << 8) | (s_hist[4 * t + 2] << 16) | (s_hist[4 * t + 3] << 24);
 }
 
 // One workgroup selects the k largest of up to kIndexerChunk unique 64-bit
@@ -198,10 +238,10 @@ __global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArg
     else
       key[j] = a.cand[ic];
   }
-  // Mode 0: the first digit's counts come from the chunk's score workgroups.
-  // Thread (word q, group g) adds word q of workgroups g, g + 16, ... in two
-  // registers of 16-bit fields (even and odd bins; at most 32 * 64 per
-  // field).
+  // Mode 0: the first digit's counts come from the chunk's 64-row blocks,
+  // counted by the score kernel.  Thread (word q, group g) adds word q of
+  // blocks g, g + 16, ... in two registers of 16-bit fields (even and odd
+  // bins; at most 32 * 64 per field).
   uint32_t hw[kHistPerThread];
   const int hq = tid % 64, hg = tid / 64;
   const int n_hw = (count + kScoreRows - 1) / kScoreRows;
@@ -360,7 +400,7 @@ __global__ void __launch_bounds__(kSortThreads) indexer_select_kernel(IndexerArg
 }  // namespace
 
 // Scratch of the allocation-free indexer entry point: the row scores, the
-// per-chunk candidate keys and the score workgroups' first-digit counts of
+// per-chunk candidate keys and the 64-row blocks' first-digit counts of
 // the largest call the indexer accepts (1,048,576 rows at k = 512: 4 MiB of
 // scores, 128 KiB of keys, 4 MiB of counts).  Each
 // device holds its own copy until the process ends; every call on a device
@@ -396,7 +436,8 @@ hipError_t indexer_scratch(void** ptr) {
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream, const Timing& tm) {
   if (a.n <= 0) return hipSuccess;
-  const unsigned g_score = (unsigned)((a.n + kScoreRows - 1) / kScoreRows);
+  const int64_t n_blocks = (a.n + kScoreRows - 1) / kScoreRows;
+  const unsigned g_score = (unsigned)(n_blocks < kScoreGrid ? n_blocks : kScoreGrid);
   if (a.Dh == 64)
     hipExtLaunchKernelGGL((indexer_score_kernel<64>), dim3(g_score), dim3(kScoreThreads), 0, stream, tm.start,
                           nullptr, 0, a);

@@ -130,7 +130,7 @@ struct IndexerArgs {
   float* out_score;     // [min(n, k)] their scores
   int k;                // 1 .. 512
   uint64_t* cand;       // [n_chunks * k] sort keys surviving each chunk
-  uint32_t* hist;       // [ceil(n / 64), 64] per score workgroup: how many of its rows' keys have each top
+  uint32_t* hist;       // [ceil(n / 64), 64] per 64-row block: how many of its rows' keys have each top
                         // byte, bins 4i .. 4i+3 in the bytes (low first) of word i
   int n_chunks;         // ceil(n / kIndexerChunk)
 };

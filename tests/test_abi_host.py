@@ -435,7 +435,7 @@ def test_snapshot_load_refuses_mismatches():
 
 def test_indexer_workspace_bytes():
     a256 = lambda v: (v + 255) // 256 * 256
-    # scores, candidate keys, then 256 bytes of first-digit counts per 64-row score workgroup
+    # scores, candidate keys, then 256 bytes of first-digit counts per 64-row block
     assert B.ds4c_indexer_workspace_bytes(16448, 512) == a256(16448 * 4) + a256(1 * 512 * 8) + 257 * 256 + 256
     assert B.ds4c_indexer_workspace_bytes(40000, 512) == a256(40000 * 4) + a256(2 * 512 * 8) + 625 * 256 + 256
     assert B.ds4c_indexer_workspace_bytes(0, 512) == 256
