@@ -271,6 +271,44 @@ def copy_calibration(mib: int, reps: int = 20) -> None:
           flush=True)
 
 
+def calls_graph_timing(step, outputs, steps, per_graph=20):
+    """Seconds per call of `step` with the host's enqueue cost taken off the
+    GPU's timeline: `per_graph` calls captured as one HIP graph, replayed
+    between two events.  None when capture is not available or one replay
+    does not reproduce the eager call's `outputs` bit for bit (the outputs
+    are poisoned first)."""
+    import torch
+    try:
+        ref = [t.clone() for t in outputs]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                step()
+        for t in outputs:
+            t.fill_(-1 if not t.is_floating_point() else float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(outputs, ref)):
+            print("graph replay differs from the eager call; wall timing kept", file=sys.stderr)
+            return None
+    except Exception as e:  # capture not supported here: keep the wall timing
+        torch.cuda.synchronize()
+        print(f"graph capture unavailable ({e}); wall timing kept", file=sys.stderr)
+        return None
+    reps = max(1, steps // per_graph)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ok = all(torch.equal(a, b) for a, b in zip(outputs, ref))
+    if not ok:
+        print("timed graph replays differ from the eager call; wall timing kept", file=sys.stderr)
+        return None
+    return ev0.elapsed_time(ev1) * 1e-3 / (reps * per_graph)
+
+
 def bench_indexer(w, args):
     """One query's indexer scoring and top-512 over 16,448 rows (64 heads x 128
     dims): the score launch reads every row once; one select launch follows."""
@@ -287,11 +325,9 @@ def bench_indexer(w, args):
     idx = torch.empty(k, dtype=torch.int32, device="cuda")
     sc = torch.empty(k, dtype=torch.float32, device="cuda")
     ws = torch.empty(B.ds4c_indexer_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream().cuda_stream
-
     def step():
         B.ds4c_indexer_topk(q.data_ptr(), hw.data_ptr(), H, Dh, rows.data_ptr(), n, k, idx.data_ptr(),
-                            sc.data_ptr(), 0, 0, ws.data_ptr(), ws.numel(), stream)
+                            sc.data_ptr(), 0, 0, ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
 
     for _ in range(warmup):
         step()
@@ -306,16 +342,22 @@ def bench_indexer(w, args):
     ms, cnt = B.ds4c_profile_read()
     B.ds4c_profile_enable(False)
     call_ms = ms[B.KCLASS_INDEXER] / max(cnt[B.KCLASS_INDEXER], 1)
+    per_call = calls_graph_timing(step, [idx, sc], steps)
+    t_call = per_call if per_call is not None else el / steps
     # Algorithmic bytes: rows read once, query and head weights, scores written
     # and read back by the sort, the selected rows and scores written.
     alg = n * Dh * 4 + H * Dh * 4 + H * 4 + 2 * n * 4 + k * 8
     gbs = alg / (call_ms * 1e-3) / 1e9
     out = {
-        "metric": METRIC, "value": steps / el, "unit": "queries/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
-        "ms_per_step": el / steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "metric": METRIC, "value": 1.0 / t_call, "unit": "queries/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": t_call * 1e3,
+        "timing": ("replays of a captured HIP graph of 20 calls between two events (one replay checked to write the "
+                   "eager call's results)" if per_call is not None else "wall clock over back-to-back calls"),
+        "wall_ms_per_step": el / steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic (seeded N(0,1) query heads and rows, N(0,1/64) head weights)",
         "config": {"workload": w.name, "rows": n, "heads": H, "head_dim": Dh, "top_k": k},
-        "rows_per_s": steps * n / el,
+        "rows_per_s": n / t_call,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                      "traffic": None, "kernel": "indexer_score_kernel + indexer_select_kernel (one call)",
                      "avg_ms": call_ms, "algorithmic_bytes": alg},
@@ -355,10 +397,9 @@ def bench_mixed_attention(w, args):
     topk = torch.from_numpy(topk_np).cuda()
     out = torch.empty(H, D, dtype=torch.float32, device="cuda")
     ws = torch.empty(B.ds4c_mixed_attention_workspace_bytes(H, D, ring_cap, k), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream().cuda_stream
-
     def step():
-        B.ds4c_mixed_attention(q, ring, first, qpos, ring_cap, comp, topk, qpos, 4, out, ws, stream)
+        B.ds4c_mixed_attention(q, ring, first, qpos, ring_cap, comp, topk, qpos, 4, out, ws,
+                               torch.cuda.current_stream().cuda_stream)
 
     for _ in range(warmup):
         step()
@@ -373,6 +414,8 @@ def bench_mixed_attention(w, args):
     ms, cnt = B.ds4c_profile_read()
     B.ds4c_profile_enable(False)
     call_ms = ms[B.KCLASS_ATTENTION] / max(cnt[B.KCLASS_ATTENTION], 1)
+    per_call = calls_graph_timing(step, [out], steps)
+    t_call = per_call if per_call is not None else el / steps
     # Algorithmic bytes: each attended row read once, the query read, the
     # output written, the list read.
     rows = ring_cap + k
@@ -380,8 +423,12 @@ def bench_mixed_attention(w, args):
     flops = 2 * 2 * H * rows * D           # logits and weighted rows
     gbs = alg / (call_ms * 1e-3) / 1e9
     res = {
-        "metric": METRIC, "value": steps / el, "unit": "queries/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
-        "ms_per_step": el / steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "metric": METRIC, "value": 1.0 / t_call, "unit": "queries/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": t_call * 1e3,
+        "timing": ("replays of a captured HIP graph of 20 calls between two events (one replay checked to write the "
+                   "eager call's results)" if per_call is not None else "wall clock over back-to-back calls"),
+        "wall_ms_per_step": el / steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic (seeded N(0,1) query heads, raw and compressed rows; a random top-512)",
         "config": {"workload": w.name, "compressed_rows": n, "heads": H, "head_dim": D, "raw_rows": ring_cap,
                    "top_k": k, "qpos": qpos},

@@ -33,14 +33,14 @@
  *     writes nothing and leaves the frontier unchanged.
  *   - One frontier must not be used by two calls at once; different
  *     frontiers may be used from different threads.
- *   - prefill, decode_one, frontier_init and the stack prefill/decode calls
- *     enqueue kernel launches only (no memset or copy nodes), so with kernel
- *     timing and cache eviction off (ds4c_profile_enable(0), no
- *     ds4c_profile_evict buffer) they may be recorded under HIP stream
- *     capture.  A captured sequence replays at the positions and buffers
- *     it was recorded with: the host counters advance at capture, not at
- *     replay, so before each replay the caller puts the frontier's device
- *     state back where it stood at capture.
+ *   - prefill, decode_one, frontier_init, the stack prefill/decode calls,
+ *     the indexer and the mixed attention enqueue kernel launches only (no
+ *     memset or copy nodes), so with kernel timing and cache eviction off
+ *     (ds4c_profile_enable(0), no ds4c_profile_evict buffer) they may be
+ *     recorded under HIP stream capture.  A captured sequence replays at the
+ *     positions and buffers it was recorded with: the host counters advance
+ *     at capture, not at replay, so before each replay the caller puts the
+ *     frontier's device state back where it stood at capture.
  *   - Little-endian hosts only (the frontier blob is little-endian).
  *   - No C++ exception crosses this interface.
  */

@@ -1,12 +1,13 @@
 """GPU: the library's calls captured in HIP graphs replay exactly like eager calls.
 
 The decode steps of a two-layer stack (ratio 4 and ratio 128, bf16, crossing
-window boundaries of both ratios) and whole prefill calls of single layers
-(the fused paths) are captured once and replayed several times.  Between the
+window boundaries of both ratios), whole prefill calls of single layers (the
+fused paths), and an indexer call with a mixed-attention call are captured
+once and replayed several times.  Between the
 replays the program does its own eager work: frontier re-initialisation, an
 eager prefill, unrelated torch kernels and synchronisations.  After every
-replay the emitted rows and the frontier tensors must equal the eager run's
-bit for bit.  The library records no memset nodes (its frontier
+replay the emitted rows and the frontier tensors (or the selection and the
+attention output) must equal the eager run's bit for bit.  The library records no memset nodes (its frontier
 initialisation is a fill kernel), so nothing here depends on how a captured
 memset replays.
 """
@@ -116,3 +117,49 @@ def test_prefill_graph_replays_match_eager(shape):
         g.replay()
         torch.cuda.synchronize()
         assert _same(_state([L], T), ref), f"replay {rep}"
+
+
+def test_indexer_and_mixed_attention_graph_replays_match_eager():
+    """An indexer call over two 32768-row chunks (score, per-chunk select and
+    final select launches) and a mixed-attention call, captured together and
+    replayed with unrelated eager work and poisoned outputs in between."""
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    from compressed_kv_attention_compressor_amd import binding as B
+
+    n, H, Dh, k = 40000, 64, 128, 512
+    q_np, w_np, rows_np = synth.indexer_inputs(WID + 2, n, H, Dh)
+    q, hw, rows = (torch.from_numpy(a).cuda() for a in (q_np, w_np, rows_np))
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    sc = torch.empty(k, dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.ds4c_indexer_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+    nc, D, ring_cap = 4096, 512, 128
+    qa_np, ring_np, comp_np, topk_np = synth.mixed_attention_inputs(WID + 3, nc, H, D, ring_cap, k)
+    qa, ring, comp = (torch.from_numpy(a).cuda() for a in (qa_np, ring_np, comp_np))
+    topk = torch.from_numpy(topk_np).cuda()
+    out = torch.empty(H, D, dtype=torch.float32, device="cuda")
+    wsa = torch.empty(B.ds4c_mixed_attention_workspace_bytes(H, D, ring_cap, k), dtype=torch.uint8, device="cuda")
+    qpos = 4 * nc - 1
+
+    def calls():
+        s = torch.cuda.current_stream().cuda_stream
+        B.ds4c_indexer_topk(q.data_ptr(), hw.data_ptr(), H, Dh, rows.data_ptr(), n, k, idx.data_ptr(),
+                            sc.data_ptr(), 0, 0, ws.data_ptr(), ws.numel(), s)
+        B.ds4c_mixed_attention(qa, ring, qpos + 1 - ring_cap, qpos, ring_cap, comp, topk, qpos, 4, out, wsa, s)
+
+    calls()
+    torch.cuda.synchronize()
+    ref = [idx.clone(), sc.clone(), out.clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()  # enqueued into the graph, not run
+    for rep in range(3):
+        print(f"[graph] indexer + mixed attention replay {rep}", flush=True)
+        idx.fill_(-1)
+        sc.fill_(float("nan"))
+        out.fill_(float("nan"))
+        ws.fill_(0xAB)
+        _eager_noise()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same([idx, sc, out], ref), f"replay {rep}"
