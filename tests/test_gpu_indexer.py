@@ -105,6 +105,22 @@ def test_indexer_ties_go_to_the_lower_row():
         assert g_scores[j] == g_scores[1000 + j]
 
 
+def test_indexer_crowded_top_byte():
+    """Rows that are one row scaled by factors within 0.1 %: a score scales
+    with its row (the ReLU commutes with a positive factor), so all 40000
+    scores share one top byte: the first radix digit leaves every key of both
+    chunks (32768 and 7232 rows) in the k-th key's bucket, and the later
+    digits, which the score order rests on, do all the narrowing."""
+    print("[indexer] crowded top byte", flush=True)
+    q, w, rows = synth.indexer_inputs(53, 40000, 64, 128)
+    scale = 1.0 + 1e-3 * np.random.default_rng(53).random(40000, dtype=np.float64)
+    rows = (rows[:1].astype(np.float64) * scale[:, None]).astype(np.float32)
+    check(q, w, rows, 512, "crowded top byte")
+    _, _, _, g_scores = run_gpu(q, w, rows, 512)
+    tops = np.unique(g_scores.view(np.uint32) >> 24)
+    assert len(tops) == 1, tops
+
+
 def test_indexer_over_compressor_rows():
     """The indexer rows a Flash ratio-4 layer writes for a 4096-token chunk (1024 rows)."""
     print("[indexer] over the r4_flash layer's indexer rows", flush=True)
