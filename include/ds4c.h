@@ -282,9 +282,12 @@ int ds4c_compress_stack_decode(const ds4c_layer *layers, int n_layers, ds4c_fron
  *   s_j = sum_h head_w[h] * max(0, <qhat_h, row_j>),
  * qhat_h = the round trip of q[h] (rotation by the orthonormal Hadamard
  * matrix of size head_dim, FP4 E2M1 in blocks of 32 with a power-of-two
- * scale; it stays rotated, like the rows).  The k rows with the largest
- * scores are written to out_idx / out_score (min(n_rows, k) entries) in
- * descending score order, equal scores to the lower row index.
+ * scale; it stays rotated, like the rows).  The dot products run on bf16
+ * matrix cores with float accumulation, each row value split into two bf16
+ * parts: exact products for rows on the FP4 grid (as the compressor writes
+ * them), and otherwise within about 2^-17 of each float product.  The k rows
+ * with the largest scores are written to out_idx / out_score (min(n_rows, k)
+ * entries) in descending score order, equal scores to the lower row index.
  *
  * q [n_heads, head_dim], head_w [n_heads], index_rows [n_rows, head_dim]
  * (row-major float32, device; q and index_rows 16-byte aligned): the layer's
