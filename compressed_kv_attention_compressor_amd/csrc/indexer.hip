@@ -53,9 +53,11 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Eight floats as bf16 rounded to nearest even (hi) and their remainders,
-// which are exact in float, rounded to bf16 again (lo): x = hi + lo to
-// within 2^-18 |x|, and exactly when x has at most 8 significant bits (as
-// every value of an FP4 row with its power-of-two scale has).
+// which are exact in float, rounded to bf16 again (lo).  Rounding to bf16's
+// 8 significant bits errs by at most 2^-8 of the value, so |x - hi| <=
+// 2^-8 |x| and x = hi + lo to within 2^-16 |x|; exactly when x has at most 8
+// significant bits (as every value of an FP4 row with its power-of-two
+// scale has).
 __device__ __forceinline__ void split_bf16(const float4& a, const float4& b, bf16x8& hi, bf16x8& lo) {
   const f32x8 x = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   hi = __builtin_convertvector(x, bf16x8);
@@ -70,7 +72,7 @@ __device__ __forceinline__ void split_bf16(const float4& a, const float4& b, bf1
 // 0..15).  The query after its FP4 round trip is exact in bf16; each row
 // value is split into two bf16 parts (split_bf16), multiplied separately and
 // summed in float, so a score differs from a float dot product only by the
-// split's 2^-18 and the order of the float additions (FP4 rows, which the
+// split's 2^-16 and the order of the float additions (FP4 rows, which the
 // compressor writes, split exactly).  The sum runs over the dims in an order
 // of the kernel's choosing, the same on both operands: lane half h = l / 32
 // takes dims Dh/2 * h .. +Dh/2 - 1, eight per MFMA, so each lane reads one

@@ -285,7 +285,7 @@ int ds4c_compress_stack_decode(const ds4c_layer *layers, int n_layers, ds4c_fron
  * scale; it stays rotated, like the rows).  The dot products run on bf16
  * matrix cores with float accumulation, each row value split into two bf16
  * parts: exact products for rows on the FP4 grid (as the compressor writes
- * them), and otherwise within about 2^-17 of each float product.  The k rows
+ * them), and otherwise within 2^-16 of each float product.  The k rows
  * with the largest scores are written to out_idx / out_score (min(n_rows, k)
  * entries) in descending score order, equal scores to the lower row index.
  *
