@@ -589,7 +589,8 @@ def decode_graph_timing(stack, layers, x, T, Td, chunk, reinit, steps):
         ev_b.record()
     torch.cuda.synchronize()
     ok = same(ref)
-    el = sum(a.elapsed_time(b) for a, _, b in evs) * 1e-3
+    step_ms = sorted(a.elapsed_time(b) for a, _, b in evs)
+    el = sum(step_ms) * 1e-3
     el_pre = sum(a.elapsed_time(m) for a, m, _ in evs) * 1e-3
     reinit()
     torch.cuda.synchronize()
@@ -597,6 +598,7 @@ def decode_graph_timing(stack, layers, x, T, Td, chunk, reinit, steps):
         print("timed decode graph replays differ from the eager steps; eager timing kept", file=sys.stderr)
         return None
     GRAPH_FIGURES.update({"graph_decode_steps": Td, "graph_ms_per_step": el / steps * 1e3,
+                          "ms_per_step_median": step_ms[len(step_ms) // 2], "ms_per_step_min": step_ms[0],
                           "prefill_ms_per_step": el_pre / steps * 1e3,
                           "decode_us_per_token": (el - el_pre) / steps / Td * 1e6})
     return el
@@ -667,6 +669,10 @@ def main():
             flops, pool_bytes, rows = flops + f, pool_bytes + pb, rows + r_
             gemm_launches += 1
         rows += ((T + Td) // s.ratio - T // s.ratio) * (2 if s.ratio == 4 else 1)
+    # Rows a step emits per lane (every step starts from empty frontiers).
+    rows_lanes = {"attention": sum((T + Td) // s.ratio for _, s in shapes if s is not None),
+                  "indexer": sum((T + Td) // 4 for _, s in shapes if s is not None and s.ratio == 4)}
+    assert rows == rows_lanes["attention"] + rows_lanes["indexer"], (rows, rows_lanes)
 
     # One step: every layer's frontier back to its initial state (kv 0,
     # score -inf, counters 0; a fill launch per layer, not timed), then the
@@ -717,7 +723,8 @@ def main():
         ev_b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    el_eager = sum(a.elapsed_time(b) for a, b in evs) * 1e-3
+    eager_steps_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    el_eager = sum(eager_steps_ms) * 1e-3
     ms, cnt = B.ds4c_profile_read()
     B.ds4c_profile_enable(False)
     if args.eager:
@@ -807,6 +814,8 @@ def main():
                    "between steps is outside them"),
         **GRAPH_FIGURES,
         "eager_ms_per_step": el_eager / steps * 1e3,
+        "eager_ms_per_step_median": eager_steps_ms[len(eager_steps_ms) // 2],
+        "eager_ms_per_step_min": eager_steps_ms[0],
         "wall_ms_per_step": wall / steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
@@ -815,6 +824,7 @@ def main():
         "data": "synthetic (seeded N(0,1) hidden states, N(0,0.02) weights, N(0,0.1) APE)",
         "config": cfg,
         "rows_per_s": steps * rows / el,
+        "rows_per_step": rows_lanes,
         "roofline": roofline,
         **({other[0]: other[1]} if other[1] is not None else {}),
         "pool_roofline": {"bound": "hbm", "achieved": pool_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
