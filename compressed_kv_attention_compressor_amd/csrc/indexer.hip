@@ -84,7 +84,7 @@ __device__ __forceinline__ void split_bf16(const float4& a, const float4& b, bf1
 // MFMAs run.
 template <int DH>
 __global__ void __launch_bounds__(kScoreThreads) indexer_score_kernel(IndexerArgs a) {
-  constexpr int kLd = DH + 8;   // padded bf16 LDS row: consecutive heads start 4 banks apart
+  constexpr int kLd = DH + 8;   // padded bf16 LDS row: consecutive heads 16 bytes apart in the banks
   constexpr int kHalf = DH / 2; // dims per lane half
   constexpr int kV = kHalf / 4; // float4 per lane
   __shared__ __attribute__((aligned(16))) __bf16 s_q[64 * kLd];
