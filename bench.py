@@ -50,6 +50,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 GEMM_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", "proj_gemm.hip")
 POOL_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", "pool.hip")
 DECODE_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", "decode.hip")
+INDEXER_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", "indexer.hip")
+ATTENTION_SOURCE = os.path.join(ROOT, "compressed_kv_attention_compressor_amd", "csrc", "attention.hip")
 
 
 def fused_call(shape, n0, T):
@@ -178,8 +180,8 @@ def read_traffic(workload: str, key: str = "gemm_hbm_bytes_per_launch"):
 
     The summary names the digest (source_digest) of the kernel sources it
     was taken on (the projection's for GEMM figures, the pool's for pool
-    figures, the decode source's for decode figures); a different digest
-    means the counters are stale and none is used.
+    figures, the decode, indexer or attention source's for theirs); a
+    different digest means the counters are stale and none is used.
     """
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
@@ -189,8 +191,10 @@ def read_traffic(workload: str, key: str = "gemm_hbm_bytes_per_launch"):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    kind = "decode" if key.startswith("decode") else "pool" if "pool" in key else "gemm"
-    source = {"decode": DECODE_SOURCE, "pool": POOL_SOURCE, "gemm": GEMM_SOURCE}[kind]
+    kind = next((k for k in ("decode", "indexer", "attention") if key.startswith(k)),
+                "pool" if "pool" in key else "gemm")
+    source = {"decode": DECODE_SOURCE, "pool": POOL_SOURCE, "gemm": GEMM_SOURCE, "indexer": INDEXER_SOURCE,
+              "attention": ATTENTION_SOURCE}[kind]
     if kv.get(f"{kind}_sources_sha256") != source_digest(source):
         return None
     try:
@@ -359,7 +363,8 @@ def bench_indexer(w, args):
         "config": {"workload": w.name, "rows": n, "heads": H, "head_dim": Dh, "top_k": k},
         "rows_per_s": n / t_call,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                     "traffic": None, "kernel": "indexer_score_kernel + indexer_select_kernel (one call)",
+                     "traffic": read_traffic("indexer_c5", "indexer_hbm_bytes_per_call"),
+                     "kernel": "indexer_score_kernel + indexer_select_kernel (one call)",
                      "avg_ms": call_ms, "algorithmic_bytes": alg},
     }
     if not args.no_cpu_baseline:
@@ -433,7 +438,8 @@ def bench_mixed_attention(w, args):
         "config": {"workload": w.name, "compressed_rows": n, "heads": H, "head_dim": D, "raw_rows": ring_cap,
                    "top_k": k, "qpos": qpos},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                     "traffic": None, "kernel": "mixed_attn_part_kernel + mixed_attn_merge_kernel (one call)",
+                     "traffic": read_traffic("mixed_attn_c5", "attention_hbm_bytes_per_call"),
+                     "kernel": "mixed_attn_part_kernel + mixed_attn_merge_kernel (one call)",
                      "avg_ms": call_ms, "algorithmic_bytes": alg, "algorithmic_flops": flops},
     }
     if not args.no_cpu_baseline:

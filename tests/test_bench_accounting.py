@@ -85,3 +85,31 @@ def test_counter_summaries_go_stale_with_any_source_they_depend_on(tmp_path, mon
     assert bench.read_traffic("w") == 123.0
     (csrc / "device_common.h").write_text((csrc / "device_common.h").read_text() + "\n// edit\n")
     assert bench.read_traffic("w") is None
+
+
+def test_indexer_and_attention_counters_follow_their_own_sources(tmp_path, monkeypatch):
+    # indexer_* and attention_* figures are keyed to indexer.hip and
+    # attention.hip (plus the shared headers), not to the projection source.
+    import os
+    import shutil
+    csrc = tmp_path / "compressed_kv_attention_compressor_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    for f in ("proj_gemm.hip", "indexer.hip", "attention.hip", "device_common.h", "kernel_args.h", "launch.h"):
+        shutil.copy(os.path.join(bench.ROOT, "compressed_kv_attention_compressor_amd", "csrc", f), csrc / f)
+    shutil.copy(os.path.join(bench.ROOT, "compressed_kv_attention_compressor_amd", "build.py"),
+                tmp_path / "compressed_kv_attention_compressor_amd" / "build.py")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    for name, f in (("GEMM_SOURCE", "proj_gemm.hip"), ("INDEXER_SOURCE", "indexer.hip"),
+                    ("ATTENTION_SOURCE", "attention.hip")):
+        monkeypatch.setattr(bench, name, str(csrc / f))
+    monkeypatch.setattr(bench, "SHARED_SOURCES", [str(csrc / f) for f in ("device_common.h", "kernel_args.h", "launch.h")]
+                        + [str(tmp_path / "compressed_kv_attention_compressor_amd" / "build.py")])
+    for kind, src in (("indexer", "indexer.hip"), ("attention", "attention.hip")):
+        (tmp_path / "profiles" / f"traffic_{kind}.txt").write_text(
+            f"{kind}_hbm_bytes_per_call = 7\n{kind}_sources_sha256 = {bench.source_digest(str(csrc / src))}\n")
+        assert bench.read_traffic(kind, f"{kind}_hbm_bytes_per_call") == 7.0
+        (csrc / "proj_gemm.hip").write_text((csrc / "proj_gemm.hip").read_text() + "\n// edit\n")
+        assert bench.read_traffic(kind, f"{kind}_hbm_bytes_per_call") == 7.0
+        (csrc / src).write_text((csrc / src).read_text() + "\n// edit\n")
+        assert bench.read_traffic(kind, f"{kind}_hbm_bytes_per_call") is None
