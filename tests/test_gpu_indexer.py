@@ -138,8 +138,9 @@ def test_indexer_over_compressor_rows():
 
 
 def test_indexer_is_deterministic():
-    """Survivors are gathered with LDS atomics, then placed by rank: the output
-    is the same on every run."""
+    """Survivors are gathered with LDS atomics in an order that depends on
+    the waves' timing, then sorted (keys are unique): the output is the same
+    on every run."""
     print("[indexer] determinism", flush=True)
     q, w, rows = synth.indexer_inputs(52, 100000, 64, 128)
     a = run_gpu(q, w, rows, 512)
