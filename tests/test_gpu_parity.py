@@ -127,6 +127,10 @@ SMALL = {
     "r128_d128_f32": synth.LayerShape(ratio=128, hidden=192, d_attn=128, d_index=0, dtype="f32"),
     # three 64-wide K tiles: the ratio-128 projection's odd-tile tail
     "r128_d256_h192_bf16": synth.LayerShape(ratio=128, hidden=192, d_attn=256, d_index=0, dtype="bf16"),
+    # a 128-dim RoPE tail: two FP8 blocks on the attention lane, the whole indexer row rotated
+    "r4_d256_rot128": synth.LayerShape(ratio=4, hidden=256, d_attn=256, d_index=128, dtype="bf16", n_rot=128),
+    # RoPE over the whole row: no FP8 dims on the attention lane
+    "r128_d128_rot128_f32": synth.LayerShape(ratio=128, hidden=192, d_attn=128, d_index=0, dtype="f32", n_rot=128),
 }
 
 
